@@ -1,0 +1,161 @@
+"""CPU oracle for the fused fp16 GEMM + elementwise epilogue.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the bench's
+CPU-baseline leg are the only callers.  The product path (the HIP library and
+its binding in dense_gemm_elementwise_amd/) never imports this package, and
+this package imports nothing from it.
+
+This module only marshals numpy arrays into liboracle.so (oracle.c), where
+the arithmetic lives: exact fp16 decode, an fp64 i-k-j triple loop, the
+epilogue in fp64 from the unrounded accumulator, and one round-to-nearest-even
+encode per output.  See oracle.c for the definition and its citations.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+# The boundary's public epilogue enum, written out here on purpose (the
+# oracle shares no header with the HIP library).
+KINDS = {
+    "LINCOMB": 0,
+    "AUX_SCALE": 1,
+    "LINCOMB_X_ACC": 2,
+    "RELU": 3,
+    "SQUARE": 4,
+    "RELU_SQUARE": 5,
+}
+HAS_AUX = {"AUX_SCALE", "LINCOMB_X_ACC", "SQUARE", "RELU_SQUARE"}
+READS_X = {"LINCOMB_X_ACC"}
+
+_lib = None
+
+
+def lib():
+    """Loads liboracle.so, building it first if it is not there yet."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    L = ctypes.CDLL(_build.LIB)
+    i64, u16p, f64p, f32p = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+    L.oracle_f16_decode.restype = ctypes.c_double
+    L.oracle_f16_decode.argtypes = [ctypes.c_uint16]
+    L.oracle_f16_encode.restype = ctypes.c_uint16
+    L.oracle_f16_encode.argtypes = [ctypes.c_double]
+    L.oracle_gemm_epi.restype = ctypes.c_int
+    L.oracle_gemm_epi.argtypes = [i64, i64, i64, i64, u16p, u16p, u16p, u16p, f32p, ctypes.c_int,
+                                  u16p, u16p, f64p, f64p]
+    L.oracle_gemm_epi_points.restype = ctypes.c_int
+    L.oracle_gemm_epi_points.argtypes = [i64, i64, i64, i64, u16p, u16p, u16p, u16p, f32p, ctypes.c_int,
+                                         i64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         u16p, u16p, f64p, f64p]
+    L.oracle_f16_decode_n.restype = None
+    L.oracle_f16_decode_n.argtypes = [u16p, f64p, i64]
+    L.oracle_f16_encode_n.restype = None
+    L.oracle_f16_encode_n.argtypes = [f64p, u16p, i64]
+    L.oracle_rounding_mode_is_nearest.restype = ctypes.c_int
+    L.oracle_kind_has_aux.restype = ctypes.c_int
+    L.oracle_kind_reads_x.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _bits(a):
+    """A float16 (or uint16 bit-pattern) array as a C-contiguous uint16 array."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float16:
+        return a.view(np.uint16)
+    if a.dtype != np.uint16:
+        raise TypeError(f"expected float16 or uint16 bits, got {a.dtype}")
+    return a
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def f16_decode(bits):
+    b = _bits(np.asarray(bits))
+    out = np.empty(b.shape, np.float64)
+    lib().oracle_f16_decode_n(_ptr(b), _ptr(out), b.size)
+    return out
+
+
+def f16_encode(x):
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, np.uint16)
+    lib().oracle_f16_encode_n(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def _shapes(A, B, C):
+    if A.ndim != 3 or B.ndim != 3 or C.ndim != 3:
+        raise ValueError("A, B, C must be (L,M,K), (L,K,N), (L,M,N)")
+    L, M, K = A.shape
+    if B.shape[0] != L or B.shape[1] != K or C.shape != (L, M, B.shape[2]):
+        raise ValueError(f"shape mismatch A{A.shape} B{B.shape} C{C.shape}")
+    return L, M, B.shape[2], K
+
+
+def gemm_epi(A, B, C, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, want64=False):
+    """Full fused GEMM + epilogue on host arrays.
+
+    A (L,M,K), B (L,K,N), C and X (L,M,N): float16 arrays (or uint16 bits).
+    Returns a dict with D (and Aux for kinds with a second output) as float16
+    arrays, plus D64 / Aux64 (unrounded float64) when want64 is set.
+    """
+    A, B, C = _bits(A), _bits(B), _bits(C)
+    X = _bits(X) if X is not None else None
+    L, M, N, K = _shapes(A, B, C)
+    sc = np.array([alpha, beta, s3], np.float32)
+    D = np.empty((L, M, N), np.uint16)
+    Aux = np.empty((L, M, N), np.uint16) if kind in HAS_AUX else None
+    D64 = np.empty((L, M, N), np.float64) if want64 else None
+    Aux64 = np.empty((L, M, N), np.float64) if (want64 and kind in HAS_AUX) else None
+    rc = lib().oracle_gemm_epi(L, M, N, K, _ptr(A), _ptr(B), _ptr(C), _ptr(X), _ptr(sc), KINDS[kind],
+                               _ptr(D), _ptr(Aux), _ptr(D64), _ptr(Aux64))
+    if rc:
+        raise ValueError(f"oracle_gemm_epi rejected the call (code {rc})")
+    out = {"D": D.view(np.float16)}
+    if Aux is not None:
+        out["Aux"] = Aux.view(np.float16)
+    if want64:
+        out["D64"] = D64
+        if Aux64 is not None:
+            out["Aux64"] = Aux64
+    return out
+
+
+def gemm_epi_points(A, B, C, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, l, i, j):
+    """The same definition at sampled output points (l[p], i[p], j[p]).
+
+    Returns a dict of 1-D arrays indexed by p: D, Aux (if the kind has one) as
+    float16, and D64 / Aux64 unrounded.
+    """
+    A, B, C = _bits(A), _bits(B), _bits(C)
+    X = _bits(X) if X is not None else None
+    L, M, N, K = _shapes(A, B, C)
+    l = np.ascontiguousarray(l, np.int64)
+    i = np.ascontiguousarray(i, np.int64)
+    j = np.ascontiguousarray(j, np.int64)
+    n = l.size
+    if i.size != n or j.size != n:
+        raise ValueError("l, i, j must have the same length")
+    sc = np.array([alpha, beta, s3], np.float32)
+    D = np.empty(n, np.uint16)
+    D64 = np.empty(n, np.float64)
+    Aux = np.empty(n, np.uint16) if kind in HAS_AUX else None
+    Aux64 = np.empty(n, np.float64) if kind in HAS_AUX else None
+    rc = lib().oracle_gemm_epi_points(L, M, N, K, _ptr(A), _ptr(B), _ptr(C), _ptr(X), _ptr(sc), KINDS[kind],
+                                      n, _ptr(l), _ptr(i), _ptr(j), _ptr(D), _ptr(Aux), _ptr(D64), _ptr(Aux64))
+    if rc:
+        raise ValueError(f"oracle_gemm_epi_points rejected the call (code {rc})")
+    out = {"D": D.view(np.float16), "D64": D64}
+    if Aux is not None:
+        out["Aux"] = Aux.view(np.float16)
+        out["Aux64"] = Aux64
+    return out

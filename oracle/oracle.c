@@ -1,0 +1,303 @@
+/*
+ * oracle.c -- plain, slow, obviously correct CPU reference for the fused
+ * fp16 GEMM + elementwise epilogue.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * bench's CPU-baseline leg may load this library.  It shares no code, header,
+ * table or constant with the HIP library under dense_gemm_elementwise_amd/;
+ * the epilogue kind numbers below are the public enum values of the boundary,
+ * written out again here on purpose.
+ *
+ * What it computes (all citations are to the three pages the method comes
+ * from):
+ *   - acc[l][i][j] = sum_k A[l][i][k] * B[l][k][j], the batched product that
+ *     the CUTLASS Operator API tutorial "Custom epilogue fusions for GEMMs"
+ *     builds in cell [2] (A is (L,M,K), B is (L,K,N), C is (L,M,N), fp16,
+ *     accumulator type fp32 in cell [4]).
+ *   - the epilogue functions of the accumulator that the pages define:
+ *       LINCOMB       D = alpha*acc + beta*C
+ *                     (CUTLASS Python examples article, "Basic GEMM" NumPy
+ *                     check, and "Epilogue" default identity activation)
+ *       AUX_SCALE     Aux = alpha*acc + beta*C ; D = s*Aux
+ *                     (tutorial cell [2], my_epilogue)
+ *       LINCOMB_X_ACC Y = acc ; D = alpha*acc + beta*C + s*X
+ *                     (Custom Epilogue Example, "Basic Example: Alpha-Beta
+ *                     Scaling", epilogue_operation)
+ *       RELU          D = ReLU(alpha*acc + beta*C)
+ *                     (Custom Epilogue Example, "Activation Functions")
+ *       SQUARE        D = alpha*acc + beta*C ; E = D*D
+ *                     (Custom Epilogue Example, "Multiple Outputs"; the page
+ *                     form is alpha = beta = 1)
+ *       RELU_SQUARE   D = ReLU(alpha*acc + beta*C) ; E = D*D
+ *                     ("Activation Functions" followed by "Multiple Outputs")
+ *     The second output (Aux, Y or E) goes to the Aux buffer.
+ *
+ * Precision (readings where the pages are silent, listed in the design doc):
+ *   - fp16 inputs are decoded exactly to double by decode_f16() below;
+ *   - every sum runs in double, k strictly increasing, starting from +0.0
+ *     (the textbook i-k-j triple loop; the loop order does not change the
+ *     order in which any one element is summed);
+ *   - the epilogue runs in double from the unrounded acc (Aux, D feed the next
+ *     operation unrounded, as the epilogue DAG's SSA values do);
+ *   - every output is rounded once, double -> fp16, round to nearest, ties to
+ *     even, overflow to +-inf (encode_f16() below);
+ *   - ReLU(t) = t > 0 ? t : +0.0 (the "where(d > 0, d, 0)" form).
+ * Build with -ffp-contract=off so that no multiply-add is fused.
+ */
+#include <fenv.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_LINCOMB 0
+#define ORACLE_AUX_SCALE 1
+#define ORACLE_LINCOMB_X_ACC 2
+#define ORACLE_RELU 3
+#define ORACLE_SQUARE 4
+#define ORACLE_RELU_SQUARE 5
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction
+ * bits.  Exponent 0 holds zero and the subnormals f * 2^-24; exponent 31 holds
+ * inf (f == 0) and NaN. */
+double oracle_f16_decode(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 31;
+    int f = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);
+    return sign ? -v : v;
+}
+
+/* double -> binary16, round to nearest, ties to even, in one step (no
+ * intermediate fp32, so no double rounding). */
+uint16_t oracle_f16_encode(double x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    if (isnan(x))
+        return (uint16_t)(sign | 0x7E00);
+    double a = fabs(x);
+    if (a >= 65520.0) /* 65520 is the midpoint between 65504 and 2^16 */
+        return (uint16_t)(sign | 0x7C00);
+    if (a < 0x1p-14) {
+        /* subnormal (or zero): the quantum is 2^-24; a * 2^24 is exact.
+         * A result of 1024 is the smallest normal, 0x0400, as it should be. */
+        double q = nearbyint(a * 0x1p24);
+        return (uint16_t)(sign | (uint16_t)q);
+    }
+    int e2;
+    double m = frexp(a, &e2);          /* a = m * 2^e2, m in [0.5, 1) */
+    double q = nearbyint(ldexp(m, 11)); /* 11 significant bits, in [1024, 2048] */
+    int E = e2 - 1 + 15;               /* biased exponent of a */
+    if (q == 2048.0) {
+        q = 1024.0;
+        E += 1;
+    }
+    if (E >= 31)
+        return (uint16_t)(sign | 0x7C00);
+    return (uint16_t)(sign | (uint16_t)(E << 10) | (uint16_t)((int)q - 1024));
+}
+
+int oracle_kind_valid(int kind) { return kind >= ORACLE_LINCOMB && kind <= ORACLE_RELU_SQUARE; }
+int oracle_kind_has_aux(int kind)
+{
+    return kind == ORACLE_AUX_SCALE || kind == ORACLE_LINCOMB_X_ACC || kind == ORACLE_SQUARE ||
+           kind == ORACLE_RELU_SQUARE;
+}
+int oracle_kind_reads_x(int kind) { return kind == ORACLE_LINCOMB_X_ACC; }
+
+static double relu(double t) { return t > 0.0 ? t : 0.0; }
+
+/* The epilogue of one element, in double, from the unrounded accumulator.
+ * Writes the unrounded first output to *d and the unrounded second output (if
+ * the kind has one) to *aux. */
+static void epilogue(int kind, double acc, double c, double x, double alpha, double beta, double s,
+                     double *d, double *aux)
+{
+    double t;
+    switch (kind) {
+    case ORACLE_LINCOMB:
+        *d = alpha * acc + beta * c;
+        break;
+    case ORACLE_AUX_SCALE:
+        t = alpha * acc + beta * c;
+        *aux = t;
+        *d = s * t;
+        break;
+    case ORACLE_LINCOMB_X_ACC:
+        *aux = acc;
+        *d = (alpha * acc + beta * c) + s * x;
+        break;
+    case ORACLE_RELU:
+        *d = relu(alpha * acc + beta * c);
+        break;
+    case ORACLE_SQUARE:
+        t = alpha * acc + beta * c;
+        *d = t;
+        *aux = t * t;
+        break;
+    case ORACLE_RELU_SQUARE:
+        t = relu(alpha * acc + beta * c);
+        *d = t;
+        *aux = t * t;
+        break;
+    }
+}
+
+/* Checks shared by both entry points.  Returns 0 when the call is valid. */
+static int check_args(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
+                      const uint16_t *C, const uint16_t *X, const float *scalars, int kind, uint16_t *D,
+                      uint16_t *Aux)
+{
+    if (L < 1 || M < 1 || N < 1 || K < 1)
+        return 1;
+    if (!A || !B || !C || !scalars)
+        return 2;
+    if (!oracle_kind_valid(kind))
+        return 4;
+    if (oracle_kind_reads_x(kind) && !X)
+        return 2;
+    if (!D || (oracle_kind_has_aux(kind) && !Aux))
+        return 3;
+    return 0;
+}
+
+/*
+ * Full product.  Host arrays, packed row-major:
+ *   A[l][i][k] at (l*M + i)*K + k, B[l][k][j] at (l*K + k)*N + j,
+ *   C, X, D, Aux [l][i][j] at (l*M + i)*N + j.
+ * scalars = {alpha, beta, s} with s = extra_scalar (AUX_SCALE) or x_factor
+ * (LINCOMB_X_ACC); unused otherwise.  X may be NULL unless the kind reads it;
+ * Aux may be NULL unless the kind writes it.  D64 / Aux64, when not NULL,
+ * receive the unrounded double outputs.  Returns 0, or a nonzero code for
+ * invalid arguments.  OpenMP splits the rows; each element's sum is the same
+ * whatever the thread count.
+ */
+int oracle_gemm_epi(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
+                    const uint16_t *C, const uint16_t *X, const float *scalars, int kind, uint16_t *D,
+                    uint16_t *Aux, double *D64, double *Aux64)
+{
+    int rc = check_args(L, M, N, K, A, B, C, X, scalars, kind, D, Aux);
+    if (rc)
+        return rc;
+    const double alpha = scalars[0], beta = scalars[1], s = scalars[2];
+    double *Bd = (double *)malloc(sizeof(double) * (size_t)K * (size_t)N);
+    if (!Bd)
+        return 7;
+    for (int64_t l = 0; l < L; l++) {
+        const uint16_t *Al = A + l * M * K;
+        const uint16_t *Bl = B + l * K * N;
+        for (int64_t q = 0; q < K * N; q++)
+            Bd[q] = oracle_f16_decode(Bl[q]);
+        int fail = 0;
+#pragma omp parallel
+        {
+            double *acc = (double *)malloc(sizeof(double) * (size_t)N);
+            if (!acc) {
+#pragma omp atomic write
+                fail = 1;
+            }
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t i = 0; i < M; i++) {
+                if (!acc)
+                    continue;
+                for (int64_t j = 0; j < N; j++)
+                    acc[j] = 0.0;
+                for (int64_t k = 0; k < K; k++) {
+                    const double a = oracle_f16_decode(Al[i * K + k]);
+                    const double *brow = Bd + k * N;
+                    for (int64_t j = 0; j < N; j++)
+                        acc[j] = acc[j] + a * brow[j];
+                }
+                const int64_t row = (l * M + i) * N;
+                for (int64_t j = 0; j < N; j++) {
+                    double c = oracle_f16_decode(C[row + j]);
+                    double x = oracle_kind_reads_x(kind) ? oracle_f16_decode(X[row + j]) : 0.0;
+                    double d = 0.0, aux = 0.0;
+                    epilogue(kind, acc[j], c, x, alpha, beta, s, &d, &aux);
+                    D[row + j] = oracle_f16_encode(d);
+                    if (D64)
+                        D64[row + j] = d;
+                    if (oracle_kind_has_aux(kind)) {
+                        Aux[row + j] = oracle_f16_encode(aux);
+                        if (Aux64)
+                            Aux64[row + j] = aux;
+                    }
+                }
+            }
+            free(acc);
+        }
+        if (fail) {
+            free(Bd);
+            return 7;
+        }
+    }
+    free(Bd);
+    return 0;
+}
+
+/*
+ * The same definition for a list of single output elements (l[p], i[p],
+ * j[p]), each summed on its own over k in increasing order, so a full-size
+ * problem can be checked at sampled points.  Outputs are indexed by p:
+ * D[p], Aux[p], D64[p], Aux64[p] (Aux / D64 / Aux64 may be NULL).
+ */
+int oracle_gemm_epi_points(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
+                           const uint16_t *C, const uint16_t *X, const float *scalars, int kind, int64_t npts,
+                           const int64_t *pl, const int64_t *pi, const int64_t *pj, uint16_t *D, uint16_t *Aux,
+                           double *D64, double *Aux64)
+{
+    int rc = check_args(L, M, N, K, A, B, C, X, scalars, kind, D, Aux);
+    if (rc)
+        return rc;
+    if (npts < 0 || (npts > 0 && (!pl || !pi || !pj)))
+        return 1;
+    for (int64_t p = 0; p < npts; p++)
+        if (pl[p] < 0 || pl[p] >= L || pi[p] < 0 || pi[p] >= M || pj[p] < 0 || pj[p] >= N)
+            return 1;
+    const double alpha = scalars[0], beta = scalars[1], s = scalars[2];
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t p = 0; p < npts; p++) {
+        const int64_t l = pl[p], i = pi[p], j = pj[p];
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; k++)
+            acc = acc + oracle_f16_decode(A[(l * M + i) * K + k]) * oracle_f16_decode(B[(l * K + k) * N + j]);
+        const int64_t o = (l * M + i) * N + j;
+        double c = oracle_f16_decode(C[o]);
+        double x = oracle_kind_reads_x(kind) ? oracle_f16_decode(X[o]) : 0.0;
+        double d = 0.0, aux = 0.0;
+        epilogue(kind, acc, c, x, alpha, beta, s, &d, &aux);
+        D[p] = oracle_f16_encode(d);
+        if (D64)
+            D64[p] = d;
+        if (oracle_kind_has_aux(kind)) {
+            if (Aux)
+                Aux[p] = oracle_f16_encode(aux);
+            if (Aux64)
+                Aux64[p] = aux;
+        }
+    }
+    return 0;
+}
+
+/* Bulk codec helpers for the tests: decode n halves / encode n doubles. */
+void oracle_f16_decode_n(const uint16_t *h, double *out, int64_t n)
+{
+    for (int64_t q = 0; q < n; q++)
+        out[q] = oracle_f16_decode(h[q]);
+}
+
+void oracle_f16_encode_n(const double *x, uint16_t *out, int64_t n)
+{
+    for (int64_t q = 0; q < n; q++)
+        out[q] = oracle_f16_encode(x[q]);
+}
+
+/* The rounding mode the encoder relies on (FE_TONEAREST); the tests check it. */
+int oracle_rounding_mode_is_nearest(void) { return fegetround() == FE_TONEAREST; }
