@@ -1,0 +1,186 @@
+"""Throughput of the fused fp16 GEMM + epilogue on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload x_acc_8192]
+                    [--no-cpu-baseline] [--all]
+
+A step is one call of the fused kernel (one gemm_epi_run) on the workload,
+with every input already resident in HBM.  The timed region is K steps on one
+stream, bracketed by torch.cuda.synchronize(); HIP events recorded on that
+same stream give the average launch duration that the roofline uses.
+Prints ONE JSON line (the headline workload); --all also reports the other
+workloads, one JSON line each on stderr.
+
+The CPU baseline is the oracle as it stands (plain fp64 triple loop),
+timed on a bounded slice of the same workload on this host's cores.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP16_TFLOPS = 2516.6  # MI355X dense fp16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ("dense_gemm_elementwise_amd/csrc/gemm_epi_kernels.hpp", "dense_gemm_elementwise_amd/csrc/gemm_epi.hip")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_src_sha256") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes")
+
+
+def bench_gpu(w, steps, warmup):
+    import torch
+    import dense_gemm_elementwise_amd as ge
+    from dense_gemm_elementwise_amd import workloads
+
+    dev = torch.device("cuda:0")
+    p = workloads.make_inputs(w)
+    t = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in p.items()}
+    D = torch.empty((w.L, w.M, w.N), dtype=torch.float16, device=dev)
+    Aux = torch.empty_like(D) if w.kind in ge.HAS_AUX else None
+    stream = torch.cuda.current_stream(dev)
+    args = (w.L, w.M, w.N, w.K, t["A"].data_ptr(), t["B"].data_ptr(), t["C"].data_ptr(),
+            t["X"].data_ptr() if t["X"] is not None else None, (w.alpha, w.beta, w.s3), ge.KINDS[w.kind],
+            D.data_ptr(), Aux.data_ptr() if Aux is not None else None, stream.cuda_stream)
+    for _ in range(warmup):
+        rc = ge.gemm_epi_run(*args)
+        if rc:
+            raise RuntimeError(ge.gemm_epi_status_string(rc))
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        ge.gemm_epi_run(*args)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = e0.elapsed_time(e1) / steps
+    rc, plan = ge.gemm_epi_plan(*args[:8], args[9], args[10], args[11])
+    return {"ms_per_step": wall * 1e3 / steps, "kernel_ms": ev_ms, "plan": plan}
+
+
+def bench_cpu_oracle(w, rows):
+    """The oracle on the first `rows` output rows of batch entry 0 (all N
+    columns, full K): a bounded slice of the same workload."""
+    import numpy as np
+    import oracle
+    from dense_gemm_elementwise_amd import workloads
+
+    p = workloads.make_inputs(w)
+    rows = min(rows, w.M)
+    sl = {k: (np.ascontiguousarray(v[:1, :rows]) if (v is not None and k != "B") else v) for k, v in p.items()}
+    sl["B"] = np.ascontiguousarray(p["B"][:1])
+    t0 = time.perf_counter()
+    oracle.gemm_epi(sl["A"], sl["B"], sl["C"], sl["X"], kind=w.kind, alpha=w.alpha, beta=w.beta, s3=w.s3)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * w.N * w.K
+    return flops / dt / 1e12, dt, rows
+
+
+def omp_threads():
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit():
+        return int(env)
+    return len(os.sched_getaffinity(0))
+
+
+def result_line(w, g, steps, warmup, cpu):
+    tflops = w.flops / (g["ms_per_step"] * 1e-3) / 1e12
+    achieved = w.flops / (g["kernel_ms"] * 1e-3) / 1e12
+    line = {
+        "metric": "fused GEMM+epilogue TFLOP/s at 8192^3 fp16; % of fp16 MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(g["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "L": w.L, "M": w.M, "N": w.N, "K": w.K, "epilogue": w.kind,
+            "alpha": w.alpha, "beta": w.beta, "s3": w.s3, "init": f"{w.init} seed {w.seed}",
+            "accumulate": "f32", "tile": [g["plan"]["bm"], g["plan"]["bn"], g["plan"]["bk"]],
+            "workgroups": g["plan"]["workgroups"], "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_FP16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
+            "traffic": measured_traffic(w.name),
+        },
+        "epilogue_hbm_gbs": round(w.epilogue_bytes / (g["kernel_ms"] * 1e-3) / 1e9, 1),
+        "cpu_baseline": cpu,
+    }
+    return line
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=6144)
+    ap.add_argument("--all", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    from dense_gemm_elementwise_amd import workloads
+    name = a.workload or workloads.HEADLINE
+    w = workloads.WORKLOADS[name]
+
+    if a.all:
+        for other in workloads.WORKLOADS.values():
+            if other.name == name:
+                continue
+            g = bench_gpu(other, a.steps, a.warmup)
+            print(json.dumps(result_line(other, g, a.steps, a.warmup, None)), file=sys.stderr, flush=True)
+
+    g = bench_gpu(w, a.steps, a.warmup)
+    cpu = None
+    if not a.no_cpu_baseline:
+        threads = omp_threads()
+        os.environ["OMP_NUM_THREADS"] = str(threads)
+        v, dt, rows = bench_cpu_oracle(w, a.cpu_rows)
+        cpu = {"value": round(v, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+               "sample": f"first {rows} of {w.M} output rows of {w.name} (all {w.N} columns, K={w.K}), "
+                         f"fp64 i-k-j triple loop + epilogue, {dt:.1f} s"}
+    print(json.dumps(result_line(w, g, a.steps, a.warmup, cpu)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,1 +1,13 @@
-"""Fused fp16 GEMM + elementwise epilogue for AMD MI355X (gfx950)."""
+"""Fused fp16 GEMM + elementwise epilogue for AMD MI355X (gfx950).
+
+    from dense_gemm_elementwise_amd import run
+    run(A, B, C, X, kind="LINCOMB_X_ACC", alpha=2.0, beta=1.0, s3=3.0, D=D, Aux=Y)
+
+The work runs in libgemm_epi.so (hand-written HIP kernels behind a C ABI,
+include/gemm_epi.h); this package only marshals arguments.
+"""
+from .binding import (EXPORTS, HAS_AUX, KINDS, READS_X, GemmEpiError, gemm_epi_last_hip_error, gemm_epi_plan,
+                      gemm_epi_run, gemm_epi_status_string, lib, run)
+
+__all__ = ["run", "gemm_epi_run", "gemm_epi_plan", "gemm_epi_status_string", "gemm_epi_last_hip_error", "lib",
+           "KINDS", "HAS_AUX", "READS_X", "GemmEpiError", "EXPORTS"]

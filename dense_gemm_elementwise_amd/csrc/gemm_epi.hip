@@ -1,0 +1,209 @@
+// gemm_epi.hip -- C ABI of libgemm_epi.so: argument checks, kernel choice and
+// launch of the fused fp16 GEMM + elementwise epilogue on gfx950.
+//
+// The entry points and their contracts are declared in include/gemm_epi.h.
+// Every check runs on the host before any HIP call, so a bad argument never
+// queues work and the checks run without a GPU.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_epi.h"
+#include "gemm_epi_kernels.hpp"
+
+using namespace gemm_epi;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+struct TileCfg {
+    int bm, bn;
+};
+
+// The tile configurations compiled into the library.
+constexpr TileCfg kTiles[] = {{256, 256}, {128, 256}, {256, 128}, {128, 128}, {64, 64}};
+
+// Relative MFMA efficiency of a tile (bigger tiles reuse each LDS operand
+// read over more MFMAs and amortise the epilogue better).
+double tile_efficiency(int bm, int bn)
+{
+    const int area = bm * bn;
+    if (area >= 256 * 256) return 1.0;
+    if (area >= 256 * 128) return 0.9;
+    if (area >= 128 * 128) return 0.75;
+    return 0.4;
+}
+
+constexpr int kNumCUs = 256;
+
+// Chooses the tile that minimises (waves of workgroups) x (tile area / its
+// efficiency): big tiles when the grid fills the chip several times, smaller
+// ones when big tiles would leave compute units idle.  Ties go to the tile
+// that pads the problem least, then to the one whose long side lies along the
+// problem's long side.
+TileCfg choose_tile(int64_t L, int64_t M, int64_t N, bool vec)
+{
+    if (!vec) return {128, 128};
+    TileCfg best = kTiles[0];
+    double best_cost = 1e300, best_pad = 1e300;
+    int best_orient = 2;
+    for (const TileCfg &t : kTiles) {
+        const int64_t tm = (M + t.bm - 1) / t.bm, tn = (N + t.bn - 1) / t.bn;
+        const int64_t tiles = L * tm * tn;
+        const double waves = (double)((tiles + kNumCUs - 1) / kNumCUs);
+        const double cost = waves * (double)t.bm * t.bn / tile_efficiency(t.bm, t.bn);
+        const double pad = (double)tiles * t.bm * t.bn;
+        const int orient = (t.bm == t.bn) ? 0 : ((t.bm > t.bn) == (M > N) ? 0 : 1);
+        const bool better = cost < best_cost - 1e-9 ||
+                            (cost < best_cost + 1e-9 &&
+                             (pad < best_pad - 0.5 || (pad < best_pad + 0.5 && orient < best_orient)));
+        if (better) {
+            best_cost = cost;
+            best_pad = pad;
+            best_orient = orient;
+            best = t;
+        }
+    }
+    return best;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int check_args(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+               const void *X, int kind, const void *D, const void *Aux)
+{
+    if (L < 1 || M < 1 || N < 1 || K < 1) return GEMM_EPI_ERR_SHAPE;
+    const int64_t lim = INT32_MAX;
+    if (M > lim || N > lim || K > lim) return GEMM_EPI_ERR_SHAPE;
+    // element counts of every tensor must fit int64 (and the grid must fit)
+    if (L > INT64_MAX / M || L * M > INT64_MAX / K || L * M > INT64_MAX / N || L > INT64_MAX / K ||
+        L * K > INT64_MAX / N)
+        return GEMM_EPI_ERR_SHAPE;
+    if (!A || !B || !C) return GEMM_EPI_ERR_NULL_INPUT;
+    if (kind < GEMM_EPI_LINCOMB || kind > GEMM_EPI_RELU_SQUARE) return GEMM_EPI_ERR_KIND;
+    if (kind_reads_x(kind) && !X) return GEMM_EPI_ERR_NULL_INPUT;
+    if (!D || (kind_has_aux(kind) && !Aux)) return GEMM_EPI_ERR_NULL_OUTPUT;
+    if (!aligned(A, 2) || !aligned(B, 2) || !aligned(C, 2) || (X && !aligned(X, 2)) || !aligned(D, 2) ||
+        (Aux && !aligned(Aux, 2)))
+        return GEMM_EPI_ERR_ALIGN;
+    return GEMM_EPI_OK;
+}
+
+bool use_fast_path(int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C, const void *X,
+                   int kind, const void *D, const void *Aux)
+{
+    if (K % 8 != 0 || N % 8 != 0) return false;
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(D, 16)) return false;
+    if (kind_reads_x(kind) && !aligned(X, 16)) return false;
+    if (kind_has_aux(kind) && !aligned(Aux, 16)) return false;
+    // 32-bit buffer offsets: one batch entry of A or B must span < 2 GiB
+    const int64_t lim = (int64_t)1 << 31;
+    if (M * K * 2 >= lim - 64 || K * N * 2 >= lim - 64) return false;
+    return true;
+}
+
+template <int BM, int BN, int KIND, bool VEC>
+hipError_t launch_one(const Params &p, hipStream_t stream)
+{
+    hipLaunchKernelGGL((gemm_epi_kernel<BM, BN, KIND, VEC>), dim3(p.num_tiles), dim3(NTHREADS), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int KIND>
+hipError_t launch_kind(const Params &p, int bm, int bn, bool vec, hipStream_t stream)
+{
+    if (!vec) return launch_one<128, 128, KIND, false>(p, stream);
+    if (bm == 256 && bn == 256) return launch_one<256, 256, KIND, true>(p, stream);
+    if (bm == 128 && bn == 256) return launch_one<128, 256, KIND, true>(p, stream);
+    if (bm == 256 && bn == 128) return launch_one<256, 128, KIND, true>(p, stream);
+    if (bm == 128 && bn == 128) return launch_one<128, 128, KIND, true>(p, stream);
+    return launch_one<64, 64, KIND, true>(p, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gemm_epi_status_string(int status)
+{
+    switch (status) {
+    case GEMM_EPI_OK: return "ok";
+    case GEMM_EPI_ERR_SHAPE: return "invalid shape: L, M, N, K must be >= 1 and every tensor size must fit";
+    case GEMM_EPI_ERR_NULL_INPUT: return "an input the epilogue reads (A, B, C, scalars, or X) is not provided";
+    case GEMM_EPI_ERR_NULL_OUTPUT: return "an output the epilogue writes (D, or Aux) is not provided";
+    case GEMM_EPI_ERR_KIND: return "unknown epilogue kind";
+    case GEMM_EPI_ERR_ALIGN: return "a tensor pointer is not 2-byte aligned";
+    case GEMM_EPI_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+    }
+}
+
+int gemm_epi_last_hip_error(void) { return g_last_hip_error; }
+
+int gemm_epi_plan(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                  const void *X, int epilogue_kind, const void *D, const void *Aux, int64_t out[6])
+{
+    int rc = check_args(L, M, N, K, A, B, C, X, epilogue_kind, D, Aux);
+    if (rc != GEMM_EPI_OK) return rc;
+    const bool vec = use_fast_path(M, N, K, A, B, C, X, epilogue_kind, D, Aux);
+    const TileCfg t = choose_tile(L, M, N, vec);
+    const int64_t tiles = L * ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+    if (tiles > INT32_MAX) return GEMM_EPI_ERR_SHAPE;
+    if (out) {
+        out[0] = t.bm;
+        out[1] = t.bn;
+        out[2] = BK;
+        out[3] = vec ? 1 : 0;
+        out[4] = tiles;
+        out[5] = NTHREADS;
+    }
+    return GEMM_EPI_OK;
+}
+
+int gemm_epi_run(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                 const void *X, const float *scalars, int epilogue_kind, void *D, void *Aux, void *stream)
+{
+    int rc = check_args(L, M, N, K, A, B, C, X, epilogue_kind, D, Aux);
+    if (rc != GEMM_EPI_OK) return rc;
+    if (!scalars) return GEMM_EPI_ERR_NULL_INPUT;
+    const bool vec = use_fast_path(M, N, K, A, B, C, X, epilogue_kind, D, Aux);
+    const TileCfg t = choose_tile(L, M, N, vec);
+    const int64_t tm = (M + t.bm - 1) / t.bm, tn = (N + t.bn - 1) / t.bn;
+    const int64_t tiles = L * tm * tn;
+    if (tiles > INT32_MAX) return GEMM_EPI_ERR_SHAPE;
+
+    Params p;
+    p.A = (const _Float16 *)A;
+    p.B = (const _Float16 *)B;
+    p.C = (const _Float16 *)C;
+    p.X = (const _Float16 *)X;
+    p.D = (_Float16 *)D;
+    p.Aux = (_Float16 *)Aux;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.tiles_m = (int)tm;
+    p.tiles_n = (int)tn;
+    p.num_tiles = (int)tiles;
+    p.alpha = scalars[0];
+    p.beta = scalars[1];
+    p.s = scalars[2];
+
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t err;
+    switch (epilogue_kind) {
+    case GEMM_EPI_LINCOMB: err = launch_kind<LINCOMB>(p, t.bm, t.bn, vec, s); break;
+    case GEMM_EPI_AUX_SCALE: err = launch_kind<AUX_SCALE>(p, t.bm, t.bn, vec, s); break;
+    case GEMM_EPI_LINCOMB_X_ACC: err = launch_kind<LINCOMB_X_ACC>(p, t.bm, t.bn, vec, s); break;
+    case GEMM_EPI_RELU: err = launch_kind<RELU>(p, t.bm, t.bn, vec, s); break;
+    case GEMM_EPI_SQUARE: err = launch_kind<SQUARE>(p, t.bm, t.bn, vec, s); break;
+    default: err = launch_kind<RELU_SQUARE>(p, t.bm, t.bn, vec, s); break;
+    }
+    if (err != hipSuccess) {
+        g_last_hip_error = (int)err;
+        return GEMM_EPI_ERR_HIP;
+    }
+    return GEMM_EPI_OK;
+}
+
+}  // extern "C"

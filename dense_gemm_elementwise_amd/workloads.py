@@ -52,6 +52,13 @@ class Workload:
         return 2 * self.L * self.M * self.N * self.K
 
     @property
+    def epilogue_bytes(self) -> int:
+        """Epilogue traffic of one call: C (and X) read once, D (and the second output) written once."""
+        n_in_mn = 1 + (1 if self.kind in READS_X else 0)
+        n_out = 1 + (1 if self.kind in HAS_AUX else 0)
+        return 2 * (n_in_mn + n_out) * self.L * self.M * self.N
+
+    @property
     def hbm_bytes(self) -> int:
         """Compulsory HBM traffic: every operand read once, every output written once."""
         n_in_mn = 1 + (1 if self.kind in READS_X else 0)

@@ -1,0 +1,151 @@
+/*
+ * gemm_epi.h -- C ABI of the fused fp16 GEMM + elementwise epilogue library
+ * (libgemm_epi.so) for AMD Instinct MI355X (gfx950).
+ *
+ * One call computes, in ONE kernel launch,
+ *
+ *     acc[l][m][n] = sum_k A[l][m][k] * B[l][k][n]      (fp16 x fp16 -> fp32)
+ *
+ * and applies an elementwise epilogue to acc before anything is written, so
+ * C (and X) are read once and D (and the second output) written once, with
+ * no intermediate tensor in HBM.  This is the GEMM-with-fused-epilogue
+ * operation of the CUTLASS Operator API tutorial "Custom epilogue fusions for
+ * GEMMs" (cells [2]-[5]: batched A (L,M,K), B (L,K,N), C (L,M,N), fp16
+ * operands, fp32 accumulator, outputs preallocated by the caller) and of the
+ * CUTLASS "Custom Epilogue Example" page (Overview: three kernels fused into
+ * one; Basic Example: batched GEMM with a custom epilogue).
+ *
+ * Layout: every tensor is packed, row-major and batched:
+ *     A[l][m][k] at element (l*M + m)*K + k
+ *     B[l][k][n] at element (l*K + k)*N + n
+ *     C, X, D, Aux [l][m][n] at element (l*M + m)*N + n
+ * (all epilogue tensors share one major order, as the "Constraints" section
+ * of the Custom Epilogue Example requires).  Offsets are 64-bit.
+ *
+ * Arithmetic: fp16 inputs, fp32 accumulation (the tutorial's
+ * accumulator_type=torch.float32; "--acc_dtype Float32" on the example's
+ * command line), epilogue in fp32 ("--epi_dtype Float32") from the unrounded
+ * accumulator, scalars in fp32 (the example's 'float' scalars), each output
+ * converted once to fp16 with round-to-nearest-even (overflow gives inf).
+ * The order of the K summation is not specified.
+ */
+#ifndef GEMM_EPI_H
+#define GEMM_EPI_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * Epilogue kinds.  s = scalars[2] (extra_scalar or x_factor); the second
+ * output (Aux, Y or E) is written to the Aux buffer.
+ *
+ * GEMM_EPI_LINCOMB        D = alpha*acc + beta*C
+ *     (CUTLASS Python examples article: the "Basic GEMM" NumPy check and the
+ *     default identity epilogue of the "Epilogue" example)
+ * GEMM_EPI_AUX_SCALE      Aux = alpha*acc + beta*C ; D = s*Aux
+ *     (tutorial cell [2], my_epilogue: alpha, beta, extra_scalar)
+ * GEMM_EPI_LINCOMB_X_ACC  Y = acc ; D = alpha*acc + beta*C + s*X
+ *     (Custom Epilogue Example, "Basic Example: Alpha-Beta Scaling",
+ *     epilogue_operation: alpha, beta, x_factor)
+ * GEMM_EPI_RELU           D = ReLU(alpha*acc + beta*C), ReLU(t) = t > 0 ? t : 0
+ *     (Custom Epilogue Example, "Activation Functions")
+ * GEMM_EPI_SQUARE         D = alpha*acc + beta*C ; E = D*D
+ *     (Custom Epilogue Example, "Multiple Outputs", with alpha = beta = 1
+ *     giving the page's D = acc + C)
+ * GEMM_EPI_RELU_SQUARE    D = ReLU(alpha*acc + beta*C) ; E = D*D
+ *     ("Activation Functions" followed by "Multiple Outputs")
+ *
+ * The intermediate values (Aux before the scaling, D before the square) are
+ * used unrounded.
+ */
+typedef enum {
+    GEMM_EPI_LINCOMB = 0,
+    GEMM_EPI_AUX_SCALE = 1,
+    GEMM_EPI_LINCOMB_X_ACC = 2,
+    GEMM_EPI_RELU = 3,
+    GEMM_EPI_SQUARE = 4,
+    GEMM_EPI_RELU_SQUARE = 5
+} gemm_epi_kind;
+
+/*
+ * Status codes.  The library never aborts; every error is a return value.
+ * The argument checks run on the host before any HIP call, so they can be
+ * exercised without a GPU.  They mirror the argument errors the tutorial's
+ * "Failure examples" raise (cells [10]-[13]: an output or argument that is
+ * not provided) and the "friendly errors" of the Python examples article
+ * ("Basic GEMM", error handling).
+ */
+typedef enum {
+    GEMM_EPI_OK = 0,
+    GEMM_EPI_ERR_SHAPE = 1,       /* L, M, N or K < 1, or an element count overflows int64 */
+    GEMM_EPI_ERR_NULL_INPUT = 2,  /* A, B, C or scalars NULL; X NULL for LINCOMB_X_ACC */
+    GEMM_EPI_ERR_NULL_OUTPUT = 3, /* D NULL; Aux NULL for a kind with a second output */
+    GEMM_EPI_ERR_KIND = 4,        /* unknown epilogue kind */
+    GEMM_EPI_ERR_ALIGN = 5,       /* a tensor pointer is not 2-byte aligned */
+    GEMM_EPI_ERR_HIP = 6          /* the launch failed; see gemm_epi_last_hip_error() */
+} gemm_epi_status;
+
+/*
+ * gemm_epi_run -- launch the fused GEMM + epilogue on `stream`.
+ *
+ *   L, M, N, K  batch count and problem sizes, each >= 1.
+ *   A, B        device pointers, fp16 (IEEE binary16), layout above.
+ *   C           device pointer, fp16, read by every kind (also when beta = 0).
+ *   X           device pointer, fp16; read only by GEMM_EPI_LINCOMB_X_ACC,
+ *               may be NULL otherwise.
+ *   scalars     HOST pointer to 3 floats {alpha, beta, s}; read during the
+ *               call and passed by value to the kernel, so the caller may
+ *               reuse the memory as soon as the call returns.
+ *   epilogue_kind  a gemm_epi_kind value.
+ *   D           device pointer, fp16 output.
+ *   Aux         device pointer, fp16 second output (Aux, Y or E) for
+ *               AUX_SCALE, LINCOMB_X_ACC, SQUARE and RELU_SQUARE; may be NULL
+ *               for LINCOMB and RELU.
+ *   stream      a hipStream_t (0 = the null stream).
+ *
+ * Ownership: the caller allocates, owns and frees every buffer.  The library
+ * allocates no device memory, frees nothing and does not synchronise: the
+ * launch is asynchronous on `stream`, and the outputs are ready once the
+ * stream reaches that point.  Outputs must not overlap each other or any
+ * input (the result is undefined otherwise).
+ *
+ * Fast path: when K % 8 == 0, N % 8 == 0 and A, B, C, X, D, Aux are 16-byte
+ * aligned (the "Constraints" section's 16-byte rule), and A and B of one batch
+ * entry each span less than 2 GiB, the kernel moves 16-byte vectors;
+ * otherwise a general kernel with element-wise edge handling runs.  Both give
+ * the same values.
+ *
+ * Returns GEMM_EPI_OK, or a gemm_epi_status error code; on an error before
+ * the launch nothing is queued on the stream.
+ */
+int gemm_epi_run(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                 const void *X, const float *scalars, int epilogue_kind, void *D, void *Aux, void *stream);
+
+/* A static, human-readable name for a status code ("unknown status" for
+ * values outside the enum).  Never NULL. */
+const char *gemm_epi_status_string(int status);
+
+/* The hipError_t value behind the calling thread's most recent
+ * GEMM_EPI_ERR_HIP (0 if there was none).  Thread-local. */
+int gemm_epi_last_hip_error(void);
+
+/*
+ * gemm_epi_plan -- host-only query: the kernel configuration gemm_epi_run
+ * would launch for these arguments, without launching anything.
+ *   out[0] tile rows (BM), out[1] tile columns (BN), out[2] K step (BK),
+ *   out[3] 1 for the 16-byte fast path, 0 for the general kernel,
+ *   out[4] number of workgroups, out[5] threads per workgroup.
+ * Returns the same argument-check status gemm_epi_run would return (pointers
+ * are checked for NULL and alignment only, never dereferenced).
+ */
+int gemm_epi_plan(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                  const void *X, int epilogue_kind, const void *D, const void *Aux, int64_t out[6]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_EPI_H */

@@ -1,0 +1,155 @@
+"""The C-ABI boundary without a GPU: the library loads, exports every function
+include/gemm_epi.h declares, and rejects bad arguments with the documented
+status codes before making any HIP call.  The status codes mirror the
+argument errors of the CUTLASS Operator API tutorial "Custom epilogue
+fusions for GEMMs" (cells [10]-[13]: an output or operand that is not
+provided) and the early, readable errors of the CUTLASS Python examples
+article ("Basic GEMM", error handling)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_gemm_elementwise_amd as ge
+from dense_gemm_elementwise_amd import binding, workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm_epi.h")
+
+# fake device addresses: never dereferenced by the checks under test
+P16 = 0x7F0000001000  # 16-byte aligned
+P2 = 0x7F0000001002   # 2-byte aligned only
+P1 = 0x7F0000001001   # misaligned
+SC = (1.0, 2.0, 0.5)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_epi_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == {"gemm_epi_run", "gemm_epi_status_string", "gemm_epi_last_hip_error", "gemm_epi_plan"}
+    raw = ctypes.CDLL(binding.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+    assert set(binding.EXPORTS) == set(names)
+
+
+def test_enum_values_match_header():
+    text = open(HEADER).read()
+    for name, val in ge.KINDS.items():
+        assert re.search(rf"GEMM_EPI_{name}\s*=\s*{val}\b", text), name
+    for val, name in binding.STATUS.items():
+        assert re.search(rf"{name}\s*=\s*{val}\b", text), name
+
+
+def test_status_strings():
+    for code in range(7):
+        s = ge.gemm_epi_status_string(code)
+        assert isinstance(s, str) and s
+    assert ge.gemm_epi_status_string(0) == "ok"
+    assert ge.gemm_epi_status_string(99) == "unknown status"
+    assert ge.gemm_epi_last_hip_error() == 0
+
+
+def run(L=1, M=8, N=8, K=8, A=P16, B=P16, C=P16, X=P16, sc=SC, kind=0, D=P16, Aux=P16):
+    return ge.gemm_epi_run(L, M, N, K, A, B, C, X, sc, kind, D, Aux, None)
+
+
+@pytest.mark.parametrize("shape", [(0, 8, 8, 8), (1, 0, 8, 8), (1, 8, 0, 8), (1, 8, 8, 0), (-1, 8, 8, 8),
+                                   (1, 2 ** 31, 8, 8), (1, 8, 8, 2 ** 31), (2 ** 40, 2 ** 20, 2 ** 20, 8)])
+def test_bad_shapes(shape):
+    L, M, N, K = shape
+    assert run(L=L, M=M, N=N, K=K) == 1
+
+
+def test_missing_inputs():
+    assert run(A=None) == 2
+    assert run(B=None) == 2
+    assert run(C=None) == 2  # every kind reads C, also with beta = 0
+    assert run(sc=None) == 2
+    assert run(kind=2, X=None) == 2  # LINCOMB_X_ACC reads X
+
+
+def test_missing_outputs():
+    assert run(D=None) == 3
+    for kind in ("AUX_SCALE", "LINCOMB_X_ACC", "SQUARE", "RELU_SQUARE"):
+        assert run(kind=ge.KINDS[kind], Aux=None) == 3, kind
+
+
+@pytest.mark.parametrize("kind", [-1, 6, 100])
+def test_unknown_kind(kind):
+    assert run(kind=kind) == 4
+
+
+def test_misaligned_pointers():
+    for arg in ("A", "B", "C", "D"):
+        assert run(**{arg: P1}) == 5, arg
+    assert run(kind=2, X=P1) == 5
+    assert run(kind=1, Aux=P1) == 5
+
+
+def test_plan_fast_and_general_paths():
+    rc, cfg = ge.gemm_epi_plan(1, 256, 256, 256, P16, P16, P16, None, 0, P16, None)
+    assert rc == 0 and cfg["vec"] == 1 and cfg["threads"] == 256 and cfg["bk"] == 64
+    # K or N not a multiple of 8, or a pointer not 16-byte aligned -> general kernel
+    for args in ((1, 256, 256, 250), (1, 256, 250, 256)):
+        rc, cfg = ge.gemm_epi_plan(*args, P16, P16, P16, None, 0, P16, None)
+        assert rc == 0 and cfg["vec"] == 0
+    rc, cfg = ge.gemm_epi_plan(1, 256, 256, 256, P2, P16, P16, None, 0, P16, None)
+    assert rc == 0 and cfg["vec"] == 0
+    # one batch entry of A at 2 GiB or more -> general kernel (32-bit buffer offsets)
+    rc, cfg = ge.gemm_epi_plan(1, 2 ** 15, 8, 2 ** 15, P16, P16, P16, None, 0, P16, None)
+    assert rc == 0 and cfg["vec"] == 0
+    # errors are reported by plan as by run
+    assert ge.gemm_epi_plan(1, 8, 8, 8, None, P16, P16, None, 0, P16, None)[0] == 2
+
+
+def test_plan_tiles_for_the_workloads():
+    want = {
+        "aux_scale_128": (64, 64, 4),
+        "aux_scale_1024": (64, 64, 256),
+        "lincomb_2400x3232x4096": (128, 256, 19 * 13),
+        "x_acc_8192": (256, 256, 1024),
+        "relu_square_16x2048x2048x1024": (256, 256, 1024),
+    }
+    for name, (bm, bn, wgs) in want.items():
+        w = workloads.WORKLOADS[name]
+        rc, cfg = ge.gemm_epi_plan(w.L, w.M, w.N, w.K, P16, P16, P16, P16, ge.KINDS[w.kind], P16, P16)
+        assert rc == 0, name
+        assert (cfg["bm"], cfg["bn"], cfg["workgroups"]) == (bm, bn, wgs), (name, cfg)
+        assert cfg["vec"] == 1
+
+
+def test_python_wrapper_rejects_bad_tensors():
+    import torch
+    A = torch.zeros(1, 8, 8, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        ge.run(A, A, A, kind="LINCOMB", D=A)  # CPU tensors
+    with pytest.raises(TypeError):
+        ge.run(A.float(), A, A, kind="LINCOMB", D=A)
+    with pytest.raises(ValueError):
+        ge.run(A[:, :, :4], A, A, kind="LINCOMB", D=A)
+
+
+def test_workload_draws_follow_the_pages():
+    """Input recipes: P1-style integers in {-2..2}; the Python article's
+    ceil(float16(uniform(-4, 4))) (values in {-4..4}, zeros are -0.0)."""
+    import numpy as np
+    a = workloads.draw("randint_pm2", 2025, 1, 64, 64, 64, False)
+    for x in a:
+        assert set(np.unique(x).tolist()) <= {-2.0, -1.0, 0.0, 1.0, 2.0}
+    c = workloads.draw("ceil_uniform_pm4", 1234, 1, 128, 128, 128, False)
+    for x in c:
+        v = set(np.unique(x).tolist())
+        assert v <= {-4.0, -3.0, -2.0, -1.0, 0.0, 1.0, 2.0, 3.0, 4.0}
+        z = x[x == 0]
+        assert z.size > 0 and np.all(np.signbit(z))
+    # the first draws equal NumPy's RandomState(1234) stream cast then ceiled
+    rs = np.random.RandomState(1234)
+    first = np.ceil(rs.uniform(-4, 4, size=(1, 128, 128)).astype(np.float16))
+    assert np.array_equal(first.view(np.uint16), c[0].view(np.uint16))

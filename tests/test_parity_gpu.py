@@ -1,0 +1,313 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
+
+Bar (per the method's exactness argument: integer-valued fp16 inputs make
+every fp32 partial sum exact, so the only rounding is the final fp16 store):
+  - integer-valued inputs: every output bit-identical to the oracle (+0 and
+    -0 compare equal);
+  - Gaussian inputs: |gpu - ref| <= 5e-2 + 1e-2 * |ref| for every compared
+    element, ref = the oracle's unrounded fp64 value, and no non-finite
+    output.
+Full-size problems that the oracle cannot finish in seconds are compared at
+sampled points (the oracle's per-element entry) plus whole-output properties
+that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import dense_gemm_elementwise_amd as ge
+from dense_gemm_elementwise_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL = 5e-2, 1e-2
+DEV = "cuda:0"
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def to_dev(p, offset=0):
+    """Uploads host arrays; offset > 0 places each tensor `offset` elements into
+    a larger buffer (misaligned pointers, the general kernel)."""
+    out = {}
+    for k, v in p.items():
+        if v is None:
+            out[k] = None
+            continue
+        if offset:
+            buf = torch.empty(v.size + offset, dtype=torch.float16, device=DEV)
+            t = buf[offset:].view(v.shape)
+            t.copy_(torch.from_numpy(v))
+        else:
+            t = torch.from_numpy(v).to(DEV)
+        out[k] = t
+    return out
+
+
+def alloc_out(L, M, N, offset=0):
+    if offset:
+        return torch.full((L * M * N + offset,), float("nan"), dtype=torch.float16, device=DEV)[offset:].view(L, M, N)
+    return torch.full((L, M, N), float("nan"), dtype=torch.float16, device=DEV)
+
+
+def gpu_run(p, kind, alpha, beta, s3, offset=0):
+    t = to_dev(p, offset)
+    L, M, K = p["A"].shape
+    N = p["B"].shape[2]
+    D = alloc_out(L, M, N, offset)
+    Aux = alloc_out(L, M, N, offset) if kind in ge.HAS_AUX else None
+    ge.run(t["A"], t["B"], t["C"], t["X"], kind=kind, alpha=alpha, beta=beta, s3=s3, D=D, Aux=Aux)
+    out = {"D": D.cpu().numpy()}
+    if Aux is not None:
+        out["Aux"] = Aux.cpu().numpy()
+    return out
+
+
+def bits(a):
+    return np.ascontiguousarray(a).view(np.uint16)
+
+
+def assert_bit_exact(got, want, what):
+    g, w = bits(got), bits(want)
+    zero = ((g & 0x7FFF) == 0) & ((w & 0x7FFF) == 0)
+    bad = (g != w) & ~zero
+    n = int(np.count_nonzero(bad))
+    if n:
+        idx = np.argwhere(bad)[:5]
+        detail = [(tuple(i), float(np.asarray(got)[tuple(i)]), float(np.asarray(want)[tuple(i)])) for i in idx]
+        raise AssertionError(f"{what}: {n} of {g.size} outputs differ from the oracle, e.g. {detail}")
+
+
+def assert_close(got, ref64, what):
+    g = np.asarray(got, np.float64)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    err = np.abs(g - ref64)
+    lim = ATOL + RTOL * np.abs(ref64)
+    bad = err > lim
+    n = int(np.count_nonzero(bad))
+    if n:
+        i = np.unravel_index(np.argmax(err - lim), err.shape)
+        raise AssertionError(f"{what}: {n} of {g.size} outside tolerance; worst at {i}: gpu {g[i]} ref {ref64[i]}")
+
+
+def check_full(p, kind, alpha, beta, s3, exact, offset=0, what=""):
+    got = gpu_run(p, kind, alpha, beta, s3, offset)
+    ref = oracle.gemm_epi(p["A"], p["B"], p["C"], p["X"], kind=kind, alpha=alpha, beta=beta, s3=s3,
+                          want64=not exact)
+    for name in ("D", "Aux"):
+        if name not in ref:
+            continue
+        if exact:
+            assert_bit_exact(got[name], ref[name], f"{what} {name}")
+        else:
+            assert_close(got[name], ref[name + "64"], f"{what} {name}")
+    return got
+
+
+# ---------------------------------------------------------------------------
+# The five workloads at their real sizes
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["aux_scale_128", "aux_scale_1024", "lincomb_2400x3232x4096"])
+def test_integer_workloads_bit_exact(name):
+    w = workloads.WORKLOADS[name]
+    log(f"[parity] {name}: L={w.L} M={w.M} N={w.N} K={w.K} {w.kind}")
+    p = workloads.make_inputs(w)
+    check_full(p, w.kind, w.alpha, w.beta, w.s3, exact=True, what=name)
+
+
+def sample_points(L, M, N, n, seed, tile=256):
+    """Random points plus every element of a few rows and columns at tile
+    edges (first/last row and column of tiles, the matrix edges)."""
+    rng = np.random.default_rng(seed)
+    l = [rng.integers(0, L, n)]
+    i = [rng.integers(0, M, n)]
+    j = [rng.integers(0, N, n)]
+    rows = sorted({0, 1, tile - 1, tile, M // 2, M - 2, M - 1} & set(range(M)))
+    cols = sorted({0, 31, 32, tile - 1, tile, N // 2, N - 1} & set(range(N)))
+    for r in rows:
+        cj = rng.choice(N, size=min(N, 512), replace=False)
+        l.append(rng.integers(0, L, cj.size))
+        i.append(np.full(cj.size, r))
+        j.append(cj)
+    for c in cols:
+        ri = rng.choice(M, size=min(M, 512), replace=False)
+        l.append(rng.integers(0, L, ri.size))
+        i.append(ri)
+        j.append(np.full(ri.size, c))
+    return np.concatenate(l), np.concatenate(i), np.concatenate(j)
+
+
+def test_x_acc_8192_sampled_and_properties():
+    w = workloads.WORKLOADS["x_acc_8192"]
+    log(f"[parity] {w.name}: L={w.L} M={w.M} N={w.N} K={w.K} {w.kind}")
+    p = workloads.make_inputs(w)
+    t = to_dev(p)
+    D = alloc_out(w.L, w.M, w.N)
+    Y = alloc_out(w.L, w.M, w.N)
+    ge.run(t["A"], t["B"], t["C"], t["X"], kind=w.kind, alpha=w.alpha, beta=w.beta, s3=w.s3, D=D, Aux=Y)
+    # whole-output properties: finite everywhere, and D agrees with the
+    # epilogue applied to the stored Y = acc (Y is acc rounded once, so
+    # |D - (alpha Y + beta C + x X)| <= alpha ulp(Y) + ulp(D)/2 + fp32 slack)
+    assert bool(torch.isfinite(D).all()) and bool(torch.isfinite(Y).all())
+    D64, Y64 = D.double(), Y.double()
+    C64, X64 = t["C"].double(), t["X"].double()
+    recon = w.alpha * Y64 + w.beta * C64 + w.s3 * X64
+    lim = 2.0 ** -10 * w.alpha * Y64.abs() + 2.0 ** -10 * D64.abs() + 1e-4
+    assert bool(((D64 - recon).abs() <= lim).all()), "D inconsistent with Y, C, X somewhere"
+    del D64, Y64, C64, X64, recon, lim
+    # sampled points against the oracle
+    l, i, j = sample_points(w.L, w.M, w.N, 20000, seed=1)
+    ref = oracle.gemm_epi_points(p["A"], p["B"], p["C"], p["X"], kind=w.kind, alpha=w.alpha, beta=w.beta,
+                                 s3=w.s3, l=l, i=i, j=j)
+    d = D.cpu().numpy()[l, i, j]
+    y = Y.cpu().numpy()[l, i, j]
+    assert_close(d, ref["D64"], "x_acc_8192 D")
+    assert_close(y, ref["Aux64"], "x_acc_8192 Y")
+
+
+def test_relu_square_batched_sampled_and_properties():
+    w = workloads.WORKLOADS["relu_square_16x2048x2048x1024"]
+    log(f"[parity] {w.name}: L={w.L} M={w.M} N={w.N} K={w.K} {w.kind}")
+    p = workloads.make_inputs(w)
+    t = to_dev(p)
+    D = alloc_out(w.L, w.M, w.N)
+    E = alloc_out(w.L, w.M, w.N)
+    ge.run(t["A"], t["B"], t["C"], kind=w.kind, alpha=w.alpha, beta=w.beta, s3=w.s3, D=D, Aux=E)
+    assert bool(torch.isfinite(D).all()) and bool(torch.isfinite(E).all())
+    assert bool((D >= 0).all()), "ReLU output negative"
+    D64, E64 = D.double(), E.double()
+    assert bool(((E64 - D64 * D64).abs() <= 2.0 ** -8 * D64 * D64 + 1e-6).all()), "E != D*D somewhere"
+    del D64, E64
+    # two whole batch entries (first and last) against the full oracle
+    Dh, Eh = D.cpu().numpy(), E.cpu().numpy()
+    for l in (0, w.L - 1):
+        sub = {k: (v[l:l + 1] if v is not None else None) for k, v in p.items()}
+        ref = oracle.gemm_epi(sub["A"], sub["B"], sub["C"], None, kind=w.kind, alpha=w.alpha, beta=w.beta,
+                              want64=True)
+        assert_close(Dh[l:l + 1], ref["D64"], f"batch {l} D")
+        assert_close(Eh[l:l + 1], ref["Aux64"], f"batch {l} E")
+    # sampled points over every batch entry
+    l, i, j = sample_points(w.L, w.M, w.N, 20000, seed=2)
+    ref = oracle.gemm_epi_points(p["A"], p["B"], p["C"], None, kind=w.kind, alpha=w.alpha, beta=w.beta,
+                                 l=l, i=i, j=j)
+    assert_close(Dh[l, i, j], ref["D64"], "relu_square D")
+    assert_close(Eh[l, i, j], ref["Aux64"], "relu_square E")
+
+
+# ---------------------------------------------------------------------------
+# Every kind, both kernels, ragged shapes
+# ---------------------------------------------------------------------------
+KIND_SCALARS = {"LINCOMB": (1.0, 2.0, 0.0), "AUX_SCALE": (1.0, 2.0, 0.5), "LINCOMB_X_ACC": (2.0, 1.0, 3.0),
+                "RELU": (1.0, -1.0, 0.0), "SQUARE": (1.0, 1.0, 0.0), "RELU_SQUARE": (0.5, 1.0, 0.0)}
+
+
+@pytest.mark.parametrize("kind", workloads.KINDS)
+@pytest.mark.parametrize("shape,offset", [((2, 200, 136, 264), 0),    # fast path, ragged M
+                                          ((2, 200, 136, 264), 1),    # misaligned -> general kernel
+                                          ((3, 77, 45, 61), 0),       # K, N not multiples of 8 -> general
+                                          ((1, 300, 520, 136), 0)])   # fast path, several tiles
+def test_every_kind_integer_inputs_bit_exact(kind, shape, offset):
+    L, M, N, K = shape
+    a, b, s = KIND_SCALARS[kind]
+    log(f"[parity] kind={kind} shape={shape} offset={offset}")
+    p = workloads.make_problem(L, M, N, K, kind, init="small_int", seed=M * N + K)
+    check_full(p, kind, a, b, s, exact=True, offset=offset, what=f"{kind} {shape} off{offset}")
+
+
+@pytest.mark.parametrize("kind", workloads.KINDS)
+def test_every_kind_gaussian_inputs(kind):
+    L, M, N, K = 3, 520, 392, 768
+    a, b, s = KIND_SCALARS[kind]
+    log(f"[parity] gaussian kind={kind}")
+    p = workloads.make_problem(L, M, N, K, kind, init="normal", seed=17)
+    check_full(p, kind, a, b, s, exact=False, what=f"gaussian {kind}")
+
+
+TAIL_SHAPES = [
+    (1, 1, 1, 1), (1, 1, 8, 8), (1, 8, 1, 8), (1, 7, 9, 5), (1, 15, 17, 63), (1, 63, 64, 65),
+    (1, 64, 64, 64), (1, 65, 63, 127), (1, 127, 129, 129), (1, 129, 128, 255), (1, 255, 256, 257),
+    (1, 257, 264, 1000), (2, 1000, 1000, 72), (1, 8, 1000, 1000), (1, 1000, 8, 16), (2, 33, 2056, 40),
+    (1, 513, 1032, 8), (4, 64, 64, 1), (1, 256, 512, 1024), (1, 512, 256, 1024), (1, 520, 776, 88),
+]
+
+
+# shapes whose tile choice is 128 x 128 and 256 x 128 (the others are reached above)
+TILE_SHAPES = [(1, 768, 2816, 72), (1, 2304, 2048, 40), (1, 2400, 1032, 24)]
+
+
+@pytest.mark.parametrize("shape", TAIL_SHAPES + TILE_SHAPES)
+def test_tails_bit_exact(shape):
+    L, M, N, K = shape
+    kind = "AUX_SCALE"
+    log(f"[parity] tails shape={shape}")
+    p = workloads.make_problem(L, M, N, K, kind, init="small_int", seed=L + M + N + K)
+    check_full(p, kind, 1.0, 2.0, 0.5, exact=True, what=f"tails {shape}")
+
+
+def test_every_tile_configuration_is_exercised():
+    """The shapes above reach all compiled tile configurations of the fast path."""
+    seen = set()
+    P = 0x7F0000001000
+    shapes = TAIL_SHAPES + TILE_SHAPES + [(2, 200, 136, 264), (1, 300, 520, 136)] + [
+        (w.L, w.M, w.N, w.K) for w in workloads.WORKLOADS.values()]
+    for (L, M, N, K) in shapes:
+        rc, cfg = ge.gemm_epi_plan(L, M, N, K, P, P, P, P, 1, P, P)
+        assert rc == 0
+        if cfg["vec"]:
+            seen.add((cfg["bm"], cfg["bn"]))
+    assert seen == {(256, 256), (128, 256), (256, 128), (128, 128), (64, 64)}, seen
+
+
+def test_identity_and_zero_closed_forms_on_gpu():
+    """A = I gives D = B exactly; A = 0 gives D = RNE(beta C) (LINCOMB)."""
+    L, M, N = 2, 192, 264
+    p = workloads.make_problem(L, M, N, M, "LINCOMB", init="normal", seed=3)
+    p["A"] = np.broadcast_to(np.eye(M, dtype=np.float16), (L, M, M)).copy()
+    got = gpu_run(p, "LINCOMB", 1.0, 0.0, 0.0)
+    assert np.array_equal(bits(got["D"]), bits(p["B"]))
+    p["A"] = np.zeros_like(p["A"])
+    got = gpu_run(p, "LINCOMB", 1.0, -0.5, 0.0)
+    want = (-0.5 * p["C"].astype(np.float64)).astype(np.float16)
+    assert_bit_exact(got["D"], want, "A = 0")
+
+
+def test_runs_on_a_side_stream():
+    L, M, N, K = 1, 384, 256, 512
+    p = workloads.make_problem(L, M, N, K, "LINCOMB", init="small_int", seed=9)
+    t = to_dev(p)
+    D = alloc_out(L, M, N)
+    s = torch.cuda.Stream(device=DEV)
+    torch.cuda.synchronize()
+    ge.run(t["A"], t["B"], t["C"], kind="LINCOMB", alpha=1.0, beta=2.0, D=D, stream=s, sync=True)
+    ref = oracle.gemm_epi(p["A"], p["B"], p["C"], kind="LINCOMB", alpha=1.0, beta=2.0)
+    assert_bit_exact(D.cpu().numpy(), ref["D"], "side stream")
+
+
+def test_large_operand_uses_general_kernel_with_64bit_offsets():
+    """One batch entry of A spans more than 2 GiB: the general kernel runs and
+    64-bit offsets reach the far end of A."""
+    L, M, N, K = 1, 16392, 24, 65536
+    P = 0x7F0000001000
+    rc, cfg = ge.gemm_epi_plan(L, M, N, K, P, P, P, None, 0, P, None)
+    assert rc == 0 and cfg["vec"] == 0
+    log(f"[parity] large operand L={L} M={M} N={N} K={K}")
+    g = torch.Generator(device="cpu").manual_seed(5)
+    A = torch.randint(-2, 3, (L, M, K), generator=g, dtype=torch.float16)
+    B = torch.randint(-2, 3, (L, K, N), generator=g, dtype=torch.float16)
+    C = torch.randint(-2, 3, (L, M, N), generator=g, dtype=torch.float16)
+    tA, tB, tC = A.to(DEV), B.to(DEV), C.to(DEV)
+    D = alloc_out(L, M, N)
+    ge.run(tA, tB, tC, kind="LINCOMB", alpha=1.0, beta=1.0, D=D)
+    rows = np.array([0, 1, 8191, 8192, 16383, 16384, M - 1])
+    l, i, j = [], [], []
+    for r in rows:
+        l.append(np.zeros(N, np.int64))
+        i.append(np.full(N, r))
+        j.append(np.arange(N))
+    l, i, j = np.concatenate(l), np.concatenate(i), np.concatenate(j)
+    ref = oracle.gemm_epi_points(A.numpy(), B.numpy(), C.numpy(), kind="LINCOMB", alpha=1.0, beta=1.0,
+                                 l=l, i=i, j=j)
+    assert_bit_exact(D.cpu().numpy()[l, i, j], ref["D"], "large operand rows")
