@@ -144,6 +144,19 @@ def result_line(w, g, steps, warmup, cpu):
     return line
 
 
+def copy_calibration(mib, steps):
+    """A plain copy of known size: reading and writing mib MiB per launch.
+    Profiling it gives the scale of the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = mib * (1 << 20) // 2
+    src = torch.randn(n, device="cuda:0").to(torch.float16)
+    dst = torch.empty_like(src)
+    for _ in range(max(steps, 1)):
+        torch.neg(src, out=dst)  # one elementwise kernel: reads n halves, writes n halves
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_mib": mib, "bytes_read": n * 2, "bytes_written": n * 2, "launches": steps}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,11 +166,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=6144)
     ap.add_argument("--all", action="store_true")
+    ap.add_argument("--copy-kernel", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (calibrates HBM byte counters)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
               file=sys.stderr)
         sys.exit(2)
+
+    if a.copy_kernel:
+        copy_calibration(a.copy_kernel, a.steps)
+        return
 
     from dense_gemm_elementwise_amd import workloads
     name = a.workload or workloads.HEADLINE
