@@ -17,11 +17,16 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 struct TileCfg {
-    int bm, bn;
+    int bm, bn;      // output tile
+    int bk, stages;  // K step per LDS stage, LDS stages in the ring
+    int wgm, wgn;    // wave grid (threads = 64 * wgm * wgn)
 };
 
-// The tile configurations compiled into the library.
-constexpr TileCfg kTiles[] = {{256, 256}, {128, 256}, {256, 128}, {128, 128}, {64, 64}};
+// The tile configurations compiled into the library (fast path), and the one
+// general-path configuration.
+constexpr TileCfg kTiles[] = {{256, 256, 64, 2, 4, 2}, {128, 256, 64, 3, 2, 2}, {256, 128, 64, 3, 2, 2},
+                              {128, 128, 64, 3, 2, 2}, {64, 64, 64, 3, 2, 2}};
+constexpr TileCfg kGeneral = {128, 128, 64, 2, 2, 2};
 
 // Relative MFMA efficiency of a tile (bigger tiles reuse each LDS operand
 // read over more MFMAs and amortise the epilogue better).
@@ -43,7 +48,7 @@ constexpr int kNumCUs = 256;
 // problem's long side.
 TileCfg choose_tile(int64_t L, int64_t M, int64_t N, bool vec)
 {
-    if (!vec) return {128, 128};
+    if (!vec) return kGeneral;
     TileCfg best = kTiles[0];
     double best_cost = 1e300, best_pad = 1e300;
     int best_orient = 2;
@@ -102,23 +107,28 @@ bool use_fast_path(int64_t M, int64_t N, int64_t K, const void *A, const void *B
     return true;
 }
 
-template <int BM, int BN, int KIND, bool VEC>
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, int KIND, bool VEC>
 hipError_t launch_one(const Params &p, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemm_epi_kernel<BM, BN, KIND, VEC>), dim3(p.num_tiles), dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL((gemm_epi_kernel<BM, BN, BK, NS, WGM, WGN, KIND, VEC>), dim3(p.num_tiles),
+                       dim3(64 * WGM * WGN), 0, stream, p);
     return hipGetLastError();
 }
 
+#define GE_LAUNCH(T, KIND, VEC) launch_one<T.bm, T.bn, T.bk, T.stages, T.wgm, T.wgn, KIND, VEC>(p, stream)
+
 template <int KIND>
-hipError_t launch_kind(const Params &p, int bm, int bn, bool vec, hipStream_t stream)
+hipError_t launch_kind(const Params &p, const TileCfg &t, bool vec, hipStream_t stream)
 {
-    if (!vec) return launch_one<128, 128, KIND, false>(p, stream);
-    if (bm == 256 && bn == 256) return launch_one<256, 256, KIND, true>(p, stream);
-    if (bm == 128 && bn == 256) return launch_one<128, 256, KIND, true>(p, stream);
-    if (bm == 256 && bn == 128) return launch_one<256, 128, KIND, true>(p, stream);
-    if (bm == 128 && bn == 128) return launch_one<128, 128, KIND, true>(p, stream);
-    return launch_one<64, 64, KIND, true>(p, stream);
+    if (!vec) return GE_LAUNCH(kGeneral, KIND, false);
+    if (t.bm == kTiles[0].bm && t.bn == kTiles[0].bn) return GE_LAUNCH(kTiles[0], KIND, true);
+    if (t.bm == kTiles[1].bm && t.bn == kTiles[1].bn) return GE_LAUNCH(kTiles[1], KIND, true);
+    if (t.bm == kTiles[2].bm && t.bn == kTiles[2].bn) return GE_LAUNCH(kTiles[2], KIND, true);
+    if (t.bm == kTiles[3].bm && t.bn == kTiles[3].bn) return GE_LAUNCH(kTiles[3], KIND, true);
+    return GE_LAUNCH(kTiles[4], KIND, true);
 }
+
+#undef GE_LAUNCH
 
 }  // namespace
 
@@ -152,10 +162,10 @@ int gemm_epi_plan(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, con
     if (out) {
         out[0] = t.bm;
         out[1] = t.bn;
-        out[2] = BK;
+        out[2] = t.bk;
         out[3] = vec ? 1 : 0;
         out[4] = tiles;
-        out[5] = NTHREADS;
+        out[5] = 64 * t.wgm * t.wgn;
     }
     return GEMM_EPI_OK;
 }
@@ -192,12 +202,12 @@ int gemm_epi_run(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, cons
     hipStream_t s = (hipStream_t)stream;
     hipError_t err;
     switch (epilogue_kind) {
-    case GEMM_EPI_LINCOMB: err = launch_kind<LINCOMB>(p, t.bm, t.bn, vec, s); break;
-    case GEMM_EPI_AUX_SCALE: err = launch_kind<AUX_SCALE>(p, t.bm, t.bn, vec, s); break;
-    case GEMM_EPI_LINCOMB_X_ACC: err = launch_kind<LINCOMB_X_ACC>(p, t.bm, t.bn, vec, s); break;
-    case GEMM_EPI_RELU: err = launch_kind<RELU>(p, t.bm, t.bn, vec, s); break;
-    case GEMM_EPI_SQUARE: err = launch_kind<SQUARE>(p, t.bm, t.bn, vec, s); break;
-    default: err = launch_kind<RELU_SQUARE>(p, t.bm, t.bn, vec, s); break;
+    case GEMM_EPI_LINCOMB: err = launch_kind<LINCOMB>(p, t, vec, s); break;
+    case GEMM_EPI_AUX_SCALE: err = launch_kind<AUX_SCALE>(p, t, vec, s); break;
+    case GEMM_EPI_LINCOMB_X_ACC: err = launch_kind<LINCOMB_X_ACC>(p, t, vec, s); break;
+    case GEMM_EPI_RELU: err = launch_kind<RELU>(p, t, vec, s); break;
+    case GEMM_EPI_SQUARE: err = launch_kind<SQUARE>(p, t, vec, s); break;
+    default: err = launch_kind<RELU_SQUARE>(p, t, vec, s); break;
     }
     if (err != hipSuccess) {
         g_last_hip_error = (int)err;

@@ -10,21 +10,27 @@
 // activation in one kernel instead of three).
 //
 // Design for gfx950 (not a translation of the pages' Blackwell kernels):
-//  * 256 threads = 4 wave64s in a 2 x 2 grid; each wave owns a
-//    (BM/2) x (BN/2) accumulator tile built from v_mfma_f32_32x32x16_f16.
-//  * K is walked in steps of BK = 64 through two LDS stages.  The fast path
-//    fills LDS with buffer_load_dwordx4 ... lds (global -> LDS without
-//    VGPRs); lanes whose 16-byte chunk lies outside the matrix get an
+//  * WGM x WGN wave64s per workgroup; each wave owns a (BM/WGM) x (BN/WGN)
+//    accumulator tile built from v_mfma_f32_32x32x16_f16.  With two waves per
+//    SIMD (8 waves), one wave's MFMAs run while the other waits on LDS or a
+//    barrier.
+//  * K is walked in steps of BK through a ring of NSTAGES LDS stages, so the
+//    loads of a stage are issued NSTAGES-1 stages before it is used.  The
+//    fast path fills LDS with buffer_load_dwordx4 ... lds (global -> LDS
+//    without VGPRs); lanes whose 16-byte chunk lies outside the matrix get an
 //    out-of-range offset, which the buffer unit turns into zeros, so M, N and
 //    K tails need no extra code in the inner loop.
-//  * A tiles are stored row-major (128 B per row); B tiles k-row-major.  The
-//    16-byte chunks of each row are XOR-swizzled so that the MFMA operand
+//  * A tiles are stored row-major (BK*2 bytes per row); B tiles k-row-major.
+//    The 16-byte chunks of each row are XOR-swizzled so that the MFMA operand
 //    reads (ds_read_b128 for A, ds_read_b64_tr_b16 for B, which transposes
 //    the N-contiguous B rows into the K-contiguous operand on the fly) hit
 //    distinct banks.
-//  * The epilogue moves each wave's accumulator through LDS so that every
-//    lane owns 4 consecutive columns; C / X are then read and D / Aux written
-//    with 8-byte vectors, one pass, predicated at the M / N edges.
+//  * The epilogue moves each wave's accumulator through LDS, one 32-row block
+//    at a time, so that every lane owns 4 consecutive columns; C / X are
+//    prefetched into registers one block ahead and D / Aux written with
+//    8-byte vectors, predicated at the M / N edges.  (Reading C / X straight
+//    in the MFMA register layout would touch 32 rows per instruction; the
+//    row-contiguous layout keeps each instruction on 4 rows.)
 //  * Workgroup ids are remapped so that the tiles one XCD runs together are
 //    neighbours (they share A row panels and B column panels in that XCD's
 //    L2).
@@ -33,6 +39,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace gemm_epi {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -40,6 +48,7 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 #define GE_LDS(T) __attribute__((address_space(3))) T
 
@@ -64,9 +73,7 @@ struct Params {
     float alpha, beta, s;
 };
 
-constexpr int BK = 64;          // K step per LDS stage
-constexpr int NTHREADS = 256;   // 4 waves
-constexpr int GROUP_M = 4;      // tile rows per L2 group
+constexpr int GROUP_M = 8;  // tile rows per L2 group
 
 // ---------------------------------------------------------------------------
 // Epilogue math, fp32.  d = first output, a = second output (if any).
@@ -125,13 +132,20 @@ __device__ __forceinline__ void map_tile(const Params &p, int &l, int &tm, int &
     tn = rr / gm;
 }
 
-// Swizzles (in 16-byte chunk units).  A rows hold 8 chunks; row r stores
-// logical chunk c at physical chunk c ^ swz_a(r).  B k-rows hold BN/8 chunks;
-// k-row kr stores logical chunk c at c ^ swz_b(kr).  Both keep every MFMA
-// operand read conflict-free whether the LDS serves 128 or 256 bytes a clock:
-// an A read has 16 consecutive rows at one logical chunk, a B transpose read
-// has 4 consecutive k-rows x 4 consecutive chunks.
-__device__ __forceinline__ int swz_a(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// Swizzles (in 16-byte chunk units).  An A row holds A_CHUNKS = BK/8 chunks;
+// row r stores logical chunk c at physical chunk c ^ swz_a(r).  A B k-row
+// holds BN/8 chunks; k-row kr stores logical chunk c at c ^ swz_b(kr).  They
+// keep every MFMA operand read conflict-free whether the LDS serves 128 or
+// 256 bytes a clock: an A read has 16 consecutive rows at one logical chunk,
+// a B transpose read has 4 consecutive k-rows x 4 consecutive chunks.
+template <int A_CHUNKS>
+__device__ __forceinline__ int swz_a(int row)
+{
+    if constexpr (A_CHUNKS == 8)
+        return (row & 7) ^ ((row >> 3) & 1);         // 128-byte rows
+    else
+        return ((row >> 1) & 3) ^ ((row >> 3) & 1);  // 64-byte rows
+}
 template <int B_CHUNKS>
 __device__ __forceinline__ int swz_b(int krow)
 {
@@ -146,11 +160,9 @@ __device__ __forceinline__ int swz_b(int krow)
 // bytes to LDS address M0 + 16*i.  Written as inline asm so that the compiler
 // does not treat every later LDS read as dependent on it (it would otherwise
 // wait for all outstanding DMA before each read, which serialises the
-// prefetch with the MFMA work); the kernel waits for the DMA itself
-// (s_waitcnt vmcnt(0) before the barrier that publishes a stage).
+// prefetch with the MFMA work); the kernel waits for the DMA itself before
+// the barrier that publishes a stage.
 // ---------------------------------------------------------------------------
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
 __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t num_bytes)
 {
     const uint64_t a = (uint64_t)base;
@@ -179,7 +191,36 @@ __device__ __forceinline__ void dma16(const i32x4 &rsrc, uint32_t lds_addr, int 
 }
 #pragma clang diagnostic pop
 
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Waits until at most N of this wave's vector-memory operations are
+// outstanding (they complete in issue order).  N is a compile-time constant.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    static_assert(N <= 16 || N == 18 || N == 20 || N == 24 || N == 28 || N == 30 || N == 32 || N == 36 ||
+                      N == 40 || N == 42 || N == 48 || N == 54 || N == 56 || N == 60,
+                  "add this vmcnt value to wait_vmcnt");
+#define GE_VMCNT_CASE(n) \
+    if constexpr (N == n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory");
+    GE_VMCNT_CASE(0) GE_VMCNT_CASE(1) GE_VMCNT_CASE(2) GE_VMCNT_CASE(3) GE_VMCNT_CASE(4) GE_VMCNT_CASE(5)
+    GE_VMCNT_CASE(6) GE_VMCNT_CASE(7) GE_VMCNT_CASE(8) GE_VMCNT_CASE(9) GE_VMCNT_CASE(10) GE_VMCNT_CASE(11)
+    GE_VMCNT_CASE(12) GE_VMCNT_CASE(13) GE_VMCNT_CASE(14) GE_VMCNT_CASE(15) GE_VMCNT_CASE(16)
+    GE_VMCNT_CASE(18) GE_VMCNT_CASE(20) GE_VMCNT_CASE(24) GE_VMCNT_CASE(28) GE_VMCNT_CASE(30)
+    GE_VMCNT_CASE(32) GE_VMCNT_CASE(36) GE_VMCNT_CASE(40) GE_VMCNT_CASE(42) GE_VMCNT_CASE(48)
+    GE_VMCNT_CASE(54) GE_VMCNT_CASE(56) GE_VMCNT_CASE(60)
+#undef GE_VMCNT_CASE
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations, not for
+// its outstanding global loads and stores (__syncthreads() would wait for
+// those too).
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Orders this wave's LDS accesses before and after it (the compiler may not
+// move memory operations across it; the wave's earlier LDS operations have
+// completed).  Enough when a wave only reads LDS that it wrote itself.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 
 __device__ __forceinline__ uint32_t lds_addr_of(const void *p)
 {
@@ -191,26 +232,33 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void *p)
 // vectors); otherwise every global access is element-wise and guarded and
 // LDS is filled through registers.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int KIND, bool VEC>
-__global__ __launch_bounds__(NTHREADS) void gemm_epi_kernel(Params p)
+template <int BM, int BN, int BK, int NSTAGES, int WGM, int WGN, int KIND, bool VEC>
+__global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
 {
-    constexpr int WM = BM / 2, WN = BN / 2;    // wave tile
+    constexpr int NW = WGM * WGN;              // waves per workgroup
+    constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile
     constexpr int TM = WM / 32, TN = WN / 32;  // 32x32 MFMA blocks per wave
     static_assert(TM >= 1 && TN >= 1, "tile too small");
-    constexpr int A_STAGE = BM * BK * 2;  // bytes
-    constexpr int B_STAGE = BK * BN * 2;
+    static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
+    static_assert(NSTAGES >= 2, "at least two stages");
+    constexpr int A_ROW = BK * 2;     // bytes per A row in LDS
+    constexpr int A_CHUNKS = BK / 8;  // 16-byte chunks per A row
+    constexpr int A_STAGE = BM * A_ROW;
+    constexpr int B_ROW = BN * 2;     // bytes per B k-row in LDS
+    constexpr int B_CHUNKS = BN / 8;
+    constexpr int B_STAGE = BK * B_ROW;
     constexpr int STAGE = A_STAGE + B_STAGE;
-    constexpr int B_ROW = BN * 2;  // bytes per B k-row in LDS
-    constexpr int MAIN_BYTES = 2 * STAGE;
-    constexpr int EPI_LD = WN + 8;  // fp32 row pitch of an epilogue slab
-    constexpr int EPI_BYTES = 4 * 32 * EPI_LD * 4;
+    constexpr int MAIN_BYTES = NSTAGES * STAGE;
+    constexpr int EPI_LD = WN + 8;  // fp32 row pitch of an epilogue slab (padded against bank conflicts)
+    constexpr int EPI_BYTES = NW * 32 * EPI_LD * 4;
     constexpr int SMEM = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
+    static_assert(SMEM <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WGN, wn = wave % WGN;
 
     int l, tm, tn;
     map_tile(p, l, tm, tn);
@@ -231,12 +279,14 @@ __global__ __launch_bounds__(NTHREADS) void gemm_epi_kernel(Params p)
     const int nk = (K + BK - 1) / BK;
 
     // ---- global -> LDS --------------------------------------------------
-    // A: BM rows x 8 chunks; one wave instruction fills 1 KB = 8 rows.
-    // B: BK k-rows x BN/8 chunks; one wave instruction fills 1 KB.
+    // One wave instruction fills 1 KB: 1024 / A_ROW rows of A, or
+    // 1024 / B_ROW k-rows of B.  DMA_PER_STAGE = this thread's DMA
+    // instructions per stage.
     constexpr int A_BLKS = A_STAGE / 1024;
     constexpr int B_BLKS = B_STAGE / 1024;
-    constexpr int B_CHUNKS = BN / 8;
-    static_assert(A_BLKS % 4 == 0 && B_BLKS % 4 == 0, "stage must split evenly over 4 waves");
+    constexpr int A_ROWS_PER_BLK = 1024 / A_ROW;
+    constexpr int DMA_PER_STAGE = (A_BLKS + B_BLKS) / NW;
+    static_assert(A_BLKS % NW == 0 && B_BLKS % NW == 0, "stage must split evenly over the waves");
     static_assert(B_ROW <= 1024 && 1024 % B_ROW == 0, "B row must divide 1 KB");
 
     i32x4 rsrc_a = {}, rsrc_b = {};
@@ -252,17 +302,17 @@ __global__ __launch_bounds__(NTHREADS) void gemm_epi_kernel(Params p)
         const int b_off = a_off + A_STAGE;
         if constexpr (VEC) {
 #pragma unroll
-            for (int q = 0; q < A_BLKS / 4; q++) {
-                const int blk = q * 4 + wave;
-                const int row = blk * 8 + (lane >> 3);
-                const int c = (lane & 7) ^ swz_a(row);
+            for (int q = 0; q < A_BLKS / NW; q++) {
+                const int blk = q * NW + wave;
+                const int row = blk * A_ROWS_PER_BLK + lane / A_CHUNKS;
+                const int c = (lane % A_CHUNKS) ^ swz_a<A_CHUNKS>(row);
                 const int gm = m0 + row, gk = k0 + c * 8;
                 const int off = (gm < M && gk < K) ? (gm * K + gk) * 2 : 0x7FFFFFF0;
                 dma16(rsrc_a, smem_lds + a_off + blk * 1024, off);
             }
 #pragma unroll
-            for (int q = 0; q < B_BLKS / 4; q++) {
-                const int blk = q * 4 + wave;
+            for (int q = 0; q < B_BLKS / NW; q++) {
+                const int blk = q * NW + wave;
                 const int lin = blk * 64 + lane;  // chunk index within the stage
                 const int krow = lin / B_CHUNKS;
                 const int c = (lin % B_CHUNKS) ^ swz_b<B_CHUNKS>(krow);
@@ -273,11 +323,11 @@ __global__ __launch_bounds__(NTHREADS) void gemm_epi_kernel(Params p)
         } else {
             // element-wise guarded loads through registers, same LDS layout
 #pragma unroll 1
-            for (int q = 0; q < A_BLKS / 4; q++) {
-                const int blk = q * 4 + wave;
-                const int row = blk * 8 + (lane >> 3);
-                const int pchunk = lane & 7;
-                const int c = pchunk ^ swz_a(row);
+            for (int q = 0; q < A_BLKS / NW; q++) {
+                const int blk = q * NW + wave;
+                const int row = blk * A_ROWS_PER_BLK + lane / A_CHUNKS;
+                const int pchunk = lane % A_CHUNKS;
+                const int c = pchunk ^ swz_a<A_CHUNKS>(row);
                 const int gm = m0 + row;
                 half8 v;
 #pragma unroll
@@ -285,11 +335,11 @@ __global__ __launch_bounds__(NTHREADS) void gemm_epi_kernel(Params p)
                     const int gk = k0 + c * 8 + e;
                     v[e] = (gm < M && gk < K) ? Al[(int64_t)gm * K + gk] : (_Float16)0.0f;
                 }
-                *(half8 *)(smem + a_off + row * 128 + pchunk * 16) = v;
+                *(half8 *)(smem + a_off + row * A_ROW + pchunk * 16) = v;
             }
 #pragma unroll 1
-            for (int q = 0; q < B_BLKS / 4; q++) {
-                const int blk = q * 4 + wave;
+            for (int q = 0; q < B_BLKS / NW; q++) {
+                const int blk = q * NW + wave;
                 const int lin = blk * 64 + lane;
                 const int krow = lin / B_CHUNKS;
                 const int pchunk = lin % B_CHUNKS;
@@ -320,8 +370,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm_epi_kernel(Params p)
 #pragma unroll
         for (int i = 0; i < TM; i++) {
             const int row = wm * WM + i * 32 + li;
-            const int c = (kk * 2 + lg) ^ swz_a(row);
-            af[i] = *(const half8 *)(a_src + row * 128 + c * 16);
+            const int c = (kk * 2 + lg) ^ swz_a<A_CHUNKS>(row);
+            af[i] = *(const half8 *)(a_src + row * A_ROW + c * 16);
         }
 #pragma unroll
         for (int j = 0; j < TN; j++) {
@@ -351,45 +401,98 @@ __global__ __launch_bounds__(NTHREADS) void gemm_epi_kernel(Params p)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
     };
 
+    // Waits until this thread's DMA for the stage about to be published has
+    // landed, when `newer` later stages (a compile-time count) may still be in
+    // flight behind it; near the end of K fewer were issued, and it waits for
+    // all.
+    auto wait_stage = [&](auto newer, bool steady) {
+        if constexpr (VEC) {
+            if (steady)
+                wait_vmcnt<decltype(newer)::value * DMA_PER_STAGE>();
+            else
+                wait_vmcnt<0>();
+        }
+    };
+    using newer_prologue = std::integral_constant<int, NSTAGES - 1>;
+    using newer_steady = std::integral_constant<int, NSTAGES - 2>;
+
     // ---- main loop ---------------------------------------------------------
-    // Two LDS stages.  Operand fragments are double-buffered in registers and
-    // read one 16-wide k step ahead of the MFMAs that use them; the barrier
-    // that publishes stage kt+1 sits between the last fragment reads of stage
-    // kt and its last MFMAs, so the MFMA pipe keeps working across it.
-    // Stage kt+2 is fetched into the buffer stage kt used, right after that
-    // barrier (by then every wave has finished reading stage kt).
+    // A ring of NSTAGES LDS slots; stage j lives in slot j % NSTAGES.  Stages
+    // 0..NSTAGES-1 are fetched up front; the barrier that publishes stage j
+    // (everyone's DMA for it landed) also frees the slot of stage j-1, into
+    // which stage j-1+NSTAGES is fetched right away.  Operand fragments are double-buffered in registers one
+    // 16-wide k step ahead of the MFMAs; the barrier sits between the last
+    // fragment reads of a stage and its last MFMAs, so the MFMA pipe keeps
+    // working across it.
     constexpr int KSTEPS = BK / 16;
     half8 fa[2][TM], fb[2][TN];
-    load_stage(0, 0);
-    if constexpr (VEC) wait_dma();
-    __syncthreads();
-    if (nk > 1) load_stage(1, BK);
+#pragma unroll
+    for (int st = 0; st < NSTAGES; st++)
+        if (st < nk) load_stage(st, st * BK);
+    wait_stage(newer_prologue{}, nk >= NSTAGES);
+    if constexpr (!VEC) __syncthreads();
+    barrier_lds();
     read_frags(0, 0, fa[0], fb[0]);
+    int cur = 0;  // ring slot of stage kt
 #pragma unroll 1
     for (int kt = 0; kt < nk; kt++) {
-        const int cur = kt & 1;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; kk++) {
             if (kk + 1 < KSTEPS) {
                 read_frags(cur, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
             } else if (kt + 1 < nk) {
-                if constexpr (VEC) wait_dma();  // this thread's part of stage kt+1 landed
-                __syncthreads();                // all of stage kt+1 landed; stage kt is free
-                if (kt + 2 < nk) load_stage(cur, (kt + 2) * BK);
-                read_frags(cur ^ 1, 0, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+                wait_stage(newer_steady{}, kt + NSTAGES <= nk);  // stage kt+1 landed (this thread's part)
+                if constexpr (!VEC) __syncthreads();
+                barrier_lds();  // everyone's part landed; stage kt's slot is free
+                if (kt + NSTAGES < nk) load_stage(cur, (kt + NSTAGES) * BK);
+                const int nxt = cur + 1 == NSTAGES ? 0 : cur + 1;
+                read_frags(nxt, 0, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
             }
             mfmas(fa[kk & 1], fb[kk & 1]);
         }
+        cur = cur + 1 == NSTAGES ? 0 : cur + 1;
     }
-    __syncthreads();  // LDS is reused by the epilogue
 
     // ---- epilogue ----------------------------------------------------------
+    // The wave tile is handled one 32-row block ("slab") at a time.  In a
+    // slab, pass p (0..7) covers rows 4p..4p+3; lane owns row 4p + lane/16
+    // and the 4-column groups 4*(lane%16) (+ WN/2).  C / X of a slab are
+    // loaded into registers one slab ahead, so the loads' latency hides
+    // behind the previous slab's work.
+    constexpr int EPI_PASSES = 8;
+    constexpr int EPI_GROUPS = WN >= 128 ? 2 : 1;
+    constexpr int EPI_HALF = WN / 2;
+    constexpr bool HAS_X = kind_reads_x(KIND);
     const float alpha = p.alpha, beta = p.beta, s = p.s;
-    float *slab = (float *)(smem + wave * (32 * EPI_LD * 4));
     const int64_t mn_base = (int64_t)l * M * N;
+    half4 cbuf[2][EPI_PASSES][EPI_GROUPS];
+    half4 xbuf[2][HAS_X ? EPI_PASSES : 1][EPI_GROUPS];
+    auto epi_prefetch = [&](int i, half4 (&cb)[EPI_PASSES][EPI_GROUPS],
+                            half4 (&xb)[HAS_X ? EPI_PASSES : 1][EPI_GROUPS]) {
+#pragma unroll
+        for (int pass = 0; pass < EPI_PASSES; pass++) {
+            const int gm = m0 + wm * WM + i * 32 + pass * 4 + (lane >> 4);
+#pragma unroll
+            for (int h = 0; h < EPI_GROUPS; h++) {
+                const int scol = 4 * (lane & 15) + h * EPI_HALF;
+                const int gn = n0 + wn * WN + scol;
+                if (scol < WN && gm < M && gn < N) {
+                    const int64_t o = mn_base + (int64_t)gm * N + gn;
+                    cb[pass][h] = *(const half4 *)(p.C + o);
+                    if constexpr (HAS_X) xb[pass][h] = *(const half4 *)(p.X + o);
+                }
+            }
+        }
+    };
+
+    // the first slab's C / X loads fly while the accumulators go to LDS
+    if constexpr (VEC) epi_prefetch(0, cbuf[0], xbuf[0]);
+    barrier_lds();  // every wave is done with the main loop's LDS, which the epilogue reuses
+
+    float *slab = (float *)(smem + wave * (32 * EPI_LD * 4));
 #pragma unroll
     for (int i = 0; i < TM; i++) {  // fully unrolled: acc must stay in registers
-        // acc block row i of this wave -> LDS slab (32 x WN fp32)
+        // acc block row i of this wave -> its LDS slab (32 x WN fp32)
 #pragma unroll
         for (int j = 0; j < TN; j++)
 #pragma unroll
@@ -398,17 +501,17 @@ __global__ __launch_bounds__(NTHREADS) void gemm_epi_kernel(Params p)
                 const int col = j * 32 + (lane & 31);
                 slab[row * EPI_LD + col] = acc[i][j][r];
             }
-        __syncthreads();
-        // each pass: 4 rows; lane owns columns 4*(lane%16) + {0..3} (+ WN/2)
-        constexpr int HALF = WN / 2;
-        constexpr int GROUPS = WN >= 128 ? 2 : 1;
-#pragma unroll 2
-        for (int pass = 0; pass < 8; pass++) {
+        wave_lds_sync();  // each wave reads back only its own slab
+        if constexpr (VEC) {
+            if (i + 1 < TM) epi_prefetch(i + 1, cbuf[(i + 1) & 1], xbuf[(i + 1) & 1]);
+        }
+#pragma unroll
+        for (int pass = 0; pass < EPI_PASSES; pass++) {
             const int srow = pass * 4 + (lane >> 4);
             const int gm = m0 + wm * WM + i * 32 + srow;
 #pragma unroll
-            for (int h = 0; h < GROUPS; h++) {
-                const int scol = 4 * (lane & 15) + h * HALF;
+            for (int h = 0; h < EPI_GROUPS; h++) {
+                const int scol = 4 * (lane & 15) + h * EPI_HALF;
                 if (scol >= WN) continue;
                 const int gn = n0 + wn * WN + scol;
                 const f32x4 a4 = *(const f32x4 *)(slab + srow * EPI_LD + scol);
@@ -416,9 +519,9 @@ __global__ __launch_bounds__(NTHREADS) void gemm_epi_kernel(Params p)
                 const int64_t o = mn_base + (int64_t)gm * N + gn;
                 if constexpr (VEC) {
                     if (gn >= N) continue;  // N % 8 == 0: a 4-column group is all in or all out
-                    const half4 c4 = *(const half4 *)(p.C + o);
+                    const half4 c4 = cbuf[i & 1][pass][h];
                     half4 x4 = {};
-                    if constexpr (kind_reads_x(KIND)) x4 = *(const half4 *)(p.X + o);
+                    if constexpr (HAS_X) x4 = xbuf[i & 1][pass][h];
                     half4 d4, e4;
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
@@ -434,7 +537,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_epi_kernel(Params p)
                     for (int e = 0; e < 4; e++) {
                         if (gn + e >= N) break;
                         const float c = (float)p.C[o + e];
-                        const float x = kind_reads_x(KIND) ? (float)p.X[o + e] : 0.0f;
+                        const float x = HAS_X ? (float)p.X[o + e] : 0.0f;
                         float d, a = 0.0f;
                         epi_elem<KIND>(a4[e], c, x, alpha, beta, s, d, a);
                         p.D[o + e] = (_Float16)d;
@@ -443,7 +546,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_epi_kernel(Params p)
                 }
             }
         }
-        __syncthreads();
+        wave_lds_sync();  // slab reads done before the next block row overwrites it
     }
 }
 
