@@ -24,7 +24,7 @@ struct TileCfg {
 
 // The tile configurations compiled into the library (fast path), and the one
 // general-path configuration.
-constexpr TileCfg kTiles[] = {{256, 256, 64, 2, 4, 2}, {128, 256, 64, 3, 2, 2}, {256, 128, 64, 3, 2, 2},
+constexpr TileCfg kTiles[] = {{256, 256, 64, 2, 4, 2}, {128, 256, 64, 3, 2, 4}, {256, 128, 64, 3, 4, 2},
                               {128, 128, 64, 3, 2, 2}, {64, 64, 64, 3, 2, 2}};
 constexpr TileCfg kGeneral = {128, 128, 64, 2, 2, 2};
 
@@ -195,6 +195,9 @@ int gemm_epi_run(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, cons
     p.tiles_m = (int)tm;
     p.tiles_n = (int)tn;
     p.num_tiles = (int)tiles;
+    // L2 grouping: 8 tile rows share B column panels in a single large
+    // product; batched products keep each XCD on few batch entries instead.
+    p.group_m = L > 1 ? 2 : 8;
     p.alpha = scalars[0];
     p.beta = scalars[1];
     p.s = scalars[2];

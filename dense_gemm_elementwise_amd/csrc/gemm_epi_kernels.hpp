@@ -70,10 +70,9 @@ struct Params {
     int M, N, K;      // each < 2^31 (checked on the host)
     int tiles_m, tiles_n;
     int num_tiles;    // L * tiles_m * tiles_n
+    int group_m;      // tile rows per L2 group (>= 1)
     float alpha, beta, s;
 };
-
-constexpr int GROUP_M = 8;  // tile rows per L2 group
 
 // ---------------------------------------------------------------------------
 // Epilogue math, fp32.  d = first output, a = second output (if any).
@@ -110,8 +109,8 @@ __device__ __forceinline__ void epi_elem(float acc, float c, float x, float alph
 // Tile scheduling: hardware workgroup id -> (batch, tile row, tile column).
 // Workgroups are handed to the 8 XCDs round-robin (id % 8), so consecutive
 // logical tiles are given to ids that land on the same XCD; within a batch
-// entry tiles are ordered in groups of GROUP_M tile rows, column-major inside
-// a group, so the tiles an XCD runs together share operand panels.
+// entry tiles are ordered in groups of p.group_m tile rows, column-major
+// inside a group, so the tiles an XCD runs together share operand panels.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void map_tile(const Params &p, int &l, int &tm, int &tn)
 {
@@ -123,10 +122,11 @@ __device__ __forceinline__ void map_tile(const Params &p, int &l, int &tm, int &
     const int tpb = p.tiles_m * p.tiles_n;
     l = t / tpb;
     const int r = t - l * tpb;
-    const int gsize_full = GROUP_M * p.tiles_n;
+    const int group_m = p.group_m;
+    const int gsize_full = group_m * p.tiles_n;
     const int g = r / gsize_full;
-    const int first_m = g * GROUP_M;
-    const int gm = min(p.tiles_m - first_m, GROUP_M);
+    const int first_m = g * group_m;
+    const int gm = min(p.tiles_m - first_m, group_m);
     const int rr = r - g * gsize_full;
     tm = first_m + rr % gm;
     tn = rr / gm;
