@@ -24,7 +24,7 @@ struct TileCfg {
 
 // The tile configurations compiled into the library (fast path), and the one
 // general-path configuration.
-constexpr TileCfg kTiles[] = {{256, 256, 64, 2, 4, 2}, {128, 256, 64, 3, 2, 4}, {256, 128, 64, 3, 4, 2},
+constexpr TileCfg kTiles[] = {{256, 256, 64, 2, 4, 2}, {128, 256, 64, 2, 2, 4}, {256, 128, 64, 2, 4, 2},
                               {128, 128, 64, 3, 2, 2}, {64, 64, 64, 3, 2, 2}};
 constexpr TileCfg kGeneral = {128, 128, 64, 2, 2, 2};
 

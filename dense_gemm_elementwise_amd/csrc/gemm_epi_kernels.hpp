@@ -211,15 +211,22 @@ __device__ __forceinline__ void wait_vmcnt()
 #undef GE_VMCNT_CASE
 }
 
-// Workgroup barrier that waits only for this wave's LDS operations, not for
-// its outstanding global loads and stores (__syncthreads() would wait for
-// those too).
-__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Workgroup barrier ordering LDS only: the fences are restricted to the LDS
+// address space, so the wave waits for its own LDS operations but not for its
+// outstanding global loads and stores (__syncthreads() would wait for those
+// too).  Being compiler-visible, the fences also tell the wait-count pass
+// that earlier LDS reads have completed.
+__device__ __forceinline__ void barrier_lds()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
-// Orders this wave's LDS accesses before and after it (the compiler may not
-// move memory operations across it; the wave's earlier LDS operations have
-// completed).  Enough when a wave only reads LDS that it wrote itself.
-__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Orders this wave's LDS accesses before and after it.  Enough when a wave
+// only reads LDS that it wrote itself (a wave's LDS operations execute in
+// order).
+__device__ __forceinline__ void wave_lds_sync() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local"); }
 
 
 __device__ __forceinline__ uint32_t lds_addr_of(const void *p)
@@ -434,23 +441,28 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     barrier_lds();
     read_frags(0, 0, fa[0], fb[0]);
     int cur = 0;  // ring slot of stage kt
+    // every stage but the last: the last k step publishes the next stage
 #pragma unroll 1
-    for (int kt = 0; kt < nk; kt++) {
+    for (int kt = 0; kt + 1 < nk; kt++) {
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; kk++) {
-            if (kk + 1 < KSTEPS) {
-                read_frags(cur, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
-            } else if (kt + 1 < nk) {
-                wait_stage(newer_steady{}, kt + NSTAGES <= nk);  // stage kt+1 landed (this thread's part)
-                if constexpr (!VEC) __syncthreads();
-                barrier_lds();  // everyone's part landed; stage kt's slot is free
-                if (kt + NSTAGES < nk) load_stage(cur, (kt + NSTAGES) * BK);
-                const int nxt = cur + 1 == NSTAGES ? 0 : cur + 1;
-                read_frags(nxt, 0, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
-            }
+        for (int kk = 0; kk + 1 < KSTEPS; kk++) {
+            read_frags(cur, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
             mfmas(fa[kk & 1], fb[kk & 1]);
         }
-        cur = cur + 1 == NSTAGES ? 0 : cur + 1;
+        wait_stage(newer_steady{}, kt + NSTAGES <= nk);  // stage kt+1 landed (this thread's part)
+        if constexpr (!VEC) __syncthreads();
+        barrier_lds();  // everyone's part landed; stage kt's slot is free
+        if (kt + NSTAGES < nk) load_stage(cur, (kt + NSTAGES) * BK);
+        const int nxt = cur + 1 == NSTAGES ? 0 : cur + 1;
+        read_frags(nxt, 0, fa[KSTEPS & 1], fb[KSTEPS & 1]);
+        mfmas(fa[(KSTEPS - 1) & 1], fb[(KSTEPS - 1) & 1]);
+        cur = nxt;
+    }
+    // the last stage
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; kk++) {
+        if (kk + 1 < KSTEPS) read_frags(cur, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+        mfmas(fa[kk & 1], fb[kk & 1]);
     }
 
     // ---- epilogue ----------------------------------------------------------
