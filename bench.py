@@ -1,7 +1,7 @@
 """Throughput of the fused fp16 GEMM + epilogue on one MI355X.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload x_acc_8192]
-                    [--no-cpu-baseline] [--all]
+                    [--no-cpu-baseline] [--all] [--compare-unfused]
 
 A step is one call of the fused kernel (one gemm_epi_run) on the workload,
 with every input already resident in HBM.  The timed region is K steps on one
@@ -81,6 +81,64 @@ def bench_gpu(w, steps, warmup):
     ev_ms = e0.elapsed_time(e1) / steps
     rc, plan = ge.gemm_epi_plan(*args[:8], args[9], args[10], args[11])
     return {"ms_per_step": wall * 1e3 / steps, "kernel_ms": ev_ms, "plan": plan}
+
+
+def bench_unfused_library(w, steps, warmup):
+    """Context, not the metric: the same workload run unfused through the
+    vendor library -- torch.matmul (hipBLASLt, fp16 output) followed by the
+    epilogue as separate torch elementwise kernels -- on the same inputs.
+    This is the three-kernel composition the fusion replaces; its
+    intermediate Y = A @ B is rounded to fp16 before the epilogue."""
+    import torch
+    from dense_gemm_elementwise_amd import workloads
+
+    dev = torch.device("cuda:0")
+    p = workloads.make_inputs(w)
+    t = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in p.items()}
+    A, B, C, X = t["A"], t["B"], t["C"], t["X"]
+    a, b, s3 = w.alpha, w.beta, w.s3
+
+    def step():
+        Y = torch.matmul(A, B)
+        if w.kind == "LINCOMB":
+            return (a * Y + b * C,)
+        if w.kind == "AUX_SCALE":
+            aux = a * Y + b * C
+            return (s3 * aux, aux)
+        if w.kind == "LINCOMB_X_ACC":
+            return (a * Y + b * C + s3 * X, Y)
+        if w.kind == "RELU":
+            return (torch.relu(a * Y + b * C),)
+        d = a * Y + b * C
+        if w.kind == "RELU_SQUARE":
+            d = torch.relu(d)
+        return (d, d * d)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # the GEMM alone, for reference
+    for _ in range(warmup):
+        torch.matmul(A, B)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        torch.matmul(A, B)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_gemm = e0.elapsed_time(e1) / steps
+    return {"what": "torch.matmul (hipBLASLt) + torch elementwise epilogue, unfused",
+            "ms_per_step": round(ms, 5), "tflops": round(w.flops / (ms * 1e-3) / 1e12, 2),
+            "gemm_only_ms": round(ms_gemm, 5), "gemm_only_tflops": round(w.flops / (ms_gemm * 1e-3) / 1e12, 2)}
 
 
 def bench_cpu_oracle(w, rows):
@@ -166,6 +224,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=6144)
     ap.add_argument("--all", action="store_true")
+    ap.add_argument("--compare-unfused", action="store_true",
+                    help="also time the unfused vendor-library composition (context, not the metric)")
     ap.add_argument("--copy-kernel", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (calibrates HBM byte counters)")
     a = ap.parse_args()
@@ -187,7 +247,10 @@ def main():
             if other.name == name:
                 continue
             g = bench_gpu(other, a.steps, a.warmup)
-            print(json.dumps(result_line(other, g, a.steps, a.warmup, None)), file=sys.stderr, flush=True)
+            line = result_line(other, g, a.steps, a.warmup, None)
+            if a.compare_unfused:
+                line["unfused_library"] = bench_unfused_library(other, a.steps, a.warmup)
+            print(json.dumps(line), file=sys.stderr, flush=True)
 
     g = bench_gpu(w, a.steps, a.warmup)
     cpu = None
@@ -198,7 +261,10 @@ def main():
         cpu = {"value": round(v, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
                "sample": f"first {rows} of {w.M} output rows of {w.name} (all {w.N} columns, K={w.K}), "
                          f"fp64 i-k-j triple loop + epilogue, {dt:.1f} s"}
-    print(json.dumps(result_line(w, g, a.steps, a.warmup, cpu)), flush=True)
+    line = result_line(w, g, a.steps, a.warmup, cpu)
+    if a.compare_unfused:
+        line["unfused_library"] = bench_unfused_library(w, a.steps, a.warmup)
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

@@ -20,13 +20,14 @@ struct TileCfg {
     int bm, bn;      // output tile
     int bk, stages;  // K step per LDS stage, LDS stages in the ring
     int wgm, wgn;    // wave grid (threads = 64 * wgm * wgn)
+    int mi;          // MFMA block: 32 (32x32x16) or 16 (16x16x32)
 };
 
 // The tile configurations compiled into the library (fast path), and the one
 // general-path configuration.
-constexpr TileCfg kTiles[] = {{256, 256, 64, 2, 4, 2}, {128, 256, 64, 2, 2, 4}, {256, 128, 64, 2, 4, 2},
-                              {128, 128, 64, 3, 2, 2}, {64, 64, 64, 3, 2, 2}};
-constexpr TileCfg kGeneral = {128, 128, 64, 2, 2, 2};
+constexpr TileCfg kTiles[] = {{256, 256, 64, 2, 4, 2, 16}, {128, 256, 64, 2, 2, 4, 32}, {256, 128, 64, 2, 4, 2, 32},
+                              {128, 128, 64, 3, 2, 2, 32}, {64, 64, 32, 4, 2, 2, 16}};
+constexpr TileCfg kGeneral = {128, 128, 64, 2, 2, 2, 32};
 
 // Relative MFMA efficiency of a tile (bigger tiles reuse each LDS operand
 // read over more MFMAs and amortise the epilogue better).
@@ -107,15 +108,15 @@ bool use_fast_path(int64_t M, int64_t N, int64_t K, const void *A, const void *B
     return true;
 }
 
-template <int BM, int BN, int BK, int NS, int WGM, int WGN, int KIND, bool VEC>
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, int MI, int KIND, bool VEC>
 hipError_t launch_one(const Params &p, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemm_epi_kernel<BM, BN, BK, NS, WGM, WGN, KIND, VEC>), dim3(p.num_tiles),
+    hipLaunchKernelGGL((gemm_epi_kernel<BM, BN, BK, NS, WGM, WGN, MI, KIND, VEC>), dim3(p.num_tiles),
                        dim3(64 * WGM * WGN), 0, stream, p);
     return hipGetLastError();
 }
 
-#define GE_LAUNCH(T, KIND, VEC) launch_one<T.bm, T.bn, T.bk, T.stages, T.wgm, T.wgn, KIND, VEC>(p, stream)
+#define GE_LAUNCH(T, KIND, VEC) launch_one<T.bm, T.bn, T.bk, T.stages, T.wgm, T.wgn, T.mi, KIND, VEC>(p, stream)
 
 template <int KIND>
 hipError_t launch_kind(const Params &p, const TileCfg &t, bool vec, hipStream_t stream)

@@ -11,9 +11,11 @@
 //
 // Design for gfx950 (not a translation of the pages' Blackwell kernels):
 //  * WGM x WGN wave64s per workgroup; each wave owns a (BM/WGM) x (BN/WGN)
-//    accumulator tile built from v_mfma_f32_32x32x16_f16.  With two waves per
-//    SIMD (8 waves), one wave's MFMAs run while the other waits on LDS or a
-//    barrier.
+//    accumulator tile built from v_mfma_f32_32x32x16_f16 (MI = 32) or
+//    v_mfma_f32_16x16x32_f16 (MI = 16) blocks.  With two waves per SIMD
+//    (8 waves), one wave's MFMAs run while the other waits on LDS or a
+//    barrier; with 4 waves of 128 x 128 each wave reuses every operand it
+//    reads from LDS over more MFMAs.
 //  * K is walked in steps of BK through a ring of NSTAGES LDS stages, so the
 //    loads of a stage are issued NSTAGES-1 stages before it is used.  The
 //    fast path fills LDS with buffer_load_dwordx4 ... lds (global -> LDS
@@ -146,13 +148,20 @@ __device__ __forceinline__ int swz_a(int row)
     else
         return ((row >> 1) & 3) ^ ((row >> 3) & 1);  // 64-byte rows
 }
-template <int B_CHUNKS>
+//
+// The B transpose reads differ by MFMA shape.  MI = 32: the 32 lanes served
+// together read 4 consecutive k-rows x 4 consecutive chunks.  MI = 16: they
+// read k-rows r..r+3 and r+8..r+11 x 2 consecutive chunks, so the swizzle also
+// separates k-rows 8 apart.
+template <int B_CHUNKS, int MI>
 __device__ __forceinline__ int swz_b(int krow)
 {
-    if constexpr (B_CHUNKS >= 16)
-        return (0xCA60 >> ((krow & 3) * 4)) & 15;  // 0, 6, 10, 12 for krow % 4 = 0..3
+    if constexpr (B_CHUNKS >= 16 && MI == 32)
+        return (0xCA60 >> ((krow & 3) * 4)) & 15;          // 0, 6, 10, 12 for krow % 4 = 0..3
+    else if constexpr (B_CHUNKS >= 16)
+        return 2 * ((krow & 3) | (((krow >> 3) & 1) << 2));  // 0, 2, .., 14 over krow % 4 and bit 3
     else
-        return 2 * (krow & 3);                     // 8-chunk rows: 0, 2, 4, 6
+        return 2 * (krow & 3);                              // 8-chunk rows: 0, 2, 4, 6
 }
 
 // ---------------------------------------------------------------------------
@@ -239,12 +248,16 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void *p)
 // vectors); otherwise every global access is element-wise and guarded and
 // LDS is filled through registers.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int NSTAGES, int WGM, int WGN, int KIND, bool VEC>
+template <int BM, int BN, int BK, int NSTAGES, int WGM, int WGN, int MI, int KIND, bool VEC>
 __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
 {
-    constexpr int NW = WGM * WGN;              // waves per workgroup
+    constexpr int NW = WGM * WGN;                // waves per workgroup
     constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile
-    constexpr int TM = WM / 32, TN = WN / 32;  // 32x32 MFMA blocks per wave
+    static_assert(MI == 32 || MI == 16, "MFMA block is 32x32x16 or 16x16x32");
+    constexpr int TM = WM / MI, TN = WN / MI;    // MFMA blocks per wave
+    constexpr int KSTEP = MI == 32 ? 16 : 32;    // k per MFMA
+    constexpr int NACC = MI == 32 ? 16 : 4;      // accumulator registers per block
+    using acc_t = typename std::conditional<MI == 32, f32x16, f32x4>::type;
     static_assert(TM >= 1 && TN >= 1, "tile too small");
     static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
     static_assert(NSTAGES >= 2, "at least two stages");
@@ -256,8 +269,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     constexpr int B_STAGE = BK * B_ROW;
     constexpr int STAGE = A_STAGE + B_STAGE;
     constexpr int MAIN_BYTES = NSTAGES * STAGE;
-    constexpr int EPI_LD = WN + 8;  // fp32 row pitch of an epilogue slab (padded against bank conflicts)
-    constexpr int EPI_BYTES = NW * 32 * EPI_LD * 4;
+    // epilogue slab: one MFMA row-block (MI rows) of the wave tile in fp32; the
+    // row pitch is padded so that the rows one store instruction writes fall
+    // on different banks
+    constexpr int SLAB = MI;
+    constexpr int EPI_LD = WN + (MI == 32 ? 8 : 4);
+    constexpr int EPI_BYTES = NW * SLAB * EPI_LD * 4;
     constexpr int SMEM = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
     static_assert(SMEM <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
@@ -275,13 +292,13 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     const _Float16 *Al = p.A + (int64_t)l * M * K;
     const _Float16 *Bl = p.B + (int64_t)l * K * N;
 
-    f32x16 acc[TM][TN];
+    acc_t acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; i++)
 #pragma unroll
         for (int j = 0; j < TN; j++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+            for (int r = 0; r < NACC; r++) acc[i][j][r] = 0.0f;
 
     const int nk = (K + BK - 1) / BK;
 
@@ -322,7 +339,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
                 const int blk = q * NW + wave;
                 const int lin = blk * 64 + lane;  // chunk index within the stage
                 const int krow = lin / B_CHUNKS;
-                const int c = (lin % B_CHUNKS) ^ swz_b<B_CHUNKS>(krow);
+                const int c = (lin % B_CHUNKS) ^ swz_b<B_CHUNKS, MI>(krow);
                 const int gk = k0 + krow, gn = n0 + c * 8;
                 const int off = (gk < K && gn < N) ? (gk * N + gn) * 2 : 0x7FFFFFF0;
                 dma16(rsrc_b, smem_lds + b_off + blk * 1024, off);
@@ -350,7 +367,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
                 const int lin = blk * 64 + lane;
                 const int krow = lin / B_CHUNKS;
                 const int pchunk = lin % B_CHUNKS;
-                const int c = pchunk ^ swz_b<B_CHUNKS>(krow);
+                const int c = pchunk ^ swz_b<B_CHUNKS, MI>(krow);
                 const int gk = k0 + krow;
                 half8 v;
 #pragma unroll
@@ -364,30 +381,34 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     };
 
     // ---- LDS -> MFMA operand fragments -------------------------------------
-    // A operand of v_mfma_f32_32x32x16_f16: lane (i + 32g) holds row i,
-    // k = 8g..8g+7 of the 32 x 16 block.  B operand: lane (j + 32g) holds
-    // column j, k = 8g..8g+7; ds_read_b64_tr_b16 gives lane q of a 16-lane
-    // block the 4 values of column q from 4 k-rows, when lane 4e + r of the
-    // block points at k-row e, columns 4r..4r+3.
-    const int li = lane & 31, lg = lane >> 5;
+    // A operand: lane (i + MI*g) holds row i of the block, k = 8g..8g+7 of the
+    // k step (one ds_read_b128).  B operand: lane (j + MI*g) holds column j,
+    // k = 8g..8g+7.  ds_read_b64_tr_b16 gives lane q of a 16-lane block the 4
+    // values of column q from 4 k-rows, when lane 4e + r of the block points
+    // at k-row e, columns 4r..4r+3; two such reads make one B operand.
+    //  MI = 32: 16-lane block b covers columns 16*(b&1).., k-group g = b>>1.
+    //  MI = 16: 16-lane block b covers the block's 16 columns, k-group g = b.
+    const int li = lane % MI, lg = lane / MI;
     const int lb = lane >> 4, lq = lane & 15;
     auto read_frags = [&](int stage, int kk, half8 (&af)[TM], half8 (&bf)[TN]) {
         const char *a_src = smem + stage * STAGE;
         const char *b_src = a_src + A_STAGE;
 #pragma unroll
         for (int i = 0; i < TM; i++) {
-            const int row = wm * WM + i * 32 + li;
-            const int c = (kk * 2 + lg) ^ swz_a<A_CHUNKS>(row);
+            const int row = wm * WM + i * MI + li;
+            const int c = (kk * (KSTEP / 8) + lg) ^ swz_a<A_CHUNKS>(row);
             af[i] = *(const half8 *)(a_src + row * A_ROW + c * 16);
         }
 #pragma unroll
         for (int j = 0; j < TN; j++) {
-            const int n = wn * WN + j * 32 + 16 * (lb & 1) + 4 * (lq & 3);
+            const int n = MI == 32 ? wn * WN + j * 32 + 16 * (lb & 1) + 4 * (lq & 3)
+                                   : wn * WN + j * 16 + 4 * (lq & 3);
+            const int kgrp = MI == 32 ? (lb >> 1) : lb;
             half8 b;
 #pragma unroll
             for (int h = 0; h < 2; h++) {
-                const int krow = kk * 16 + 8 * (lb >> 1) + 4 * h + (lq >> 2);
-                const int c = (n >> 3) ^ swz_b<B_CHUNKS>(krow);
+                const int krow = kk * KSTEP + 8 * kgrp + 4 * h + (lq >> 2);
+                const int c = (n >> 3) ^ swz_b<B_CHUNKS, MI>(krow);
                 fp16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
                     (GE_LDS(fp16x4_t) *)(b_src + krow * B_ROW + c * 16 + (n & 7) * 2));
                 const half4 t4 = __builtin_bit_cast(half4, t);
@@ -404,8 +425,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
 #pragma unroll
         for (int i = 0; i < TM; i++)
 #pragma unroll
-            for (int j = 0; j < TN; j++)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < TN; j++) {
+                if constexpr (MI == 32)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+                else
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+            }
     };
 
     // Waits until this thread's DMA for the stage about to be published has
@@ -431,7 +456,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     // 16-wide k step ahead of the MFMAs; the barrier sits between the last
     // fragment reads of a stage and its last MFMAs, so the MFMA pipe keeps
     // working across it.
-    constexpr int KSTEPS = BK / 16;
+    constexpr int KSTEPS = BK / KSTEP;
     half8 fa[2][TM], fb[2][TN];
 #pragma unroll
     for (int st = 0; st < NSTAGES; st++)
@@ -440,38 +465,72 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     if constexpr (!VEC) __syncthreads();
     barrier_lds();
     read_frags(0, 0, fa[0], fb[0]);
-    int cur = 0;  // ring slot of stage kt
-    // every stage but the last: the last k step publishes the next stage
-#pragma unroll 1
-    for (int kt = 0; kt + 1 < nk; kt++) {
+
+    // Fragment buffers alternate with every k step across the whole K loop;
+    // P (compile time) is the buffer holding the first k step of a stage.
+    // When a stage has an odd number of k steps, P flips from stage to
+    // stage, so the stage loop is unrolled by two.
+    //
+    // A stage that is followed by another: its last k step publishes the next
+    // stage (barrier) and starts reading it before its own last MFMAs.
+    auto stage_with_next = [&](int kt, int cur, int nxt, auto P) {
+        constexpr int p0 = decltype(P)::value;
 #pragma unroll
         for (int kk = 0; kk + 1 < KSTEPS; kk++) {
-            read_frags(cur, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
-            mfmas(fa[kk & 1], fb[kk & 1]);
+            read_frags(cur, kk + 1, fa[(p0 + kk + 1) & 1], fb[(p0 + kk + 1) & 1]);
+            mfmas(fa[(p0 + kk) & 1], fb[(p0 + kk) & 1]);
         }
         wait_stage(newer_steady{}, kt + NSTAGES <= nk);  // stage kt+1 landed (this thread's part)
         if constexpr (!VEC) __syncthreads();
         barrier_lds();  // everyone's part landed; stage kt's slot is free
         if (kt + NSTAGES < nk) load_stage(cur, (kt + NSTAGES) * BK);
-        const int nxt = cur + 1 == NSTAGES ? 0 : cur + 1;
-        read_frags(nxt, 0, fa[KSTEPS & 1], fb[KSTEPS & 1]);
-        mfmas(fa[(KSTEPS - 1) & 1], fb[(KSTEPS - 1) & 1]);
-        cur = nxt;
-    }
-    // the last stage
+        read_frags(nxt, 0, fa[(p0 + KSTEPS) & 1], fb[(p0 + KSTEPS) & 1]);
+        mfmas(fa[(p0 + KSTEPS - 1) & 1], fb[(p0 + KSTEPS - 1) & 1]);
+    };
+    auto last_stage = [&](int cur, auto P) {
+        constexpr int p0 = decltype(P)::value;
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; kk++) {
-        if (kk + 1 < KSTEPS) read_frags(cur, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
-        mfmas(fa[kk & 1], fb[kk & 1]);
+        for (int kk = 0; kk < KSTEPS; kk++) {
+            if (kk + 1 < KSTEPS) read_frags(cur, kk + 1, fa[(p0 + kk + 1) & 1], fb[(p0 + kk + 1) & 1]);
+            mfmas(fa[(p0 + kk) & 1], fb[(p0 + kk) & 1]);
+        }
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    auto next_slot = [](int c) { return c + 1 == NSTAGES ? 0 : c + 1; };
+    int cur = 0;  // ring slot of stage kt
+    int kt = 0;
+    if constexpr (KSTEPS % 2 == 0) {
+#pragma unroll 1
+        for (; kt + 1 < nk; kt++) {
+            stage_with_next(kt, cur, next_slot(cur), P0{});
+            cur = next_slot(cur);
+        }
+        last_stage(cur, P0{});
+    } else {
+#pragma unroll 1
+        for (; kt + 2 < nk; kt += 2) {
+            stage_with_next(kt, cur, next_slot(cur), P0{});
+            cur = next_slot(cur);
+            stage_with_next(kt + 1, cur, next_slot(cur), P1{});
+            cur = next_slot(cur);
+        }
+        if (kt + 1 < nk) {  // two stages left: kt (buffer 0) and kt+1 (buffer 1)
+            stage_with_next(kt, cur, next_slot(cur), P0{});
+            cur = next_slot(cur);
+            last_stage(cur, P1{});
+        } else {            // one stage left, starting in buffer 0
+            last_stage(cur, P0{});
+        }
     }
 
     // ---- epilogue ----------------------------------------------------------
-    // The wave tile is handled one 32-row block ("slab") at a time.  In a
-    // slab, pass p (0..7) covers rows 4p..4p+3; lane owns row 4p + lane/16
-    // and the 4-column groups 4*(lane%16) (+ WN/2).  C / X of a slab are
-    // loaded into registers one slab ahead, so the loads' latency hides
-    // behind the previous slab's work.
-    constexpr int EPI_PASSES = 8;
+    // The wave tile is handled one MFMA row-block (SLAB rows) at a time.  In a
+    // slab, pass p covers rows 4p..4p+3; lane owns row 4p + lane/16 and the
+    // 4-column groups 4*(lane%16) (+ WN/2).  C / X of a slab are loaded into
+    // registers one slab ahead, so the loads' latency hides behind the
+    // previous slab's work.
+    constexpr int EPI_PASSES = SLAB / 4;
     constexpr int EPI_GROUPS = WN >= 128 ? 2 : 1;
     constexpr int EPI_HALF = WN / 2;
     constexpr bool HAS_X = kind_reads_x(KIND);
@@ -483,7 +542,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
                             half4 (&xb)[HAS_X ? EPI_PASSES : 1][EPI_GROUPS]) {
 #pragma unroll
         for (int pass = 0; pass < EPI_PASSES; pass++) {
-            const int gm = m0 + wm * WM + i * 32 + pass * 4 + (lane >> 4);
+            const int gm = m0 + wm * WM + i * SLAB + pass * 4 + (lane >> 4);
 #pragma unroll
             for (int h = 0; h < EPI_GROUPS; h++) {
                 const int scol = 4 * (lane & 15) + h * EPI_HALF;
@@ -501,16 +560,18 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     if constexpr (VEC) epi_prefetch(0, cbuf[0], xbuf[0]);
     barrier_lds();  // every wave is done with the main loop's LDS, which the epilogue reuses
 
-    float *slab = (float *)(smem + wave * (32 * EPI_LD * 4));
+    float *slab = (float *)(smem + wave * (SLAB * EPI_LD * 4));
 #pragma unroll
     for (int i = 0; i < TM; i++) {  // fully unrolled: acc must stay in registers
-        // acc block row i of this wave -> its LDS slab (32 x WN fp32)
+        // acc block row i of this wave -> its LDS slab (SLAB x WN fp32).  Output
+        // layouts: MI = 32: lane l, register r holds row 8(r/4) + 4(l/32) + r%4,
+        // column l%32; MI = 16: row 4(l/16) + r, column l%16.
 #pragma unroll
         for (int j = 0; j < TN; j++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const int col = j * 32 + (lane & 31);
+            for (int r = 0; r < NACC; r++) {
+                const int row = MI == 32 ? 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) : 4 * (lane >> 4) + r;
+                const int col = j * MI + (lane % MI);
                 slab[row * EPI_LD + col] = acc[i][j][r];
             }
         wave_lds_sync();  // each wave reads back only its own slab
@@ -520,7 +581,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
 #pragma unroll
         for (int pass = 0; pass < EPI_PASSES; pass++) {
             const int srow = pass * 4 + (lane >> 4);
-            const int gm = m0 + wm * WM + i * 32 + srow;
+            const int gm = m0 + wm * WM + i * SLAB + srow;
 #pragma unroll
             for (int h = 0; h < EPI_GROUPS; h++) {
                 const int scol = 4 * (lane & 15) + h * EPI_HALF;

@@ -95,7 +95,7 @@ def test_misaligned_pointers():
 
 def test_plan_fast_and_general_paths():
     rc, cfg = ge.gemm_epi_plan(1, 256, 256, 256, P16, P16, P16, None, 0, P16, None)
-    assert rc == 0 and cfg["vec"] == 1 and cfg["threads"] == 256 and cfg["bk"] == 64
+    assert rc == 0 and cfg["vec"] == 1 and cfg["threads"] in (256, 512) and cfg["bk"] in (32, 64)
     # K or N not a multiple of 8, or a pointer not 16-byte aligned -> general kernel
     for args in ((1, 256, 256, 250), (1, 256, 250, 256)):
         rc, cfg = ge.gemm_epi_plan(*args, P16, P16, P16, None, 0, P16, None)
