@@ -313,37 +313,59 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     static_assert(A_BLKS % NW == 0 && B_BLKS % NW == 0, "stage must split evenly over the waves");
     static_assert(B_ROW <= 1024 && 1024 % B_ROW == 0, "B row must divide 1 KB");
 
-    i32x4 rsrc_a = {}, rsrc_b = {};
-    if constexpr (VEC) {
-        // one buffer per batch entry; every offset is < 2^31 (checked on the host)
-        rsrc_a = make_rsrc(Al, (uint32_t)((int64_t)M * K * 2));
-        rsrc_b = make_rsrc(Bl, (uint32_t)((int64_t)K * N * 2));
-    }
+    // Fast-path DMA addressing.  Every DMA chunk of this thread sits at a
+    // fixed byte offset from the first k column (A) / k-row (B) of its stage,
+    // so the offsets are computed once; a stage moves the buffer base to its
+    // k0 instead (a few scalar instructions) and shrinks the record count with
+    // it.  Lanes outside M (A) or N (B) keep the offset 0x7FFFFFF0, beyond
+    // every record count (one batch entry spans < 2^31 - 64 bytes), so they
+    // read zeros at every stage.  B k-rows at or past K fall beyond the shrunk record count
+    // by themselves; A k columns past K lie inside the buffer (they are the
+    // next row), so a stage that crosses K takes per-lane checked offsets.
+    constexpr int A_DMA = A_BLKS / NW, B_DMA = B_BLKS / NW;
+    constexpr uint32_t kParked = 0x7FFFFFF0u;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const uint32_t smem_lds = lds_addr_of(smem);
+    uint32_t a_voff[A_DMA], b_voff[B_DMA];
+    if constexpr (VEC) {
+#pragma unroll
+        for (int q = 0; q < A_DMA; q++) {
+            const int row = (q * NW + wave) * A_ROWS_PER_BLK + lane / A_CHUNKS;
+            const int c = (lane % A_CHUNKS) ^ swz_a<A_CHUNKS>(row);
+            const int gm = m0 + row;
+            a_voff[q] = gm < M ? (uint32_t)(gm * K + c * 8) * 2u : kParked;
+        }
+#pragma unroll
+        for (int q = 0; q < B_DMA; q++) {
+            const int lin = (q * NW + wave) * 64 + lane;  // chunk index within the stage
+            const int krow = lin / B_CHUNKS;
+            const int c = (lin % B_CHUNKS) ^ swz_b<B_CHUNKS, MI>(krow);
+            const int gn = n0 + c * 8;
+            b_voff[q] = gn < N ? (uint32_t)(krow * N + gn) * 2u : kParked;
+        }
+    }
 
     auto load_stage = [&](int stage, int k0) {
         const int a_off = stage * STAGE;
         const int b_off = a_off + A_STAGE;
         if constexpr (VEC) {
+            const uint32_t a_lds = smem_lds + a_off + wave_u * 1024;
+            const uint32_t b_lds = smem_lds + b_off + wave_u * 1024;
+            const i32x4 ra = make_rsrc(Al + k0, (uint32_t)(((int64_t)M * K - k0) * 2));
+            const i32x4 rb = make_rsrc(Bl + (int64_t)k0 * N, (uint32_t)((int64_t)(K - k0) * N * 2));
+            if (k0 + BK <= K) {
 #pragma unroll
-            for (int q = 0; q < A_BLKS / NW; q++) {
-                const int blk = q * NW + wave;
-                const int row = blk * A_ROWS_PER_BLK + lane / A_CHUNKS;
-                const int c = (lane % A_CHUNKS) ^ swz_a<A_CHUNKS>(row);
-                const int gm = m0 + row, gk = k0 + c * 8;
-                const int off = (gm < M && gk < K) ? (gm * K + gk) * 2 : 0x7FFFFFF0;
-                dma16(rsrc_a, smem_lds + a_off + blk * 1024, off);
+                for (int q = 0; q < A_DMA; q++) dma16(ra, a_lds + q * NW * 1024, (int)a_voff[q]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < A_DMA; q++) {
+                    const int row = (q * NW + wave) * A_ROWS_PER_BLK + lane / A_CHUNKS;
+                    const int c = (lane % A_CHUNKS) ^ swz_a<A_CHUNKS>(row);
+                    dma16(ra, a_lds + q * NW * 1024, (int)(k0 + c * 8 < K ? a_voff[q] : kParked));
+                }
             }
 #pragma unroll
-            for (int q = 0; q < B_BLKS / NW; q++) {
-                const int blk = q * NW + wave;
-                const int lin = blk * 64 + lane;  // chunk index within the stage
-                const int krow = lin / B_CHUNKS;
-                const int c = (lin % B_CHUNKS) ^ swz_b<B_CHUNKS, MI>(krow);
-                const int gk = k0 + krow, gn = n0 + c * 8;
-                const int off = (gk < K && gn < N) ? (gk * N + gn) * 2 : 0x7FFFFFF0;
-                dma16(rsrc_b, smem_lds + b_off + blk * 1024, off);
-            }
+            for (int q = 0; q < B_DMA; q++) dma16(rb, b_lds + q * NW * 1024, (int)b_voff[q]);
         } else {
             // element-wise guarded loads through registers, same LDS layout
 #pragma unroll 1
