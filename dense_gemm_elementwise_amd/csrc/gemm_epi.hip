@@ -25,7 +25,7 @@ struct TileCfg {
 
 // The tile configurations compiled into the library (fast path), and the one
 // general-path configuration.
-constexpr TileCfg kTiles[] = {{256, 256, 64, 2, 4, 2, 16}, {128, 256, 64, 2, 2, 4, 32}, {256, 128, 64, 2, 4, 2, 32},
+constexpr TileCfg kTiles[] = {{256, 256, 64, 2, 4, 2, 16}, {128, 256, 64, 2, 2, 4, 16}, {256, 128, 64, 2, 4, 2, 16},
                               {128, 128, 64, 3, 2, 2, 32}, {64, 64, 32, 4, 2, 2, 16}};
 constexpr TileCfg kGeneral = {128, 128, 64, 2, 2, 2, 32};
 

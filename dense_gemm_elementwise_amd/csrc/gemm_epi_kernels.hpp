@@ -136,17 +136,22 @@ __device__ __forceinline__ void map_tile(const Params &p, int &l, int &tm, int &
 
 // Swizzles (in 16-byte chunk units).  An A row holds A_CHUNKS = BK/8 chunks;
 // row r stores logical chunk c at physical chunk c ^ swz_a(r).  A B k-row
-// holds BN/8 chunks; k-row kr stores logical chunk c at c ^ swz_b(kr).  They
-// keep every MFMA operand read conflict-free whether the LDS serves 128 or
-// 256 bytes a clock: an A read has 16 consecutive rows at one logical chunk,
-// a B transpose read has 4 consecutive k-rows x 4 consecutive chunks.
+// holds BN/8 chunks; k-row kr stores logical chunk c at c ^ swz_b(kr).
+//
+// An A operand read (ds_read_b128) has 16 or 32 consecutive rows at one
+// logical chunk per group of lanes.  The swizzle depends on the row pair
+// only (row >> 1): the two rows of a pair keep their relative position and
+// each pair moves to its own chunk.  Swizzles that also mix the row's low bit
+// into the chunk conflict 2-way on gfx950 for this read, with 128-byte and
+// with 64-byte rows and for both MFMA shapes (measured with the LDS
+// bank-conflict counter).
 template <int A_CHUNKS>
 __device__ __forceinline__ int swz_a(int row)
 {
     if constexpr (A_CHUNKS == 8)
-        return (row & 7) ^ ((row >> 3) & 1);         // 128-byte rows
+        return (row >> 1) & 7;  // 128-byte rows
     else
-        return ((row >> 1) & 3) ^ ((row >> 3) & 1);  // 64-byte rows
+        return (row >> 1) & 3;  // 64-byte rows
 }
 //
 // The B transpose reads differ by MFMA shape.  MI = 32: the 32 lanes served
