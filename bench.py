@@ -25,7 +25,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_FP16_TFLOPS = 2516.6  # MI355X dense fp16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
-PEAK_HBM_GBS = 8000.0
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 KERNEL_SOURCES = ("dense_gemm_elementwise_amd/csrc/gemm_epi_kernels.hpp", "dense_gemm_elementwise_amd/csrc/gemm_epi.hip")
 
 
@@ -50,6 +50,31 @@ def measured_traffic(workload_name):
     return rec.get("traffic_bytes")
 
 
+def _device_args(w, t, D, Aux, stream, ge):
+    return (w.L, w.M, w.N, w.K, t["A"].data_ptr(), t["B"].data_ptr(), t["C"].data_ptr(),
+            t["X"].data_ptr() if t["X"] is not None else None, (w.alpha, w.beta, w.s3), ge.KINDS[w.kind],
+            D.data_ptr(), Aux.data_ptr() if Aux is not None else None, stream.cuda_stream)
+
+
+def _timed_launches(launch, steps, stream):
+    """Times `steps` launches between two synchronisations.  One HIP event
+    before every launch and one after the last give each launch's duration
+    on the launch stream; the wall clock covers the whole timed region."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i].record(stream)
+        launch(i)
+    ev[steps].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    total = ev[0].elapsed_time(ev[steps])
+    return wall * 1e3 / steps, total / steps, {"median": per[steps // 2], "min": per[0], "mean": total / steps}
+
+
 def bench_gpu(w, steps, warmup):
     import torch
     import dense_gemm_elementwise_amd as ge
@@ -61,26 +86,46 @@ def bench_gpu(w, steps, warmup):
     D = torch.empty((w.L, w.M, w.N), dtype=torch.float16, device=dev)
     Aux = torch.empty_like(D) if w.kind in ge.HAS_AUX else None
     stream = torch.cuda.current_stream(dev)
-    args = (w.L, w.M, w.N, w.K, t["A"].data_ptr(), t["B"].data_ptr(), t["C"].data_ptr(),
-            t["X"].data_ptr() if t["X"] is not None else None, (w.alpha, w.beta, w.s3), ge.KINDS[w.kind],
-            D.data_ptr(), Aux.data_ptr() if Aux is not None else None, stream.cuda_stream)
+    args = _device_args(w, t, D, Aux, stream, ge)
     for _ in range(warmup):
         rc = ge.gemm_epi_run(*args)
         if rc:
             raise RuntimeError(ge.gemm_epi_status_string(rc))
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(steps):
-        ge.gemm_epi_run(*args)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ev_ms = e0.elapsed_time(e1) / steps
+    wall_ms, ev_ms, stats = _timed_launches(lambda i: ge.gemm_epi_run(*args), steps, stream)
     rc, plan = ge.gemm_epi_plan(*args[:8], args[9], args[10], args[11])
-    return {"ms_per_step": wall * 1e3 / steps, "kernel_ms": ev_ms, "plan": plan}
+    return {"ms_per_step": wall_ms, "kernel_ms": ev_ms, "launch_ms": stats, "plan": plan}
+
+
+MALL_BYTES = 256 << 20  # MI355X Infinity Cache
+
+
+def bench_gpu_cold(w, steps, warmup):
+    """The same launches with every step on its own copy of the inputs and
+    outputs, rotating through enough copies (more than twice the 256 MB
+    MALL) that no step finds its operands in a cache."""
+    import torch
+    import dense_gemm_elementwise_amd as ge
+    from dense_gemm_elementwise_amd import workloads
+
+    dev = torch.device("cuda:0")
+    p = workloads.make_inputs(w)
+    base = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in p.items()}
+    sets = min(4096, -(-2 * MALL_BYTES // w.hbm_bytes) + 1)
+    copies = []
+    for _ in range(sets):
+        t = {k: (v.clone() if v is not None else None) for k, v in base.items()}
+        D = torch.empty((w.L, w.M, w.N), dtype=torch.float16, device=dev)
+        Aux = torch.empty_like(D) if w.kind in ge.HAS_AUX else None
+        copies.append((t, D, Aux))
+    stream = torch.cuda.current_stream(dev)
+    arglist = [_device_args(w, t, D, Aux, stream, ge) for (t, D, Aux) in copies]
+    for i in range(warmup):
+        ge.gemm_epi_run(*arglist[i % sets])
+    _, ev_ms, stats = _timed_launches(lambda i: ge.gemm_epi_run(*arglist[(i + warmup) % sets]), steps, stream)
+    del copies
+    return {"copies": sets, "kernel_ms": round(ev_ms, 5), "launch_ms": {k: round(v, 5) for k, v in stats.items()},
+            "tflops": round(w.flops / (ev_ms * 1e-3) / 1e12, 2),
+            "epilogue_hbm_gbs": round(w.epilogue_bytes / (ev_ms * 1e-3) / 1e9, 1)}
 
 
 def bench_unfused_library(w, steps, warmup):
@@ -166,9 +211,24 @@ def omp_threads():
     return len(os.sched_getaffinity(0))
 
 
+def roofline(w, kernel_ms):
+    """The bound of this workload's kernel (the larger of its MFMA time and
+    its algorithmic-bytes time at peak) and what the measured launch
+    reaches against it."""
+    t_mfma = w.flops / (PEAK_FP16_TFLOPS * 1e12)
+    t_hbm = w.hbm_bytes / (PEAK_HBM_GBS * 1e9)
+    t = kernel_ms * 1e-3
+    if t_mfma >= t_hbm:
+        achieved, peak, unit, bound = w.flops / t / 1e12, PEAK_FP16_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        achieved, peak, unit, bound = w.hbm_bytes / t / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name),
+            "attainable_frac": round(max(t_mfma, t_hbm) / t, 4)}
+
+
 def result_line(w, g, steps, warmup, cpu):
     tflops = w.flops / (g["ms_per_step"] * 1e-3) / 1e12
-    achieved = w.flops / (g["kernel_ms"] * 1e-3) / 1e12
     line = {
         "metric": "fused GEMM+epilogue TFLOP/s at 8192^3 fp16; % of fp16 MFMA peak",
         "value": round(tflops, 2),
@@ -188,14 +248,8 @@ def result_line(w, g, steps, warmup, cpu):
             "accumulate": "f32", "tile": [g["plan"]["bm"], g["plan"]["bn"], g["plan"]["bk"]],
             "workgroups": g["plan"]["workgroups"], "parallelism": "single GPU",
         },
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round(achieved, 2),
-            "peak": PEAK_FP16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
-            "traffic": measured_traffic(w.name),
-        },
+        "roofline": roofline(w, g["kernel_ms"]),
+        "launch_ms": {k: round(v, 5) for k, v in g["launch_ms"].items()},
         "epilogue_hbm_gbs": round(w.epilogue_bytes / (g["kernel_ms"] * 1e-3) / 1e9, 1),
         "cpu_baseline": cpu,
     }
@@ -248,6 +302,7 @@ def main():
                 continue
             g = bench_gpu(other, a.steps, a.warmup)
             line = result_line(other, g, a.steps, a.warmup, None)
+            line["cold"] = bench_gpu_cold(other, a.steps, a.warmup)
             if a.compare_unfused:
                 line["unfused_library"] = bench_unfused_library(other, a.steps, a.warmup)
             print(json.dumps(line), file=sys.stderr, flush=True)
