@@ -30,10 +30,18 @@ KERNEL_SOURCES = ("dense_gemm_elementwise_amd/csrc/gemm_epi_kernels.hpp", "dense
 
 
 def kernel_source_hash():
+    """sha256 of the kernel sources with comments and blank lines removed, so
+    that a change of wording does not invalidate counters taken on the same
+    code."""
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+        h.update("\n".join(lines).encode())
     return h.hexdigest()
 
 

@@ -11,28 +11,28 @@
 //
 // Design for gfx950 (not a translation of the pages' Blackwell kernels):
 //  * WGM x WGN wave64s per workgroup; each wave owns a (BM/WGM) x (BN/WGN)
-//    accumulator tile built from v_mfma_f32_32x32x16_f16 (MI = 32) or
-//    v_mfma_f32_16x16x32_f16 (MI = 16) blocks.  With two waves per SIMD
+//    accumulator tile built from v_mfma_f32_16x16x32_f16 (MI = 16) or
+//    v_mfma_f32_32x32x16_f16 (MI = 32) blocks.  With two waves per SIMD
 //    (8 waves), one wave's MFMAs run while the other waits on LDS or a
-//    barrier; with 4 waves of 128 x 128 each wave reuses every operand it
-//    reads from LDS over more MFMAs.
+//    barrier.
 //  * K is walked in steps of BK through a ring of NSTAGES LDS stages, so the
 //    loads of a stage are issued NSTAGES-1 stages before it is used.  The
 //    fast path fills LDS with buffer_load_dwordx4 ... lds (global -> LDS
-//    without VGPRs); lanes whose 16-byte chunk lies outside the matrix get an
-//    out-of-range offset, which the buffer unit turns into zeros, so M, N and
-//    K tails need no extra code in the inner loop.
+//    without VGPRs).  Each thread's DMA offsets are fixed; a stage only moves
+//    the buffer descriptor's base, and lanes outside the matrix get an
+//    out-of-range offset that the buffer unit turns into zeros, so M, N and K
+//    tails cost no extra code in the inner loop.
 //  * A tiles are stored row-major (BK*2 bytes per row); B tiles k-row-major.
 //    The 16-byte chunks of each row are XOR-swizzled so that the MFMA operand
 //    reads (ds_read_b128 for A, ds_read_b64_tr_b16 for B, which transposes
 //    the N-contiguous B rows into the K-contiguous operand on the fly) hit
 //    distinct banks.
-//  * The epilogue moves each wave's accumulator through LDS, one 32-row block
-//    at a time, so that every lane owns 4 consecutive columns; C / X are
-//    prefetched into registers one block ahead and D / Aux written with
+//  * The epilogue moves each wave's accumulator through LDS, one MFMA row
+//    block at a time, so that every lane owns 4 consecutive columns; C / X
+//    are prefetched into registers one block ahead and D / Aux written with
 //    8-byte vectors, predicated at the M / N edges.  (Reading C / X straight
-//    in the MFMA register layout would touch 32 rows per instruction; the
-//    row-contiguous layout keeps each instruction on 4 rows.)
+//    in the MFMA register layout would touch 16 or 32 rows per instruction;
+//    the row-contiguous layout keeps each instruction on 4 rows.)
 //  * Workgroup ids are remapped so that the tiles one XCD runs together are
 //    neighbours (they share A row panels and B column panels in that XCD's
 //    L2).
