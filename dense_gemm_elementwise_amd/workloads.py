@@ -4,7 +4,7 @@ This module only draws inputs: it holds none of the method's arithmetic (no
 product, no epilogue, no rounding of results).  Both the HIP path and the CPU
 oracle are fed from it, so a workload's inputs are bit-identical on both
 sides.  All tensors are packed row-major host arrays of float16:
-A (L,M,K), B (L,K,N), C and X (L,M,N).
+A (L,M,K), B (L,K,N), C and X (L,M,N), row_bias (N,) and col_bias (M,).
 
 The draws follow the constructions on the pages:
   - "randint_pm2": integers uniform in {-2..2}, drawn A, then B, then C from
@@ -18,6 +18,10 @@ The draws follow the constructions on the pages:
   - "normal": N(0, 1) drawn in float32 from a generator seeded 2025, then
     rounded to float16, in the order A, B, C, X (the pages do not show how the
     Alpha-Beta example fills its tensors).
+For the bias kind (tutorial cell [9]) C is not drawn; the row bias (N,) and
+the column bias (M,) follow A and B from the same generator: N(0, 1) rounded
+to float16 as the page draws them (torch.randn in float16), or integers in
+{-3..3} for the integer test recipe, so that those cases stay exact.
 """
 from dataclasses import dataclass, field
 from typing import Dict, Optional
@@ -25,9 +29,13 @@ from typing import Dict, Optional
 import numpy as np
 import torch
 
-KINDS = ("LINCOMB", "AUX_SCALE", "LINCOMB_X_ACC", "RELU", "SQUARE", "RELU_SQUARE")
-HAS_AUX = ("AUX_SCALE", "LINCOMB_X_ACC", "SQUARE", "RELU_SQUARE")
+KINDS = ("LINCOMB", "AUX_SCALE", "LINCOMB_X_ACC", "RELU", "SQUARE", "RELU_SQUARE", "RELU_AUX_STORE",
+         "RELU_SCALE_ACC", "BIAS_ROW_COL")
+HAS_AUX = ("AUX_SCALE", "LINCOMB_X_ACC", "SQUARE", "RELU_SQUARE", "RELU_AUX_STORE", "RELU_SCALE_ACC")
 READS_X = ("LINCOMB_X_ACC",)
+READS_C = tuple(k for k in KINDS if k != "BIAS_ROW_COL")
+READS_BIAS = ("BIAS_ROW_COL",)
+HAS_ACC = ("RELU_SCALE_ACC",)  # also writes the fp32 accumulator
 
 
 @dataclass(frozen=True)
@@ -53,20 +61,23 @@ class Workload:
 
     @property
     def epilogue_bytes(self) -> int:
-        """Epilogue traffic of one call: C (and X) read once, D (and the second output) written once."""
-        n_in_mn = 1 + (1 if self.kind in READS_X else 0)
-        n_out = 1 + (1 if self.kind in HAS_AUX else 0)
-        return 2 * (n_in_mn + n_out) * self.L * self.M * self.N
+        """Epilogue traffic of one call: C / X / the biases read once, D, the second output and the
+        fp32 accumulator (if the kind has them) written once."""
+        return epilogue_bytes(self.kind, self.L, self.M, self.N)
 
     @property
     def hbm_bytes(self) -> int:
         """Compulsory HBM traffic: every operand read once, every output written once."""
-        n_in_mn = 1 + (1 if self.kind in READS_X else 0)
-        n_out = 1 + (1 if self.kind in HAS_AUX else 0)
-        return 2 * (self.L * self.M * self.K + self.L * self.K * self.N + (n_in_mn + n_out) * self.L * self.M * self.N)
+        return 2 * (self.L * self.M * self.K + self.L * self.K * self.N) + self.epilogue_bytes
 
 
-# The five workloads, smallest first.  The third is the pages' "run a bigger
+def epilogue_bytes(kind: str, L: int, M: int, N: int) -> int:
+    halves_mn = ((kind in READS_C) + (kind in READS_X) + 1 + (kind in HAS_AUX) + 2 * (kind in HAS_ACC))
+    bias = (M + N) if kind in READS_BIAS else 0
+    return 2 * (halves_mn * L * M * N + bias)
+
+
+# The workloads.  The first five, smallest first: the third is the pages' "run a bigger
 # problem" case (not tile multiples), the fourth is the Alpha-Beta example's
 # command line, the fifth is the batched multi-output case.
 WORKLOADS: Dict[str, Workload] = {w.name: w for w in (
@@ -76,47 +87,68 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in (
     Workload("x_acc_8192", 1, 8192, 8192, 8192, "LINCOMB_X_ACC", 2.0, 1.0, 3.0, "normal", 2025, False),
     Workload("relu_square_16x2048x2048x1024", 16, 2048, 2048, 1024, "RELU_SQUARE", 1.0, 1.0, 0.0, "normal", 2025,
              False),
+    # the tutorial's further epilogues, on its own shape and draws (cells [2], [6], [7], [9])
+    Workload("relu_aux_store_1024", 1, 1024, 1024, 1024, "RELU_AUX_STORE", 3.0, 2.0, 0.0, "randint_pm2", 2025, True),
+    Workload("relu_scale_acc_1024", 1, 1024, 1024, 1024, "RELU_SCALE_ACC", 1.0, 2.0, 0.5, "randint_pm2", 2025, True),
+    Workload("bias_row_col_1024", 1, 1024, 1024, 1024, "BIAS_ROW_COL", 1.0, 0.0, 0.0, "randint_pm2", 2025, False),
+    # the heaviest and the lightest of those epilogues at the headline size
+    Workload("relu_scale_acc_8192", 1, 8192, 8192, 8192, "RELU_SCALE_ACC", 1.0, 2.0, 0.5, "normal", 2025, False),
+    Workload("bias_row_col_8192", 1, 8192, 8192, 8192, "BIAS_ROW_COL", 1.0, 0.0, 0.0, "normal", 2025, False),
 )}
 
 # The workload the headline throughput is quoted on.
 HEADLINE = "x_acc_8192"
 
 
-def _shapes(L, M, N, K, with_x):
-    shapes = [(L, M, K), (L, K, N), (L, M, N)]
-    if with_x:
+def draw(init: str, seed: int, L: int, M: int, N: int, K: int, with_x: bool, kind: str = "LINCOMB"):
+    """Draws the inputs of one problem with the named recipe, in the order
+    A, B, then C (and X) or, for the bias kind, the row and column biases.
+    Returns a list of float16 numpy arrays in that order."""
+    bias = kind in READS_BIAS
+    shapes = [(L, M, K), (L, K, N)]
+    if not bias:
         shapes.append((L, M, N))
-    return shapes
-
-
-def draw(init: str, seed: int, L: int, M: int, N: int, K: int, with_x: bool):
-    """Draws A, B, C (and X) as float16 numpy arrays with the named recipe."""
-    shapes = _shapes(L, M, N, K, with_x)
+        if with_x:
+            shapes.append((L, M, N))
     if init == "randint_pm2":
         g = torch.Generator().manual_seed(seed)
         out = [torch.randint(-2, 3, s, generator=g, dtype=torch.float16).numpy() for s in shapes]
+        if bias:
+            out += [torch.randn(s, generator=g, dtype=torch.float16).numpy() for s in ((N,), (M,))]
     elif init == "ceil_uniform_pm4":
         rs = np.random.RandomState(seed)
         out = [np.ceil(rs.uniform(-4, 4, size=s).astype(np.float16)) for s in shapes]
+        if bias:
+            out += [np.ceil(rs.uniform(-4, 4, size=s).astype(np.float16)) for s in ((N,), (M,))]
     elif init == "normal":
         g = torch.Generator().manual_seed(seed)
         out = [torch.randn(s, generator=g, dtype=torch.float32).to(torch.float16).numpy() for s in shapes]
+        if bias:
+            out += [torch.randn(s, generator=g, dtype=torch.float32).to(torch.float16).numpy() for s in ((N,), (M,))]
     elif init == "small_int":
         # integers uniform in {-3..3}; used by the tail and kind sweeps
         g = torch.Generator().manual_seed(seed)
         out = [torch.randint(-3, 4, s, generator=g, dtype=torch.float16).numpy() for s in shapes]
+        if bias:
+            out += [torch.randint(-3, 4, s, generator=g, dtype=torch.float16).numpy() for s in ((N,), (M,))]
     else:
         raise ValueError(f"unknown init recipe {init!r}")
     return [np.ascontiguousarray(a) for a in out]
 
 
+def _as_dict(arrs, kind):
+    if kind in READS_BIAS:
+        return {"A": arrs[0], "B": arrs[1], "C": None, "X": None, "row_bias": arrs[2], "col_bias": arrs[3]}
+    return {"A": arrs[0], "B": arrs[1], "C": arrs[2], "X": arrs[3] if len(arrs) > 3 else None,
+            "row_bias": None, "col_bias": None}
+
+
 def make_inputs(w: Workload) -> Dict[str, Optional[np.ndarray]]:
-    """Inputs of a named workload: dict with A, B, C and X (None if unused)."""
-    arrs = draw(w.init, w.seed, w.L, w.M, w.N, w.K, w.kind in READS_X)
-    return {"A": arrs[0], "B": arrs[1], "C": arrs[2], "X": arrs[3] if len(arrs) > 3 else None}
+    """Inputs of a named workload: dict with A, B, C, X, row_bias, col_bias
+    (None where the kind does not read them)."""
+    return _as_dict(draw(w.init, w.seed, w.L, w.M, w.N, w.K, w.kind in READS_X, w.kind), w.kind)
 
 
 def make_problem(L, M, N, K, kind, init="small_int", seed=0):
-    """Inputs for an arbitrary shape (tests): dict with A, B, C and X (None if unused)."""
-    arrs = draw(init, seed, L, M, N, K, kind in READS_X)
-    return {"A": arrs[0], "B": arrs[1], "C": arrs[2], "X": arrs[3] if len(arrs) > 3 else None}
+    """Inputs for an arbitrary shape (tests), as make_inputs returns them."""
+    return _as_dict(draw(init, seed, L, M, N, K, kind in READS_X, kind), kind)

@@ -26,9 +26,15 @@ KINDS = {
     "RELU": 3,
     "SQUARE": 4,
     "RELU_SQUARE": 5,
+    "RELU_AUX_STORE": 6,
+    "RELU_SCALE_ACC": 7,
+    "BIAS_ROW_COL": 8,
 }
-HAS_AUX = {"AUX_SCALE", "LINCOMB_X_ACC", "SQUARE", "RELU_SQUARE"}
+HAS_AUX = {"AUX_SCALE", "LINCOMB_X_ACC", "SQUARE", "RELU_SQUARE", "RELU_AUX_STORE", "RELU_SCALE_ACC"}
 READS_X = {"LINCOMB_X_ACC"}
+READS_C = set(KINDS) - {"BIAS_ROW_COL"}
+READS_BIAS = {"BIAS_ROW_COL"}
+HAS_ACC = {"RELU_SCALE_ACC"}
 
 _lib = None
 
@@ -49,6 +55,13 @@ def lib():
     L.oracle_gemm_epi.restype = ctypes.c_int
     L.oracle_gemm_epi.argtypes = [i64, i64, i64, i64, u16p, u16p, u16p, u16p, f32p, ctypes.c_int,
                                   u16p, u16p, f64p, f64p]
+    L.oracle_gemm_epi_ext.restype = ctypes.c_int
+    L.oracle_gemm_epi_ext.argtypes = [i64, i64, i64, i64, u16p, u16p, u16p, u16p, u16p, u16p, f32p, ctypes.c_int,
+                                      u16p, u16p, f32p, f64p, f64p, f64p]
+    L.oracle_gemm_epi_points_ext.restype = ctypes.c_int
+    L.oracle_gemm_epi_points_ext.argtypes = [i64, i64, i64, i64, u16p, u16p, u16p, u16p, u16p, u16p, f32p,
+                                             ctypes.c_int, i64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             u16p, u16p, f32p, f64p, f64p, f64p]
     L.oracle_gemm_epi_points.restype = ctypes.c_int
     L.oracle_gemm_epi_points.argtypes = [i64, i64, i64, i64, u16p, u16p, u16p, u16p, f32p, ctypes.c_int,
                                          i64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -60,6 +73,9 @@ def lib():
     L.oracle_rounding_mode_is_nearest.restype = ctypes.c_int
     L.oracle_kind_has_aux.restype = ctypes.c_int
     L.oracle_kind_reads_x.restype = ctypes.c_int
+    L.oracle_kind_reads_c.restype = ctypes.c_int
+    L.oracle_kind_reads_bias.restype = ctypes.c_int
+    L.oracle_kind_has_acc_out.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -93,52 +109,76 @@ def f16_encode(x):
 
 
 def _shapes(A, B, C):
-    if A.ndim != 3 or B.ndim != 3 or C.ndim != 3:
+    if A.ndim != 3 or B.ndim != 3 or (C is not None and C.ndim != 3):
         raise ValueError("A, B, C must be (L,M,K), (L,K,N), (L,M,N)")
     L, M, K = A.shape
-    if B.shape[0] != L or B.shape[1] != K or C.shape != (L, M, B.shape[2]):
-        raise ValueError(f"shape mismatch A{A.shape} B{B.shape} C{C.shape}")
+    if B.shape[0] != L or B.shape[1] != K or (C is not None and C.shape != (L, M, B.shape[2])):
+        raise ValueError(f"shape mismatch A{A.shape} B{B.shape} C{None if C is None else C.shape}")
     return L, M, B.shape[2], K
 
 
-def gemm_epi(A, B, C, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, want64=False):
+def _biases(row_bias, col_bias, M, N):
+    rb = _bits(np.asarray(row_bias).reshape(-1)) if row_bias is not None else None
+    cb = _bits(np.asarray(col_bias).reshape(-1)) if col_bias is not None else None
+    if rb is not None and rb.size != N:
+        raise ValueError(f"row_bias must have N = {N} entries")
+    if cb is not None and cb.size != M:
+        raise ValueError(f"col_bias must have M = {M} entries")
+    return rb, cb
+
+
+def gemm_epi(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, row_bias=None, col_bias=None,
+             want64=False):
     """Full fused GEMM + epilogue on host arrays.
 
-    A (L,M,K), B (L,K,N), C and X (L,M,N): float16 arrays (or uint16 bits).
-    Returns a dict with D (and Aux for kinds with a second output) as float16
-    arrays, plus D64 / Aux64 (unrounded float64) when want64 is set.
+    A (L,M,K), B (L,K,N), C and X (L,M,N): float16 arrays (or uint16 bits);
+    row_bias (N,) and col_bias (M,) or (M, 1) for BIAS_ROW_COL.  Returns a dict
+    with D (and Aux for kinds with a second output) as float16 arrays, Acc
+    (float32) for kinds that return the accumulator, plus D64 / Aux64 / Acc64
+    (unrounded float64) when want64 is set.
     """
-    A, B, C = _bits(A), _bits(B), _bits(C)
+    A, B = _bits(A), _bits(B)
+    C = _bits(C) if C is not None else None
     X = _bits(X) if X is not None else None
     L, M, N, K = _shapes(A, B, C)
+    rb, cb = _biases(row_bias, col_bias, M, N)
     sc = np.array([alpha, beta, s3], np.float32)
     D = np.empty((L, M, N), np.uint16)
     Aux = np.empty((L, M, N), np.uint16) if kind in HAS_AUX else None
+    Acc = np.empty((L, M, N), np.float32) if kind in HAS_ACC else None
     D64 = np.empty((L, M, N), np.float64) if want64 else None
     Aux64 = np.empty((L, M, N), np.float64) if (want64 and kind in HAS_AUX) else None
-    rc = lib().oracle_gemm_epi(L, M, N, K, _ptr(A), _ptr(B), _ptr(C), _ptr(X), _ptr(sc), KINDS[kind],
-                               _ptr(D), _ptr(Aux), _ptr(D64), _ptr(Aux64))
+    Acc64 = np.empty((L, M, N), np.float64) if want64 else None
+    rc = lib().oracle_gemm_epi_ext(L, M, N, K, _ptr(A), _ptr(B), _ptr(C), _ptr(X), _ptr(rb), _ptr(cb), _ptr(sc),
+                                   KINDS[kind], _ptr(D), _ptr(Aux), _ptr(Acc), _ptr(D64), _ptr(Aux64), _ptr(Acc64))
     if rc:
-        raise ValueError(f"oracle_gemm_epi rejected the call (code {rc})")
+        raise ValueError(f"oracle_gemm_epi_ext rejected the call (code {rc})")
     out = {"D": D.view(np.float16)}
     if Aux is not None:
         out["Aux"] = Aux.view(np.float16)
+    if Acc is not None:
+        out["Acc"] = Acc
     if want64:
         out["D64"] = D64
+        out["Acc64"] = Acc64
         if Aux64 is not None:
             out["Aux64"] = Aux64
     return out
 
 
-def gemm_epi_points(A, B, C, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, l, i, j):
+def gemm_epi_points(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, row_bias=None, col_bias=None,
+                    l, i, j):
     """The same definition at sampled output points (l[p], i[p], j[p]).
 
     Returns a dict of 1-D arrays indexed by p: D, Aux (if the kind has one) as
-    float16, and D64 / Aux64 unrounded.
+    float16, Acc (float32, if the kind returns it), and D64 / Aux64 / Acc64
+    unrounded.
     """
-    A, B, C = _bits(A), _bits(B), _bits(C)
+    A, B = _bits(A), _bits(B)
+    C = _bits(C) if C is not None else None
     X = _bits(X) if X is not None else None
     L, M, N, K = _shapes(A, B, C)
+    rb, cb = _biases(row_bias, col_bias, M, N)
     l = np.ascontiguousarray(l, np.int64)
     i = np.ascontiguousarray(i, np.int64)
     j = np.ascontiguousarray(j, np.int64)
@@ -148,14 +188,19 @@ def gemm_epi_points(A, B, C, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, l, i,
     sc = np.array([alpha, beta, s3], np.float32)
     D = np.empty(n, np.uint16)
     D64 = np.empty(n, np.float64)
+    Acc64 = np.empty(n, np.float64)
     Aux = np.empty(n, np.uint16) if kind in HAS_AUX else None
     Aux64 = np.empty(n, np.float64) if kind in HAS_AUX else None
-    rc = lib().oracle_gemm_epi_points(L, M, N, K, _ptr(A), _ptr(B), _ptr(C), _ptr(X), _ptr(sc), KINDS[kind],
-                                      n, _ptr(l), _ptr(i), _ptr(j), _ptr(D), _ptr(Aux), _ptr(D64), _ptr(Aux64))
+    Acc = np.empty(n, np.float32) if kind in HAS_ACC else None
+    rc = lib().oracle_gemm_epi_points_ext(L, M, N, K, _ptr(A), _ptr(B), _ptr(C), _ptr(X), _ptr(rb), _ptr(cb),
+                                          _ptr(sc), KINDS[kind], n, _ptr(l), _ptr(i), _ptr(j), _ptr(D), _ptr(Aux),
+                                          _ptr(Acc), _ptr(D64), _ptr(Aux64), _ptr(Acc64))
     if rc:
-        raise ValueError(f"oracle_gemm_epi_points rejected the call (code {rc})")
-    out = {"D": D.view(np.float16), "D64": D64}
+        raise ValueError(f"oracle_gemm_epi_points_ext rejected the call (code {rc})")
+    out = {"D": D.view(np.float16), "D64": D64, "Acc64": Acc64}
     if Aux is not None:
         out["Aux"] = Aux.view(np.float16)
         out["Aux64"] = Aux64
+    if Acc is not None:
+        out["Acc"] = Acc
     return out

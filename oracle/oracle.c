@@ -30,7 +30,18 @@
  *                     form is alpha = beta = 1)
  *       RELU_SQUARE   D = ReLU(alpha*acc + beta*C) ; E = D*D
  *                     ("Activation Functions" followed by "Multiple Outputs")
- *     The second output (Aux, Y or E) goes to the Aux buffer.
+ *       RELU_AUX_STORE F = alpha*acc + beta*C ; D = ReLU(F)
+ *                     (tutorial cell [6], relu_aux_store, whose beta is the
+ *                     constant 2.0; cell [8] is the same with alpha = 1,
+ *                     beta = 0.5)
+ *       RELU_SCALE_ACC F = ReLU(alpha*acc + beta*C) ; D = s*F ; and the
+ *                     accumulator itself as an fp32 output
+ *                     (tutorial cell [7], relu_scale_return_acc)
+ *       BIAS_ROW_COL  D = (alpha*acc + row_bias[j]) + col_bias[i]
+ *                     (tutorial cell [9], broadcast_epilogue: row_bias has
+ *                     shape (N,), col_bias (M, 1); C is not read)
+ *     The second output (Aux, Y, E or F) goes to the Aux buffer; the biases
+ *     are shared by every batch entry.
  *
  * Precision (readings where the pages are silent, listed in the design doc):
  *   - fp16 inputs are decoded exactly to double by decode_f16() below;
@@ -40,7 +51,8 @@
  *   - the epilogue runs in double from the unrounded acc (Aux, D feed the next
  *     operation unrounded, as the epilogue DAG's SSA values do);
  *   - every output is rounded once, double -> fp16, round to nearest, ties to
- *     even, overflow to +-inf (encode_f16() below);
+ *     even, overflow to +-inf (encode_f16() below); the fp32 accumulator
+ *     output is the exact sum rounded once to fp32 (nearest, ties to even);
  *   - ReLU(t) = t > 0 ? t : +0.0 (the "where(d > 0, d, 0)" form).
  * Build with -ffp-contract=off so that no multiply-add is fused.
  */
@@ -56,6 +68,9 @@
 #define ORACLE_RELU 3
 #define ORACLE_SQUARE 4
 #define ORACLE_RELU_SQUARE 5
+#define ORACLE_RELU_AUX_STORE 6
+#define ORACLE_RELU_SCALE_ACC 7
+#define ORACLE_BIAS_ROW_COL 8
 
 /* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction
  * bits.  Exponent 0 holds zero and the subnormals f * 2^-24; exponent 31 holds
@@ -104,21 +119,25 @@ uint16_t oracle_f16_encode(double x)
     return (uint16_t)(sign | (uint16_t)(E << 10) | (uint16_t)((int)q - 1024));
 }
 
-int oracle_kind_valid(int kind) { return kind >= ORACLE_LINCOMB && kind <= ORACLE_RELU_SQUARE; }
+int oracle_kind_valid(int kind) { return kind >= ORACLE_LINCOMB && kind <= ORACLE_BIAS_ROW_COL; }
 int oracle_kind_has_aux(int kind)
 {
     return kind == ORACLE_AUX_SCALE || kind == ORACLE_LINCOMB_X_ACC || kind == ORACLE_SQUARE ||
-           kind == ORACLE_RELU_SQUARE;
+           kind == ORACLE_RELU_SQUARE || kind == ORACLE_RELU_AUX_STORE || kind == ORACLE_RELU_SCALE_ACC;
 }
 int oracle_kind_reads_x(int kind) { return kind == ORACLE_LINCOMB_X_ACC; }
+int oracle_kind_reads_c(int kind) { return kind != ORACLE_BIAS_ROW_COL; }
+int oracle_kind_reads_bias(int kind) { return kind == ORACLE_BIAS_ROW_COL; }
+int oracle_kind_has_acc_out(int kind) { return kind == ORACLE_RELU_SCALE_ACC; }
 
 static double relu(double t) { return t > 0.0 ? t : 0.0; }
 
 /* The epilogue of one element, in double, from the unrounded accumulator.
- * Writes the unrounded first output to *d and the unrounded second output (if
- * the kind has one) to *aux. */
-static void epilogue(int kind, double acc, double c, double x, double alpha, double beta, double s,
-                     double *d, double *aux)
+ * rb / cb are the row-broadcast bias of the element's column and the
+ * column-broadcast bias of its row.  Writes the unrounded first output to *d
+ * and the unrounded second output (if the kind has one) to *aux. */
+static void epilogue(int kind, double acc, double c, double x, double rb, double cb, double alpha, double beta,
+                     double s, double *d, double *aux)
 {
     double t;
     switch (kind) {
@@ -147,23 +166,37 @@ static void epilogue(int kind, double acc, double c, double x, double alpha, dou
         *d = t;
         *aux = t * t;
         break;
+    case ORACLE_RELU_AUX_STORE:
+        t = alpha * acc + beta * c;
+        *aux = t;
+        *d = relu(t);
+        break;
+    case ORACLE_RELU_SCALE_ACC:
+        t = relu(alpha * acc + beta * c);
+        *aux = t;
+        *d = s * t;
+        break;
+    case ORACLE_BIAS_ROW_COL:
+        *d = (alpha * acc + rb) + cb;
+        break;
     }
 }
 
-/* Checks shared by both entry points.  Returns 0 when the call is valid. */
+/* Checks shared by the entry points.  Returns 0 when the call is valid. */
 static int check_args(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
-                      const uint16_t *C, const uint16_t *X, const float *scalars, int kind, uint16_t *D,
-                      uint16_t *Aux)
+                      const uint16_t *C, const uint16_t *X, const uint16_t *RB, const uint16_t *CB,
+                      const float *scalars, int kind, uint16_t *D, uint16_t *Aux, float *Acc)
 {
     if (L < 1 || M < 1 || N < 1 || K < 1)
         return 1;
-    if (!A || !B || !C || !scalars)
+    if (!A || !B || !scalars)
         return 2;
     if (!oracle_kind_valid(kind))
         return 4;
-    if (oracle_kind_reads_x(kind) && !X)
+    if ((oracle_kind_reads_c(kind) && !C) || (oracle_kind_reads_x(kind) && !X) ||
+        (oracle_kind_reads_bias(kind) && (!RB || !CB)))
         return 2;
-    if (!D || (oracle_kind_has_aux(kind) && !Aux))
+    if (!D || (oracle_kind_has_aux(kind) && !Aux) || (oracle_kind_has_acc_out(kind) && !Acc))
         return 3;
     return 0;
 }
@@ -171,19 +204,22 @@ static int check_args(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t
 /*
  * Full product.  Host arrays, packed row-major:
  *   A[l][i][k] at (l*M + i)*K + k, B[l][k][j] at (l*K + k)*N + j,
- *   C, X, D, Aux [l][i][j] at (l*M + i)*N + j.
- * scalars = {alpha, beta, s} with s = extra_scalar (AUX_SCALE) or x_factor
- * (LINCOMB_X_ACC); unused otherwise.  X may be NULL unless the kind reads it;
- * Aux may be NULL unless the kind writes it.  D64 / Aux64, when not NULL,
- * receive the unrounded double outputs.  Returns 0, or a nonzero code for
+ *   C, X, D, Aux, Acc [l][i][j] at (l*M + i)*N + j,
+ *   RB[j] (N entries), CB[i] (M entries), shared by every batch entry.
+ * scalars = {alpha, beta, s} with s = extra_scalar (AUX_SCALE), x_factor
+ * (LINCOMB_X_ACC) or scale (RELU_SCALE_ACC); unused otherwise.  Inputs a kind
+ * does not read and outputs it does not write may be NULL.  D64 / Aux64 /
+ * Acc64, when not NULL, receive the unrounded double outputs (Acc64: the
+ * exact accumulator, for every kind).  Returns 0, or a nonzero code for
  * invalid arguments.  OpenMP splits the rows; each element's sum is the same
  * whatever the thread count.
  */
-int oracle_gemm_epi(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
-                    const uint16_t *C, const uint16_t *X, const float *scalars, int kind, uint16_t *D,
-                    uint16_t *Aux, double *D64, double *Aux64)
+int oracle_gemm_epi_ext(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
+                        const uint16_t *C, const uint16_t *X, const uint16_t *RB, const uint16_t *CB,
+                        const float *scalars, int kind, uint16_t *D, uint16_t *Aux, float *Acc, double *D64,
+                        double *Aux64, double *Acc64)
 {
-    int rc = check_args(L, M, N, K, A, B, C, X, scalars, kind, D, Aux);
+    int rc = check_args(L, M, N, K, A, B, C, X, RB, CB, scalars, kind, D, Aux, Acc);
     if (rc)
         return rc;
     const double alpha = scalars[0], beta = scalars[1], s = scalars[2];
@@ -216,11 +252,13 @@ int oracle_gemm_epi(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *
                         acc[j] = acc[j] + a * brow[j];
                 }
                 const int64_t row = (l * M + i) * N;
+                const double cb = oracle_kind_reads_bias(kind) ? oracle_f16_decode(CB[i]) : 0.0;
                 for (int64_t j = 0; j < N; j++) {
-                    double c = oracle_f16_decode(C[row + j]);
+                    double c = oracle_kind_reads_c(kind) ? oracle_f16_decode(C[row + j]) : 0.0;
                     double x = oracle_kind_reads_x(kind) ? oracle_f16_decode(X[row + j]) : 0.0;
+                    double rb = oracle_kind_reads_bias(kind) ? oracle_f16_decode(RB[j]) : 0.0;
                     double d = 0.0, aux = 0.0;
-                    epilogue(kind, acc[j], c, x, alpha, beta, s, &d, &aux);
+                    epilogue(kind, acc[j], c, x, rb, cb, alpha, beta, s, &d, &aux);
                     D[row + j] = oracle_f16_encode(d);
                     if (D64)
                         D64[row + j] = d;
@@ -229,6 +267,10 @@ int oracle_gemm_epi(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *
                         if (Aux64)
                             Aux64[row + j] = aux;
                     }
+                    if (oracle_kind_has_acc_out(kind))
+                        Acc[row + j] = (float)acc[j]; /* one rounding, nearest-even */
+                    if (Acc64)
+                        Acc64[row + j] = acc[j];
                 }
             }
             free(acc);
@@ -242,18 +284,31 @@ int oracle_gemm_epi(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *
     return 0;
 }
 
+/* The entry point without bias inputs or accumulator output (kinds 0-6). */
+int oracle_gemm_epi(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
+                    const uint16_t *C, const uint16_t *X, const float *scalars, int kind, uint16_t *D,
+                    uint16_t *Aux, double *D64, double *Aux64)
+{
+    return oracle_gemm_epi_ext(L, M, N, K, A, B, C, X, NULL, NULL, scalars, kind, D, Aux, NULL, D64, Aux64,
+                               NULL);
+}
+
 /*
  * The same definition for a list of single output elements (l[p], i[p],
  * j[p]), each summed on its own over k in increasing order, so a full-size
  * problem can be checked at sampled points.  Outputs are indexed by p:
- * D[p], Aux[p], D64[p], Aux64[p] (Aux / D64 / Aux64 may be NULL).
+ * D[p], Aux[p], Acc[p], D64[p], Aux64[p], Acc64[p] (all but D may be NULL).
  */
-int oracle_gemm_epi_points(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
-                           const uint16_t *C, const uint16_t *X, const float *scalars, int kind, int64_t npts,
-                           const int64_t *pl, const int64_t *pi, const int64_t *pj, uint16_t *D, uint16_t *Aux,
-                           double *D64, double *Aux64)
+int oracle_gemm_epi_points_ext(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A,
+                               const uint16_t *B, const uint16_t *C, const uint16_t *X, const uint16_t *RB,
+                               const uint16_t *CB, const float *scalars, int kind, int64_t npts, const int64_t *pl,
+                               const int64_t *pi, const int64_t *pj, uint16_t *D, uint16_t *Aux, float *Acc,
+                               double *D64, double *Aux64, double *Acc64)
 {
-    int rc = check_args(L, M, N, K, A, B, C, X, scalars, kind, D, Aux);
+    /* the per-point outputs are optional: check the inputs with stand-ins */
+    uint16_t dummy16 = 0;
+    float dummy32 = 0.0f;
+    int rc = check_args(L, M, N, K, A, B, C, X, RB, CB, scalars, kind, D, &dummy16, &dummy32);
     if (rc)
         return rc;
     if (npts < 0 || (npts > 0 && (!pl || !pi || !pj)))
@@ -269,10 +324,12 @@ int oracle_gemm_epi_points(int64_t L, int64_t M, int64_t N, int64_t K, const uin
         for (int64_t k = 0; k < K; k++)
             acc = acc + oracle_f16_decode(A[(l * M + i) * K + k]) * oracle_f16_decode(B[(l * K + k) * N + j]);
         const int64_t o = (l * M + i) * N + j;
-        double c = oracle_f16_decode(C[o]);
+        double c = oracle_kind_reads_c(kind) ? oracle_f16_decode(C[o]) : 0.0;
         double x = oracle_kind_reads_x(kind) ? oracle_f16_decode(X[o]) : 0.0;
+        double rb = oracle_kind_reads_bias(kind) ? oracle_f16_decode(RB[j]) : 0.0;
+        double cb = oracle_kind_reads_bias(kind) ? oracle_f16_decode(CB[i]) : 0.0;
         double d = 0.0, aux = 0.0;
-        epilogue(kind, acc, c, x, alpha, beta, s, &d, &aux);
+        epilogue(kind, acc, c, x, rb, cb, alpha, beta, s, &d, &aux);
         D[p] = oracle_f16_encode(d);
         if (D64)
             D64[p] = d;
@@ -282,8 +339,21 @@ int oracle_gemm_epi_points(int64_t L, int64_t M, int64_t N, int64_t K, const uin
             if (Aux64)
                 Aux64[p] = aux;
         }
+        if (Acc && oracle_kind_has_acc_out(kind))
+            Acc[p] = (float)acc;
+        if (Acc64)
+            Acc64[p] = acc;
     }
     return 0;
+}
+
+int oracle_gemm_epi_points(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
+                           const uint16_t *C, const uint16_t *X, const float *scalars, int kind, int64_t npts,
+                           const int64_t *pl, const int64_t *pi, const int64_t *pj, uint16_t *D, uint16_t *Aux,
+                           double *D64, double *Aux64)
+{
+    return oracle_gemm_epi_points_ext(L, M, N, K, A, B, C, X, NULL, NULL, scalars, kind, npts, pl, pi, pj, D,
+                                      Aux, NULL, D64, Aux64, NULL);
 }
 
 /* Bulk codec helpers for the tests: decode n halves / encode n doubles. */

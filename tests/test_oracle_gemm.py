@@ -1,12 +1,13 @@
 """Pins for the oracle's fused GEMM + epilogue (CPU only).
 
 The oracle computes the plain definition epi(A @ B, ...) of the pages:
-my_epilogue (CUTLASS Operator API tutorial "Custom epilogue fusions for
-GEMMs", cell [2]), the Alpha-Beta example's epilogue_operation, ReLU and the
-multi-output pair (CUTLASS "Custom Epilogue Example": "Basic Example",
-"Activation Functions", "Multiple Outputs") and D = alpha*(A@B) + beta*C
-(CUTLASS Python examples article, "Basic GEMM" / "Epilogue").  It is pinned
-here to things other than itself:
+my_epilogue, relu_aux_store, relu_scale_return_acc and the row/column
+broadcast epilogue (CUTLASS Operator API tutorial "Custom epilogue fusions
+for GEMMs", cells [2], [6], [7], [9]), the Alpha-Beta example's
+epilogue_operation, ReLU and the multi-output pair (CUTLASS "Custom Epilogue
+Example": "Basic Example", "Activation Functions", "Multiple Outputs") and
+D = alpha*(A@B) + beta*C (CUTLASS Python examples article, "Basic GEMM" /
+"Epilogue").  It is pinned here to things other than itself:
   - exact rational arithmetic (fractions.Fraction) on tiny problems, with an
     independent nearest-fp16 search, for every epilogue kind;
   - NumPy's float64 matmul, which is exact on small-integer inputs (the
@@ -65,18 +66,44 @@ def frac(x):
     return Fraction(float(x))
 
 
-def exact_outputs(A, B, C, X, kind, alpha, beta, s3):
-    """Exact rational outputs of the definition, per element (lists of lists)."""
+def exact_rne_f32(q: Fraction) -> float:
+    """Nearest float32 (ties to even) of an exact rational, found with integer
+    arithmetic (no intermediate double rounding)."""
+    if q == 0:
+        return 0.0
+    neg = q < 0
+    a = -q if neg else q
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)                    # subnormals share the quantum 2^-149
+    scaled = a / Fraction(2) ** (e - 23)  # in [2^23, 2^24) for normal values
+    n = scaled.numerator // scaled.denominator
+    rem = scaled - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    v = float(Fraction(n) * Fraction(2) ** (e - 23))
+    if v > float(np.finfo(np.float32).max):
+        v = float("inf")
+    return -v if neg else v
+
+
+def exact_outputs(A, B, C, X, kind, alpha, beta, s3, row_bias=None, col_bias=None):
+    """Exact rational outputs of the definition, per element: D, the second
+    output (or None) and the accumulator."""
     L, M, K = A.shape
     N = B.shape[2]
     al, be, s = frac(np.float32(alpha)), frac(np.float32(beta)), frac(np.float32(s3))
     D = np.empty((L, M, N), dtype=object)
     Aux = np.empty((L, M, N), dtype=object)
+    Acc = np.empty((L, M, N), dtype=object)
     for l in range(L):
         for i in range(M):
             for j in range(N):
                 acc = sum((frac(A[l, i, k]) * frac(B[l, k, j]) for k in range(K)), Fraction(0))
-                c = frac(C[l, i, j])
+                c = frac(C[l, i, j]) if C is not None else Fraction(0)
                 t = al * acc + be * c
                 if kind == "LINCOMB":
                     d, aux = t, None
@@ -91,9 +118,17 @@ def exact_outputs(A, B, C, X, kind, alpha, beta, s3):
                 elif kind == "RELU_SQUARE":
                     r = t if t > 0 else Fraction(0)
                     d, aux = r, r * r
+                elif kind == "RELU_AUX_STORE":
+                    d, aux = (t if t > 0 else Fraction(0)), t
+                elif kind == "RELU_SCALE_ACC":
+                    r = t if t > 0 else Fraction(0)
+                    d, aux = s * r, r
+                elif kind == "BIAS_ROW_COL":
+                    d, aux = al * acc + frac(row_bias[j]) + frac(col_bias[i]), None
                 D[l, i, j] = d
                 Aux[l, i, j] = aux
-    return D, Aux
+                Acc[l, i, j] = acc
+    return D, Aux, Acc
 
 
 def bits(a):
@@ -110,7 +145,7 @@ def same_value_bits(got_bits, want_bits):
 
 def run_oracle(p, kind, alpha, beta, s3, want64=False):
     return oracle.gemm_epi(p["A"], p["B"], p["C"], p["X"], kind=kind, alpha=alpha, beta=beta, s3=s3,
-                           want64=want64)
+                           row_bias=p.get("row_bias"), col_bias=p.get("col_bias"), want64=want64)
 
 
 # ---------------------------------------------------------------------------
@@ -129,11 +164,17 @@ def test_exhaustive_2x2x2_over_minus1_0_1():
     X = rng.integers(-3, 4, (Lb, 2, 2)).astype(np.float16)
     # exact products of small integers: the sums are small integers too
     acc = np.einsum("lik,lkj->lij", A.astype(np.int64), B.astype(np.int64))
+    rb = rng.integers(-3, 4, 2).astype(np.float16)   # row bias, one per column
+    cb = rng.integers(-3, 4, 2).astype(np.float16)   # column bias, one per row
     for kind, (alpha, beta, s3) in {"LINCOMB": (1.0, 2.0, 0.0), "AUX_SCALE": (1.0, 2.0, 0.5),
                                     "LINCOMB_X_ACC": (2.0, 1.0, 3.0), "RELU": (1.0, -1.0, 0.0),
-                                    "SQUARE": (-1.0, 1.0, 0.0), "RELU_SQUARE": (3.0, 1.0, 0.0)}.items():
-        out = oracle.gemm_epi(A, B, C, X if kind == "LINCOMB_X_ACC" else None, kind=kind, alpha=alpha,
-                              beta=beta, s3=s3)
+                                    "SQUARE": (-1.0, 1.0, 0.0), "RELU_SQUARE": (3.0, 1.0, 0.0),
+                                    "RELU_AUX_STORE": (3.0, 2.0, 0.0), "RELU_SCALE_ACC": (1.0, -2.0, 0.5),
+                                    "BIAS_ROW_COL": (-1.0, 0.0, 0.0)}.items():
+        bias = kind == "BIAS_ROW_COL"
+        out = oracle.gemm_epi(A, B, None if bias else C, X if kind == "LINCOMB_X_ACC" else None, kind=kind,
+                              alpha=alpha, beta=beta, s3=s3, row_bias=rb if bias else None,
+                              col_bias=cb if bias else None)
         # exact rational epilogue per element, then the independent RNE search
         t = [Fraction(int(a)) * Fraction(alpha) + Fraction(beta) * frac(c)
              for a, c in zip(acc.ravel(), C.ravel())]
@@ -149,14 +190,26 @@ def test_exhaustive_2x2x2_over_minus1_0_1():
             d, aux = [max(v, Fraction(0)) for v in t], None
         elif kind == "SQUARE":
             d, aux = t, [v * v for v in t]
-        else:
+        elif kind == "RELU_SQUARE":
             r = [max(v, Fraction(0)) for v in t]
             d, aux = r, [v * v for v in r]
+        elif kind == "RELU_AUX_STORE":
+            d, aux = [max(v, Fraction(0)) for v in t], t
+        elif kind == "RELU_SCALE_ACC":
+            r = [max(v, Fraction(0)) for v in t]
+            d, aux = [Fraction(s3) * v for v in r], r
+        else:  # BIAS_ROW_COL: element (l, i, j) gets row_bias[j] + col_bias[i]
+            ij = np.indices((Lb, 2, 2)).reshape(3, -1).T
+            d = [Fraction(alpha) * Fraction(int(a)) + frac(rb[j]) + frac(cb[i])
+                 for a, (_, i, j) in zip(acc.ravel(), ij)]
+            aux = None
         want_d = np.array([exact_rne_bits(v) for v in d], np.uint16)
         assert same_value_bits(bits(out["D"]).ravel(), want_d), kind
         if aux is not None:
             want_a = np.array([exact_rne_bits(v) for v in aux], np.uint16)
             assert same_value_bits(bits(out["Aux"]).ravel(), want_a), kind
+        if kind in workloads.HAS_ACC:
+            assert np.array_equal(out["Acc"].ravel(), acc.ravel().astype(np.float32)), kind
 
 
 @pytest.mark.parametrize("shape", [(1, 4, 4, 4), (2, 3, 5, 2), (3, 2, 3, 7), (1, 1, 1, 1), (1, 5, 1, 3)])
@@ -171,7 +224,8 @@ def test_random_fp16_tiny_against_exact(shape, kind):
     p = workloads.make_problem(L, M, N, K, kind, init="normal", seed=sum(shape) * 31 + len(kind))
     alpha, beta, s3 = 1.5, -0.75, 2.0
     out = run_oracle(p, kind, alpha, beta, s3, want64=True)
-    exD, exAux = exact_outputs(p["A"], p["B"], p["C"], p["X"], kind, alpha, beta, s3)
+    exD, exAux, exAcc = exact_outputs(p["A"], p["B"], p["C"], p["X"], kind, alpha, beta, s3,
+                                      p["row_bias"], p["col_bias"])
     A64 = p["A"].astype(np.float64)
     B64 = p["B"].astype(np.float64)
     absprod = np.einsum("lik,lkj->lij", np.abs(A64), np.abs(B64))
@@ -193,6 +247,14 @@ def test_random_fp16_tiny_against_exact(shape, kind):
             hi = exact_rne_bits(e + Fraction(float(bound[idx])))
             if lo == hi == want:
                 assert same_value_bits([got[idx]], [want]), (name, idx)
+    if kind in workloads.HAS_ACC:
+        for idx in np.ndindex(out["Acc"].shape):
+            e = exAcc[idx]
+            b = Fraction(float(bound[idx]))
+            assert abs(Fraction(float(out["Acc64"][idx])) - e) <= b
+            want = exact_rne_f32(e)
+            if exact_rne_f32(e - b) == exact_rne_f32(e + b) == want:
+                assert float(out["Acc"][idx]) == want, idx
 
 
 # ---------------------------------------------------------------------------
@@ -233,7 +295,7 @@ def test_zero_A_closed_forms(kind):
     p["A"] = np.zeros_like(p["A"])
     alpha, beta, s3 = 1.25, -2.0, 0.5
     out = run_oracle(p, kind, alpha, beta, s3)
-    bc = beta * p["C"].astype(np.float64)  # exact: |beta| is a power of two
+    bc = beta * p["C"].astype(np.float64) if p["C"] is not None else None  # exact: |beta| is a power of two
     if kind == "LINCOMB":
         d, aux = bc, None
     elif kind == "AUX_SCALE":
@@ -244,13 +306,24 @@ def test_zero_A_closed_forms(kind):
         d, aux = np.maximum(bc, 0.0), None
     elif kind == "SQUARE":
         d, aux = bc, bc * bc
-    else:
+    elif kind == "RELU_SQUARE":
         d = np.maximum(bc, 0.0)
         aux = d * d
+    elif kind == "RELU_AUX_STORE":
+        d, aux = np.maximum(bc, 0.0), bc
+    elif kind == "RELU_SCALE_ACC":
+        aux = np.maximum(bc, 0.0)
+        d = s3 * aux
+    else:  # BIAS_ROW_COL: row bias of the column plus column bias of the row
+        d = (p["row_bias"].astype(np.float64)[None, None, :] + p["col_bias"].astype(np.float64)[None, :, None]
+             + np.zeros((L, M, N)))
+        aux = None
     # each of these is exact in float64, so NumPy's float16 cast is the single rounding
     assert same_value_bits(bits(out["D"]), d.astype(np.float16).view(np.uint16))
     if aux is not None:
         assert same_value_bits(bits(out["Aux"]), aux.astype(np.float16).view(np.uint16))
+    if kind in workloads.HAS_ACC:
+        assert np.all(out["Acc"] == 0.0)
 
 
 def test_identity_A_gives_B_and_identity_B_gives_A():
@@ -342,12 +415,21 @@ def _golden_cases():
 def test_hand_worked(case):
     def arr(x):
         return np.array([[float(v) for v in row] for row in x], np.float16)[None]
-    A, B, C = arr(case["A"]), arr(case["B"]), arr(case["C"])
+
+    def vec(x):
+        return np.array([float(v) for v in x], np.float16)
+    A, B = arr(case["A"]), arr(case["B"])
+    C = arr(case["C"]) if "C" in case else None
     X = arr(case["X"]) if "X" in case else None
-    out = oracle.gemm_epi(A, B, C, X, kind=case["kind"], alpha=case["alpha"], beta=case["beta"], s3=case["s3"])
+    rb = vec(case["row_bias"]) if "row_bias" in case else None
+    cb = vec(case["col_bias"]) if "col_bias" in case else None
+    out = oracle.gemm_epi(A, B, C, X, kind=case["kind"], alpha=case["alpha"], beta=case["beta"], s3=case["s3"],
+                          row_bias=rb, col_bias=cb)
     assert np.array_equal(out["D"][0].astype(np.float64), arr(case["D"])[0].astype(np.float64))
     if "Aux" in case:
         assert np.array_equal(out["Aux"][0].astype(np.float64), arr(case["Aux"])[0].astype(np.float64))
+    if "Acc" in case:
+        assert np.array_equal(out["Acc"][0].astype(np.float64), arr(case["Acc"])[0].astype(np.float64))
 
 
 # ---------------------------------------------------------------------------
@@ -376,11 +458,14 @@ def test_points_equal_full(kind):
     n = 200
     l, i, j = rng.integers(0, L, n), rng.integers(0, M, n), rng.integers(0, N, n)
     pts = oracle.gemm_epi_points(p["A"], p["B"], p["C"], p["X"], kind=kind, alpha=1.5, beta=0.5, s3=2.0,
-                                 l=l, i=i, j=j)
+                                 row_bias=p["row_bias"], col_bias=p["col_bias"], l=l, i=i, j=j)
     assert np.array_equal(bits(pts["D"]), bits(full["D"][l, i, j]))
     assert np.array_equal(pts["D64"], full["D64"][l, i, j])
+    assert np.array_equal(pts["Acc64"], full["Acc64"][l, i, j])
     if kind in workloads.HAS_AUX:
         assert np.array_equal(bits(pts["Aux"]), bits(full["Aux"][l, i, j]))
+    if kind in workloads.HAS_ACC:
+        assert np.array_equal(pts["Acc"], full["Acc"][l, i, j])
 
 
 def test_rejects_invalid_arguments(oracle_lib):
@@ -397,4 +482,17 @@ def test_rejects_invalid_arguments(oracle_lib):
     assert f(1, 1, 1, 1, P, P, P, P, S, 1, P, None, None, None) == 3
     assert f(1, 1, 1, 1, P, P, P, P, S, 0, None, None, None, None) == 3
     assert f(1, 1, 1, 1, P, P, P, None, S, 0, P, None, None, None) == 0
+    # the entry point without bias inputs / accumulator output rejects the kinds that need them
+    assert f(1, 1, 1, 1, P, P, P, P, S, 8, P, P, None, None) == 2
+    assert f(1, 1, 1, 1, P, P, P, P, S, 7, P, P, None, None) == 3
+    g = oracle_lib.oracle_gemm_epi_ext
+    acc = np.zeros(4, np.float32)
+    Q = acc.ctypes.data
+    assert g(1, 1, 1, 1, P, P, None, None, P, P, S, 8, P, None, None, None, None, None) == 0  # no C
+    assert g(1, 1, 1, 1, P, P, None, None, P, None, S, 8, P, None, None, None, None, None) == 2
+    assert g(1, 1, 1, 1, P, P, None, None, P, P, S, 7, P, P, Q, None, None, None) == 2     # kind 7 reads C
+    assert g(1, 1, 1, 1, P, P, P, None, None, None, S, 7, P, P, None, None, None, None) == 3
+    assert g(1, 1, 1, 1, P, P, P, None, None, None, S, 7, P, P, Q, None, None, None) == 0
+    assert g(1, 1, 1, 1, P, P, P, None, None, None, S, 6, P, None, None, None, None, None) == 3
+    assert g(1, 1, 1, 1, P, P, P, P, P, P, S, 9, P, P, Q, None, None, None) == 4
     del ctypes
