@@ -3,7 +3,7 @@
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload x_acc_8192]
                     [--no-cpu-baseline] [--all] [--compare-unfused]
 
-A step is one call of the fused kernel (one gemm_epi_run) on the workload,
+A step is one call of the fused kernel (one gemm_epi_run_ext) on the workload,
 with every input already resident in HBM.  The timed region is K steps on one
 stream, bracketed by torch.cuda.synchronize(); HIP events recorded on that
 same stream give the average launch duration that the roofline uses.
@@ -58,10 +58,25 @@ def measured_traffic(workload_name):
     return rec.get("traffic_bytes")
 
 
-def _device_args(w, t, D, Aux, stream, ge):
-    return (w.L, w.M, w.N, w.K, t["A"].data_ptr(), t["B"].data_ptr(), t["C"].data_ptr(),
-            t["X"].data_ptr() if t["X"] is not None else None, (w.alpha, w.beta, w.s3), ge.KINDS[w.kind],
-            D.data_ptr(), Aux.data_ptr() if Aux is not None else None, stream.cuda_stream)
+def _device_args(w, t, D, Aux, Acc, stream, ge):
+    """Arguments of gemm_epi_run_ext for workload w on device tensors t."""
+    def ptr(x):
+        return x.data_ptr() if x is not None else None
+    return (w.L, w.M, w.N, w.K, ptr(t["A"]), ptr(t["B"]), ptr(t["C"]), ptr(t["X"]), ptr(t["row_bias"]),
+            ptr(t["col_bias"]), (w.alpha, w.beta, w.s3), ge.KINDS[w.kind], ptr(D), ptr(Aux), ptr(Acc),
+            stream.cuda_stream)
+
+
+def _outputs(w, ge, dev):
+    import torch
+    D = torch.empty((w.L, w.M, w.N), dtype=torch.float16, device=dev)
+    Aux = torch.empty_like(D) if w.kind in ge.HAS_AUX else None
+    Acc = torch.empty((w.L, w.M, w.N), dtype=torch.float32, device=dev) if w.kind in ge.HAS_ACC else None
+    return D, Aux, Acc
+
+
+def _plan(args, ge):
+    return ge.gemm_epi_plan_ext(*args[:10], args[11], args[12], args[13], args[14])
 
 
 def _timed_launches(launch, steps, stream):
@@ -91,16 +106,15 @@ def bench_gpu(w, steps, warmup):
     dev = torch.device("cuda:0")
     p = workloads.make_inputs(w)
     t = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in p.items()}
-    D = torch.empty((w.L, w.M, w.N), dtype=torch.float16, device=dev)
-    Aux = torch.empty_like(D) if w.kind in ge.HAS_AUX else None
+    D, Aux, Acc = _outputs(w, ge, dev)
     stream = torch.cuda.current_stream(dev)
-    args = _device_args(w, t, D, Aux, stream, ge)
+    args = _device_args(w, t, D, Aux, Acc, stream, ge)
     for _ in range(warmup):
-        rc = ge.gemm_epi_run(*args)
+        rc = ge.gemm_epi_run_ext(*args)
         if rc:
             raise RuntimeError(ge.gemm_epi_status_string(rc))
-    wall_ms, ev_ms, stats = _timed_launches(lambda i: ge.gemm_epi_run(*args), steps, stream)
-    rc, plan = ge.gemm_epi_plan(*args[:8], args[9], args[10], args[11])
+    wall_ms, ev_ms, stats = _timed_launches(lambda i: ge.gemm_epi_run_ext(*args), steps, stream)
+    rc, plan = _plan(args, ge)
     return {"ms_per_step": wall_ms, "kernel_ms": ev_ms, "launch_ms": stats, "plan": plan}
 
 
@@ -122,14 +136,12 @@ def bench_gpu_cold(w, steps, warmup):
     copies = []
     for _ in range(sets):
         t = {k: (v.clone() if v is not None else None) for k, v in base.items()}
-        D = torch.empty((w.L, w.M, w.N), dtype=torch.float16, device=dev)
-        Aux = torch.empty_like(D) if w.kind in ge.HAS_AUX else None
-        copies.append((t, D, Aux))
+        copies.append((t,) + _outputs(w, ge, dev))
     stream = torch.cuda.current_stream(dev)
-    arglist = [_device_args(w, t, D, Aux, stream, ge) for (t, D, Aux) in copies]
+    arglist = [_device_args(w, t, D, Aux, Acc, stream, ge) for (t, D, Aux, Acc) in copies]
     for i in range(warmup):
-        ge.gemm_epi_run(*arglist[i % sets])
-    _, ev_ms, stats = _timed_launches(lambda i: ge.gemm_epi_run(*arglist[(i + warmup) % sets]), steps, stream)
+        ge.gemm_epi_run_ext(*arglist[i % sets])
+    _, ev_ms, stats = _timed_launches(lambda i: ge.gemm_epi_run_ext(*arglist[(i + warmup) % sets]), steps, stream)
     del copies
     return {"copies": sets, "kernel_ms": round(ev_ms, 5), "launch_ms": {k: round(v, 5) for k, v in stats.items()},
             "tflops": round(w.flops / (ev_ms * 1e-3) / 1e12, 2),
@@ -149,10 +161,19 @@ def bench_unfused_library(w, steps, warmup):
     p = workloads.make_inputs(w)
     t = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in p.items()}
     A, B, C, X = t["A"], t["B"], t["C"], t["X"]
+    rb, cb = t["row_bias"], t["col_bias"]
     a, b, s3 = w.alpha, w.beta, w.s3
 
     def step():
         Y = torch.matmul(A, B)
+        if w.kind == "BIAS_ROW_COL":
+            return (a * Y + rb[None, None, :] + cb[None, :, None],)
+        if w.kind == "RELU_AUX_STORE":
+            f = a * Y + b * C
+            return (torch.relu(f), f)
+        if w.kind == "RELU_SCALE_ACC":
+            f = torch.relu(a * Y + b * C)
+            return (s3 * f, f, Y.float())
         if w.kind == "LINCOMB":
             return (a * Y + b * C,)
         if w.kind == "AUX_SCALE":

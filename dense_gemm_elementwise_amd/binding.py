@@ -20,9 +20,15 @@ KINDS = {
     "RELU": 3,
     "SQUARE": 4,
     "RELU_SQUARE": 5,
+    "RELU_AUX_STORE": 6,
+    "RELU_SCALE_ACC": 7,
+    "BIAS_ROW_COL": 8,
 }
-HAS_AUX = ("AUX_SCALE", "LINCOMB_X_ACC", "SQUARE", "RELU_SQUARE")
+HAS_AUX = ("AUX_SCALE", "LINCOMB_X_ACC", "SQUARE", "RELU_SQUARE", "RELU_AUX_STORE", "RELU_SCALE_ACC")
 READS_X = ("LINCOMB_X_ACC",)
+READS_C = tuple(k for k in KINDS if k != "BIAS_ROW_COL")
+READS_BIAS = ("BIAS_ROW_COL",)
+HAS_ACC = ("RELU_SCALE_ACC",)
 
 STATUS = {
     0: "GEMM_EPI_OK",
@@ -35,7 +41,8 @@ STATUS = {
 }
 
 # every function include/gemm_epi.h declares
-EXPORTS = ("gemm_epi_run", "gemm_epi_status_string", "gemm_epi_last_hip_error", "gemm_epi_plan")
+EXPORTS = ("gemm_epi_run", "gemm_epi_run_ext", "gemm_epi_status_string", "gemm_epi_last_hip_error",
+           "gemm_epi_plan", "gemm_epi_plan_ext")
 
 
 class GemmEpiError(RuntimeError):
@@ -60,12 +67,18 @@ def lib():
     L.gemm_epi_run.restype = ctypes.c_int
     L.gemm_epi_run.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_float), ctypes.c_int,
                                vp, vp, vp]
+    L.gemm_epi_run_ext.restype = ctypes.c_int
+    L.gemm_epi_run_ext.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_float),
+                                   ctypes.c_int, vp, vp, vp, vp]
     L.gemm_epi_status_string.restype = ctypes.c_char_p
     L.gemm_epi_status_string.argtypes = [ctypes.c_int]
     L.gemm_epi_last_hip_error.restype = ctypes.c_int
     L.gemm_epi_last_hip_error.argtypes = []
     L.gemm_epi_plan.restype = ctypes.c_int
     L.gemm_epi_plan.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, ctypes.c_int, vp, vp, ctypes.POINTER(i64)]
+    L.gemm_epi_plan_ext.restype = ctypes.c_int
+    L.gemm_epi_plan_ext.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
+                                    ctypes.POINTER(i64)]
     _lib = L
     return L
 
@@ -93,6 +106,24 @@ def gemm_epi_run(L, M, N, K, A, B, C, X, scalars, epilogue_kind, D, Aux, stream)
                               stream)
 
 
+def gemm_epi_run_ext(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilogue_kind, D, Aux, acc_out,
+                     stream) -> int:
+    """Pointer-level call of gemm_epi_run_ext (adds the row / column bias
+    inputs and the fp32 accumulator output).  Returns the status code."""
+    sc = (ctypes.c_float * 3)(*[float(v) for v in scalars]) if scalars is not None else None
+    return lib().gemm_epi_run_ext(int(L), int(M), int(N), int(K), A, B, C, X, row_bias, col_bias, sc,
+                                  _kind_id(epilogue_kind), D, Aux, acc_out, stream)
+
+
+def gemm_epi_plan_ext(L, M, N, K, A, B, C, X, row_bias, col_bias, epilogue_kind, D, Aux, acc_out):
+    """Host-only query of the launch configuration for gemm_epi_run_ext."""
+    out = (ctypes.c_int64 * 6)()
+    rc = lib().gemm_epi_plan_ext(int(L), int(M), int(N), int(K), A, B, C, X, row_bias, col_bias,
+                                 _kind_id(epilogue_kind), D, Aux, acc_out, out)
+    keys = ("bm", "bn", "bk", "vec", "workgroups", "threads")
+    return rc, dict(zip(keys, list(out)))
+
+
 def gemm_epi_plan(L, M, N, K, A, B, C, X, epilogue_kind, D, Aux):
     """Host-only query of the launch configuration.  Returns (status, dict)."""
     out = (ctypes.c_int64 * 6)()
@@ -101,12 +132,13 @@ def gemm_epi_plan(L, M, N, K, A, B, C, X, epilogue_kind, D, Aux):
     return rc, dict(zip(keys, list(out)))
 
 
-def _check_tensor(name, t, shape):
+def _check_tensor(name, t, shape, dtype=None):
     import torch
+    dtype = dtype or torch.float16
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.dtype != torch.float16:
-        raise TypeError(f"{name} must be float16, got {t.dtype}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on a GPU device, got {t.device}")
     if not t.is_contiguous():
@@ -115,13 +147,20 @@ def _check_tensor(name, t, shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def run(A, B, C, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, D, Aux=None, stream=None, sync=True):
-    """D (and Aux) <- fused epilogue of A @ B on torch tensors.
+def _ptr(t):
+    return t.data_ptr() if t is not None else None
+
+
+def run(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, D, Aux=None, row_bias=None, col_bias=None,
+        acc_out=None, stream=None, sync=True):
+    """D (and Aux, acc_out) <- fused epilogue of A @ B on torch tensors.
 
     A (L,M,K), B (L,K,N), C, X, D, Aux (L,M,N): contiguous float16 CUDA
-    tensors.  s3 is extra_scalar (AUX_SCALE) or x_factor (LINCOMB_X_ACC).
-    The kernel is queued on `stream` (a torch.cuda.Stream; default: the
-    current stream); with sync=True the call waits for it.
+    tensors; row_bias (N,) and col_bias (M,) or (M, 1) float16 for
+    BIAS_ROW_COL; acc_out (L,M,N) float32 for RELU_SCALE_ACC.  s3 is
+    extra_scalar (AUX_SCALE), x_factor (LINCOMB_X_ACC) or scale
+    (RELU_SCALE_ACC).  The kernel is queued on `stream` (a torch.cuda.Stream;
+    default: the current stream); with sync=True the call waits for it.
     """
     import torch
     if A.dim() != 3 or B.dim() != 3:
@@ -130,26 +169,39 @@ def run(A, B, C, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, D, Aux=None, stre
     N = B.shape[2]
     _check_tensor("A", A, (L, M, K))
     _check_tensor("B", B, (L, K, N))
-    _check_tensor("C", C, (L, M, N))
     _check_tensor("D", D, (L, M, N))
     kname = kind if isinstance(kind, str) else {v: k for k, v in KINDS.items()}[int(kind)]
+    if kname in READS_C:
+        if C is None:
+            raise ValueError(f"{kname} reads C")
+        _check_tensor("C", C, (L, M, N))
     if kname in READS_X:
         if X is None:
             raise ValueError(f"{kname} reads X")
         _check_tensor("X", X, (L, M, N))
+    if kname in READS_BIAS:
+        if row_bias is None or col_bias is None:
+            raise ValueError(f"{kname} reads row_bias (N,) and col_bias (M,)")
+        _check_tensor("row_bias", row_bias.reshape(-1) if row_bias.dim() == 2 else row_bias, (N,))
+        _check_tensor("col_bias", col_bias.reshape(-1) if col_bias.dim() == 2 else col_bias, (M,))
     if kname in HAS_AUX:
         if Aux is None:
             raise ValueError(f"{kname} writes a second output: pass Aux")
         _check_tensor("Aux", Aux, (L, M, N))
-    devs = {t.device for t in (A, B, C, D, X, Aux) if t is not None}
+    if kname in HAS_ACC:
+        if acc_out is None:
+            raise ValueError(f"{kname} writes the fp32 accumulator: pass acc_out")
+        _check_tensor("acc_out", acc_out, (L, M, N), torch.float32)
+    used = [t for t in (A, B, C, D, X, Aux, row_bias, col_bias, acc_out) if t is not None]
+    devs = {t.device for t in used}
     if len(devs) != 1:
         raise ValueError(f"all tensors must be on one device, got {devs}")
     dev = A.device
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
-        rc = gemm_epi_run(L, M, N, K, A.data_ptr(), B.data_ptr(), C.data_ptr(),
-                          X.data_ptr() if X is not None else None, (alpha, beta, s3), KINDS[kname], D.data_ptr(),
-                          Aux.data_ptr() if Aux is not None else None, s.cuda_stream)
+        rc = gemm_epi_run_ext(L, M, N, K, A.data_ptr(), B.data_ptr(), _ptr(C), _ptr(X), _ptr(row_bias),
+                              _ptr(col_bias), (alpha, beta, s3), KINDS[kname], D.data_ptr(), _ptr(Aux),
+                              _ptr(acc_out), s.cuda_stream)
     if rc != 0:
         msg = gemm_epi_status_string(rc)
         if rc == 6:

@@ -75,33 +75,45 @@ TileCfg choose_tile(int64_t L, int64_t M, int64_t N, bool vec)
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-int check_args(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
-               const void *X, int kind, const void *D, const void *Aux)
+// Host-side operand set of one call (the pointers gemm_epi_run_ext takes).
+struct Operands {
+    const void *A, *B, *C, *X, *row_bias, *col_bias;
+    const void *D, *Aux, *acc_out;
+};
+
+int check_args(int64_t L, int64_t M, int64_t N, int64_t K, const Operands &o, int kind)
 {
     if (L < 1 || M < 1 || N < 1 || K < 1) return GEMM_EPI_ERR_SHAPE;
     const int64_t lim = INT32_MAX;
     if (M > lim || N > lim || K > lim) return GEMM_EPI_ERR_SHAPE;
-    // element counts of every tensor must fit int64 (and the grid must fit)
+    // element counts of every tensor must fit int64 (and the grid must fit);
+    // the fp32 accumulator output needs twice the bytes of an fp16 output
     if (L > INT64_MAX / M || L * M > INT64_MAX / K || L * M > INT64_MAX / N || L > INT64_MAX / K ||
-        L * K > INT64_MAX / N)
+        L * K > INT64_MAX / N || L * M * N > INT64_MAX / 4)
         return GEMM_EPI_ERR_SHAPE;
-    if (!A || !B || !C) return GEMM_EPI_ERR_NULL_INPUT;
-    if (kind < GEMM_EPI_LINCOMB || kind > GEMM_EPI_RELU_SQUARE) return GEMM_EPI_ERR_KIND;
-    if (kind_reads_x(kind) && !X) return GEMM_EPI_ERR_NULL_INPUT;
-    if (!D || (kind_has_aux(kind) && !Aux)) return GEMM_EPI_ERR_NULL_OUTPUT;
-    if (!aligned(A, 2) || !aligned(B, 2) || !aligned(C, 2) || (X && !aligned(X, 2)) || !aligned(D, 2) ||
-        (Aux && !aligned(Aux, 2)))
-        return GEMM_EPI_ERR_ALIGN;
+    if (!o.A || !o.B) return GEMM_EPI_ERR_NULL_INPUT;
+    if (kind < GEMM_EPI_LINCOMB || kind > GEMM_EPI_BIAS_ROW_COL) return GEMM_EPI_ERR_KIND;
+    if ((kind_reads_c(kind) && !o.C) || (kind_reads_x(kind) && !o.X) ||
+        (kind_reads_bias(kind) && (!o.row_bias || !o.col_bias)))
+        return GEMM_EPI_ERR_NULL_INPUT;
+    if (!o.D || (kind_has_aux(kind) && !o.Aux) || (kind_has_acc_out(kind) && !o.acc_out))
+        return GEMM_EPI_ERR_NULL_OUTPUT;
+    const void *halves[] = {o.A, o.B, o.C, o.X, o.row_bias, o.col_bias, o.D, o.Aux};
+    for (const void *h : halves)
+        if (h && !aligned(h, 2)) return GEMM_EPI_ERR_ALIGN;
+    if (o.acc_out && !aligned(o.acc_out, 4)) return GEMM_EPI_ERR_ALIGN;
     return GEMM_EPI_OK;
 }
 
-bool use_fast_path(int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C, const void *X,
-                   int kind, const void *D, const void *Aux)
+bool use_fast_path(int64_t M, int64_t N, int64_t K, const Operands &o, int kind)
 {
     if (K % 8 != 0 || N % 8 != 0) return false;
-    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(D, 16)) return false;
-    if (kind_reads_x(kind) && !aligned(X, 16)) return false;
-    if (kind_has_aux(kind) && !aligned(Aux, 16)) return false;
+    if (!aligned(o.A, 16) || !aligned(o.B, 16) || !aligned(o.D, 16)) return false;
+    if (kind_reads_c(kind) && !aligned(o.C, 16)) return false;
+    if (kind_reads_x(kind) && !aligned(o.X, 16)) return false;
+    if (kind_reads_bias(kind) && !aligned(o.row_bias, 16)) return false;
+    if (kind_has_aux(kind) && !aligned(o.Aux, 16)) return false;
+    if (kind_has_acc_out(kind) && !aligned(o.acc_out, 16)) return false;
     // 32-bit buffer offsets: one batch entry of A or B must span < 2 GiB
     const int64_t lim = (int64_t)1 << 31;
     if (M * K * 2 >= lim - 64 || K * N * 2 >= lim - 64) return false;
@@ -140,10 +152,11 @@ const char *gemm_epi_status_string(int status)
     switch (status) {
     case GEMM_EPI_OK: return "ok";
     case GEMM_EPI_ERR_SHAPE: return "invalid shape: L, M, N, K must be >= 1 and every tensor size must fit";
-    case GEMM_EPI_ERR_NULL_INPUT: return "an input the epilogue reads (A, B, C, scalars, or X) is not provided";
-    case GEMM_EPI_ERR_NULL_OUTPUT: return "an output the epilogue writes (D, or Aux) is not provided";
+    case GEMM_EPI_ERR_NULL_INPUT:
+        return "an input the epilogue reads (A, B, C, X, a bias vector, or scalars) is not provided";
+    case GEMM_EPI_ERR_NULL_OUTPUT: return "an output the epilogue writes (D, Aux, or acc_out) is not provided";
     case GEMM_EPI_ERR_KIND: return "unknown epilogue kind";
-    case GEMM_EPI_ERR_ALIGN: return "a tensor pointer is not 2-byte aligned";
+    case GEMM_EPI_ERR_ALIGN: return "a tensor pointer is not aligned to its element size";
     case GEMM_EPI_ERR_HIP: return "HIP launch error";
     default: return "unknown status";
     }
@@ -151,12 +164,14 @@ const char *gemm_epi_status_string(int status)
 
 int gemm_epi_last_hip_error(void) { return g_last_hip_error; }
 
-int gemm_epi_plan(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
-                  const void *X, int epilogue_kind, const void *D, const void *Aux, int64_t out[6])
+int gemm_epi_plan_ext(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                      const void *X, const void *row_bias, const void *col_bias, int epilogue_kind, const void *D,
+                      const void *Aux, const void *acc_out, int64_t out[6])
 {
-    int rc = check_args(L, M, N, K, A, B, C, X, epilogue_kind, D, Aux);
+    const Operands o = {A, B, C, X, row_bias, col_bias, D, Aux, acc_out};
+    int rc = check_args(L, M, N, K, o, epilogue_kind);
     if (rc != GEMM_EPI_OK) return rc;
-    const bool vec = use_fast_path(M, N, K, A, B, C, X, epilogue_kind, D, Aux);
+    const bool vec = use_fast_path(M, N, K, o, epilogue_kind);
     const TileCfg t = choose_tile(L, M, N, vec);
     const int64_t tiles = L * ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
     if (tiles > INT32_MAX) return GEMM_EPI_ERR_SHAPE;
@@ -171,13 +186,21 @@ int gemm_epi_plan(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, con
     return GEMM_EPI_OK;
 }
 
-int gemm_epi_run(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
-                 const void *X, const float *scalars, int epilogue_kind, void *D, void *Aux, void *stream)
+int gemm_epi_plan(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                  const void *X, int epilogue_kind, const void *D, const void *Aux, int64_t out[6])
 {
-    int rc = check_args(L, M, N, K, A, B, C, X, epilogue_kind, D, Aux);
+    return gemm_epi_plan_ext(L, M, N, K, A, B, C, X, nullptr, nullptr, epilogue_kind, D, Aux, nullptr, out);
+}
+
+int gemm_epi_run_ext(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                     const void *X, const void *row_bias, const void *col_bias, const float *scalars,
+                     int epilogue_kind, void *D, void *Aux, void *acc_out, void *stream)
+{
+    const Operands o = {A, B, C, X, row_bias, col_bias, D, Aux, acc_out};
+    int rc = check_args(L, M, N, K, o, epilogue_kind);
     if (rc != GEMM_EPI_OK) return rc;
     if (!scalars) return GEMM_EPI_ERR_NULL_INPUT;
-    const bool vec = use_fast_path(M, N, K, A, B, C, X, epilogue_kind, D, Aux);
+    const bool vec = use_fast_path(M, N, K, o, epilogue_kind);
     const TileCfg t = choose_tile(L, M, N, vec);
     const int64_t tm = (M + t.bm - 1) / t.bm, tn = (N + t.bn - 1) / t.bn;
     const int64_t tiles = L * tm * tn;
@@ -190,6 +213,9 @@ int gemm_epi_run(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, cons
     p.X = (const _Float16 *)X;
     p.D = (_Float16 *)D;
     p.Aux = (_Float16 *)Aux;
+    p.row_bias = (const _Float16 *)row_bias;
+    p.col_bias = (const _Float16 *)col_bias;
+    p.acc_out = (float *)acc_out;
     p.M = (int)M;
     p.N = (int)N;
     p.K = (int)K;
@@ -211,13 +237,23 @@ int gemm_epi_run(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, cons
     case GEMM_EPI_LINCOMB_X_ACC: err = launch_kind<LINCOMB_X_ACC>(p, t, vec, s); break;
     case GEMM_EPI_RELU: err = launch_kind<RELU>(p, t, vec, s); break;
     case GEMM_EPI_SQUARE: err = launch_kind<SQUARE>(p, t, vec, s); break;
-    default: err = launch_kind<RELU_SQUARE>(p, t, vec, s); break;
+    case GEMM_EPI_RELU_SQUARE: err = launch_kind<RELU_SQUARE>(p, t, vec, s); break;
+    case GEMM_EPI_RELU_AUX_STORE: err = launch_kind<RELU_AUX_STORE>(p, t, vec, s); break;
+    case GEMM_EPI_RELU_SCALE_ACC: err = launch_kind<RELU_SCALE_ACC>(p, t, vec, s); break;
+    default: err = launch_kind<BIAS_ROW_COL>(p, t, vec, s); break;
     }
     if (err != hipSuccess) {
         g_last_hip_error = (int)err;
         return GEMM_EPI_ERR_HIP;
     }
     return GEMM_EPI_OK;
+}
+
+int gemm_epi_run(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                 const void *X, const float *scalars, int epilogue_kind, void *D, void *Aux, void *stream)
+{
+    return gemm_epi_run_ext(L, M, N, K, A, B, C, X, nullptr, nullptr, scalars, epilogue_kind, D, Aux, nullptr,
+                            stream);
 }
 
 }  // extern "C"

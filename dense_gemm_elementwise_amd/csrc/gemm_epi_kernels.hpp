@@ -54,13 +54,27 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 #define GE_LDS(T) __attribute__((address_space(3))) T
 
-enum Kind : int { LINCOMB = 0, AUX_SCALE = 1, LINCOMB_X_ACC = 2, RELU = 3, SQUARE = 4, RELU_SQUARE = 5 };
+enum Kind : int {
+    LINCOMB = 0,
+    AUX_SCALE = 1,
+    LINCOMB_X_ACC = 2,
+    RELU = 3,
+    SQUARE = 4,
+    RELU_SQUARE = 5,
+    RELU_AUX_STORE = 6,
+    RELU_SCALE_ACC = 7,
+    BIAS_ROW_COL = 8
+};
 
 __host__ __device__ constexpr bool kind_has_aux(int k)
 {
-    return k == AUX_SCALE || k == LINCOMB_X_ACC || k == SQUARE || k == RELU_SQUARE;
+    return k == AUX_SCALE || k == LINCOMB_X_ACC || k == SQUARE || k == RELU_SQUARE || k == RELU_AUX_STORE ||
+           k == RELU_SCALE_ACC;
 }
 __host__ __device__ constexpr bool kind_reads_x(int k) { return k == LINCOMB_X_ACC; }
+__host__ __device__ constexpr bool kind_reads_c(int k) { return k != BIAS_ROW_COL; }
+__host__ __device__ constexpr bool kind_reads_bias(int k) { return k == BIAS_ROW_COL; }
+__host__ __device__ constexpr bool kind_has_acc_out(int k) { return k == RELU_SCALE_ACC; }
 
 struct Params {
     const _Float16 *A;
@@ -69,6 +83,9 @@ struct Params {
     const _Float16 *X;
     _Float16 *D;
     _Float16 *Aux;
+    const _Float16 *row_bias;  // N values, shared by the batch entries
+    const _Float16 *col_bias;  // M values, shared by the batch entries
+    float *acc_out;            // (L, M, N) fp32 accumulator output
     int M, N, K;      // each < 2^31 (checked on the host)
     int tiles_m, tiles_n;
     int num_tiles;    // L * tiles_m * tiles_n
@@ -77,11 +94,13 @@ struct Params {
 };
 
 // ---------------------------------------------------------------------------
-// Epilogue math, fp32.  d = first output, a = second output (if any).
+// Epilogue math, fp32.  d = first output, a = second output (if any); rb /
+// cb are the row-broadcast bias of the element's column and the
+// column-broadcast bias of its row.
 // ---------------------------------------------------------------------------
 template <int KIND>
-__device__ __forceinline__ void epi_elem(float acc, float c, float x, float alpha, float beta, float s, float &d,
-                                         float &a)
+__device__ __forceinline__ void epi_elem(float acc, float c, float x, float rb, float cb, float alpha, float beta,
+                                         float s, float &d, float &a)
 {
     if constexpr (KIND == LINCOMB) {
         d = alpha * acc + beta * c;
@@ -99,11 +118,22 @@ __device__ __forceinline__ void epi_elem(float acc, float c, float x, float alph
         float t = alpha * acc + beta * c;
         d = t;
         a = t * t;
-    } else {  // RELU_SQUARE
+    } else if constexpr (KIND == RELU_SQUARE) {
         float t = alpha * acc + beta * c;
         t = t > 0.0f ? t : 0.0f;
         d = t;
         a = t * t;
+    } else if constexpr (KIND == RELU_AUX_STORE) {
+        float t = alpha * acc + beta * c;
+        a = t;
+        d = t > 0.0f ? t : 0.0f;
+    } else if constexpr (KIND == RELU_SCALE_ACC) {
+        float t = alpha * acc + beta * c;
+        t = t > 0.0f ? t : 0.0f;
+        a = t;
+        d = s * t;
+    } else {  // BIAS_ROW_COL
+        d = (alpha * acc + rb) + cb;
     }
 }
 
@@ -554,37 +584,53 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     // ---- epilogue ----------------------------------------------------------
     // The wave tile is handled one MFMA row-block (SLAB rows) at a time.  In a
     // slab, pass p covers rows 4p..4p+3; lane owns row 4p + lane/16 and the
-    // 4-column groups 4*(lane%16) (+ WN/2).  C / X of a slab are loaded into
-    // registers one slab ahead, so the loads' latency hides behind the
-    // previous slab's work.
+    // 4-column groups 4*(lane%16) (+ WN/2).  C / X (and the column bias) of a
+    // slab are loaded into registers one slab ahead, so the loads' latency
+    // hides behind the previous slab's work; a lane's columns are the same in
+    // every slab, so its row-bias values are loaded once.
     constexpr int EPI_PASSES = SLAB / 4;
     constexpr int EPI_GROUPS = WN >= 128 ? 2 : 1;
     constexpr int EPI_HALF = WN / 2;
+    constexpr bool HAS_C = kind_reads_c(KIND);
     constexpr bool HAS_X = kind_reads_x(KIND);
+    constexpr bool HAS_BIAS = kind_reads_bias(KIND);
+    constexpr int CP = HAS_C ? EPI_PASSES : 1, XP = HAS_X ? EPI_PASSES : 1, BP = HAS_BIAS ? EPI_PASSES : 1;
     const float alpha = p.alpha, beta = p.beta, s = p.s;
     const int64_t mn_base = (int64_t)l * M * N;
-    half4 cbuf[2][EPI_PASSES][EPI_GROUPS];
-    half4 xbuf[2][HAS_X ? EPI_PASSES : 1][EPI_GROUPS];
-    auto epi_prefetch = [&](int i, half4 (&cb)[EPI_PASSES][EPI_GROUPS],
-                            half4 (&xb)[HAS_X ? EPI_PASSES : 1][EPI_GROUPS]) {
+    half4 cbuf[2][CP][EPI_GROUPS];
+    half4 xbuf[2][XP][EPI_GROUPS];
+    _Float16 cbias[2][BP];
+    half4 rbias[EPI_GROUPS];
+    auto epi_prefetch = [&](int i, half4 (&cb)[CP][EPI_GROUPS], half4 (&xb)[XP][EPI_GROUPS], _Float16 (&colb)[BP]) {
 #pragma unroll
         for (int pass = 0; pass < EPI_PASSES; pass++) {
             const int gm = m0 + wm * WM + i * SLAB + pass * 4 + (lane >> 4);
+            if constexpr (HAS_BIAS) colb[pass] = gm < M ? p.col_bias[gm] : (_Float16)0.0f;
 #pragma unroll
             for (int h = 0; h < EPI_GROUPS; h++) {
                 const int scol = 4 * (lane & 15) + h * EPI_HALF;
                 const int gn = n0 + wn * WN + scol;
                 if (scol < WN && gm < M && gn < N) {
                     const int64_t o = mn_base + (int64_t)gm * N + gn;
-                    cb[pass][h] = *(const half4 *)(p.C + o);
+                    if constexpr (HAS_C) cb[pass][h] = *(const half4 *)(p.C + o);
                     if constexpr (HAS_X) xb[pass][h] = *(const half4 *)(p.X + o);
                 }
             }
         }
     };
 
-    // the first slab's C / X loads fly while the accumulators go to LDS
-    if constexpr (VEC) epi_prefetch(0, cbuf[0], xbuf[0]);
+    // the first slab's loads fly while the accumulators go to LDS
+    if constexpr (VEC) {
+        if constexpr (HAS_BIAS) {
+#pragma unroll
+            for (int h = 0; h < EPI_GROUPS; h++) {
+                const int scol = 4 * (lane & 15) + h * EPI_HALF;
+                const int gn = n0 + wn * WN + scol;
+                rbias[h] = (scol < WN && gn < N) ? *(const half4 *)(p.row_bias + gn) : half4{};
+            }
+        }
+        epi_prefetch(0, cbuf[0], xbuf[0], cbias[0]);
+    }
     barrier_lds();  // every wave is done with the main loop's LDS, which the epilogue reuses
 
     float *slab = (float *)(smem + wave * (SLAB * EPI_LD * 4));
@@ -603,7 +649,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
             }
         wave_lds_sync();  // each wave reads back only its own slab
         if constexpr (VEC) {
-            if (i + 1 < TM) epi_prefetch(i + 1, cbuf[(i + 1) & 1], xbuf[(i + 1) & 1]);
+            if (i + 1 < TM) epi_prefetch(i + 1, cbuf[(i + 1) & 1], xbuf[(i + 1) & 1], cbias[(i + 1) & 1]);
         }
 #pragma unroll
         for (int pass = 0; pass < EPI_PASSES; pass++) {
@@ -619,29 +665,38 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
                 const int64_t o = mn_base + (int64_t)gm * N + gn;
                 if constexpr (VEC) {
                     if (gn >= N) continue;  // N % 8 == 0: a 4-column group is all in or all out
-                    const half4 c4 = cbuf[i & 1][pass][h];
-                    half4 x4 = {};
+                    half4 c4 = {}, x4 = {}, rb4 = {};
+                    float cbv = 0.0f;
+                    if constexpr (HAS_C) c4 = cbuf[i & 1][pass][h];
                     if constexpr (HAS_X) x4 = xbuf[i & 1][pass][h];
+                    if constexpr (HAS_BIAS) {
+                        rb4 = rbias[h];
+                        cbv = (float)cbias[i & 1][pass];
+                    }
                     half4 d4, e4;
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
                         float d, a = 0.0f;
-                        epi_elem<KIND>(a4[e], (float)c4[e], (float)x4[e], alpha, beta, s, d, a);
+                        epi_elem<KIND>(a4[e], (float)c4[e], (float)x4[e], (float)rb4[e], cbv, alpha, beta, s, d, a);
                         d4[e] = (_Float16)d;
                         e4[e] = (_Float16)a;
                     }
                     *(half4 *)(p.D + o) = d4;
                     if constexpr (kind_has_aux(KIND)) *(half4 *)(p.Aux + o) = e4;
+                    if constexpr (kind_has_acc_out(KIND)) *(f32x4 *)(p.acc_out + o) = a4;
                 } else {
+                    const float cbv = HAS_BIAS ? (float)p.col_bias[gm] : 0.0f;
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
                         if (gn + e >= N) break;
-                        const float c = (float)p.C[o + e];
+                        const float c = HAS_C ? (float)p.C[o + e] : 0.0f;
                         const float x = HAS_X ? (float)p.X[o + e] : 0.0f;
+                        const float rb = HAS_BIAS ? (float)p.row_bias[gn + e] : 0.0f;
                         float d, a = 0.0f;
-                        epi_elem<KIND>(a4[e], c, x, alpha, beta, s, d, a);
+                        epi_elem<KIND>(a4[e], c, x, rb, cbv, alpha, beta, s, d, a);
                         p.D[o + e] = (_Float16)d;
                         if constexpr (kind_has_aux(KIND)) p.Aux[o + e] = (_Float16)a;
+                        if constexpr (kind_has_acc_out(KIND)) p.acc_out[o + e] = a4[e];
                     }
                 }
             }

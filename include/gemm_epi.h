@@ -39,8 +39,8 @@ extern "C" {
 #endif
 
 /*
- * Epilogue kinds.  s = scalars[2] (extra_scalar or x_factor); the second
- * output (Aux, Y or E) is written to the Aux buffer.
+ * Epilogue kinds.  s = scalars[2] (extra_scalar, x_factor or scale); the
+ * second output (Aux, Y, E or F) is written to the Aux buffer.
  *
  * GEMM_EPI_LINCOMB        D = alpha*acc + beta*C
  *     (CUTLASS Python examples article: the "Basic GEMM" NumPy check and the
@@ -57,9 +57,21 @@ extern "C" {
  *     giving the page's D = acc + C)
  * GEMM_EPI_RELU_SQUARE    D = ReLU(alpha*acc + beta*C) ; E = D*D
  *     ("Activation Functions" followed by "Multiple Outputs")
+ * GEMM_EPI_RELU_AUX_STORE F = alpha*acc + beta*C ; D = ReLU(F)
+ *     (tutorial cell [6], relu_aux_store, whose beta is the constant 2.0;
+ *     cell [8] is the same function with alpha = 1, beta = 0.5); F goes to
+ *     the Aux buffer.
+ * GEMM_EPI_RELU_SCALE_ACC F = ReLU(alpha*acc + beta*C) ; D = s*F, and acc
+ *     itself as an fp32 output (tutorial cell [7], relu_scale_return_acc,
+ *     with s = scale); F goes to the Aux buffer, acc to acc_out.  Needs
+ *     gemm_epi_run_ext.
+ * GEMM_EPI_BIAS_ROW_COL   D = (alpha*acc + row_bias[n]) + col_bias[m]
+ *     (tutorial cell [9], broadcast_epilogue: row_bias has one value per
+ *     column, shape (N,), col_bias one per row, shape (M, 1)); C is not read.
+ *     Needs gemm_epi_run_ext.
  *
- * The intermediate values (Aux before the scaling, D before the square) are
- * used unrounded.
+ * The intermediate values (Aux before the scaling, D before the square, F
+ * before the scaling) are used unrounded.
  */
 typedef enum {
     GEMM_EPI_LINCOMB = 0,
@@ -67,7 +79,10 @@ typedef enum {
     GEMM_EPI_LINCOMB_X_ACC = 2,
     GEMM_EPI_RELU = 3,
     GEMM_EPI_SQUARE = 4,
-    GEMM_EPI_RELU_SQUARE = 5
+    GEMM_EPI_RELU_SQUARE = 5,
+    GEMM_EPI_RELU_AUX_STORE = 6,
+    GEMM_EPI_RELU_SCALE_ACC = 7,
+    GEMM_EPI_BIAS_ROW_COL = 8
 } gemm_epi_kind;
 
 /*
@@ -81,10 +96,14 @@ typedef enum {
 typedef enum {
     GEMM_EPI_OK = 0,
     GEMM_EPI_ERR_SHAPE = 1,       /* L, M, N or K < 1, or an element count overflows int64 */
-    GEMM_EPI_ERR_NULL_INPUT = 2,  /* A, B, C or scalars NULL; X NULL for LINCOMB_X_ACC */
-    GEMM_EPI_ERR_NULL_OUTPUT = 3, /* D NULL; Aux NULL for a kind with a second output */
+    GEMM_EPI_ERR_NULL_INPUT = 2,  /* A, B or scalars NULL; C NULL for a kind that reads it (all but
+                                     BIAS_ROW_COL); X NULL for LINCOMB_X_ACC; row_bias or col_bias
+                                     NULL for BIAS_ROW_COL */
+    GEMM_EPI_ERR_NULL_OUTPUT = 3, /* D NULL; Aux NULL for a kind with a second output; acc_out NULL
+                                     for RELU_SCALE_ACC */
     GEMM_EPI_ERR_KIND = 4,        /* unknown epilogue kind */
-    GEMM_EPI_ERR_ALIGN = 5,       /* a tensor pointer is not 2-byte aligned */
+    GEMM_EPI_ERR_ALIGN = 5,       /* an fp16 pointer is not 2-byte aligned, or acc_out is not 4-byte
+                                     aligned */
     GEMM_EPI_ERR_HIP = 6          /* the launch failed; see gemm_epi_last_hip_error() */
 } gemm_epi_status;
 
@@ -93,7 +112,8 @@ typedef enum {
  *
  *   L, M, N, K  batch count and problem sizes, each >= 1.
  *   A, B        device pointers, fp16 (IEEE binary16), layout above.
- *   C           device pointer, fp16, read by every kind (also when beta = 0).
+ *   C           device pointer, fp16, read by every kind but BIAS_ROW_COL
+ *               (also when beta = 0); may be NULL for BIAS_ROW_COL.
  *   X           device pointer, fp16; read only by GEMM_EPI_LINCOMB_X_ACC,
  *               may be NULL otherwise.
  *   scalars     HOST pointer to 3 floats {alpha, beta, s}; read during the
@@ -101,9 +121,9 @@ typedef enum {
  *               reuse the memory as soon as the call returns.
  *   epilogue_kind  a gemm_epi_kind value.
  *   D           device pointer, fp16 output.
- *   Aux         device pointer, fp16 second output (Aux, Y or E) for
- *               AUX_SCALE, LINCOMB_X_ACC, SQUARE and RELU_SQUARE; may be NULL
- *               for LINCOMB and RELU.
+ *   Aux         device pointer, fp16 second output (Aux, Y, E or F) for
+ *               AUX_SCALE, LINCOMB_X_ACC, SQUARE, RELU_SQUARE, RELU_AUX_STORE
+ *               and RELU_SCALE_ACC; may be NULL for the other kinds.
  *   stream      a hipStream_t (0 = the null stream).
  *
  * Ownership: the caller allocates, owns and frees every buffer.  The library
@@ -119,10 +139,36 @@ typedef enum {
  * the same values.
  *
  * Returns GEMM_EPI_OK, or a gemm_epi_status error code; on an error before
- * the launch nothing is queued on the stream.
+ * the launch nothing is queued on the stream.  RELU_SCALE_ACC and
+ * BIAS_ROW_COL need operands this entry point does not take: use
+ * gemm_epi_run_ext (here they return GEMM_EPI_ERR_NULL_OUTPUT and
+ * GEMM_EPI_ERR_NULL_INPUT).
  */
 int gemm_epi_run(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
                  const void *X, const float *scalars, int epilogue_kind, void *D, void *Aux, void *stream);
+
+/*
+ * gemm_epi_run_ext -- gemm_epi_run with the operands of the broadcast and
+ * accumulator-returning kinds (tutorial cells [7] and [9]); every kind can be
+ * launched through it.  The arguments shared with gemm_epi_run mean the
+ * same; in addition:
+ *
+ *   row_bias    device pointer, fp16, N values (one per output column),
+ *               shared by every batch entry; read only by BIAS_ROW_COL, may
+ *               be NULL otherwise.
+ *   col_bias    device pointer, fp16, M values (one per output row), shared
+ *               by every batch entry; read only by BIAS_ROW_COL, may be NULL
+ *               otherwise.
+ *   acc_out     device pointer, fp32 (IEEE binary32), (L,M,N) packed
+ *               row-major like D: the accumulator itself, written only by
+ *               RELU_SCALE_ACC; may be NULL otherwise.
+ *
+ * Ownership, asynchrony and the status codes are those of gemm_epi_run.  The
+ * fast path additionally needs row_bias and acc_out 16-byte aligned.
+ */
+int gemm_epi_run_ext(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                     const void *X, const void *row_bias, const void *col_bias, const float *scalars,
+                     int epilogue_kind, void *D, void *Aux, void *acc_out, void *stream);
 
 /* A static, human-readable name for a status code ("unknown status" for
  * values outside the enum).  Never NULL. */
@@ -143,6 +189,11 @@ int gemm_epi_last_hip_error(void);
  */
 int gemm_epi_plan(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
                   const void *X, int epilogue_kind, const void *D, const void *Aux, int64_t out[6]);
+
+/* gemm_epi_plan for the arguments of gemm_epi_run_ext. */
+int gemm_epi_plan_ext(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                      const void *X, const void *row_bias, const void *col_bias, int epilogue_kind, const void *D,
+                      const void *Aux, const void *acc_out, int64_t out[6]);
 
 #ifdef __cplusplus
 }

@@ -32,7 +32,8 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert set(names) == {"gemm_epi_run", "gemm_epi_status_string", "gemm_epi_last_hip_error", "gemm_epi_plan"}
+    assert set(names) == {"gemm_epi_run", "gemm_epi_run_ext", "gemm_epi_status_string", "gemm_epi_last_hip_error",
+                          "gemm_epi_plan", "gemm_epi_plan_ext"}
     raw = ctypes.CDLL(binding.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -70,20 +71,67 @@ def test_bad_shapes(shape):
 def test_missing_inputs():
     assert run(A=None) == 2
     assert run(B=None) == 2
-    assert run(C=None) == 2  # every kind reads C, also with beta = 0
+    assert run(C=None) == 2  # every kind but the bias kind reads C, also with beta = 0
     assert run(sc=None) == 2
     assert run(kind=2, X=None) == 2  # LINCOMB_X_ACC reads X
 
 
 def test_missing_outputs():
     assert run(D=None) == 3
-    for kind in ("AUX_SCALE", "LINCOMB_X_ACC", "SQUARE", "RELU_SQUARE"):
+    for kind in ("AUX_SCALE", "LINCOMB_X_ACC", "SQUARE", "RELU_SQUARE", "RELU_AUX_STORE"):
         assert run(kind=ge.KINDS[kind], Aux=None) == 3, kind
 
 
-@pytest.mark.parametrize("kind", [-1, 6, 100])
+@pytest.mark.parametrize("kind", [-1, 9, 100])
 def test_unknown_kind(kind):
     assert run(kind=kind) == 4
+
+
+def run_ext(L=1, M=8, N=8, K=8, A=P16, B=P16, C=P16, X=P16, rb=P16, cb=P16, sc=SC, kind=0, D=P16, Aux=P16,
+            acc=P16):
+    return ge.gemm_epi_run_ext(L, M, N, K, A, B, C, X, rb, cb, sc, kind, D, Aux, acc, None)
+
+
+def plan_ext(L=1, M=256, N=256, K=256, A=P16, B=P16, C=P16, X=None, rb=None, cb=None, kind=0, D=P16, Aux=None,
+             acc=None):
+    return ge.gemm_epi_plan_ext(L, M, N, K, A, B, C, X, rb, cb, kind, D, Aux, acc)
+
+
+def test_kinds_needing_ext_operands_are_rejected_by_the_plain_entry_point():
+    # gemm_epi_run has no bias inputs and no accumulator output
+    assert run(kind=ge.KINDS["BIAS_ROW_COL"]) == 2
+    assert run(kind=ge.KINDS["RELU_SCALE_ACC"]) == 3
+    assert ge.gemm_epi_plan(1, 8, 8, 8, P16, P16, P16, None, ge.KINDS["BIAS_ROW_COL"], P16, None)[0] == 2
+
+
+def test_ext_operand_checks():
+    bias, acc = ge.KINDS["BIAS_ROW_COL"], ge.KINDS["RELU_SCALE_ACC"]
+    assert run_ext(kind=bias, rb=None) == 2
+    assert run_ext(kind=bias, cb=None) == 2
+    assert run_ext(kind=acc, acc=None) == 3
+    assert run_ext(kind=acc, Aux=None) == 3
+    assert run_ext(kind=acc, C=None) == 2          # RELU_SCALE_ACC reads C
+    assert run_ext(kind=ge.KINDS["RELU_AUX_STORE"], Aux=None) == 3
+    assert run_ext(kind=acc, acc=P2) == 5          # fp32 output not 4-byte aligned
+    assert run_ext(kind=bias, rb=P1) == 5
+    assert run_ext(kind=bias, cb=P1) == 5
+    assert run_ext(kind=bias, sc=None) == 2
+    # valid argument sets (checked by the host-only planner, nothing is launched)
+    assert plan_ext(kind=bias, C=None, rb=P16, cb=P16)[0] == 0   # the bias kind does not read C
+    assert plan_ext(kind=acc, Aux=P16, acc=P16)[0] == 0
+    assert plan_ext(kind=ge.KINDS["RELU_AUX_STORE"], Aux=P16)[0] == 0
+
+
+def test_ext_fast_path_conditions():
+    bias, acc = ge.KINDS["BIAS_ROW_COL"], ge.KINDS["RELU_SCALE_ACC"]
+    rc, cfg = plan_ext(kind=bias, C=None, rb=P16, cb=P2)
+    assert rc == 0 and cfg["vec"] == 1             # the column bias is read one value at a time
+    rc, cfg = plan_ext(kind=bias, C=None, rb=P2, cb=P16)
+    assert rc == 0 and cfg["vec"] == 0             # the row bias is read in 8-byte vectors
+    rc, cfg = plan_ext(kind=acc, Aux=P16, acc=P16)
+    assert rc == 0 and cfg["vec"] == 1
+    rc, cfg = plan_ext(kind=acc, Aux=P16, acc=0x7F0000001004)
+    assert rc == 0 and cfg["vec"] == 0             # fp32 output stored in 16-byte vectors
 
 
 def test_misaligned_pointers():
@@ -116,10 +164,17 @@ def test_plan_tiles_for_the_workloads():
         "lincomb_2400x3232x4096": (128, 256, 19 * 13),
         "x_acc_8192": (256, 256, 1024),
         "relu_square_16x2048x2048x1024": (256, 256, 1024),
+        "relu_aux_store_1024": (64, 64, 256),
+        "relu_scale_acc_1024": (64, 64, 256),
+        "bias_row_col_1024": (64, 64, 256),
+        "relu_scale_acc_8192": (256, 256, 1024),
+        "bias_row_col_8192": (256, 256, 1024),
     }
+    assert set(want) == set(workloads.WORKLOADS)
     for name, (bm, bn, wgs) in want.items():
         w = workloads.WORKLOADS[name]
-        rc, cfg = ge.gemm_epi_plan(w.L, w.M, w.N, w.K, P16, P16, P16, P16, ge.KINDS[w.kind], P16, P16)
+        rc, cfg = ge.gemm_epi_plan_ext(w.L, w.M, w.N, w.K, P16, P16, P16, P16, P16, P16, ge.KINDS[w.kind], P16, P16,
+                                       P16)
         assert rc == 0, name
         assert (cfg["bm"], cfg["bn"], cfg["workgroups"]) == (bm, bn, wgs), (name, cfg)
         assert cfg["vec"] == 1

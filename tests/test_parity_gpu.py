@@ -47,10 +47,10 @@ def to_dev(p, offset=0):
     return out
 
 
-def alloc_out(L, M, N, offset=0):
+def alloc_out(L, M, N, offset=0, dtype=torch.float16):
     if offset:
-        return torch.full((L * M * N + offset,), float("nan"), dtype=torch.float16, device=DEV)[offset:].view(L, M, N)
-    return torch.full((L, M, N), float("nan"), dtype=torch.float16, device=DEV)
+        return torch.full((L * M * N + offset,), float("nan"), dtype=dtype, device=DEV)[offset:].view(L, M, N)
+    return torch.full((L, M, N), float("nan"), dtype=dtype, device=DEV)
 
 
 def gpu_run(p, kind, alpha, beta, s3, offset=0):
@@ -59,11 +59,25 @@ def gpu_run(p, kind, alpha, beta, s3, offset=0):
     N = p["B"].shape[2]
     D = alloc_out(L, M, N, offset)
     Aux = alloc_out(L, M, N, offset) if kind in ge.HAS_AUX else None
-    ge.run(t["A"], t["B"], t["C"], t["X"], kind=kind, alpha=alpha, beta=beta, s3=s3, D=D, Aux=Aux)
+    acc = alloc_out(L, M, N, offset, torch.float32) if kind in ge.HAS_ACC else None
+    ge.run(t["A"], t["B"], t["C"], t["X"], kind=kind, alpha=alpha, beta=beta, s3=s3, D=D, Aux=Aux,
+           row_bias=t.get("row_bias"), col_bias=t.get("col_bias"), acc_out=acc)
     out = {"D": D.cpu().numpy()}
     if Aux is not None:
         out["Aux"] = Aux.cpu().numpy()
+    if acc is not None:
+        out["Acc"] = acc.cpu().numpy()
     return out
+
+
+def oracle_full(p, kind, alpha, beta, s3, want64):
+    return oracle.gemm_epi(p["A"], p["B"], p["C"], p["X"], kind=kind, alpha=alpha, beta=beta, s3=s3,
+                           row_bias=p.get("row_bias"), col_bias=p.get("col_bias"), want64=want64)
+
+
+def oracle_points(p, kind, alpha, beta, s3, l, i, j):
+    return oracle.gemm_epi_points(p["A"], p["B"], p["C"], p["X"], kind=kind, alpha=alpha, beta=beta, s3=s3,
+                                  row_bias=p.get("row_bias"), col_bias=p.get("col_bias"), l=l, i=i, j=j)
 
 
 def bits(a):
@@ -95,8 +109,7 @@ def assert_close(got, ref64, what):
 
 def check_full(p, kind, alpha, beta, s3, exact, offset=0, what=""):
     got = gpu_run(p, kind, alpha, beta, s3, offset)
-    ref = oracle.gemm_epi(p["A"], p["B"], p["C"], p["X"], kind=kind, alpha=alpha, beta=beta, s3=s3,
-                          want64=not exact)
+    ref = oracle_full(p, kind, alpha, beta, s3, want64=not exact)
     for name in ("D", "Aux"):
         if name not in ref:
             continue
@@ -104,18 +117,34 @@ def check_full(p, kind, alpha, beta, s3, exact, offset=0, what=""):
             assert_bit_exact(got[name], ref[name], f"{what} {name}")
         else:
             assert_close(got[name], ref[name + "64"], f"{what} {name}")
+    if kind in ge.HAS_ACC:
+        if exact:  # integer inputs: every fp32 partial sum is exact
+            n = int(np.count_nonzero(got["Acc"] != ref["Acc"]))
+            assert n == 0, f"{what} acc_out: {n} values differ from the oracle"
+        else:
+            assert_close(got["Acc"], ref["Acc64"], f"{what} acc_out")
     return got
 
 
 # ---------------------------------------------------------------------------
 # The five workloads at their real sizes
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["aux_scale_128", "aux_scale_1024", "lincomb_2400x3232x4096"])
+@pytest.mark.parametrize("name", ["aux_scale_128", "aux_scale_1024", "lincomb_2400x3232x4096",
+                                  "relu_aux_store_1024", "relu_scale_acc_1024"])
 def test_integer_workloads_bit_exact(name):
     w = workloads.WORKLOADS[name]
     log(f"[parity] {name}: L={w.L} M={w.M} N={w.N} K={w.K} {w.kind}")
     p = workloads.make_inputs(w)
     check_full(p, w.kind, w.alpha, w.beta, w.s3, exact=True, what=name)
+
+
+def test_bias_workload_1024():
+    """The tutorial's broadcast epilogue on its own draws: integer A, B and
+    Gaussian fp16 biases, so the tolerance applies."""
+    w = workloads.WORKLOADS["bias_row_col_1024"]
+    log(f"[parity] {w.name}: L={w.L} M={w.M} N={w.N} K={w.K} {w.kind}")
+    p = workloads.make_inputs(w)
+    check_full(p, w.kind, w.alpha, w.beta, w.s3, exact=False, what=w.name)
 
 
 def sample_points(L, M, N, n, seed, tile=256):
@@ -197,11 +226,50 @@ def test_relu_square_batched_sampled_and_properties():
     assert_close(Eh[l, i, j], ref["Aux64"], "relu_square E")
 
 
+def test_relu_scale_acc_8192_sampled_and_properties():
+    w = workloads.WORKLOADS["relu_scale_acc_8192"]
+    log(f"[parity] {w.name}: L={w.L} M={w.M} N={w.N} K={w.K} {w.kind}")
+    p = workloads.make_inputs(w)
+    t = to_dev(p)
+    D = alloc_out(w.L, w.M, w.N)
+    F = alloc_out(w.L, w.M, w.N)
+    acc = alloc_out(w.L, w.M, w.N, dtype=torch.float32)
+    ge.run(t["A"], t["B"], t["C"], kind=w.kind, alpha=w.alpha, beta=w.beta, s3=w.s3, D=D, Aux=F, acc_out=acc)
+    # whole-output properties: F >= 0, D = s * F exactly (s = 1/2 halves a normal
+    # value), and F agrees with relu(alpha acc + beta C) built from the stored acc
+    assert bool(torch.isfinite(D).all()) and bool(torch.isfinite(F).all()) and bool(torch.isfinite(acc).all())
+    assert bool((F >= 0).all())
+    normal = F.abs() >= 2.0 ** -13
+    assert bool((D[normal].double() == 0.5 * F[normal].double()).all()), "D != F / 2 somewhere"
+    recon = torch.relu(w.alpha * acc.double() + w.beta * t["C"].double())
+    assert bool(((F.double() - recon).abs() <= 2.0 ** -10 * recon + 1e-6).all()), "F inconsistent with acc, C"
+    del recon, normal
+    l, i, j = sample_points(w.L, w.M, w.N, 20000, seed=3)
+    ref = oracle_points(p, w.kind, w.alpha, w.beta, w.s3, l, i, j)
+    assert_close(D.cpu().numpy()[l, i, j], ref["D64"], "relu_scale_acc D")
+    assert_close(F.cpu().numpy()[l, i, j], ref["Aux64"], "relu_scale_acc F")
+    assert_close(acc.cpu().numpy()[l, i, j], ref["Acc64"], "relu_scale_acc acc_out")
+
+
+def test_bias_row_col_8192_sampled_and_properties():
+    w = workloads.WORKLOADS["bias_row_col_8192"]
+    log(f"[parity] {w.name}: L={w.L} M={w.M} N={w.N} K={w.K} {w.kind}")
+    p = workloads.make_inputs(w)
+    t = to_dev(p)
+    D = alloc_out(w.L, w.M, w.N)
+    ge.run(t["A"], t["B"], kind=w.kind, alpha=w.alpha, D=D, row_bias=t["row_bias"], col_bias=t["col_bias"])
+    assert bool(torch.isfinite(D).all())
+    l, i, j = sample_points(w.L, w.M, w.N, 20000, seed=4)
+    ref = oracle_points(p, w.kind, w.alpha, w.beta, w.s3, l, i, j)
+    assert_close(D.cpu().numpy()[l, i, j], ref["D64"], "bias_row_col D")
+
+
 # ---------------------------------------------------------------------------
 # Every kind, both kernels, ragged shapes
 # ---------------------------------------------------------------------------
 KIND_SCALARS = {"LINCOMB": (1.0, 2.0, 0.0), "AUX_SCALE": (1.0, 2.0, 0.5), "LINCOMB_X_ACC": (2.0, 1.0, 3.0),
-                "RELU": (1.0, -1.0, 0.0), "SQUARE": (1.0, 1.0, 0.0), "RELU_SQUARE": (0.5, 1.0, 0.0)}
+                "RELU": (1.0, -1.0, 0.0), "SQUARE": (1.0, 1.0, 0.0), "RELU_SQUARE": (0.5, 1.0, 0.0),
+                "RELU_AUX_STORE": (3.0, 2.0, 0.0), "RELU_SCALE_ACC": (1.0, 2.0, 0.5), "BIAS_ROW_COL": (1.5, 0.0, 0.0)}
 
 
 @pytest.mark.parametrize("kind", workloads.KINDS)
