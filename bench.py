@@ -148,6 +148,32 @@ def bench_gpu_cold(w, steps, warmup):
             "epilogue_hbm_gbs": round(w.epilogue_bytes / (ev_ms * 1e-3) / 1e9, 1)}
 
 
+def bench_unfused_own(w, steps, warmup):
+    """Context, not the metric: the same workload through this library's own
+    unfused composition (gemm_epi_run_unfused: the GEMM writes the fp32
+    accumulator to HBM, a second launch applies the epilogue).  Same
+    results as the fused kernel; the difference is the fusion's saving."""
+    import torch
+    import dense_gemm_elementwise_amd as ge
+    from dense_gemm_elementwise_amd import workloads
+
+    dev = torch.device("cuda:0")
+    p = workloads.make_inputs(w)
+    t = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in p.items()}
+    D, Aux, Acc = _outputs(w, ge, dev)
+    ws = torch.empty(w.L * w.M * w.N, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    args = _device_args(w, t, D, Aux, Acc, stream, ge)
+    uargs = args[:15] + (ws.data_ptr(), ws.numel() * 4, args[15])
+    for _ in range(warmup):
+        rc = ge.gemm_epi_run_unfused(*uargs)
+        if rc:
+            raise RuntimeError(ge.gemm_epi_status_string(rc))
+    _, ev_ms, stats = _timed_launches(lambda i: ge.gemm_epi_run_unfused(*uargs), steps, stream)
+    return {"what": "own GEMM kernel writing the fp32 accumulator + own elementwise epilogue kernel",
+            "ms_per_step": round(ev_ms, 5), "tflops": round(w.flops / (ev_ms * 1e-3) / 1e12, 2)}
+
+
 def bench_unfused_library(w, steps, warmup):
     """Context, not the metric: the same workload run unfused through the
     vendor library -- torch.matmul (hipBLASLt, fp16 output) followed by the
@@ -308,7 +334,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=6144)
     ap.add_argument("--all", action="store_true")
     ap.add_argument("--compare-unfused", action="store_true",
-                    help="also time the unfused vendor-library composition (context, not the metric)")
+                    help="also time the unfused compositions, this library's own and the vendor library's "
+                         "(context, not the metric)")
     ap.add_argument("--copy-kernel", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (calibrates HBM byte counters)")
     a = ap.parse_args()
@@ -333,6 +360,7 @@ def main():
             line = result_line(other, g, a.steps, a.warmup, None)
             line["cold"] = bench_gpu_cold(other, a.steps, a.warmup)
             if a.compare_unfused:
+                line["unfused_own"] = bench_unfused_own(other, a.steps, a.warmup)
                 line["unfused_library"] = bench_unfused_library(other, a.steps, a.warmup)
             print(json.dumps(line), file=sys.stderr, flush=True)
 
@@ -347,6 +375,7 @@ def main():
                          f"fp64 i-k-j triple loop + epilogue, {dt:.1f} s"}
     line = result_line(w, g, a.steps, a.warmup, cpu)
     if a.compare_unfused:
+        line["unfused_own"] = bench_unfused_own(w, a.steps, a.warmup)
         line["unfused_library"] = bench_unfused_library(w, a.steps, a.warmup)
     print(json.dumps(line), flush=True)
 

@@ -38,11 +38,12 @@ STATUS = {
     4: "GEMM_EPI_ERR_KIND",
     5: "GEMM_EPI_ERR_ALIGN",
     6: "GEMM_EPI_ERR_HIP",
+    7: "GEMM_EPI_ERR_WORKSPACE",
 }
 
 # every function include/gemm_epi.h declares
-EXPORTS = ("gemm_epi_run", "gemm_epi_run_ext", "gemm_epi_status_string", "gemm_epi_last_hip_error",
-           "gemm_epi_plan", "gemm_epi_plan_ext")
+EXPORTS = ("gemm_epi_run", "gemm_epi_run_ext", "gemm_epi_run_unfused", "gemm_epi_status_string",
+           "gemm_epi_last_hip_error", "gemm_epi_plan", "gemm_epi_plan_ext")
 
 
 class GemmEpiError(RuntimeError):
@@ -70,6 +71,9 @@ def lib():
     L.gemm_epi_run_ext.restype = ctypes.c_int
     L.gemm_epi_run_ext.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_float),
                                    ctypes.c_int, vp, vp, vp, vp]
+    L.gemm_epi_run_unfused.restype = ctypes.c_int
+    L.gemm_epi_run_unfused.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_float),
+                                       ctypes.c_int, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.gemm_epi_status_string.restype = ctypes.c_char_p
     L.gemm_epi_status_string.argtypes = [ctypes.c_int]
     L.gemm_epi_last_hip_error.restype = ctypes.c_int
@@ -115,6 +119,17 @@ def gemm_epi_run_ext(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilog
                                   _kind_id(epilogue_kind), D, Aux, acc_out, stream)
 
 
+def gemm_epi_run_unfused(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilogue_kind, D, Aux, acc_out,
+                         workspace, workspace_bytes, stream) -> int:
+    """Pointer-level call of gemm_epi_run_unfused: the same operation in two
+    launches (GEMM to an fp32 workspace, then the elementwise epilogue).
+    Returns the status code."""
+    sc = (ctypes.c_float * 3)(*[float(v) for v in scalars]) if scalars is not None else None
+    return lib().gemm_epi_run_unfused(int(L), int(M), int(N), int(K), A, B, C, X, row_bias, col_bias, sc,
+                                      _kind_id(epilogue_kind), D, Aux, acc_out, workspace, int(workspace_bytes),
+                                      stream)
+
+
 def gemm_epi_plan_ext(L, M, N, K, A, B, C, X, row_bias, col_bias, epilogue_kind, D, Aux, acc_out):
     """Host-only query of the launch configuration for gemm_epi_run_ext."""
     out = (ctypes.c_int64 * 6)()
@@ -152,7 +167,7 @@ def _ptr(t):
 
 
 def run(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, D, Aux=None, row_bias=None, col_bias=None,
-        acc_out=None, stream=None, sync=True):
+        acc_out=None, stream=None, sync=True, unfused_workspace=None):
     """D (and Aux, acc_out) <- fused epilogue of A @ B on torch tensors.
 
     A (L,M,K), B (L,K,N), C, X, D, Aux (L,M,N): contiguous float16 CUDA
@@ -161,6 +176,9 @@ def run(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, D, Aux=None,
     extra_scalar (AUX_SCALE), x_factor (LINCOMB_X_ACC) or scale
     (RELU_SCALE_ACC).  The kernel is queued on `stream` (a torch.cuda.Stream;
     default: the current stream); with sync=True the call waits for it.
+    With unfused_workspace (a float32 CUDA tensor of at least L*M*N
+    elements) the unfused two-launch composition runs instead of the fused
+    kernel (for comparison; the outputs are the same).
     """
     import torch
     if A.dim() != 3 or B.dim() != 3:
@@ -198,10 +216,18 @@ def run(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, D, Aux=None,
         raise ValueError(f"all tensors must be on one device, got {devs}")
     dev = A.device
     s = stream if stream is not None else torch.cuda.current_stream(dev)
+    ws = unfused_workspace
+    if ws is not None and (ws.dtype != torch.float32 or ws.device != dev or not ws.is_contiguous()):
+        raise ValueError("unfused_workspace must be a contiguous float32 tensor on the operands' device")
     with torch.cuda.device(dev):
-        rc = gemm_epi_run_ext(L, M, N, K, A.data_ptr(), B.data_ptr(), _ptr(C), _ptr(X), _ptr(row_bias),
-                              _ptr(col_bias), (alpha, beta, s3), KINDS[kname], D.data_ptr(), _ptr(Aux),
-                              _ptr(acc_out), s.cuda_stream)
+        if ws is None:
+            rc = gemm_epi_run_ext(L, M, N, K, A.data_ptr(), B.data_ptr(), _ptr(C), _ptr(X), _ptr(row_bias),
+                                  _ptr(col_bias), (alpha, beta, s3), KINDS[kname], D.data_ptr(), _ptr(Aux),
+                                  _ptr(acc_out), s.cuda_stream)
+        else:
+            rc = gemm_epi_run_unfused(L, M, N, K, A.data_ptr(), B.data_ptr(), _ptr(C), _ptr(X), _ptr(row_bias),
+                                      _ptr(col_bias), (alpha, beta, s3), KINDS[kname], D.data_ptr(), _ptr(Aux),
+                                      _ptr(acc_out), ws.data_ptr(), ws.numel() * 4, s.cuda_stream)
     if rc != 0:
         msg = gemm_epi_status_string(rc)
         if rc == 6:

@@ -5,6 +5,7 @@
 // Every check runs on the host before any HIP call, so a bad argument never
 // queues work and the checks run without a GPU.
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "gemm_epi.h"
@@ -108,7 +109,8 @@ int check_args(int64_t L, int64_t M, int64_t N, int64_t K, const Operands &o, in
 bool use_fast_path(int64_t M, int64_t N, int64_t K, const Operands &o, int kind)
 {
     if (K % 8 != 0 || N % 8 != 0) return false;
-    if (!aligned(o.A, 16) || !aligned(o.B, 16) || !aligned(o.D, 16)) return false;
+    if (!aligned(o.A, 16) || !aligned(o.B, 16)) return false;
+    if (kind_writes_d(kind) && !aligned(o.D, 16)) return false;
     if (kind_reads_c(kind) && !aligned(o.C, 16)) return false;
     if (kind_reads_x(kind) && !aligned(o.X, 16)) return false;
     if (kind_reads_bias(kind) && !aligned(o.row_bias, 16)) return false;
@@ -143,6 +145,18 @@ hipError_t launch_kind(const Params &p, const TileCfg &t, bool vec, hipStream_t 
 
 #undef GE_LAUNCH
 
+// The elementwise stage of the unfused composition.
+template <int KIND>
+hipError_t launch_epilogue(const EpiParams &q, bool vec, hipStream_t stream)
+{
+    const int64_t blocks = q.rows < 8192 ? q.rows : 8192;
+    if (vec)
+        hipLaunchKernelGGL((epilogue_kernel<KIND, true>), dim3((unsigned)blocks), dim3(256), 0, stream, q);
+    else
+        hipLaunchKernelGGL((epilogue_kernel<KIND, false>), dim3((unsigned)blocks), dim3(256), 0, stream, q);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 extern "C" {
@@ -158,6 +172,7 @@ const char *gemm_epi_status_string(int status)
     case GEMM_EPI_ERR_KIND: return "unknown epilogue kind";
     case GEMM_EPI_ERR_ALIGN: return "a tensor pointer is not aligned to its element size";
     case GEMM_EPI_ERR_HIP: return "HIP launch error";
+    case GEMM_EPI_ERR_WORKSPACE: return "the workspace is missing or smaller than L*M*N*4 bytes";
     default: return "unknown status";
     }
 }
@@ -241,6 +256,84 @@ int gemm_epi_run_ext(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, 
     case GEMM_EPI_RELU_AUX_STORE: err = launch_kind<RELU_AUX_STORE>(p, t, vec, s); break;
     case GEMM_EPI_RELU_SCALE_ACC: err = launch_kind<RELU_SCALE_ACC>(p, t, vec, s); break;
     default: err = launch_kind<BIAS_ROW_COL>(p, t, vec, s); break;
+    }
+    if (err != hipSuccess) {
+        g_last_hip_error = (int)err;
+        return GEMM_EPI_ERR_HIP;
+    }
+    return GEMM_EPI_OK;
+}
+
+int gemm_epi_run_unfused(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                         const void *X, const void *row_bias, const void *col_bias, const float *scalars,
+                         int epilogue_kind, void *D, void *Aux, void *acc_out, void *workspace,
+                         size_t workspace_bytes, void *stream)
+{
+    const Operands o = {A, B, C, X, row_bias, col_bias, D, Aux, acc_out};
+    int rc = check_args(L, M, N, K, o, epilogue_kind);
+    if (rc != GEMM_EPI_OK) return rc;
+    if (!scalars) return GEMM_EPI_ERR_NULL_INPUT;
+    // the accumulator goes to acc_out when the kind returns it, else to the workspace
+    float *acc = (float *)(kind_has_acc_out(epilogue_kind) ? acc_out : workspace);
+    if (!kind_has_acc_out(epilogue_kind)) {
+        if (!workspace || workspace_bytes / 4 < (size_t)(L * M * N)) return GEMM_EPI_ERR_WORKSPACE;
+        if (!aligned(workspace, 4)) return GEMM_EPI_ERR_ALIGN;
+    }
+
+    // stage 1: the GEMM, writing only the fp32 accumulator
+    const Operands o1 = {A, B, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, acc};
+    const bool vec1 = use_fast_path(M, N, K, o1, ACC_STORE);
+    const TileCfg t = choose_tile(L, M, N, vec1);
+    const int64_t tm = (M + t.bm - 1) / t.bm, tn = (N + t.bn - 1) / t.bn;
+    const int64_t tiles = L * tm * tn;
+    if (tiles > INT32_MAX) return GEMM_EPI_ERR_SHAPE;
+    Params p = {};
+    p.A = (const _Float16 *)A;
+    p.B = (const _Float16 *)B;
+    p.acc_out = acc;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.tiles_m = (int)tm;
+    p.tiles_n = (int)tn;
+    p.num_tiles = (int)tiles;
+    p.group_m = L > 1 ? 2 : 8;
+    p.alpha = 1.0f;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t err = launch_kind<ACC_STORE>(p, t, vec1, s);
+
+    // stage 2: the epilogue, elementwise, from the accumulator in HBM
+    if (err == hipSuccess) {
+        EpiParams q;
+        q.acc = acc;
+        q.C = (const _Float16 *)C;
+        q.X = (const _Float16 *)X;
+        q.row_bias = (const _Float16 *)row_bias;
+        q.col_bias = (const _Float16 *)col_bias;
+        q.D = (_Float16 *)D;
+        q.Aux = (_Float16 *)Aux;
+        q.rows = L * M;
+        q.M = (int)M;
+        q.N = (int)N;
+        q.alpha = scalars[0];
+        q.beta = scalars[1];
+        q.s = scalars[2];
+        bool vec2 = N % 4 == 0 && aligned(acc, 16) && aligned(D, 8);
+        if (kind_reads_c(epilogue_kind)) vec2 = vec2 && aligned(C, 8);
+        if (kind_reads_x(epilogue_kind)) vec2 = vec2 && aligned(X, 8);
+        if (kind_reads_bias(epilogue_kind)) vec2 = vec2 && aligned(row_bias, 8);
+        if (kind_has_aux(epilogue_kind)) vec2 = vec2 && aligned(Aux, 8);
+        switch (epilogue_kind) {
+        case GEMM_EPI_LINCOMB: err = launch_epilogue<LINCOMB>(q, vec2, s); break;
+        case GEMM_EPI_AUX_SCALE: err = launch_epilogue<AUX_SCALE>(q, vec2, s); break;
+        case GEMM_EPI_LINCOMB_X_ACC: err = launch_epilogue<LINCOMB_X_ACC>(q, vec2, s); break;
+        case GEMM_EPI_RELU: err = launch_epilogue<RELU>(q, vec2, s); break;
+        case GEMM_EPI_SQUARE: err = launch_epilogue<SQUARE>(q, vec2, s); break;
+        case GEMM_EPI_RELU_SQUARE: err = launch_epilogue<RELU_SQUARE>(q, vec2, s); break;
+        case GEMM_EPI_RELU_AUX_STORE: err = launch_epilogue<RELU_AUX_STORE>(q, vec2, s); break;
+        case GEMM_EPI_RELU_SCALE_ACC: err = launch_epilogue<RELU_SCALE_ACC>(q, vec2, s); break;
+        default: err = launch_epilogue<BIAS_ROW_COL>(q, vec2, s); break;
+        }
     }
     if (err != hipSuccess) {
         g_last_hip_error = (int)err;

@@ -63,7 +63,10 @@ enum Kind : int {
     RELU_SQUARE = 5,
     RELU_AUX_STORE = 6,
     RELU_SCALE_ACC = 7,
-    BIAS_ROW_COL = 8
+    BIAS_ROW_COL = 8,
+    // not a public kind: the GEMM stage of the unfused composition, which
+    // writes only the fp32 accumulator
+    ACC_STORE = 16
 };
 
 __host__ __device__ constexpr bool kind_has_aux(int k)
@@ -72,9 +75,10 @@ __host__ __device__ constexpr bool kind_has_aux(int k)
            k == RELU_SCALE_ACC;
 }
 __host__ __device__ constexpr bool kind_reads_x(int k) { return k == LINCOMB_X_ACC; }
-__host__ __device__ constexpr bool kind_reads_c(int k) { return k != BIAS_ROW_COL; }
+__host__ __device__ constexpr bool kind_reads_c(int k) { return k != BIAS_ROW_COL && k != ACC_STORE; }
 __host__ __device__ constexpr bool kind_reads_bias(int k) { return k == BIAS_ROW_COL; }
-__host__ __device__ constexpr bool kind_has_acc_out(int k) { return k == RELU_SCALE_ACC; }
+__host__ __device__ constexpr bool kind_has_acc_out(int k) { return k == RELU_SCALE_ACC || k == ACC_STORE; }
+__host__ __device__ constexpr bool kind_writes_d(int k) { return k != ACC_STORE; }
 
 struct Params {
     const _Float16 *A;
@@ -132,8 +136,10 @@ __device__ __forceinline__ void epi_elem(float acc, float c, float x, float rb, 
         t = t > 0.0f ? t : 0.0f;
         a = t;
         d = s * t;
-    } else {  // BIAS_ROW_COL
+    } else if constexpr (KIND == BIAS_ROW_COL) {
         d = (alpha * acc + rb) + cb;
+    } else {  // ACC_STORE: nothing but the accumulator itself is written
+        d = acc;
     }
 }
 
@@ -681,7 +687,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
                         d4[e] = (_Float16)d;
                         e4[e] = (_Float16)a;
                     }
-                    *(half4 *)(p.D + o) = d4;
+                    if constexpr (kind_writes_d(KIND)) *(half4 *)(p.D + o) = d4;
                     if constexpr (kind_has_aux(KIND)) *(half4 *)(p.Aux + o) = e4;
                     if constexpr (kind_has_acc_out(KIND)) *(f32x4 *)(p.acc_out + o) = a4;
                 } else {
@@ -694,7 +700,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
                         const float rb = HAS_BIAS ? (float)p.row_bias[gn + e] : 0.0f;
                         float d, a = 0.0f;
                         epi_elem<KIND>(a4[e], c, x, rb, cbv, alpha, beta, s, d, a);
-                        p.D[o + e] = (_Float16)d;
+                        if constexpr (kind_writes_d(KIND)) p.D[o + e] = (_Float16)d;
                         if constexpr (kind_has_aux(KIND)) p.Aux[o + e] = (_Float16)a;
                         if constexpr (kind_has_acc_out(KIND)) p.acc_out[o + e] = a4[e];
                     }
@@ -702,6 +708,70 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
             }
         }
         wave_lds_sync();  // slab reads done before the next block row overwrites it
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The elementwise stage of the unfused composition: the same epilogue math on
+// an fp32 accumulator that a separate GEMM launch wrote to HBM.  It exists to
+// measure what the fusion saves (one more launch, the accumulator's write and
+// read); its results equal the fused kernel's bit for bit.  One row of one
+// batch entry per iteration of a block, so a lane knows its row and column
+// without a division; VEC: 4 consecutive columns per lane (N % 4 == 0,
+// 16-byte aligned accumulator, 8-byte aligned fp16 tensors).
+// ---------------------------------------------------------------------------
+struct EpiParams {
+    const float *acc;  // (L, M, N) fp32 accumulator
+    const _Float16 *C;
+    const _Float16 *X;
+    const _Float16 *row_bias;
+    const _Float16 *col_bias;
+    _Float16 *D;
+    _Float16 *Aux;
+    int64_t rows;  // L * M
+    int M, N;
+    float alpha, beta, s;
+};
+
+template <int KIND, bool VEC>
+__global__ __launch_bounds__(256) void epilogue_kernel(EpiParams q)
+{
+    const float alpha = q.alpha, beta = q.beta, s = q.s;
+    for (int64_t row = blockIdx.x; row < q.rows; row += gridDim.x) {
+        const int m = (int)(row % q.M);
+        const int64_t base = row * q.N;
+        const float cbv = kind_reads_bias(KIND) ? (float)q.col_bias[m] : 0.0f;
+        if constexpr (VEC) {
+            for (int n = 4 * threadIdx.x; n < q.N; n += 4 * blockDim.x) {
+                const int64_t o = base + n;
+                const f32x4 a4 = *(const f32x4 *)(q.acc + o);
+                half4 c4 = {}, x4 = {}, rb4 = {};
+                if constexpr (kind_reads_c(KIND)) c4 = *(const half4 *)(q.C + o);
+                if constexpr (kind_reads_x(KIND)) x4 = *(const half4 *)(q.X + o);
+                if constexpr (kind_reads_bias(KIND)) rb4 = *(const half4 *)(q.row_bias + n);
+                half4 d4, e4;
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    float d, a = 0.0f;
+                    epi_elem<KIND>(a4[e], (float)c4[e], (float)x4[e], (float)rb4[e], cbv, alpha, beta, s, d, a);
+                    d4[e] = (_Float16)d;
+                    e4[e] = (_Float16)a;
+                }
+                *(half4 *)(q.D + o) = d4;
+                if constexpr (kind_has_aux(KIND)) *(half4 *)(q.Aux + o) = e4;
+            }
+        } else {
+            for (int n = threadIdx.x; n < q.N; n += blockDim.x) {
+                const int64_t o = base + n;
+                const float c = kind_reads_c(KIND) ? (float)q.C[o] : 0.0f;
+                const float x = kind_reads_x(KIND) ? (float)q.X[o] : 0.0f;
+                const float rb = kind_reads_bias(KIND) ? (float)q.row_bias[n] : 0.0f;
+                float d, a = 0.0f;
+                epi_elem<KIND>(q.acc[o], c, x, rb, cbv, alpha, beta, s, d, a);
+                q.D[o] = (_Float16)d;
+                if constexpr (kind_has_aux(KIND)) q.Aux[o] = (_Float16)a;
+            }
+        }
     }
 }
 

@@ -32,6 +32,7 @@
 #ifndef GEMM_EPI_H
 #define GEMM_EPI_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -104,7 +105,8 @@ typedef enum {
     GEMM_EPI_ERR_KIND = 4,        /* unknown epilogue kind */
     GEMM_EPI_ERR_ALIGN = 5,       /* an fp16 pointer is not 2-byte aligned, or acc_out is not 4-byte
                                      aligned */
-    GEMM_EPI_ERR_HIP = 6          /* the launch failed; see gemm_epi_last_hip_error() */
+    GEMM_EPI_ERR_HIP = 6,         /* the launch failed; see gemm_epi_last_hip_error() */
+    GEMM_EPI_ERR_WORKSPACE = 7    /* gemm_epi_run_unfused: workspace NULL or smaller than L*M*N*4 bytes */
 } gemm_epi_status;
 
 /*
@@ -169,6 +171,33 @@ int gemm_epi_run(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, cons
 int gemm_epi_run_ext(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
                      const void *X, const void *row_bias, const void *col_bias, const float *scalars,
                      int epilogue_kind, void *D, void *Aux, void *acc_out, void *stream);
+
+/*
+ * gemm_epi_run_unfused -- the same operation as gemm_epi_run_ext, NOT fused:
+ * one launch computes the GEMM and writes the fp32 accumulator to HBM, a
+ * second, elementwise launch reads it back with C / X / the biases and
+ * writes the outputs.  This is the composition the pages' fusion replaces
+ * (Custom Epilogue Example, Overview: matmul, then scale/add, then the
+ * activation as separate kernels, with intermediates in global memory); it
+ * is here to measure what the fusion saves.  Its outputs equal those of
+ * gemm_epi_run_ext bit for bit (the same accumulator, the same fp32
+ * epilogue arithmetic).
+ *
+ *   workspace        device pointer to at least L*M*N*4 bytes (4-byte
+ *                    aligned; 16-byte aligned for the vector path) that
+ *                    receives the fp32 accumulator; owned by the caller.
+ *                    RELU_SCALE_ACC writes its accumulator to acc_out
+ *                    instead and may pass NULL.
+ *   workspace_bytes  its size in bytes.
+ *
+ * The other arguments, the ownership rules and the status codes are those of
+ * gemm_epi_run_ext; GEMM_EPI_ERR_WORKSPACE when the workspace is missing or
+ * too small.  The two launches are queued on `stream` in order.
+ */
+int gemm_epi_run_unfused(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                         const void *X, const void *row_bias, const void *col_bias, const float *scalars,
+                         int epilogue_kind, void *D, void *Aux, void *acc_out, void *workspace,
+                         size_t workspace_bytes, void *stream);
 
 /* A static, human-readable name for a status code ("unknown status" for
  * values outside the enum).  Never NULL. */

@@ -32,8 +32,8 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert set(names) == {"gemm_epi_run", "gemm_epi_run_ext", "gemm_epi_status_string", "gemm_epi_last_hip_error",
-                          "gemm_epi_plan", "gemm_epi_plan_ext"}
+    assert set(names) == {"gemm_epi_run", "gemm_epi_run_ext", "gemm_epi_run_unfused", "gemm_epi_status_string",
+                          "gemm_epi_last_hip_error", "gemm_epi_plan", "gemm_epi_plan_ext"}
     raw = ctypes.CDLL(binding.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -49,7 +49,7 @@ def test_enum_values_match_header():
 
 
 def test_status_strings():
-    for code in range(7):
+    for code in range(8):
         s = ge.gemm_epi_status_string(code)
         assert isinstance(s, str) and s
     assert ge.gemm_epi_status_string(0) == "ok"
@@ -120,6 +120,18 @@ def test_ext_operand_checks():
     assert plan_ext(kind=bias, C=None, rb=P16, cb=P16)[0] == 0   # the bias kind does not read C
     assert plan_ext(kind=acc, Aux=P16, acc=P16)[0] == 0
     assert plan_ext(kind=ge.KINDS["RELU_AUX_STORE"], Aux=P16)[0] == 0
+
+
+def test_unfused_workspace_checks():
+    def unfused(kind=0, ws=P16, ws_bytes=8 * 8 * 4, acc=None, Aux=P16):
+        return ge.gemm_epi_run_unfused(1, 8, 8, 8, P16, P16, P16, P16, P16, P16, SC, kind, P16, Aux, acc, ws,
+                                       ws_bytes, None)
+    assert unfused(ws=None) == 7
+    assert unfused(ws_bytes=8 * 8 * 4 - 1) == 7
+    assert unfused(ws=P2) == 5                      # fp32 workspace not 4-byte aligned
+    assert unfused(kind=ge.KINDS["RELU_SCALE_ACC"], ws=None, acc=None) == 3   # needs acc_out
+    assert unfused(kind=-3) == 4
+    assert ge.gemm_epi_status_string(7).startswith("the workspace")
 
 
 def test_ext_fast_path_conditions():
