@@ -118,6 +118,36 @@ def bench_gpu(w, steps, warmup):
     return {"ms_per_step": wall_ms, "kernel_ms": ev_ms, "launch_ms": stats, "plan": plan}
 
 
+def bench_gpu_stream_k(w, steps, warmup):
+    """The same workload through gemm_epi_run_ws, which splits K across
+    workgroups (stream-K) when the problem has too few tiles; None when no
+    split is planned for it."""
+    import torch
+    import dense_gemm_elementwise_amd as ge
+    from dense_gemm_elementwise_amd import workloads
+
+    dev = torch.device("cuda:0")
+    p = workloads.make_inputs(w)
+    t = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in p.items()}
+    D, Aux, Acc = _outputs(w, ge, dev)
+    stream = torch.cuda.current_stream(dev)
+    args = _device_args(w, t, D, Aux, Acc, stream, ge)
+    rc, plan = ge.gemm_epi_plan_ws(*args[:10], args[11], args[12], args[13], args[14])
+    if rc or plan["workspace_bytes"] == 0:
+        return None
+    ws = torch.zeros(plan["workspace_bytes"], dtype=torch.uint8, device=dev)
+    wargs = args[:15] + (ws.data_ptr(), plan["workspace_bytes"], args[15])
+    for _ in range(warmup):
+        rc = ge.gemm_epi_run_ws(*wargs)
+        if rc:
+            raise RuntimeError(ge.gemm_epi_status_string(rc))
+    _, ev_ms, stats = _timed_launches(lambda i: ge.gemm_epi_run_ws(*wargs), steps, stream)
+    return {"tile": [plan["bm"], plan["bn"], plan["bk"]], "workgroups": plan["workgroups"],
+            "workspace_bytes": plan["workspace_bytes"], "kernel_ms": round(ev_ms, 5),
+            "launch_ms": {k: round(v, 5) for k, v in stats.items()},
+            "tflops": round(w.flops / (ev_ms * 1e-3) / 1e12, 2), "roofline": roofline(w, ev_ms)}
+
+
 MALL_BYTES = 256 << 20  # MI355X Infinity Cache
 
 
@@ -359,6 +389,9 @@ def main():
             g = bench_gpu(other, a.steps, a.warmup)
             line = result_line(other, g, a.steps, a.warmup, None)
             line["cold"] = bench_gpu_cold(other, a.steps, a.warmup)
+            sk = bench_gpu_stream_k(other, a.steps, a.warmup)
+            if sk is not None:
+                line["stream_k"] = sk
             if a.compare_unfused:
                 line["unfused_own"] = bench_unfused_own(other, a.steps, a.warmup)
                 line["unfused_library"] = bench_unfused_library(other, a.steps, a.warmup)

@@ -42,8 +42,8 @@ STATUS = {
 }
 
 # every function include/gemm_epi.h declares
-EXPORTS = ("gemm_epi_run", "gemm_epi_run_ext", "gemm_epi_run_unfused", "gemm_epi_status_string",
-           "gemm_epi_last_hip_error", "gemm_epi_plan", "gemm_epi_plan_ext")
+EXPORTS = ("gemm_epi_run", "gemm_epi_run_ext", "gemm_epi_run_ws", "gemm_epi_run_unfused", "gemm_epi_status_string",
+           "gemm_epi_last_hip_error", "gemm_epi_plan", "gemm_epi_plan_ext", "gemm_epi_plan_ws")
 
 
 class GemmEpiError(RuntimeError):
@@ -74,6 +74,12 @@ def lib():
     L.gemm_epi_run_unfused.restype = ctypes.c_int
     L.gemm_epi_run_unfused.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_float),
                                        ctypes.c_int, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.gemm_epi_run_ws.restype = ctypes.c_int
+    L.gemm_epi_run_ws.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_float),
+                                  ctypes.c_int, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.gemm_epi_plan_ws.restype = ctypes.c_int
+    L.gemm_epi_plan_ws.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
+                                   ctypes.POINTER(i64)]
     L.gemm_epi_status_string.restype = ctypes.c_char_p
     L.gemm_epi_status_string.argtypes = [ctypes.c_int]
     L.gemm_epi_last_hip_error.restype = ctypes.c_int
@@ -130,6 +136,25 @@ def gemm_epi_run_unfused(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, ep
                                       stream)
 
 
+def gemm_epi_run_ws(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilogue_kind, D, Aux, acc_out,
+                    workspace, workspace_bytes, stream) -> int:
+    """Pointer-level call of gemm_epi_run_ws (may split K across workgroups,
+    stream-K, using the caller's zero-initialised workspace)."""
+    sc = (ctypes.c_float * 3)(*[float(v) for v in scalars]) if scalars is not None else None
+    return lib().gemm_epi_run_ws(int(L), int(M), int(N), int(K), A, B, C, X, row_bias, col_bias, sc,
+                                 _kind_id(epilogue_kind), D, Aux, acc_out, workspace, int(workspace_bytes), stream)
+
+
+def gemm_epi_plan_ws(L, M, N, K, A, B, C, X, row_bias, col_bias, epilogue_kind, D, Aux, acc_out):
+    """Host-only plan of gemm_epi_run_ws: (status, dict) with the keys of
+    gemm_epi_plan plus workspace_bytes (0: no split)."""
+    out = (ctypes.c_int64 * 7)()
+    rc = lib().gemm_epi_plan_ws(int(L), int(M), int(N), int(K), A, B, C, X, row_bias, col_bias,
+                                _kind_id(epilogue_kind), D, Aux, acc_out, out)
+    keys = ("bm", "bn", "bk", "vec", "workgroups", "threads", "workspace_bytes")
+    return rc, dict(zip(keys, list(out)))
+
+
 def gemm_epi_plan_ext(L, M, N, K, A, B, C, X, row_bias, col_bias, epilogue_kind, D, Aux, acc_out):
     """Host-only query of the launch configuration for gemm_epi_run_ext."""
     out = (ctypes.c_int64 * 6)()
@@ -167,7 +192,7 @@ def _ptr(t):
 
 
 def run(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, D, Aux=None, row_bias=None, col_bias=None,
-        acc_out=None, stream=None, sync=True, unfused_workspace=None):
+        acc_out=None, stream=None, sync=True, unfused_workspace=None, stream_k_workspace=None):
     """D (and Aux, acc_out) <- fused epilogue of A @ B on torch tensors.
 
     A (L,M,K), B (L,K,N), C, X, D, Aux (L,M,N): contiguous float16 CUDA
@@ -178,7 +203,10 @@ def run(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, D, Aux=None,
     default: the current stream); with sync=True the call waits for it.
     With unfused_workspace (a float32 CUDA tensor of at least L*M*N
     elements) the unfused two-launch composition runs instead of the fused
-    kernel (for comparison; the outputs are the same).
+    kernel (for comparison; the outputs are the same).  With
+    stream_k_workspace (a zero-initialised CUDA tensor of at least the
+    workspace_bytes gemm_epi_plan_ws reports) the call may split K across
+    workgroups (gemm_epi_run_ws).
     """
     import torch
     if A.dim() != 3 or B.dim() != 3:
@@ -219,8 +247,15 @@ def run(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, D, Aux=None,
     ws = unfused_workspace
     if ws is not None and (ws.dtype != torch.float32 or ws.device != dev or not ws.is_contiguous()):
         raise ValueError("unfused_workspace must be a contiguous float32 tensor on the operands' device")
+    skw = stream_k_workspace
+    if skw is not None and (skw.device != dev or not skw.is_contiguous()):
+        raise ValueError("stream_k_workspace must be a contiguous tensor on the operands' device")
     with torch.cuda.device(dev):
-        if ws is None:
+        if skw is not None:
+            rc = gemm_epi_run_ws(L, M, N, K, A.data_ptr(), B.data_ptr(), _ptr(C), _ptr(X), _ptr(row_bias),
+                                 _ptr(col_bias), (alpha, beta, s3), KINDS[kname], D.data_ptr(), _ptr(Aux),
+                                 _ptr(acc_out), skw.data_ptr(), skw.numel() * skw.element_size(), s.cuda_stream)
+        elif ws is None:
             rc = gemm_epi_run_ext(L, M, N, K, A.data_ptr(), B.data_ptr(), _ptr(C), _ptr(X), _ptr(row_bias),
                                   _ptr(col_bias), (alpha, beta, s3), KINDS[kname], D.data_ptr(), _ptr(Aux),
                                   _ptr(acc_out), s.cuda_stream)

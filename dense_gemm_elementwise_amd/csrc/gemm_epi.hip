@@ -5,6 +5,7 @@
 // Every check runs on the host before any HIP call, so a bad argument never
 // queues work and the checks run without a GPU.
 #include <hip/hip_runtime.h>
+#include <algorithm>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -122,15 +123,16 @@ bool use_fast_path(int64_t M, int64_t N, int64_t K, const Operands &o, int kind)
     return true;
 }
 
-template <int BM, int BN, int BK, int NS, int WGM, int WGN, int MI, int KIND, bool VEC>
-hipError_t launch_one(const Params &p, hipStream_t stream)
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, int MI, int KIND, bool VEC, bool SK = false>
+hipError_t launch_one(const Params &p, hipStream_t stream, int grid)
 {
-    hipLaunchKernelGGL((gemm_epi_kernel<BM, BN, BK, NS, WGM, WGN, MI, KIND, VEC>), dim3(p.num_tiles),
+    hipLaunchKernelGGL((gemm_epi_kernel<BM, BN, BK, NS, WGM, WGN, MI, KIND, VEC, SK>), dim3(grid),
                        dim3(64 * WGM * WGN), 0, stream, p);
     return hipGetLastError();
 }
 
-#define GE_LAUNCH(T, KIND, VEC) launch_one<T.bm, T.bn, T.bk, T.stages, T.wgm, T.wgn, T.mi, KIND, VEC>(p, stream)
+#define GE_LAUNCH(T, KIND, VEC) \
+    launch_one<T.bm, T.bn, T.bk, T.stages, T.wgm, T.wgn, T.mi, KIND, VEC>(p, stream, p.num_tiles)
 
 template <int KIND>
 hipError_t launch_kind(const Params &p, const TileCfg &t, bool vec, hipStream_t stream)
@@ -144,6 +146,89 @@ hipError_t launch_kind(const Params &p, const TileCfg &t, bool vec, hipStream_t 
 }
 
 #undef GE_LAUNCH
+
+// ---- stream-K ---------------------------------------------------------------
+// Tiles with a stream-K build: a workgroup walks a contiguous range of
+// (tile, k stage) units, so a few tiles can keep every CU busy.  (The
+// 8-wave 256 x 256 tile has no registers to spare for the range loop.)
+constexpr TileCfg kSkTiles[] = {{128, 128, 64, 3, 2, 2, 32}};
+
+struct SkPlan {
+    bool on = false;
+    TileCfg t{};
+    int groups = 0;
+    int64_t tiles = 0, units = 0;
+    size_t workspace = 0;  // bytes: partial slots, then one counter per tile
+};
+
+size_t sk_partials_bytes(const TileCfg &t, int groups) { return (size_t)2 * groups * t.bm * t.bn * 4; }
+
+// Chooses between the one-tile-per-workgroup grid and a stream-K split, and
+// the split's workgroup count, by a cost model in units of (tile area /
+// efficiency) x K: waves x K for the former; for the latter the busiest
+// workgroup's k stages plus, when a tile is split, a fixed cost and a cost
+// per contributor of the most-split tile.  Both were fitted to run times of a
+// 256 x 256 x 65536 product split over 16..256 workgroups on MI355X (one k
+// stage of the 128 x 128 x 64 tile took about 0.76 us): about 8.5 stages for
+// the device-scope fences and the counter, and about 1.6 stages for each
+// partial sum the last contributor reads back.  Contributors of one tile
+// work at different k, so their operand streams (32 KB per k stage and
+// workgroup) share little in L2: past about 5.5 TB/s of such streams (some
+// 128 workgroups at that stage time) a stage takes longer in proportion, as
+// measured on 512..1024-square tiles with K of 8192..65536.  Fewer
+// workgroups mean more k stages each but fewer partial sums per tile, so the
+// count is searched.  A split is taken only when it wins clearly (by 15%).
+SkPlan plan_stream_k(int64_t L, int64_t M, int64_t N, int64_t K, bool vec)
+{
+    constexpr double kFixedStages = 8.5, kPerContributorStages = 1.6;
+    constexpr double kStageSeconds = 0.76e-6, kOperandBytesPerSecond = 5.5e12;
+    SkPlan best;
+    if (!vec) return best;
+    const TileCfg dp = choose_tile(L, M, N, vec);
+    const int64_t dp_tiles = L * ((M + dp.bm - 1) / dp.bm) * ((N + dp.bn - 1) / dp.bn);
+    const double dp_cost = (double)((dp_tiles + kNumCUs - 1) / kNumCUs) * ((K + dp.bk - 1) / dp.bk) * dp.bk *
+                           dp.bm * dp.bn / tile_efficiency(dp.bm, dp.bn);
+    double best_cost = 0.85 * dp_cost;
+    for (const TileCfg &t : kSkTiles) {
+        const int64_t tiles = L * ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+        const int64_t nk = (K + t.bk - 1) / t.bk;
+        const int64_t units = tiles * nk;
+        if (tiles > INT32_MAX || units < 2) continue;
+        const double stage = (double)t.bk * t.bm * t.bn / tile_efficiency(t.bm, t.bn);
+        for (int groups = kNumCUs; groups >= 1; groups /= 2) {
+            if (groups > units) continue;
+            const int64_t per = (units + groups - 1) / groups;
+            const bool split = per < nk || units % groups != 0 || (units / groups) % nk != 0;
+            // a tile's k stages meet at most this many workgroup ranges
+            const int64_t contrib = split ? std::min<int64_t>((nk + per - 2) / per + 1, groups) : 1;
+            const double stream = (double)groups * (t.bm + t.bn) * t.bk * 2 / kOperandBytesPerSecond;
+            const double slowdown = std::max(1.0, stream / kStageSeconds);
+            const double cost =
+                (per * slowdown + (split ? kFixedStages + kPerContributorStages * (double)contrib : 0.0)) * stage;
+            if (cost < best_cost) {
+                best_cost = cost;
+                best.on = true;
+                best.t = t;
+                best.groups = groups;
+                best.tiles = tiles;
+                best.units = units;
+                best.workspace = sk_partials_bytes(t, groups) + (size_t)tiles * 4;
+            }
+        }
+    }
+    return best;
+}
+
+template <int KIND>
+hipError_t launch_kind_sk(Params p, const SkPlan &sk, void *workspace, hipStream_t stream)
+{
+    p.sk_q = sk.units / sk.groups;
+    p.sk_r = sk.units % sk.groups;
+    p.partials = (float *)workspace;
+    p.counters = (int *)((char *)workspace + sk_partials_bytes(sk.t, sk.groups));
+    constexpr TileCfg T = kSkTiles[0];
+    return launch_one<T.bm, T.bn, T.bk, T.stages, T.wgm, T.wgn, T.mi, KIND, true, true>(p, stream, sk.groups);
+}
 
 // The elementwise stage of the unfused composition.
 template <int KIND>
@@ -172,7 +257,7 @@ const char *gemm_epi_status_string(int status)
     case GEMM_EPI_ERR_KIND: return "unknown epilogue kind";
     case GEMM_EPI_ERR_ALIGN: return "a tensor pointer is not aligned to its element size";
     case GEMM_EPI_ERR_HIP: return "HIP launch error";
-    case GEMM_EPI_ERR_WORKSPACE: return "the workspace is missing or smaller than L*M*N*4 bytes";
+    case GEMM_EPI_ERR_WORKSPACE: return "the workspace is missing or smaller than the call needs";
     default: return "unknown status";
     }
 }
@@ -334,6 +419,92 @@ int gemm_epi_run_unfused(int64_t L, int64_t M, int64_t N, int64_t K, const void 
         case GEMM_EPI_RELU_SCALE_ACC: err = launch_epilogue<RELU_SCALE_ACC>(q, vec2, s); break;
         default: err = launch_epilogue<BIAS_ROW_COL>(q, vec2, s); break;
         }
+    }
+    if (err != hipSuccess) {
+        g_last_hip_error = (int)err;
+        return GEMM_EPI_ERR_HIP;
+    }
+    return GEMM_EPI_OK;
+}
+
+int gemm_epi_plan_ws(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                     const void *X, const void *row_bias, const void *col_bias, int epilogue_kind, const void *D,
+                     const void *Aux, const void *acc_out, int64_t out[7])
+{
+    const Operands o = {A, B, C, X, row_bias, col_bias, D, Aux, acc_out};
+    int rc = check_args(L, M, N, K, o, epilogue_kind);
+    if (rc != GEMM_EPI_OK) return rc;
+    const bool vec = use_fast_path(M, N, K, o, epilogue_kind);
+    const SkPlan sk = plan_stream_k(L, M, N, K, vec);
+    if (!sk.on) {
+        int64_t o6[6];
+        rc = gemm_epi_plan_ext(L, M, N, K, A, B, C, X, row_bias, col_bias, epilogue_kind, D, Aux, acc_out, o6);
+        if (rc == GEMM_EPI_OK && out) {
+            for (int q = 0; q < 6; q++) out[q] = o6[q];
+            out[6] = 0;
+        }
+        return rc;
+    }
+    if (out) {
+        out[0] = sk.t.bm;
+        out[1] = sk.t.bn;
+        out[2] = sk.t.bk;
+        out[3] = 1;
+        out[4] = sk.groups;
+        out[5] = 64 * sk.t.wgm * sk.t.wgn;
+        out[6] = (int64_t)sk.workspace;
+    }
+    return GEMM_EPI_OK;
+}
+
+int gemm_epi_run_ws(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                    const void *X, const void *row_bias, const void *col_bias, const float *scalars, int epilogue_kind,
+                    void *D, void *Aux, void *acc_out, void *workspace, size_t workspace_bytes, void *stream)
+{
+    const Operands o = {A, B, C, X, row_bias, col_bias, D, Aux, acc_out};
+    int rc = check_args(L, M, N, K, o, epilogue_kind);
+    if (rc != GEMM_EPI_OK) return rc;
+    if (!scalars) return GEMM_EPI_ERR_NULL_INPUT;
+    const bool vec = use_fast_path(M, N, K, o, epilogue_kind);
+    const SkPlan sk = plan_stream_k(L, M, N, K, vec);
+    if (!sk.on)
+        return gemm_epi_run_ext(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilogue_kind, D, Aux,
+                                acc_out, stream);
+    if (!workspace || workspace_bytes < sk.workspace) return GEMM_EPI_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return GEMM_EPI_ERR_ALIGN;
+
+    Params p = {};
+    p.A = (const _Float16 *)A;
+    p.B = (const _Float16 *)B;
+    p.C = (const _Float16 *)C;
+    p.X = (const _Float16 *)X;
+    p.D = (_Float16 *)D;
+    p.Aux = (_Float16 *)Aux;
+    p.row_bias = (const _Float16 *)row_bias;
+    p.col_bias = (const _Float16 *)col_bias;
+    p.acc_out = (float *)acc_out;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.tiles_m = (int)((M + sk.t.bm - 1) / sk.t.bm);
+    p.tiles_n = (int)((N + sk.t.bn - 1) / sk.t.bn);
+    p.num_tiles = (int)sk.tiles;
+    p.group_m = L > 1 ? 2 : 8;
+    p.alpha = scalars[0];
+    p.beta = scalars[1];
+    p.s = scalars[2];
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t err;
+    switch (epilogue_kind) {
+    case GEMM_EPI_LINCOMB: err = launch_kind_sk<LINCOMB>(p, sk, workspace, s); break;
+    case GEMM_EPI_AUX_SCALE: err = launch_kind_sk<AUX_SCALE>(p, sk, workspace, s); break;
+    case GEMM_EPI_LINCOMB_X_ACC: err = launch_kind_sk<LINCOMB_X_ACC>(p, sk, workspace, s); break;
+    case GEMM_EPI_RELU: err = launch_kind_sk<RELU>(p, sk, workspace, s); break;
+    case GEMM_EPI_SQUARE: err = launch_kind_sk<SQUARE>(p, sk, workspace, s); break;
+    case GEMM_EPI_RELU_SQUARE: err = launch_kind_sk<RELU_SQUARE>(p, sk, workspace, s); break;
+    case GEMM_EPI_RELU_AUX_STORE: err = launch_kind_sk<RELU_AUX_STORE>(p, sk, workspace, s); break;
+    case GEMM_EPI_RELU_SCALE_ACC: err = launch_kind_sk<RELU_SCALE_ACC>(p, sk, workspace, s); break;
+    default: err = launch_kind_sk<BIAS_ROW_COL>(p, sk, workspace, s); break;
     }
     if (err != hipSuccess) {
         g_last_hip_error = (int)err;

@@ -95,6 +95,12 @@ struct Params {
     int num_tiles;    // L * tiles_m * tiles_n
     int group_m;      // tile rows per L2 group (>= 1)
     float alpha, beta, s;
+    // stream-K split (only read by the kernels built for it): the L*tiles
+    // (tile, k stage) units in tile-major order, sk_q or sk_q + 1 of them per
+    // workgroup (the first sk_r workgroups take one more)
+    int64_t sk_q, sk_r;
+    float *partials;  // 2 slots of BM*BN floats per workgroup
+    int *counters;    // one per tile, zero between calls
 };
 
 // ---------------------------------------------------------------------------
@@ -150,13 +156,17 @@ __device__ __forceinline__ void epi_elem(float acc, float c, float x, float rb, 
 // entry tiles are ordered in groups of p.group_m tile rows, column-major
 // inside a group, so the tiles an XCD runs together share operand panels.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void map_tile(const Params &p, int &l, int &tm, int &tn)
+// logical index of workgroup w among nwg: consecutive on one XCD
+__device__ __forceinline__ int xcd_logical_id(int nwg, int w)
 {
-    const int nwg = p.num_tiles;
-    const int w = blockIdx.x;
     const int xcd = w & 7, j = w >> 3;
     const int per = nwg >> 3, rem = nwg & 7;
-    const int t = xcd * per + (xcd < rem ? xcd : rem) + j;
+    return xcd * per + (xcd < rem ? xcd : rem) + j;
+}
+
+// logical tile t -> (batch, tile row, tile column) in the grouped order
+__device__ __forceinline__ void tile_coords(const Params &p, int t, int &l, int &tm, int &tn)
+{
     const int tpb = p.tiles_m * p.tiles_n;
     l = t / tpb;
     const int r = t - l * tpb;
@@ -168,6 +178,29 @@ __device__ __forceinline__ void map_tile(const Params &p, int &l, int &tm, int &
     const int rr = r - g * gsize_full;
     tm = first_m + rr % gm;
     tn = rr / gm;
+}
+
+__device__ __forceinline__ void map_tile(const Params &p, int &l, int &tm, int &tn)
+{
+    tile_coords(p, xcd_logical_id(p.num_tiles, blockIdx.x), l, tm, tn);
+}
+
+// Stream-K bookkeeping.  Units are (tile, k stage) pairs in tile-major order;
+// workgroup w (logical) owns units [sk_begin(w), sk_begin(w + 1)).
+__device__ __forceinline__ int64_t sk_begin(const Params &p, int w)
+{
+    return (int64_t)w * p.sk_q + (w < p.sk_r ? w : p.sk_r);
+}
+__device__ __forceinline__ int sk_owner(const Params &p, int64_t u)  // the workgroup owning unit u
+{
+    const int64_t big = p.sk_r * (p.sk_q + 1);
+    return u < big ? (int)(u / (p.sk_q + 1)) : (int)(p.sk_r + (u - big) / p.sk_q);
+}
+// A workgroup contributes partial sums to at most two tiles: the one its
+// range starts in (slot 2w) and the one it ends in (slot 2w + 1).
+__device__ __forceinline__ int sk_slot(const Params &p, int w, int t, int nk_tile)
+{
+    return 2 * w + (sk_begin(p, w) / nk_tile == t ? 0 : 1);
 }
 
 // Swizzles (in 16-byte chunk units).  An A row holds A_CHUNKS = BK/8 chunks;
@@ -289,7 +322,7 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void *p)
 // vectors); otherwise every global access is element-wise and guarded and
 // LDS is filled through registers.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int NSTAGES, int WGM, int WGN, int MI, int KIND, bool VEC>
+template <int BM, int BN, int BK, int NSTAGES, int WGM, int WGN, int MI, int KIND, bool VEC, bool SK = false>
 __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
 {
     constexpr int NW = WGM * WGN;                // waves per workgroup
@@ -325,11 +358,17 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     const int wave = tid >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
 
-    int l, tm, tn;
-    map_tile(p, l, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
     const int M = p.M, N = p.N, K = p.K;
+    const int nk_tile = (K + BK - 1) / BK;
+    __shared__ int sk_ticket;
 
+    // One segment: the k stages [kb, ke) of tile t = (l, tm, tn).  It ends
+    // with the epilogue, unless it covers only part of the tile's k range
+    // (stream-K), in which case it publishes its partial sum and only the
+    // last contributor of the tile goes on to the epilogue.
+    auto segment = [&](const int l, const int tm, const int tn, const int t, const int kb, const int ke,
+                       const int lw) {
+    const int m0 = tm * BM, n0 = tn * BN;
     const _Float16 *Al = p.A + (int64_t)l * M * K;
     const _Float16 *Bl = p.B + (int64_t)l * K * N;
 
@@ -341,7 +380,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
 #pragma unroll
             for (int r = 0; r < NACC; r++) acc[i][j][r] = 0.0f;
 
-    const int nk = (K + BK - 1) / BK;
+    const int nk = ke - kb;  // k stages in this segment
 
     // ---- global -> LDS --------------------------------------------------
     // One wave instruction fills 1 KB: 1024 / A_ROW rows of A, or
@@ -523,7 +562,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     half8 fa[2][TM], fb[2][TN];
 #pragma unroll
     for (int st = 0; st < NSTAGES; st++)
-        if (st < nk) load_stage(st, st * BK);
+        if (st < nk) load_stage(st, (kb + st) * BK);
     wait_stage(newer_prologue{}, nk >= NSTAGES);
     if constexpr (!VEC) __syncthreads();
     barrier_lds();
@@ -546,7 +585,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
         wait_stage(newer_steady{}, kt + NSTAGES <= nk);  // stage kt+1 landed (this thread's part)
         if constexpr (!VEC) __syncthreads();
         barrier_lds();  // everyone's part landed; stage kt's slot is free
-        if (kt + NSTAGES < nk) load_stage(cur, (kt + NSTAGES) * BK);
+        if (kt + NSTAGES < nk) load_stage(cur, (kb + kt + NSTAGES) * BK);
         read_frags(nxt, 0, fa[(p0 + KSTEPS) & 1], fb[(p0 + KSTEPS) & 1]);
         mfmas(fa[(p0 + KSTEPS - 1) & 1], fb[(p0 + KSTEPS - 1) & 1]);
     };
@@ -584,6 +623,66 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
             last_stage(cur, P1{});
         } else {            // one stage left, starting in buffer 0
             last_stage(cur, P0{});
+        }
+    }
+
+    // ---- stream-K: partial sums of a split tile -------------------------------
+    if constexpr (SK) {
+        if (kb != 0 || ke != nk_tile) {
+            constexpr int SLOT = BM * BN;  // floats
+            const int64_t u0 = (int64_t)t * nk_tile;
+            const int w_first = sk_owner(p, u0), w_last = sk_owner(p, u0 + nk_tile - 1);
+            const int ncontrib = w_last - w_first + 1;
+            // This contributor's sum in the accumulator register layout, 16 bytes
+            // per lane and store: one instruction writes 1 KB, contiguous.  The
+            // device-scope release fence makes it visible to every XCD before the
+            // tile's counter is incremented; the last contributor's acquire fence
+            // makes every contributor's sum visible to it.
+            constexpr int NQ = NACC / 4;
+            float *mine = p.partials + (int64_t)sk_slot(p, lw, t, nk_tile) * SLOT;
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int j = 0; j < TN; j++)
+#pragma unroll
+                    for (int q = 0; q < NQ; q++) {
+                        f32x4 v;
+#pragma unroll
+                        for (int e = 0; e < 4; e++) v[e] = acc[i][j][4 * q + e];
+                        *(f32x4 *)(mine + ((((wave * TM + i) * TN + j) * NQ + q) * 64 + lane) * 4) = v;
+                    }
+            __threadfence();  // release (device scope)
+            __syncthreads();
+            if (tid == 0)
+                sk_ticket = __hip_atomic_fetch_add(p.counters + t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            if (sk_ticket != ncontrib - 1) return;  // another contributor finishes this tile
+            __threadfence();  // acquire (device scope)
+            // The sum in contributor (k) order, the same whichever contributor is
+            // last.  All of one contributor's loads are issued before any add, so
+            // each contributor costs one memory round trip, not one per load.
+            for (int c = 0; c < ncontrib; c++) {
+                const float *src = p.partials + (int64_t)sk_slot(p, w_first + c, t, nk_tile) * SLOT;
+                f32x4 v[TM][TN][NQ];
+#pragma unroll
+                for (int i = 0; i < TM; i++)
+#pragma unroll
+                    for (int j = 0; j < TN; j++)
+#pragma unroll
+                        for (int q = 0; q < NQ; q++)
+                            v[i][j][q] = *(const f32x4 *)(src + ((((wave * TM + i) * TN + j) * NQ + q) * 64 + lane) * 4);
+#pragma unroll
+                for (int i = 0; i < TM; i++)
+#pragma unroll
+                    for (int j = 0; j < TN; j++)
+#pragma unroll
+                        for (int q = 0; q < NQ; q++)
+#pragma unroll
+                            for (int e = 0; e < 4; e++)
+                                acc[i][j][4 * q + e] = c == 0 ? v[i][j][q][e] : acc[i][j][4 * q + e] + v[i][j][q][e];
+            }
+            if (tid == 0)  // every contributor has arrived: ready for the next call
+                __hip_atomic_store(p.counters + t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 
@@ -708,6 +807,28 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
             }
         }
         wave_lds_sync();  // slab reads done before the next block row overwrites it
+    }
+    };  // segment
+
+    if constexpr (!SK) {
+        int l, tm, tn;
+        map_tile(p, l, tm, tn);
+        segment(l, tm, tn, 0, 0, nk_tile, 0);
+    } else {
+        // stream-K: this workgroup's contiguous range of (tile, k stage) units
+        const int lw = xcd_logical_id(gridDim.x, blockIdx.x);
+        int64_t u = sk_begin(p, lw);
+        const int64_t ue = sk_begin(p, lw + 1);
+        while (u < ue) {
+            const int t = (int)(u / nk_tile);
+            const int kb = (int)(u - (int64_t)t * nk_tile);
+            const int ke = (int)min((int64_t)nk_tile, (int64_t)kb + (ue - u));
+            int l, tm, tn;
+            tile_coords(p, t, l, tm, tn);
+            segment(l, tm, tn, t, kb, ke, lw);
+            u += ke - kb;
+            __syncthreads();  // LDS free before the next segment's DMA
+        }
     }
 }
 

@@ -94,6 +94,9 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in (
     # the heaviest and the lightest of those epilogues at the headline size
     Workload("relu_scale_acc_8192", 1, 8192, 8192, 8192, "RELU_SCALE_ACC", 1.0, 2.0, 0.5, "normal", 2025, False),
     Workload("bias_row_col_8192", 1, 8192, 8192, 8192, "BIAS_ROW_COL", 1.0, 0.0, 0.0, "normal", 2025, False),
+    # few output tiles and a deep K (not one of the pages' runs): the case a
+    # stream-K split of K across workgroups is for
+    Workload("lincomb_deep_k_256x256x65536", 1, 256, 256, 65536, "LINCOMB", 1.0, 2.0, 0.0, "normal", 2025, False),
 )}
 
 # The workload the headline throughput is quoted on.

@@ -106,7 +106,8 @@ typedef enum {
     GEMM_EPI_ERR_ALIGN = 5,       /* an fp16 pointer is not 2-byte aligned, or acc_out is not 4-byte
                                      aligned */
     GEMM_EPI_ERR_HIP = 6,         /* the launch failed; see gemm_epi_last_hip_error() */
-    GEMM_EPI_ERR_WORKSPACE = 7    /* gemm_epi_run_unfused: workspace NULL or smaller than L*M*N*4 bytes */
+    GEMM_EPI_ERR_WORKSPACE = 7    /* the workspace is NULL or smaller than the call needs
+                                     (gemm_epi_run_unfused, gemm_epi_run_ws) */
 } gemm_epi_status;
 
 /*
@@ -198,6 +199,41 @@ int gemm_epi_run_unfused(int64_t L, int64_t M, int64_t N, int64_t K, const void 
                          const void *X, const void *row_bias, const void *col_bias, const float *scalars,
                          int epilogue_kind, void *D, void *Aux, void *acc_out, void *workspace,
                          size_t workspace_bytes, void *stream);
+
+/*
+ * gemm_epi_run_ws -- gemm_epi_run_ext that may split the K range of tiles
+ * across workgroups (stream-K scheduling, the Python examples article's
+ * "Basic GEMM" swizzling option) when the problem has too few tiles to keep
+ * every compute unit busy.  The partial sums of a split tile go to the
+ * workspace; the last workgroup to finish its part of the tile adds them up,
+ * in k order, and applies the epilogue (the epilogue is not linear, so it
+ * only ever sees the full sum).  Where splitting does not pay, the call is
+ * exactly gemm_epi_run_ext and the workspace is not touched.
+ *
+ *   workspace        device pointer, 16-byte aligned, of at least the size
+ *                    gemm_epi_plan_ws reports in out[6] (0 when no split is
+ *                    planned: NULL is then accepted); owned by the caller.  It
+ *                    must be zero-filled before its first use (e.g. one
+ *                    hipMemset); every call leaves it ready for the next.
+ *   workspace_bytes  its size in bytes.
+ *
+ * Calls that share one workspace must not overlap in time (two streams
+ * running them concurrently race).  The sum of a split tile is ordered the
+ * same way on every call, so results are deterministic; they can differ
+ * from gemm_epi_run_ext's in the last bits of fp32 summation order
+ * (identical on integer-valued inputs).  Status codes as gemm_epi_run_ext,
+ * plus GEMM_EPI_ERR_WORKSPACE.
+ */
+int gemm_epi_run_ws(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                    const void *X, const void *row_bias, const void *col_bias, const float *scalars, int epilogue_kind,
+                    void *D, void *Aux, void *acc_out, void *workspace, size_t workspace_bytes, void *stream);
+
+/* gemm_epi_plan_ext for gemm_epi_run_ws: out[0..5] as gemm_epi_plan (out[4] is
+ * the number of workgroups, the split's workgroup count when it splits), and
+ * out[6] the workspace bytes the call needs (0: no split). */
+int gemm_epi_plan_ws(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                     const void *X, const void *row_bias, const void *col_bias, int epilogue_kind, const void *D,
+                     const void *Aux, const void *acc_out, int64_t out[7]);
 
 /* A static, human-readable name for a status code ("unknown status" for
  * values outside the enum).  Never NULL. */

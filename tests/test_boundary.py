@@ -32,8 +32,9 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert set(names) == {"gemm_epi_run", "gemm_epi_run_ext", "gemm_epi_run_unfused", "gemm_epi_status_string",
-                          "gemm_epi_last_hip_error", "gemm_epi_plan", "gemm_epi_plan_ext"}
+    assert set(names) == {"gemm_epi_run", "gemm_epi_run_ext", "gemm_epi_run_ws", "gemm_epi_run_unfused",
+                          "gemm_epi_status_string", "gemm_epi_last_hip_error", "gemm_epi_plan", "gemm_epi_plan_ext",
+                          "gemm_epi_plan_ws"}
     raw = ctypes.CDLL(binding.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -134,6 +135,39 @@ def test_unfused_workspace_checks():
     assert ge.gemm_epi_status_string(7).startswith("the workspace")
 
 
+def test_stream_k_plan_and_workspace_checks():
+    def plan_ws(L, M, N, K):
+        return ge.gemm_epi_plan_ws(L, M, N, K, P16, P16, P16, None, None, None, 0, P16, None, None)
+    # few tiles, long K: split over 128 x 128 tiles.  The workgroup count is
+    # searched: a shorter K per workgroup against more partial sums per tile
+    # (for 256 x 256 x 65536, 128 workgroups measured fastest of 16..256).  The
+    # workspace holds two partial slots per workgroup plus a counter per tile.
+    rc, cfg = plan_ws(1, 256, 256, 65536)
+    assert rc == 0 and (cfg["bm"], cfg["bn"], cfg["workgroups"]) == (128, 128, 128)
+    assert cfg["workspace_bytes"] == 2 * 128 * 128 * 128 * 4 + 4 * 4
+    rc, cfg = plan_ws(1, 256, 256, 16384)
+    assert rc == 0 and (cfg["bm"], cfg["bn"], cfg["workgroups"]) == (128, 128, 64)
+    assert cfg["workspace_bytes"] == 2 * 64 * 128 * 128 * 4 + 4 * 4
+    for shape in ((1, 200, 304, 12000), (2, 128, 384, 8192), (1, 512, 512, 8192)):
+        rc, cfg = plan_ws(*shape)
+        assert rc == 0 and cfg["workspace_bytes"] > 0, shape
+    # enough tiles (or too short a K for the split's fixed cost): no split, no
+    # workspace, the same plan as gemm_epi_plan
+    # (1024 x 1024 x 8192 measured slower split at 256 workgroups: the
+    # contributors' operand streams share little in L2)
+    for shape in ((1, 8192, 8192, 8192), (1, 1024, 1024, 1024), (1, 128, 128, 128), (1, 1024, 1024, 8192)):
+        rc, cfg = plan_ws(*shape)
+        rc0, cfg0 = ge.gemm_epi_plan(*shape, P16, P16, P16, None, 0, P16, None)
+        assert rc == rc0 == 0 and cfg["workspace_bytes"] == 0
+        assert all(cfg[k] == cfg0[k] for k in cfg0), shape
+    # a split call without (enough) workspace is refused before any launch
+    need = 2 * 64 * 128 * 128 * 4 + 4 * 4
+    args = (1, 256, 256, 16384, P16, P16, P16, None, None, None, SC, 0, P16, None, None)
+    assert ge.gemm_epi_run_ws(*args, None, need, None) == 7
+    assert ge.gemm_epi_run_ws(*args, P16, need - 1, None) == 7
+    assert ge.gemm_epi_run_ws(*args, 0x7F0000001008, need, None) == 5   # not 16-byte aligned
+
+
 def test_ext_fast_path_conditions():
     bias, acc = ge.KINDS["BIAS_ROW_COL"], ge.KINDS["RELU_SCALE_ACC"]
     rc, cfg = plan_ext(kind=bias, C=None, rb=P16, cb=P2)
@@ -181,6 +215,7 @@ def test_plan_tiles_for_the_workloads():
         "bias_row_col_1024": (64, 64, 256),
         "relu_scale_acc_8192": (256, 256, 1024),
         "bias_row_col_8192": (256, 256, 1024),
+        "lincomb_deep_k_256x256x65536": (64, 64, 16),
     }
     assert set(want) == set(workloads.WORKLOADS)
     for name, (bm, bn, wgs) in want.items():
