@@ -106,44 +106,45 @@ struct Params {
 // ---------------------------------------------------------------------------
 // Epilogue math, fp32.  d = first output, a = second output (if any); rb /
 // cb are the row-broadcast bias of the element's column and the
-// column-broadcast bias of its row.
+// column-broadcast bias of its row.  The roundings are fixed here, not left
+// to the compiler's contraction of multiply-adds (which follows the shape of
+// the calling code): alpha*acc + beta*c is fma(alpha, acc, beta*c), + s*x is
+// one more fma, and nothing else is contracted.  So every kernel that applies
+// an epilogue (the fused GEMM, the elementwise stage of the unfused
+// composition) gives bit-identical outputs.
 // ---------------------------------------------------------------------------
 template <int KIND>
 __device__ __forceinline__ void epi_elem(float acc, float c, float x, float rb, float cb, float alpha, float beta,
                                          float s, float &d, float &a)
 {
+#pragma clang fp contract(off)
+    const float lin = __builtin_fmaf(alpha, acc, beta * c);
     if constexpr (KIND == LINCOMB) {
-        d = alpha * acc + beta * c;
+        d = lin;
     } else if constexpr (KIND == AUX_SCALE) {
-        float t = alpha * acc + beta * c;
-        a = t;
-        d = s * t;
+        a = lin;
+        d = s * lin;
     } else if constexpr (KIND == LINCOMB_X_ACC) {
         a = acc;
-        d = (alpha * acc + beta * c) + s * x;
+        d = __builtin_fmaf(s, x, lin);
     } else if constexpr (KIND == RELU) {
-        float t = alpha * acc + beta * c;
-        d = t > 0.0f ? t : 0.0f;
+        d = lin > 0.0f ? lin : 0.0f;
     } else if constexpr (KIND == SQUARE) {
-        float t = alpha * acc + beta * c;
-        d = t;
-        a = t * t;
+        d = lin;
+        a = lin * lin;
     } else if constexpr (KIND == RELU_SQUARE) {
-        float t = alpha * acc + beta * c;
-        t = t > 0.0f ? t : 0.0f;
+        const float t = lin > 0.0f ? lin : 0.0f;
         d = t;
         a = t * t;
     } else if constexpr (KIND == RELU_AUX_STORE) {
-        float t = alpha * acc + beta * c;
-        a = t;
-        d = t > 0.0f ? t : 0.0f;
+        a = lin;
+        d = lin > 0.0f ? lin : 0.0f;
     } else if constexpr (KIND == RELU_SCALE_ACC) {
-        float t = alpha * acc + beta * c;
-        t = t > 0.0f ? t : 0.0f;
+        const float t = lin > 0.0f ? lin : 0.0f;
         a = t;
         d = s * t;
     } else if constexpr (KIND == BIAS_ROW_COL) {
-        d = (alpha * acc + rb) + cb;
+        d = __builtin_fmaf(alpha, acc, rb) + cb;
     } else {  // ACC_STORE: nothing but the accumulator itself is written
         d = acc;
     }
@@ -710,13 +711,21 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
 
     // ---- epilogue ----------------------------------------------------------
     // The wave tile is handled one MFMA row-block (SLAB rows) at a time.  In a
-    // slab, pass p covers rows 4p..4p+3; lane owns row 4p + lane/16 and the
-    // 4-column groups 4*(lane%16) (+ WN/2).  C / X (and the column bias) of a
-    // slab are loaded into registers one slab ahead, so the loads' latency
-    // hides behind the previous slab's work; a lane's columns are the same in
-    // every slab, so its row-bias values are loaded once.
+    // slab, pass p covers rows 4p..4p+3; lane owns row 4p + lane/16 and CPL
+    // consecutive columns from CPL*(lane%16) (+ a second group at WN/2 for a
+    // 128-wide tile read 4 columns per lane).  CPL = 8 where the wave tile is
+    // 128 wide: 16-byte loads and stores, half the vector memory instructions
+    // of 4 columns per lane (measured 5% faster on the 16-batch products).  A
+    // kind with the fp32 accumulator output keeps 4 columns per lane: with 8,
+    // each 16-byte fp32 store instruction would fill only half of every cache
+    // line it touches (measured 6% slower).  C / X (and the column bias) of a slab are loaded
+    // into registers one slab ahead, so the loads' latency hides behind the
+    // previous slab's work; a lane's columns are the same in every slab, so its
+    // row-bias values are loaded once.
+    constexpr int CPL = WN % 128 == 0 && !kind_has_acc_out(KIND) ? 8 : 4;
+    using hvec = typename std::conditional<CPL == 8, half8, half4>::type;
     constexpr int EPI_PASSES = SLAB / 4;
-    constexpr int EPI_GROUPS = WN >= 128 ? 2 : 1;
+    constexpr int EPI_GROUPS = CPL == 4 && WN >= 128 ? 2 : 1;
     constexpr int EPI_HALF = WN / 2;
     constexpr bool HAS_C = kind_reads_c(KIND);
     constexpr bool HAS_X = kind_reads_x(KIND);
@@ -724,23 +733,24 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     constexpr int CP = HAS_C ? EPI_PASSES : 1, XP = HAS_X ? EPI_PASSES : 1, BP = HAS_BIAS ? EPI_PASSES : 1;
     const float alpha = p.alpha, beta = p.beta, s = p.s;
     const int64_t mn_base = (int64_t)l * M * N;
-    half4 cbuf[2][CP][EPI_GROUPS];
-    half4 xbuf[2][XP][EPI_GROUPS];
+    auto lane_col = [&](int h) { return CPL * (lane & 15) + h * EPI_HALF; };
+    hvec cbuf[2][CP][EPI_GROUPS];
+    hvec xbuf[2][XP][EPI_GROUPS];
     _Float16 cbias[2][BP];
-    half4 rbias[EPI_GROUPS];
-    auto epi_prefetch = [&](int i, half4 (&cb)[CP][EPI_GROUPS], half4 (&xb)[XP][EPI_GROUPS], _Float16 (&colb)[BP]) {
+    hvec rbias[EPI_GROUPS];
+    auto epi_prefetch = [&](int i, hvec (&cb)[CP][EPI_GROUPS], hvec (&xb)[XP][EPI_GROUPS], _Float16 (&colb)[BP]) {
 #pragma unroll
         for (int pass = 0; pass < EPI_PASSES; pass++) {
             const int gm = m0 + wm * WM + i * SLAB + pass * 4 + (lane >> 4);
             if constexpr (HAS_BIAS) colb[pass] = gm < M ? p.col_bias[gm] : (_Float16)0.0f;
 #pragma unroll
             for (int h = 0; h < EPI_GROUPS; h++) {
-                const int scol = 4 * (lane & 15) + h * EPI_HALF;
+                const int scol = lane_col(h);
                 const int gn = n0 + wn * WN + scol;
                 if (scol < WN && gm < M && gn < N) {
                     const int64_t o = mn_base + (int64_t)gm * N + gn;
-                    if constexpr (HAS_C) cb[pass][h] = *(const half4 *)(p.C + o);
-                    if constexpr (HAS_X) xb[pass][h] = *(const half4 *)(p.X + o);
+                    if constexpr (HAS_C) cb[pass][h] = *(const hvec *)(p.C + o);
+                    if constexpr (HAS_X) xb[pass][h] = *(const hvec *)(p.X + o);
                 }
             }
         }
@@ -751,9 +761,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
         if constexpr (HAS_BIAS) {
 #pragma unroll
             for (int h = 0; h < EPI_GROUPS; h++) {
-                const int scol = 4 * (lane & 15) + h * EPI_HALF;
+                const int scol = lane_col(h);
                 const int gn = n0 + wn * WN + scol;
-                rbias[h] = (scol < WN && gn < N) ? *(const half4 *)(p.row_bias + gn) : half4{};
+                rbias[h] = (scol < WN && gn < N) ? *(const hvec *)(p.row_bias + gn) : hvec{};
             }
         }
         epi_prefetch(0, cbuf[0], xbuf[0], cbias[0]);
@@ -784,15 +794,21 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
             const int gm = m0 + wm * WM + i * SLAB + srow;
 #pragma unroll
             for (int h = 0; h < EPI_GROUPS; h++) {
-                const int scol = 4 * (lane & 15) + h * EPI_HALF;
+                const int scol = lane_col(h);
                 if (scol >= WN) continue;
                 const int gn = n0 + wn * WN + scol;
-                const f32x4 a4 = *(const f32x4 *)(slab + srow * EPI_LD + scol);
+                float av[CPL];
+#pragma unroll
+                for (int q = 0; q < CPL / 4; q++) {
+                    const f32x4 a4 = *(const f32x4 *)(slab + srow * EPI_LD + scol + 4 * q);
+#pragma unroll
+                    for (int e = 0; e < 4; e++) av[4 * q + e] = a4[e];
+                }
                 if (gm >= M) continue;
                 const int64_t o = mn_base + (int64_t)gm * N + gn;
                 if constexpr (VEC) {
-                    if (gn >= N) continue;  // N % 8 == 0: a 4-column group is all in or all out
-                    half4 c4 = {}, x4 = {}, rb4 = {};
+                    if (gn >= N) continue;  // N % 8 == 0: a lane's column group is all in or all out
+                    hvec c4 = {}, x4 = {}, rb4 = {};
                     float cbv = 0.0f;
                     if constexpr (HAS_C) c4 = cbuf[i & 1][pass][h];
                     if constexpr (HAS_X) x4 = xbuf[i & 1][pass][h];
@@ -800,30 +816,34 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
                         rb4 = rbias[h];
                         cbv = (float)cbias[i & 1][pass];
                     }
-                    half4 d4, e4;
+                    hvec d4, e4;
 #pragma unroll
-                    for (int e = 0; e < 4; e++) {
+                    for (int e = 0; e < CPL; e++) {
                         float d, a = 0.0f;
-                        epi_elem<KIND>(a4[e], (float)c4[e], (float)x4[e], (float)rb4[e], cbv, alpha, beta, s, d, a);
+                        epi_elem<KIND>(av[e], (float)c4[e], (float)x4[e], (float)rb4[e], cbv, alpha, beta, s, d, a);
                         d4[e] = (_Float16)d;
                         e4[e] = (_Float16)a;
                     }
-                    if constexpr (kind_writes_d(KIND)) *(half4 *)(p.D + o) = d4;
-                    if constexpr (kind_has_aux(KIND)) *(half4 *)(p.Aux + o) = e4;
-                    if constexpr (kind_has_acc_out(KIND)) *(f32x4 *)(p.acc_out + o) = a4;
+                    if constexpr (kind_writes_d(KIND)) *(hvec *)(p.D + o) = d4;
+                    if constexpr (kind_has_aux(KIND)) *(hvec *)(p.Aux + o) = e4;
+                    if constexpr (kind_has_acc_out(KIND)) {
+#pragma unroll
+                        for (int q = 0; q < CPL / 4; q++)
+                            *(f32x4 *)(p.acc_out + o + 4 * q) = f32x4{av[4 * q], av[4 * q + 1], av[4 * q + 2], av[4 * q + 3]};
+                    }
                 } else {
                     const float cbv = HAS_BIAS ? (float)p.col_bias[gm] : 0.0f;
 #pragma unroll
-                    for (int e = 0; e < 4; e++) {
+                    for (int e = 0; e < CPL; e++) {
                         if (gn + e >= N) break;
                         const float c = HAS_C ? (float)p.C[o + e] : 0.0f;
                         const float x = HAS_X ? (float)p.X[o + e] : 0.0f;
                         const float rb = HAS_BIAS ? (float)p.row_bias[gn + e] : 0.0f;
                         float d, a = 0.0f;
-                        epi_elem<KIND>(a4[e], c, x, rb, cbv, alpha, beta, s, d, a);
+                        epi_elem<KIND>(av[e], c, x, rb, cbv, alpha, beta, s, d, a);
                         if constexpr (kind_writes_d(KIND)) p.D[o + e] = (_Float16)d;
                         if constexpr (kind_has_aux(KIND)) p.Aux[o + e] = (_Float16)a;
-                        if constexpr (kind_has_acc_out(KIND)) p.acc_out[o + e] = a4[e];
+                        if constexpr (kind_has_acc_out(KIND)) p.acc_out[o + e] = av[e];
                     }
                 }
             }

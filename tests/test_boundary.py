@@ -173,7 +173,7 @@ def test_ext_fast_path_conditions():
     rc, cfg = plan_ext(kind=bias, C=None, rb=P16, cb=P2)
     assert rc == 0 and cfg["vec"] == 1             # the column bias is read one value at a time
     rc, cfg = plan_ext(kind=bias, C=None, rb=P2, cb=P16)
-    assert rc == 0 and cfg["vec"] == 0             # the row bias is read in 8-byte vectors
+    assert rc == 0 and cfg["vec"] == 0             # the row bias is read in 16-byte vectors
     rc, cfg = plan_ext(kind=acc, Aux=P16, acc=P16)
     assert rc == 0 and cfg["vec"] == 1
     rc, cfg = plan_ext(kind=acc, Aux=P16, acc=0x7F0000001004)
