@@ -40,6 +40,25 @@
  *       BIAS_ROW_COL  D = (alpha*acc + row_bias[j]) + col_bias[i]
  *                     (tutorial cell [9], broadcast_epilogue: row_bias has
  *                     shape (N,), col_bias (M, 1); C is not read)
+ *       SIGMOID, TANH, GELU, SILU, LEAKY_RELU, HARDSWISH
+ *                     D = act(alpha*acc + beta*C) with the activations the
+ *                     Python examples article's "Epilogue" section lists as
+ *                     built in (besides identity = LINCOMB and relu = RELU;
+ *                     the Custom Epilogue Example's "Supported Operations"
+ *                     names the same family).  The pages give no formulas;
+ *                     the standard definitions are used:
+ *                       sigmoid(t)    = 1 / (1 + e^-t)
+ *                       tanh(t)       = the hyperbolic tangent (C library)
+ *                       gelu(t)       = t * Phi(t), Phi the standard normal
+ *                                       distribution function, written
+ *                                       0.5 * t * erfc(-t / sqrt 2) (Hendrycks
+ *                                       and Gimpel's exact form, not the tanh
+ *                                       approximation)
+ *                       silu(t)       = t * sigmoid(t)
+ *                       leaky_relu(t) = t > 0 ? t : s * t, the slope s given
+ *                                       as the third scalar
+ *                       hardswish(t)  = t * min(max(t + 3, 0), 6) / 6
+ *                                       (Howard et al., MobileNetV3)
  *     The second output (Aux, Y, E or F) goes to the Aux buffer; the biases
  *     are shared by every batch entry.
  *
@@ -71,6 +90,12 @@
 #define ORACLE_RELU_AUX_STORE 6
 #define ORACLE_RELU_SCALE_ACC 7
 #define ORACLE_BIAS_ROW_COL 8
+#define ORACLE_SIGMOID 9
+#define ORACLE_TANH 10
+#define ORACLE_GELU 11
+#define ORACLE_SILU 12
+#define ORACLE_LEAKY_RELU 13
+#define ORACLE_HARDSWISH 14
 
 /* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction
  * bits.  Exponent 0 holds zero and the subnormals f * 2^-24; exponent 31 holds
@@ -119,7 +144,7 @@ uint16_t oracle_f16_encode(double x)
     return (uint16_t)(sign | (uint16_t)(E << 10) | (uint16_t)((int)q - 1024));
 }
 
-int oracle_kind_valid(int kind) { return kind >= ORACLE_LINCOMB && kind <= ORACLE_BIAS_ROW_COL; }
+int oracle_kind_valid(int kind) { return kind >= ORACLE_LINCOMB && kind <= ORACLE_HARDSWISH; }
 int oracle_kind_has_aux(int kind)
 {
     return kind == ORACLE_AUX_SCALE || kind == ORACLE_LINCOMB_X_ACC || kind == ORACLE_SQUARE ||
@@ -131,6 +156,11 @@ int oracle_kind_reads_bias(int kind) { return kind == ORACLE_BIAS_ROW_COL; }
 int oracle_kind_has_acc_out(int kind) { return kind == ORACLE_RELU_SCALE_ACC; }
 
 static double relu(double t) { return t > 0.0 ? t : 0.0; }
+static double sigmoid(double t) { return 1.0 / (1.0 + exp(-t)); }
+static double gelu(double t) { return 0.5 * t * erfc(-t / sqrt(2.0)); }
+static double silu(double t) { return t * sigmoid(t); }
+static double leaky_relu(double t, double slope) { return t > 0.0 ? t : slope * t; }
+static double hardswish(double t) { return t * fmin(fmax(t + 3.0, 0.0), 6.0) / 6.0; }
 
 /* The epilogue of one element, in double, from the unrounded accumulator.
  * rb / cb are the row-broadcast bias of the element's column and the
@@ -179,6 +209,24 @@ static void epilogue(int kind, double acc, double c, double x, double rb, double
     case ORACLE_BIAS_ROW_COL:
         *d = (alpha * acc + rb) + cb;
         break;
+    case ORACLE_SIGMOID:
+        *d = sigmoid(alpha * acc + beta * c);
+        break;
+    case ORACLE_TANH:
+        *d = tanh(alpha * acc + beta * c);
+        break;
+    case ORACLE_GELU:
+        *d = gelu(alpha * acc + beta * c);
+        break;
+    case ORACLE_SILU:
+        *d = silu(alpha * acc + beta * c);
+        break;
+    case ORACLE_LEAKY_RELU:
+        *d = leaky_relu(alpha * acc + beta * c, s);
+        break;
+    case ORACLE_HARDSWISH:
+        *d = hardswish(alpha * acc + beta * c);
+        break;
     }
 }
 
@@ -207,7 +255,8 @@ static int check_args(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t
  *   C, X, D, Aux, Acc [l][i][j] at (l*M + i)*N + j,
  *   RB[j] (N entries), CB[i] (M entries), shared by every batch entry.
  * scalars = {alpha, beta, s} with s = extra_scalar (AUX_SCALE), x_factor
- * (LINCOMB_X_ACC) or scale (RELU_SCALE_ACC); unused otherwise.  Inputs a kind
+ * (LINCOMB_X_ACC), scale (RELU_SCALE_ACC) or the negative slope (LEAKY_RELU);
+ * unused otherwise.  Inputs a kind
  * does not read and outputs it does not write may be NULL.  D64 / Aux64 /
  * Acc64, when not NULL, receive the unrounded double outputs (Acc64: the
  * exact accumulator, for every kind).  Returns 0, or a nonzero code for

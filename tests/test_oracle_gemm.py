@@ -478,7 +478,8 @@ def test_rejects_invalid_arguments(oracle_lib):
     assert f(0, 1, 1, 1, P, P, P, P, S, 0, P, P, None, None) == 1
     assert f(1, 1, 1, 1, None, P, P, P, S, 0, P, P, None, None) == 2
     assert f(1, 1, 1, 1, P, P, P, None, S, 2, P, P, None, None) == 2
-    assert f(1, 1, 1, 1, P, P, P, P, S, 9, P, P, None, None) == 4
+    assert f(1, 1, 1, 1, P, P, P, P, S, 15, P, P, None, None) == 4
+    assert f(1, 1, 1, 1, P, P, P, P, S, -1, P, P, None, None) == 4
     assert f(1, 1, 1, 1, P, P, P, P, S, 1, P, None, None, None) == 3
     assert f(1, 1, 1, 1, P, P, P, P, S, 0, None, None, None, None) == 3
     assert f(1, 1, 1, 1, P, P, P, None, S, 0, P, None, None, None) == 0
@@ -494,5 +495,5 @@ def test_rejects_invalid_arguments(oracle_lib):
     assert g(1, 1, 1, 1, P, P, P, None, None, None, S, 7, P, P, None, None, None, None) == 3
     assert g(1, 1, 1, 1, P, P, P, None, None, None, S, 7, P, P, Q, None, None, None) == 0
     assert g(1, 1, 1, 1, P, P, P, None, None, None, S, 6, P, None, None, None, None, None) == 3
-    assert g(1, 1, 1, 1, P, P, P, P, P, P, S, 9, P, P, Q, None, None, None) == 4
+    assert g(1, 1, 1, 1, P, P, P, P, P, P, S, 15, P, P, Q, None, None, None) == 4
     del ctypes
