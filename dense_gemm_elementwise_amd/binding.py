@@ -23,7 +23,14 @@ KINDS = {
     "RELU_AUX_STORE": 6,
     "RELU_SCALE_ACC": 7,
     "BIAS_ROW_COL": 8,
+    "SIGMOID": 9,
+    "TANH": 10,
+    "GELU": 11,
+    "SILU": 12,
+    "LEAKY_RELU": 13,
+    "HARDSWISH": 14,
 }
+ACTIVATIONS = ("SIGMOID", "TANH", "GELU", "SILU", "LEAKY_RELU", "HARDSWISH")
 HAS_AUX = ("AUX_SCALE", "LINCOMB_X_ACC", "SQUARE", "RELU_SQUARE", "RELU_AUX_STORE", "RELU_SCALE_ACC")
 READS_X = ("LINCOMB_X_ACC",)
 READS_C = tuple(k for k in KINDS if k != "BIAS_ROW_COL")

@@ -94,7 +94,7 @@ int check_args(int64_t L, int64_t M, int64_t N, int64_t K, const Operands &o, in
         L * K > INT64_MAX / N || L * M * N > INT64_MAX / 4)
         return GEMM_EPI_ERR_SHAPE;
     if (!o.A || !o.B) return GEMM_EPI_ERR_NULL_INPUT;
-    if (kind < GEMM_EPI_LINCOMB || kind > GEMM_EPI_BIAS_ROW_COL) return GEMM_EPI_ERR_KIND;
+    if (kind < GEMM_EPI_LINCOMB || kind > GEMM_EPI_HARDSWISH) return GEMM_EPI_ERR_KIND;
     if ((kind_reads_c(kind) && !o.C) || (kind_reads_x(kind) && !o.X) ||
         (kind_reads_bias(kind) && (!o.row_bias || !o.col_bias)))
         return GEMM_EPI_ERR_NULL_INPUT;
@@ -121,6 +121,30 @@ bool use_fast_path(int64_t M, int64_t N, int64_t K, const Operands &o, int kind)
     const int64_t lim = (int64_t)1 << 31;
     if (M * K * 2 >= lim - 64 || K * N * 2 >= lim - 64) return false;
     return true;
+}
+
+// Calls f(std::integral_constant<int, KIND>) for a public kind (checked by
+// check_args before any call).
+template <typename F>
+hipError_t dispatch_kind(int kind, F &&f)
+{
+    switch (kind) {
+    case GEMM_EPI_LINCOMB: return f(std::integral_constant<int, LINCOMB>{});
+    case GEMM_EPI_AUX_SCALE: return f(std::integral_constant<int, AUX_SCALE>{});
+    case GEMM_EPI_LINCOMB_X_ACC: return f(std::integral_constant<int, LINCOMB_X_ACC>{});
+    case GEMM_EPI_RELU: return f(std::integral_constant<int, RELU>{});
+    case GEMM_EPI_SQUARE: return f(std::integral_constant<int, SQUARE>{});
+    case GEMM_EPI_RELU_SQUARE: return f(std::integral_constant<int, RELU_SQUARE>{});
+    case GEMM_EPI_RELU_AUX_STORE: return f(std::integral_constant<int, RELU_AUX_STORE>{});
+    case GEMM_EPI_RELU_SCALE_ACC: return f(std::integral_constant<int, RELU_SCALE_ACC>{});
+    case GEMM_EPI_BIAS_ROW_COL: return f(std::integral_constant<int, BIAS_ROW_COL>{});
+    case GEMM_EPI_SIGMOID: return f(std::integral_constant<int, SIGMOID>{});
+    case GEMM_EPI_TANH: return f(std::integral_constant<int, TANH>{});
+    case GEMM_EPI_GELU: return f(std::integral_constant<int, GELU>{});
+    case GEMM_EPI_SILU: return f(std::integral_constant<int, SILU>{});
+    case GEMM_EPI_LEAKY_RELU: return f(std::integral_constant<int, LEAKY_RELU>{});
+    default: return f(std::integral_constant<int, HARDSWISH>{});
+    }
 }
 
 template <int BM, int BN, int BK, int NS, int WGM, int WGN, int MI, int KIND, bool VEC, bool SK = false>
@@ -331,17 +355,7 @@ int gemm_epi_run_ext(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, 
 
     hipStream_t s = (hipStream_t)stream;
     hipError_t err;
-    switch (epilogue_kind) {
-    case GEMM_EPI_LINCOMB: err = launch_kind<LINCOMB>(p, t, vec, s); break;
-    case GEMM_EPI_AUX_SCALE: err = launch_kind<AUX_SCALE>(p, t, vec, s); break;
-    case GEMM_EPI_LINCOMB_X_ACC: err = launch_kind<LINCOMB_X_ACC>(p, t, vec, s); break;
-    case GEMM_EPI_RELU: err = launch_kind<RELU>(p, t, vec, s); break;
-    case GEMM_EPI_SQUARE: err = launch_kind<SQUARE>(p, t, vec, s); break;
-    case GEMM_EPI_RELU_SQUARE: err = launch_kind<RELU_SQUARE>(p, t, vec, s); break;
-    case GEMM_EPI_RELU_AUX_STORE: err = launch_kind<RELU_AUX_STORE>(p, t, vec, s); break;
-    case GEMM_EPI_RELU_SCALE_ACC: err = launch_kind<RELU_SCALE_ACC>(p, t, vec, s); break;
-    default: err = launch_kind<BIAS_ROW_COL>(p, t, vec, s); break;
-    }
+    err = dispatch_kind(epilogue_kind, [&](auto k) { return launch_kind<decltype(k)::value>(p, t, vec, s); });
     if (err != hipSuccess) {
         g_last_hip_error = (int)err;
         return GEMM_EPI_ERR_HIP;
@@ -408,17 +422,7 @@ int gemm_epi_run_unfused(int64_t L, int64_t M, int64_t N, int64_t K, const void 
         if (kind_reads_x(epilogue_kind)) vec2 = vec2 && aligned(X, 8);
         if (kind_reads_bias(epilogue_kind)) vec2 = vec2 && aligned(row_bias, 8);
         if (kind_has_aux(epilogue_kind)) vec2 = vec2 && aligned(Aux, 8);
-        switch (epilogue_kind) {
-        case GEMM_EPI_LINCOMB: err = launch_epilogue<LINCOMB>(q, vec2, s); break;
-        case GEMM_EPI_AUX_SCALE: err = launch_epilogue<AUX_SCALE>(q, vec2, s); break;
-        case GEMM_EPI_LINCOMB_X_ACC: err = launch_epilogue<LINCOMB_X_ACC>(q, vec2, s); break;
-        case GEMM_EPI_RELU: err = launch_epilogue<RELU>(q, vec2, s); break;
-        case GEMM_EPI_SQUARE: err = launch_epilogue<SQUARE>(q, vec2, s); break;
-        case GEMM_EPI_RELU_SQUARE: err = launch_epilogue<RELU_SQUARE>(q, vec2, s); break;
-        case GEMM_EPI_RELU_AUX_STORE: err = launch_epilogue<RELU_AUX_STORE>(q, vec2, s); break;
-        case GEMM_EPI_RELU_SCALE_ACC: err = launch_epilogue<RELU_SCALE_ACC>(q, vec2, s); break;
-        default: err = launch_epilogue<BIAS_ROW_COL>(q, vec2, s); break;
-        }
+        err = dispatch_kind(epilogue_kind, [&](auto k) { return launch_epilogue<decltype(k)::value>(q, vec2, s); });
     }
     if (err != hipSuccess) {
         g_last_hip_error = (int)err;
@@ -495,17 +499,7 @@ int gemm_epi_run_ws(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, c
     p.s = scalars[2];
     hipStream_t s = (hipStream_t)stream;
     hipError_t err;
-    switch (epilogue_kind) {
-    case GEMM_EPI_LINCOMB: err = launch_kind_sk<LINCOMB>(p, sk, workspace, s); break;
-    case GEMM_EPI_AUX_SCALE: err = launch_kind_sk<AUX_SCALE>(p, sk, workspace, s); break;
-    case GEMM_EPI_LINCOMB_X_ACC: err = launch_kind_sk<LINCOMB_X_ACC>(p, sk, workspace, s); break;
-    case GEMM_EPI_RELU: err = launch_kind_sk<RELU>(p, sk, workspace, s); break;
-    case GEMM_EPI_SQUARE: err = launch_kind_sk<SQUARE>(p, sk, workspace, s); break;
-    case GEMM_EPI_RELU_SQUARE: err = launch_kind_sk<RELU_SQUARE>(p, sk, workspace, s); break;
-    case GEMM_EPI_RELU_AUX_STORE: err = launch_kind_sk<RELU_AUX_STORE>(p, sk, workspace, s); break;
-    case GEMM_EPI_RELU_SCALE_ACC: err = launch_kind_sk<RELU_SCALE_ACC>(p, sk, workspace, s); break;
-    default: err = launch_kind_sk<BIAS_ROW_COL>(p, sk, workspace, s); break;
-    }
+    err = dispatch_kind(epilogue_kind, [&](auto k) { return launch_kind_sk<decltype(k)::value>(p, sk, workspace, s); });
     if (err != hipSuccess) {
         g_last_hip_error = (int)err;
         return GEMM_EPI_ERR_HIP;

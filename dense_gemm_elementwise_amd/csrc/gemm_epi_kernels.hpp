@@ -64,6 +64,12 @@ enum Kind : int {
     RELU_AUX_STORE = 6,
     RELU_SCALE_ACC = 7,
     BIAS_ROW_COL = 8,
+    SIGMOID = 9,
+    TANH = 10,
+    GELU = 11,
+    SILU = 12,
+    LEAKY_RELU = 13,
+    HARDSWISH = 14,
     // not a public kind: the GEMM stage of the unfused composition, which
     // writes only the fp32 accumulator
     ACC_STORE = 16
@@ -113,6 +119,62 @@ struct Params {
 // an epilogue (the fused GEMM, the elementwise stage of the unfused
 // composition) gives bit-identical outputs.
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Activations, fp32, written from the mathematics (no library call).  Their
+// error is a few fp32 units in the last place or about 1e-6 relative, far
+// below the fp16 output's 2^-11.
+// ---------------------------------------------------------------------------
+// e^x = 2^(x log2 e) on the hardware base-2 exponential (v_exp_f32)
+__device__ __forceinline__ float act_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+__device__ __forceinline__ float act_sigmoid(float x) { return 1.0f / (1.0f + act_exp(-x)); }
+// tanh: for |x| < 1/4 its Maclaurin series to x^9 (truncation below 1e-8
+// relative); otherwise (1 - e^-2|x|) / (1 + e^-2|x|) with the sign of x, where
+// e^-2|x| <= 0.61 so nothing cancels
+__device__ __forceinline__ float act_tanh(float x)
+{
+#pragma clang fp contract(off)
+    const float ax = __builtin_fabsf(x);
+    if (ax < 0.25f) {
+        const float x2 = x * x;
+        float p = 62.0f / 2835.0f;
+        p = __builtin_fmaf(p, x2, -17.0f / 315.0f);
+        p = __builtin_fmaf(p, x2, 2.0f / 15.0f);
+        p = __builtin_fmaf(p, x2, -1.0f / 3.0f);
+        return __builtin_fmaf(x * x2, p, x);
+    }
+    const float e = act_exp(-2.0f * ax);
+    return __builtin_copysignf((1.0f - e) / (1.0f + e), x);
+}
+// gelu(x) = x Phi(x), Phi(x) = erfc(-x / sqrt 2) / 2, in the form that keeps
+// relative accuracy in the left tail: with z = |x| / sqrt 2,
+// x >= 0: x (1 - erfc(z) / 2); x < 0: x erfc(z) / 2.  erfc(z) = e^{-z^2} P(t),
+// t = 2 / (2 + z), P a degree-8 polynomial fitted to the scaled
+// complementary error function by fit_erfc.py (relative error 7e-8)
+__device__ __forceinline__ float act_erfc_pos(float z)
+{
+#pragma clang fp contract(off)
+    constexpr float c[9] = {-2.037919330e-04f, 2.859725058e-01f, 2.504409850e-01f, 3.914754093e-01f,
+                            -2.268847674e-01f, 7.775521874e-01f, -6.962806582e-01f, 2.504747510e-01f,
+                            -3.254655749e-02f};
+    const float t = 2.0f / (2.0f + z);
+    float p = c[8];
+#pragma unroll
+    for (int k = 7; k >= 0; k--) p = __builtin_fmaf(p, t, c[k]);
+    return p * act_exp(-(z * z));
+}
+__device__ __forceinline__ float act_gelu(float x)
+{
+#pragma clang fp contract(off)
+    const float ec = act_erfc_pos(__builtin_fabsf(x) * 0.707106781186547524f);
+    return x >= 0.0f ? x * (1.0f - 0.5f * ec) : x * (0.5f * ec);
+}
+__device__ __forceinline__ float act_silu(float x) { return x / (1.0f + act_exp(-x)); }
+__device__ __forceinline__ float act_hardswish(float x)
+{
+#pragma clang fp contract(off)
+    return x * __builtin_fminf(__builtin_fmaxf(x + 3.0f, 0.0f), 6.0f) / 6.0f;
+}
+
 template <int KIND>
 __device__ __forceinline__ void epi_elem(float acc, float c, float x, float rb, float cb, float alpha, float beta,
                                          float s, float &d, float &a)
@@ -145,6 +207,18 @@ __device__ __forceinline__ void epi_elem(float acc, float c, float x, float rb, 
         d = s * t;
     } else if constexpr (KIND == BIAS_ROW_COL) {
         d = __builtin_fmaf(alpha, acc, rb) + cb;
+    } else if constexpr (KIND == SIGMOID) {
+        d = act_sigmoid(lin);
+    } else if constexpr (KIND == TANH) {
+        d = act_tanh(lin);
+    } else if constexpr (KIND == GELU) {
+        d = act_gelu(lin);
+    } else if constexpr (KIND == SILU) {
+        d = act_silu(lin);
+    } else if constexpr (KIND == LEAKY_RELU) {
+        d = lin > 0.0f ? lin : s * lin;
+    } else if constexpr (KIND == HARDSWISH) {
+        d = act_hardswish(lin);
     } else {  // ACC_STORE: nothing but the accumulator itself is written
         d = acc;
     }

@@ -29,8 +29,12 @@ from typing import Dict, Optional
 import numpy as np
 import torch
 
+ACTIVATIONS = ("SIGMOID", "TANH", "GELU", "SILU", "LEAKY_RELU", "HARDSWISH")
 KINDS = ("LINCOMB", "AUX_SCALE", "LINCOMB_X_ACC", "RELU", "SQUARE", "RELU_SQUARE", "RELU_AUX_STORE",
-         "RELU_SCALE_ACC", "BIAS_ROW_COL")
+         "RELU_SCALE_ACC", "BIAS_ROW_COL") + ACTIVATIONS
+# kinds made of + - * and ReLU only: exact on integer inputs and rational
+# arithmetic (the activations have their own bar and pins)
+EXACT_KINDS = tuple(k for k in KINDS if k not in ACTIVATIONS)
 HAS_AUX = ("AUX_SCALE", "LINCOMB_X_ACC", "SQUARE", "RELU_SQUARE", "RELU_AUX_STORE", "RELU_SCALE_ACC")
 READS_X = ("LINCOMB_X_ACC",)
 READS_C = tuple(k for k in KINDS if k != "BIAS_ROW_COL")
@@ -97,6 +101,14 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in (
     # few output tiles and a deep K (not one of the pages' runs): the case a
     # stream-K split of K across workgroups is for
     Workload("lincomb_deep_k_256x256x65536", 1, 256, 256, 65536, "LINCOMB", 1.0, 2.0, 0.0, "normal", 2025, False),
+    # the built-in activations on the Python examples article's Epilogue
+    # example: m = n = k = 256, inputs built as in its Basic GEMM example,
+    # plan.run's default alpha = 1, beta = 0 (leaky ReLU's slope: 1/8)
+    *(Workload(f"{a.lower()}_256", 1, 256, 256, 256, a, 1.0, 0.0, 0.125 if a == "LEAKY_RELU" else 0.0,
+               "ceil_uniform_pm4", 1234, False) for a in ACTIVATIONS),
+    # GELU at the headline size; alpha = 1/64 puts alpha*acc + beta*C (acc has
+    # standard deviation sqrt(K) = 90.5) where the activation is not flat
+    Workload("gelu_8192", 1, 8192, 8192, 8192, "GELU", 1.0 / 64, 1.0, 0.0, "normal", 2025, False),
 )}
 
 # The workload the headline throughput is quoted on.

@@ -40,7 +40,7 @@ extern "C" {
 #endif
 
 /*
- * Epilogue kinds.  s = scalars[2] (extra_scalar, x_factor or scale); the
+ * Epilogue kinds.  s = scalars[2] (extra_scalar, x_factor, scale or a slope); the
  * second output (Aux, Y, E or F) is written to the Aux buffer.
  *
  * GEMM_EPI_LINCOMB        D = alpha*acc + beta*C
@@ -70,6 +70,15 @@ extern "C" {
  *     (tutorial cell [9], broadcast_epilogue: row_bias has one value per
  *     column, shape (N,), col_bias one per row, shape (M, 1)); C is not read.
  *     Needs gemm_epi_run_ext.
+ * GEMM_EPI_SIGMOID, GEMM_EPI_TANH, GEMM_EPI_GELU, GEMM_EPI_SILU,
+ * GEMM_EPI_LEAKY_RELU, GEMM_EPI_HARDSWISH
+ *                         D = act(alpha*acc + beta*C): the built-in
+ *     activations of the Python examples article's "Epilogue" section
+ *     (identity and relu are LINCOMB and RELU above).  sigmoid 1/(1+e^-t);
+ *     tanh; gelu t*Phi(t) in its exact (erf) form; silu t*sigmoid(t);
+ *     leaky_relu t > 0 ? t : s*t with the slope s = scalars[2]; hardswish
+ *     t*min(max(t+3, 0), 6)/6.  Computed in fp32 (about 1e-6 relative or a
+ *     few fp32 ulps), D rounded once to fp16.  No second output.
  *
  * The intermediate values (Aux before the scaling, D before the square, F
  * before the scaling) are used unrounded.
@@ -83,7 +92,13 @@ typedef enum {
     GEMM_EPI_RELU_SQUARE = 5,
     GEMM_EPI_RELU_AUX_STORE = 6,
     GEMM_EPI_RELU_SCALE_ACC = 7,
-    GEMM_EPI_BIAS_ROW_COL = 8
+    GEMM_EPI_BIAS_ROW_COL = 8,
+    GEMM_EPI_SIGMOID = 9,
+    GEMM_EPI_TANH = 10,
+    GEMM_EPI_GELU = 11,
+    GEMM_EPI_SILU = 12,
+    GEMM_EPI_LEAKY_RELU = 13,
+    GEMM_EPI_HARDSWISH = 14
 } gemm_epi_kind;
 
 /*

@@ -83,7 +83,7 @@ def test_missing_outputs():
         assert run(kind=ge.KINDS[kind], Aux=None) == 3, kind
 
 
-@pytest.mark.parametrize("kind", [-1, 9, 100])
+@pytest.mark.parametrize("kind", [-1, 15, 100])
 def test_unknown_kind(kind):
     assert run(kind=kind) == 4
 
@@ -216,7 +216,9 @@ def test_plan_tiles_for_the_workloads():
         "relu_scale_acc_8192": (256, 256, 1024),
         "bias_row_col_8192": (256, 256, 1024),
         "lincomb_deep_k_256x256x65536": (64, 64, 16),
+        "gelu_8192": (256, 256, 1024),
     }
+    want.update({f"{a.lower()}_256": (64, 64, 16) for a in workloads.ACTIVATIONS})
     assert set(want) == set(workloads.WORKLOADS)
     for name, (bm, bn, wgs) in want.items():
         w = workloads.WORKLOADS[name]

@@ -213,7 +213,7 @@ def test_exhaustive_2x2x2_over_minus1_0_1():
 
 
 @pytest.mark.parametrize("shape", [(1, 4, 4, 4), (2, 3, 5, 2), (3, 2, 3, 7), (1, 1, 1, 1), (1, 5, 1, 3)])
-@pytest.mark.parametrize("kind", workloads.KINDS)
+@pytest.mark.parametrize("kind", workloads.EXACT_KINDS)
 def test_random_fp16_tiny_against_exact(shape, kind):
     """Gaussian fp16 inputs on tiny non-square shapes (a transposed operand or a
     wrong index cannot pass): the unrounded fp64 outputs lie within the fp64
@@ -288,7 +288,7 @@ def test_page_workload_aux_scale_128_accumulator_exact():
 # ---------------------------------------------------------------------------
 # Closed forms
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("kind", workloads.KINDS)
+@pytest.mark.parametrize("kind", workloads.EXACT_KINDS)
 def test_zero_A_closed_forms(kind):
     L, M, N, K = 2, 19, 23, 11
     p = workloads.make_problem(L, M, N, K, kind, init="normal", seed=5)

@@ -7,6 +7,12 @@ every fp32 partial sum exact, so the only rounding is the final fp16 store):
   - Gaussian inputs: |gpu - ref| <= 5e-2 + 1e-2 * |ref| for every compared
     element, ref = the oracle's unrounded fp64 value, and no non-finite
     output.
+  - activation kinds (sigmoid, tanh, GELU, SiLU, leaky ReLU, hardswish) on
+    integer-valued inputs with scalars that keep alpha*acc + beta*C exact in
+    fp32: within one fp16 unit in the last place of the oracle's unrounded
+    value, and at least 98% bit-identical to the oracle's fp16 (the fp32
+    activations are accurate to about 1e-6, so they differ from the correctly
+    rounded value only next to a rounding boundary).
 Full-size problems that the oracle cannot finish in seconds are compared at
 sampled points (the oracle's per-element entry) plus whole-output properties
 that hold at any size.
@@ -107,16 +113,50 @@ def assert_close(got, ref64, what):
         raise AssertionError(f"{what}: {n} of {g.size} outside tolerance; worst at {i}: gpu {g[i]} ref {ref64[i]}")
 
 
+def ulp16(x):
+    """fp16 spacing at |x| (2^-24 in the subnormal range)."""
+    ax = np.abs(np.asarray(x, np.float64))
+    return 2.0 ** (np.floor(np.log2(np.maximum(ax, 2.0 ** -14))) - 10)
+
+
+def assert_within_ulp(got, ref64, ref16, what, min_exact=0.98):
+    """Activation outputs: within one fp16 ulp of the oracle's unrounded value,
+    and mostly bit-identical to the oracle's correctly rounded fp16."""
+    g = np.asarray(got, np.float64)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    err = np.abs(g - ref64)
+    lim = ulp16(ref64)
+    bad = err > lim
+    n = int(np.count_nonzero(bad))
+    if n:
+        i = np.unravel_index(np.argmax(err / lim), err.shape)
+        raise AssertionError(f"{what}: {n} of {g.size} more than 1 ulp off; worst at {i}: gpu {g[i]} ref {ref64[i]}")
+    same = float(np.mean(g == np.asarray(ref16, np.float64)))
+    assert same >= min_exact, f"{what}: only {same:.4f} of the outputs equal the oracle's fp16"
+
+
+def oracle_ref(p, kind, alpha, beta, s3, exact):
+    return oracle_full(p, kind, alpha, beta, s3, want64=(not exact) or kind in ge.ACTIVATIONS)
+
+
+def assert_output(got, ref, name, kind, exact, what):
+    """The bar for one output: bit-exact (integer inputs), the activation ulp
+    bound (integer inputs, activation kinds), or the tolerance (Gaussian)."""
+    if exact and kind in ge.ACTIVATIONS:
+        assert_within_ulp(got, ref[name + "64"], ref[name], what)
+    elif exact:
+        assert_bit_exact(got, ref[name], what)
+    else:
+        assert_close(got, ref[name + "64"], what)
+
+
 def check_full(p, kind, alpha, beta, s3, exact, offset=0, what=""):
     got = gpu_run(p, kind, alpha, beta, s3, offset)
-    ref = oracle_full(p, kind, alpha, beta, s3, want64=not exact)
+    ref = oracle_ref(p, kind, alpha, beta, s3, exact)
     for name in ("D", "Aux"):
         if name not in ref:
             continue
-        if exact:
-            assert_bit_exact(got[name], ref[name], f"{what} {name}")
-        else:
-            assert_close(got[name], ref[name + "64"], f"{what} {name}")
+        assert_output(got[name], ref, name, kind, exact, f"{what} {name}")
     if kind in ge.HAS_ACC:
         if exact:  # integer inputs: every fp32 partial sum is exact
             n = int(np.count_nonzero(got["Acc"] != ref["Acc"]))
@@ -270,6 +310,9 @@ def test_bias_row_col_8192_sampled_and_properties():
 KIND_SCALARS = {"LINCOMB": (1.0, 2.0, 0.0), "AUX_SCALE": (1.0, 2.0, 0.5), "LINCOMB_X_ACC": (2.0, 1.0, 3.0),
                 "RELU": (1.0, -1.0, 0.0), "SQUARE": (1.0, 1.0, 0.0), "RELU_SQUARE": (0.5, 1.0, 0.0),
                 "RELU_AUX_STORE": (3.0, 2.0, 0.0), "RELU_SCALE_ACC": (1.0, 2.0, 0.5), "BIAS_ROW_COL": (1.5, 0.0, 0.0)}
+# activations: alpha = 1/32 and beta = 1/2 keep alpha*acc + beta*C exact in fp32
+# on integer inputs and put it where the activations are not flat
+KIND_SCALARS.update({a: (2.0 ** -5, 0.5, 0.125 if a == "LEAKY_RELU" else 0.0) for a in workloads.ACTIVATIONS})
 
 
 @pytest.mark.parametrize("kind", workloads.KINDS)

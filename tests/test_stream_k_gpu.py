@@ -15,7 +15,8 @@ import torch
 import dense_gemm_elementwise_amd as ge
 from dense_gemm_elementwise_amd import workloads
 
-from test_parity_gpu import KIND_SCALARS, alloc_out, assert_bit_exact, assert_close, log, oracle_full, to_dev
+from test_parity_gpu import (KIND_SCALARS, alloc_out, assert_bit_exact, assert_close, assert_output, log, oracle_full,
+                             oracle_ref, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -73,13 +74,13 @@ def test_stream_k_integer_bit_exact(shape, kind):
     log(f"[stream-k] kind={kind} shape={shape} workgroups={cfg['workgroups']} ws={cfg['workspace_bytes']}")
     ws = workspace(cfg)
     p = workloads.make_problem(L, M, N, K, kind, init="small_int", seed=L + M + 3 * N + K)
-    ref = oracle_full(p, kind, a, b, s, want64=False)
+    ref = oracle_ref(p, kind, a, b, s, exact=True)
     outs = run_ws(p, kind, a, b, s, ws, times=2)   # the second call reuses the workspace
     assert counters_are_zero(ws, cfg)
     for n, got in enumerate(outs):
         for name in ("D", "Aux"):
             if name in ref:
-                assert_bit_exact(got[name], ref[name], f"stream-k call {n} {kind} {shape} {name}")
+                assert_output(got[name], ref, name, kind, True, f"stream-k call {n} {kind} {shape} {name}")
         if kind in ge.HAS_ACC:
             assert np.array_equal(got["Acc"], ref["Acc"]), f"stream-k call {n} acc_out"
 

@@ -17,7 +17,7 @@ import oracle
 import dense_gemm_elementwise_amd as ge
 from dense_gemm_elementwise_amd import workloads
 
-from test_parity_gpu import KIND_SCALARS, alloc_out, assert_bit_exact, log, oracle_full, to_dev
+from test_parity_gpu import KIND_SCALARS, alloc_out, assert_bit_exact, assert_output, log, oracle_full, oracle_ref, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -55,13 +55,13 @@ def test_unfused_equals_fused_and_oracle(kind, shape, offset):
     log(f"[unfused] kind={kind} shape={shape} offset={offset}")
     p = workloads.make_problem(L, M, N, K, kind, init="small_int", seed=M + N * K)
     fused, unfused = run_both(p, kind, a, b, s, offset)
-    ref = oracle_full(p, kind, a, b, s, want64=False)
+    ref = oracle_ref(p, kind, a, b, s, exact=True)
     for name in fused:
         assert np.array_equal(fused[name].view(np.uint8), unfused[name].view(np.uint8)), f"{kind} {name} fused != unfused"
         if name == "Acc":
             assert np.array_equal(unfused[name], ref[name]), f"{kind} acc_out"
         else:
-            assert_bit_exact(unfused[name], ref[name], f"unfused {kind} {name}")
+            assert_output(unfused[name], ref, name, kind, True, f"unfused {kind} {name}")
 
 
 @pytest.mark.parametrize("kind", ["LINCOMB_X_ACC", "RELU_SCALE_ACC", "BIAS_ROW_COL"])
