@@ -37,6 +37,8 @@ KINDS = {
     "HARDSWISH": 14,
 }
 ACTIVATIONS = ("SIGMOID", "TANH", "GELU", "SILU", "LEAKY_RELU", "HARDSWISH")
+# element types of the 16-bit tensors, the boundary's enum values
+DTYPES = {"f16": 0, "bf16": 1}
 HAS_AUX = {"AUX_SCALE", "LINCOMB_X_ACC", "SQUARE", "RELU_SQUARE", "RELU_AUX_STORE", "RELU_SCALE_ACC"}
 READS_X = {"LINCOMB_X_ACC"}
 READS_C = set(KINDS) - {"BIAS_ROW_COL"}
@@ -65,6 +67,21 @@ def lib():
     L.oracle_gemm_epi_ext.restype = ctypes.c_int
     L.oracle_gemm_epi_ext.argtypes = [i64, i64, i64, i64, u16p, u16p, u16p, u16p, u16p, u16p, f32p, ctypes.c_int,
                                       u16p, u16p, f32p, f64p, f64p, f64p]
+    L.oracle_gemm_epi_typed.restype = ctypes.c_int
+    L.oracle_gemm_epi_typed.argtypes = [i64, i64, i64, i64, u16p, u16p, u16p, u16p, u16p, u16p, f32p, ctypes.c_int,
+                                        u16p, u16p, f32p, f64p, f64p, f64p, ctypes.c_int]
+    L.oracle_gemm_epi_points_typed.restype = ctypes.c_int
+    L.oracle_gemm_epi_points_typed.argtypes = [i64, i64, i64, i64, u16p, u16p, u16p, u16p, u16p, u16p, f32p,
+                                               ctypes.c_int, i64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                               u16p, u16p, f32p, f64p, f64p, f64p, ctypes.c_int]
+    L.oracle_bf16_decode.restype = ctypes.c_double
+    L.oracle_bf16_decode.argtypes = [ctypes.c_uint16]
+    L.oracle_bf16_encode.restype = ctypes.c_uint16
+    L.oracle_bf16_encode.argtypes = [ctypes.c_double]
+    L.oracle_bf16_decode_n.restype = None
+    L.oracle_bf16_decode_n.argtypes = [u16p, f64p, i64]
+    L.oracle_bf16_encode_n.restype = None
+    L.oracle_bf16_encode_n.argtypes = [f64p, u16p, i64]
     L.oracle_gemm_epi_points_ext.restype = ctypes.c_int
     L.oracle_gemm_epi_points_ext.argtypes = [i64, i64, i64, i64, u16p, u16p, u16p, u16p, u16p, u16p, f32p,
                                              ctypes.c_int, i64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -87,13 +104,15 @@ def lib():
     return L
 
 
-def _bits(a):
-    """A float16 (or uint16 bit-pattern) array as a C-contiguous uint16 array."""
+def _bits(a, dtype="f16"):
+    """A float16 (or uint16 bit-pattern) array as a C-contiguous uint16 array.
+    bfloat16 tensors are passed as uint16 bit patterns (numpy has no such
+    type)."""
     a = np.ascontiguousarray(a)
-    if a.dtype == np.float16:
+    if a.dtype == np.float16 and dtype == "f16":
         return a.view(np.uint16)
     if a.dtype != np.uint16:
-        raise TypeError(f"expected float16 or uint16 bits, got {a.dtype}")
+        raise TypeError(f"expected {'float16 or ' if dtype == 'f16' else ''}uint16 bits, got {a.dtype}")
     return a
 
 
@@ -115,6 +134,20 @@ def f16_encode(x):
     return out
 
 
+def bf16_decode(bits):
+    b = _bits(np.asarray(bits), "bf16")
+    out = np.empty(b.shape, np.float64)
+    lib().oracle_bf16_decode_n(_ptr(b), _ptr(out), b.size)
+    return out
+
+
+def bf16_encode(x):
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, np.uint16)
+    lib().oracle_bf16_encode_n(_ptr(x), _ptr(out), x.size)
+    return out
+
+
 def _shapes(A, B, C):
     if A.ndim != 3 or B.ndim != 3 or (C is not None and C.ndim != 3):
         raise ValueError("A, B, C must be (L,M,K), (L,K,N), (L,M,N)")
@@ -124,9 +157,9 @@ def _shapes(A, B, C):
     return L, M, B.shape[2], K
 
 
-def _biases(row_bias, col_bias, M, N):
-    rb = _bits(np.asarray(row_bias).reshape(-1)) if row_bias is not None else None
-    cb = _bits(np.asarray(col_bias).reshape(-1)) if col_bias is not None else None
+def _biases(row_bias, col_bias, M, N, dtype="f16"):
+    rb = _bits(np.asarray(row_bias).reshape(-1), dtype) if row_bias is not None else None
+    cb = _bits(np.asarray(col_bias).reshape(-1), dtype) if col_bias is not None else None
     if rb is not None and rb.size != N:
         raise ValueError(f"row_bias must have N = {N} entries")
     if cb is not None and cb.size != M:
@@ -135,20 +168,21 @@ def _biases(row_bias, col_bias, M, N):
 
 
 def gemm_epi(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, row_bias=None, col_bias=None,
-             want64=False):
+             want64=False, dtype="f16"):
     """Full fused GEMM + epilogue on host arrays.
 
     A (L,M,K), B (L,K,N), C and X (L,M,N): float16 arrays (or uint16 bits);
     row_bias (N,) and col_bias (M,) or (M, 1) for BIAS_ROW_COL.  Returns a dict
     with D (and Aux for kinds with a second output) as float16 arrays, Acc
     (float32) for kinds that return the accumulator, plus D64 / Aux64 / Acc64
-    (unrounded float64) when want64 is set.
+    (unrounded float64) when want64 is set.  dtype "bf16": the 16-bit tensors
+    are bfloat16, passed and returned as uint16 bit patterns.
     """
-    A, B = _bits(A), _bits(B)
-    C = _bits(C) if C is not None else None
-    X = _bits(X) if X is not None else None
+    A, B = _bits(A, dtype), _bits(B, dtype)
+    C = _bits(C, dtype) if C is not None else None
+    X = _bits(X, dtype) if X is not None else None
     L, M, N, K = _shapes(A, B, C)
-    rb, cb = _biases(row_bias, col_bias, M, N)
+    rb, cb = _biases(row_bias, col_bias, M, N, dtype)
     sc = np.array([alpha, beta, s3], np.float32)
     D = np.empty((L, M, N), np.uint16)
     Aux = np.empty((L, M, N), np.uint16) if kind in HAS_AUX else None
@@ -156,13 +190,15 @@ def gemm_epi(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, row_bia
     D64 = np.empty((L, M, N), np.float64) if want64 else None
     Aux64 = np.empty((L, M, N), np.float64) if (want64 and kind in HAS_AUX) else None
     Acc64 = np.empty((L, M, N), np.float64) if want64 else None
-    rc = lib().oracle_gemm_epi_ext(L, M, N, K, _ptr(A), _ptr(B), _ptr(C), _ptr(X), _ptr(rb), _ptr(cb), _ptr(sc),
-                                   KINDS[kind], _ptr(D), _ptr(Aux), _ptr(Acc), _ptr(D64), _ptr(Aux64), _ptr(Acc64))
+    rc = lib().oracle_gemm_epi_typed(L, M, N, K, _ptr(A), _ptr(B), _ptr(C), _ptr(X), _ptr(rb), _ptr(cb), _ptr(sc),
+                                     KINDS[kind], _ptr(D), _ptr(Aux), _ptr(Acc), _ptr(D64), _ptr(Aux64), _ptr(Acc64),
+                                     DTYPES[dtype])
     if rc:
-        raise ValueError(f"oracle_gemm_epi_ext rejected the call (code {rc})")
-    out = {"D": D.view(np.float16)}
+        raise ValueError(f"oracle_gemm_epi_typed rejected the call (code {rc})")
+    view = (lambda a: a.view(np.float16)) if dtype == "f16" else (lambda a: a)
+    out = {"D": view(D)}
     if Aux is not None:
-        out["Aux"] = Aux.view(np.float16)
+        out["Aux"] = view(Aux)
     if Acc is not None:
         out["Acc"] = Acc
     if want64:
@@ -174,18 +210,18 @@ def gemm_epi(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, row_bia
 
 
 def gemm_epi_points(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, row_bias=None, col_bias=None,
-                    l, i, j):
+                    l, i, j, dtype="f16"):
     """The same definition at sampled output points (l[p], i[p], j[p]).
 
     Returns a dict of 1-D arrays indexed by p: D, Aux (if the kind has one) as
     float16, Acc (float32, if the kind returns it), and D64 / Aux64 / Acc64
-    unrounded.
+    unrounded.  dtype as for gemm_epi.
     """
-    A, B = _bits(A), _bits(B)
-    C = _bits(C) if C is not None else None
-    X = _bits(X) if X is not None else None
+    A, B = _bits(A, dtype), _bits(B, dtype)
+    C = _bits(C, dtype) if C is not None else None
+    X = _bits(X, dtype) if X is not None else None
     L, M, N, K = _shapes(A, B, C)
-    rb, cb = _biases(row_bias, col_bias, M, N)
+    rb, cb = _biases(row_bias, col_bias, M, N, dtype)
     l = np.ascontiguousarray(l, np.int64)
     i = np.ascontiguousarray(i, np.int64)
     j = np.ascontiguousarray(j, np.int64)
@@ -199,14 +235,15 @@ def gemm_epi_points(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, 
     Aux = np.empty(n, np.uint16) if kind in HAS_AUX else None
     Aux64 = np.empty(n, np.float64) if kind in HAS_AUX else None
     Acc = np.empty(n, np.float32) if kind in HAS_ACC else None
-    rc = lib().oracle_gemm_epi_points_ext(L, M, N, K, _ptr(A), _ptr(B), _ptr(C), _ptr(X), _ptr(rb), _ptr(cb),
-                                          _ptr(sc), KINDS[kind], n, _ptr(l), _ptr(i), _ptr(j), _ptr(D), _ptr(Aux),
-                                          _ptr(Acc), _ptr(D64), _ptr(Aux64), _ptr(Acc64))
+    rc = lib().oracle_gemm_epi_points_typed(L, M, N, K, _ptr(A), _ptr(B), _ptr(C), _ptr(X), _ptr(rb), _ptr(cb),
+                                            _ptr(sc), KINDS[kind], n, _ptr(l), _ptr(i), _ptr(j), _ptr(D), _ptr(Aux),
+                                            _ptr(Acc), _ptr(D64), _ptr(Aux64), _ptr(Acc64), DTYPES[dtype])
     if rc:
-        raise ValueError(f"oracle_gemm_epi_points_ext rejected the call (code {rc})")
-    out = {"D": D.view(np.float16), "D64": D64, "Acc64": Acc64}
+        raise ValueError(f"oracle_gemm_epi_points_typed rejected the call (code {rc})")
+    view = (lambda a: a.view(np.float16)) if dtype == "f16" else (lambda a: a)
+    out = {"D": view(D), "D64": D64, "Acc64": Acc64}
     if Aux is not None:
-        out["Aux"] = Aux.view(np.float16)
+        out["Aux"] = view(Aux)
         out["Aux64"] = Aux64
     if Acc is not None:
         out["Acc"] = Acc

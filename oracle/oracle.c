@@ -63,14 +63,19 @@
  *     are shared by every batch entry.
  *
  * Precision (readings where the pages are silent, listed in the design doc):
- *   - fp16 inputs are decoded exactly to double by decode_f16() below;
+ *   - fp16 inputs are decoded exactly to double by oracle_f16_decode() below;
+ *     the same definition runs on bfloat16 tensors (the Custom Epilogue
+ *     Example's "Data Type Support": BF16 inputs and outputs) through
+ *     oracle_gemm_epi_typed(), with oracle_bf16_decode() and
+ *     oracle_bf16_encode() in place of the fp16 codec;
  *   - every sum runs in double, k strictly increasing, starting from +0.0
  *     (the textbook i-k-j triple loop; the loop order does not change the
  *     order in which any one element is summed);
  *   - the epilogue runs in double from the unrounded acc (Aux, D feed the next
  *     operation unrounded, as the epilogue DAG's SSA values do);
  *   - every output is rounded once, double -> fp16, round to nearest, ties to
- *     even, overflow to +-inf (encode_f16() below); the fp32 accumulator
+ *     even, overflow to +-inf (oracle_f16_encode() below; oracle_bf16_encode()
+ *     for bfloat16); the fp32 accumulator
  *     output is the exact sum rounded once to fp32 (nearest, ties to even);
  *   - ReLU(t) = t > 0 ? t : +0.0 (the "where(d > 0, d, 0)" form).
  * Build with -ffp-contract=off so that no multiply-add is fused.
@@ -143,6 +148,62 @@ uint16_t oracle_f16_encode(double x)
         return (uint16_t)(sign | 0x7C00);
     return (uint16_t)(sign | (uint16_t)(E << 10) | (uint16_t)((int)q - 1024));
 }
+
+/* bfloat16 (brain floating point; the upper half of an IEEE 754 binary32):
+ * 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits.  Exponent 0 holds
+ * zero and the subnormals f * 2^-133; exponent 255 holds inf (f == 0) and
+ * NaN. */
+double oracle_bf16_decode(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 7) & 255;
+    int f = h & 127;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -133);
+    else if (e == 255)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(128 + f), e - 134);
+    return sign ? -v : v;
+}
+
+/* double -> bfloat16, round to nearest, ties to even, in one step. */
+uint16_t oracle_bf16_encode(double x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    if (isnan(x))
+        return (uint16_t)(sign | 0x7FC0);
+    double a = fabs(x);
+    /* (2 - 2^-8) * 2^127 is the midpoint between the largest finite value,
+     * (2 - 2^-7) * 2^127, and 2^128; the tie goes to the even neighbour, inf */
+    if (a >= ldexp(2.0 - 0x1p-8, 127))
+        return (uint16_t)(sign | 0x7F80);
+    if (a < 0x1p-126) {
+        /* subnormal (or zero): the quantum is 2^-133; a * 2^133 is exact.  A
+         * result of 128 is the smallest normal, 0x0080. */
+        double q = nearbyint(a * 0x1p133);
+        return (uint16_t)(sign | (uint16_t)q);
+    }
+    int e2;
+    double m = frexp(a, &e2);         /* a = m * 2^e2, m in [0.5, 1) */
+    double q = nearbyint(ldexp(m, 8)); /* 8 significant bits, in [128, 256] */
+    int E = e2 - 1 + 127;             /* biased exponent of a */
+    if (q == 256.0) {
+        q = 128.0;
+        E += 1;
+    }
+    if (E >= 255)
+        return (uint16_t)(sign | 0x7F80);
+    return (uint16_t)(sign | (uint16_t)(E << 7) | (uint16_t)((int)q - 128));
+}
+
+/* Element types of the 16-bit tensors (A, B, C, X, the biases, D, Aux): the
+ * boundary's public enum values, written out again here. */
+#define ORACLE_DTYPE_F16 0
+#define ORACLE_DTYPE_BF16 1
+typedef double (*decode_fn)(uint16_t);
+typedef uint16_t (*encode_fn)(double);
 
 int oracle_kind_valid(int kind) { return kind >= ORACLE_LINCOMB && kind <= ORACLE_HARDSWISH; }
 int oracle_kind_has_aux(int kind)
@@ -263,14 +324,18 @@ static int check_args(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t
  * invalid arguments.  OpenMP splits the rows; each element's sum is the same
  * whatever the thread count.
  */
-int oracle_gemm_epi_ext(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
-                        const uint16_t *C, const uint16_t *X, const uint16_t *RB, const uint16_t *CB,
-                        const float *scalars, int kind, uint16_t *D, uint16_t *Aux, float *Acc, double *D64,
-                        double *Aux64, double *Acc64)
+int oracle_gemm_epi_typed(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
+                          const uint16_t *C, const uint16_t *X, const uint16_t *RB, const uint16_t *CB,
+                          const float *scalars, int kind, uint16_t *D, uint16_t *Aux, float *Acc, double *D64,
+                          double *Aux64, double *Acc64, int dtype)
 {
     int rc = check_args(L, M, N, K, A, B, C, X, RB, CB, scalars, kind, D, Aux, Acc);
     if (rc)
         return rc;
+    if (dtype != ORACLE_DTYPE_F16 && dtype != ORACLE_DTYPE_BF16)
+        return 8;
+    const decode_fn dec = dtype == ORACLE_DTYPE_BF16 ? oracle_bf16_decode : oracle_f16_decode;
+    const encode_fn enc = dtype == ORACLE_DTYPE_BF16 ? oracle_bf16_encode : oracle_f16_encode;
     const double alpha = scalars[0], beta = scalars[1], s = scalars[2];
     double *Bd = (double *)malloc(sizeof(double) * (size_t)K * (size_t)N);
     if (!Bd)
@@ -279,7 +344,7 @@ int oracle_gemm_epi_ext(int64_t L, int64_t M, int64_t N, int64_t K, const uint16
         const uint16_t *Al = A + l * M * K;
         const uint16_t *Bl = B + l * K * N;
         for (int64_t q = 0; q < K * N; q++)
-            Bd[q] = oracle_f16_decode(Bl[q]);
+            Bd[q] = dec(Bl[q]);
         int fail = 0;
 #pragma omp parallel
         {
@@ -295,24 +360,24 @@ int oracle_gemm_epi_ext(int64_t L, int64_t M, int64_t N, int64_t K, const uint16
                 for (int64_t j = 0; j < N; j++)
                     acc[j] = 0.0;
                 for (int64_t k = 0; k < K; k++) {
-                    const double a = oracle_f16_decode(Al[i * K + k]);
+                    const double a = dec(Al[i * K + k]);
                     const double *brow = Bd + k * N;
                     for (int64_t j = 0; j < N; j++)
                         acc[j] = acc[j] + a * brow[j];
                 }
                 const int64_t row = (l * M + i) * N;
-                const double cb = oracle_kind_reads_bias(kind) ? oracle_f16_decode(CB[i]) : 0.0;
+                const double cb = oracle_kind_reads_bias(kind) ? dec(CB[i]) : 0.0;
                 for (int64_t j = 0; j < N; j++) {
-                    double c = oracle_kind_reads_c(kind) ? oracle_f16_decode(C[row + j]) : 0.0;
-                    double x = oracle_kind_reads_x(kind) ? oracle_f16_decode(X[row + j]) : 0.0;
-                    double rb = oracle_kind_reads_bias(kind) ? oracle_f16_decode(RB[j]) : 0.0;
+                    double c = oracle_kind_reads_c(kind) ? dec(C[row + j]) : 0.0;
+                    double x = oracle_kind_reads_x(kind) ? dec(X[row + j]) : 0.0;
+                    double rb = oracle_kind_reads_bias(kind) ? dec(RB[j]) : 0.0;
                     double d = 0.0, aux = 0.0;
                     epilogue(kind, acc[j], c, x, rb, cb, alpha, beta, s, &d, &aux);
-                    D[row + j] = oracle_f16_encode(d);
+                    D[row + j] = enc(d);
                     if (D64)
                         D64[row + j] = d;
                     if (oracle_kind_has_aux(kind)) {
-                        Aux[row + j] = oracle_f16_encode(aux);
+                        Aux[row + j] = enc(aux);
                         if (Aux64)
                             Aux64[row + j] = aux;
                     }
@@ -333,6 +398,16 @@ int oracle_gemm_epi_ext(int64_t L, int64_t M, int64_t N, int64_t K, const uint16
     return 0;
 }
 
+/* fp16 tensors (the boundary's default element type). */
+int oracle_gemm_epi_ext(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
+                        const uint16_t *C, const uint16_t *X, const uint16_t *RB, const uint16_t *CB,
+                        const float *scalars, int kind, uint16_t *D, uint16_t *Aux, float *Acc, double *D64,
+                        double *Aux64, double *Acc64)
+{
+    return oracle_gemm_epi_typed(L, M, N, K, A, B, C, X, RB, CB, scalars, kind, D, Aux, Acc, D64, Aux64, Acc64,
+                                 ORACLE_DTYPE_F16);
+}
+
 /* The entry point without bias inputs or accumulator output (kinds 0-6). */
 int oracle_gemm_epi(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
                     const uint16_t *C, const uint16_t *X, const float *scalars, int kind, uint16_t *D,
@@ -348,11 +423,11 @@ int oracle_gemm_epi(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *
  * problem can be checked at sampled points.  Outputs are indexed by p:
  * D[p], Aux[p], Acc[p], D64[p], Aux64[p], Acc64[p] (all but D may be NULL).
  */
-int oracle_gemm_epi_points_ext(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A,
-                               const uint16_t *B, const uint16_t *C, const uint16_t *X, const uint16_t *RB,
-                               const uint16_t *CB, const float *scalars, int kind, int64_t npts, const int64_t *pl,
-                               const int64_t *pi, const int64_t *pj, uint16_t *D, uint16_t *Aux, float *Acc,
-                               double *D64, double *Aux64, double *Acc64)
+int oracle_gemm_epi_points_typed(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A,
+                                 const uint16_t *B, const uint16_t *C, const uint16_t *X, const uint16_t *RB,
+                                 const uint16_t *CB, const float *scalars, int kind, int64_t npts,
+                                 const int64_t *pl, const int64_t *pi, const int64_t *pj, uint16_t *D,
+                                 uint16_t *Aux, float *Acc, double *D64, double *Aux64, double *Acc64, int dtype)
 {
     /* the per-point outputs are optional: check the inputs with stand-ins */
     uint16_t dummy16 = 0;
@@ -362,6 +437,10 @@ int oracle_gemm_epi_points_ext(int64_t L, int64_t M, int64_t N, int64_t K, const
         return rc;
     if (npts < 0 || (npts > 0 && (!pl || !pi || !pj)))
         return 1;
+    if (dtype != ORACLE_DTYPE_F16 && dtype != ORACLE_DTYPE_BF16)
+        return 8;
+    const decode_fn dec = dtype == ORACLE_DTYPE_BF16 ? oracle_bf16_decode : oracle_f16_decode;
+    const encode_fn enc = dtype == ORACLE_DTYPE_BF16 ? oracle_bf16_encode : oracle_f16_encode;
     for (int64_t p = 0; p < npts; p++)
         if (pl[p] < 0 || pl[p] >= L || pi[p] < 0 || pi[p] >= M || pj[p] < 0 || pj[p] >= N)
             return 1;
@@ -371,20 +450,20 @@ int oracle_gemm_epi_points_ext(int64_t L, int64_t M, int64_t N, int64_t K, const
         const int64_t l = pl[p], i = pi[p], j = pj[p];
         double acc = 0.0;
         for (int64_t k = 0; k < K; k++)
-            acc = acc + oracle_f16_decode(A[(l * M + i) * K + k]) * oracle_f16_decode(B[(l * K + k) * N + j]);
+            acc = acc + dec(A[(l * M + i) * K + k]) * dec(B[(l * K + k) * N + j]);
         const int64_t o = (l * M + i) * N + j;
-        double c = oracle_kind_reads_c(kind) ? oracle_f16_decode(C[o]) : 0.0;
-        double x = oracle_kind_reads_x(kind) ? oracle_f16_decode(X[o]) : 0.0;
-        double rb = oracle_kind_reads_bias(kind) ? oracle_f16_decode(RB[j]) : 0.0;
-        double cb = oracle_kind_reads_bias(kind) ? oracle_f16_decode(CB[i]) : 0.0;
+        double c = oracle_kind_reads_c(kind) ? dec(C[o]) : 0.0;
+        double x = oracle_kind_reads_x(kind) ? dec(X[o]) : 0.0;
+        double rb = oracle_kind_reads_bias(kind) ? dec(RB[j]) : 0.0;
+        double cb = oracle_kind_reads_bias(kind) ? dec(CB[i]) : 0.0;
         double d = 0.0, aux = 0.0;
         epilogue(kind, acc, c, x, rb, cb, alpha, beta, s, &d, &aux);
-        D[p] = oracle_f16_encode(d);
+        D[p] = enc(d);
         if (D64)
             D64[p] = d;
         if (oracle_kind_has_aux(kind)) {
             if (Aux)
-                Aux[p] = oracle_f16_encode(aux);
+                Aux[p] = enc(aux);
             if (Aux64)
                 Aux64[p] = aux;
         }
@@ -394,6 +473,16 @@ int oracle_gemm_epi_points_ext(int64_t L, int64_t M, int64_t N, int64_t K, const
             Acc64[p] = acc;
     }
     return 0;
+}
+
+int oracle_gemm_epi_points_ext(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A,
+                               const uint16_t *B, const uint16_t *C, const uint16_t *X, const uint16_t *RB,
+                               const uint16_t *CB, const float *scalars, int kind, int64_t npts, const int64_t *pl,
+                               const int64_t *pi, const int64_t *pj, uint16_t *D, uint16_t *Aux, float *Acc,
+                               double *D64, double *Aux64, double *Acc64)
+{
+    return oracle_gemm_epi_points_typed(L, M, N, K, A, B, C, X, RB, CB, scalars, kind, npts, pl, pi, pj, D, Aux,
+                                        Acc, D64, Aux64, Acc64, ORACLE_DTYPE_F16);
 }
 
 int oracle_gemm_epi_points(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
@@ -416,6 +505,18 @@ void oracle_f16_encode_n(const double *x, uint16_t *out, int64_t n)
 {
     for (int64_t q = 0; q < n; q++)
         out[q] = oracle_f16_encode(x[q]);
+}
+
+void oracle_bf16_decode_n(const uint16_t *h, double *out, int64_t n)
+{
+    for (int64_t q = 0; q < n; q++)
+        out[q] = oracle_bf16_decode(h[q]);
+}
+
+void oracle_bf16_encode_n(const double *x, uint16_t *out, int64_t n)
+{
+    for (int64_t q = 0; q < n; q++)
+        out[q] = oracle_bf16_encode(x[q]);
 }
 
 /* The rounding mode the encoder relies on (FE_TONEAREST); the tests check it. */
