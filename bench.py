@@ -20,6 +20,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -67,9 +69,32 @@ def _device_args(w, t, D, Aux, Acc, stream, ge):
             stream.cuda_stream)
 
 
+def _upload(p, w, dev):
+    """Host inputs of workload w as device tensors (bfloat16 workloads hold
+    uint16 bit patterns on the host)."""
+    import torch
+
+    def one(v):
+        if v is None:
+            return None
+        if w.dtype == "bf16":
+            return torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(v).to(dev)
+    return {k: one(v) for k, v in p.items()}
+
+
+def _launcher(w, ge):
+    """The entry point for workload w: gemm_epi_run_ext, or gemm_epi_run_typed
+    with the workload's element type (same arguments plus dtype)."""
+    if w.dtype == "f16":
+        return ge.gemm_epi_run_ext
+    dt = ge.DTYPES[w.dtype]
+    return lambda *a: ge.gemm_epi_run_typed(*a[:-1], dt, a[-1])
+
+
 def _outputs(w, ge, dev):
     import torch
-    D = torch.empty((w.L, w.M, w.N), dtype=torch.float16, device=dev)
+    D = torch.empty((w.L, w.M, w.N), dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float16, device=dev)
     Aux = torch.empty_like(D) if w.kind in ge.HAS_AUX else None
     Acc = torch.empty((w.L, w.M, w.N), dtype=torch.float32, device=dev) if w.kind in ge.HAS_ACC else None
     return D, Aux, Acc
@@ -105,15 +130,16 @@ def bench_gpu(w, steps, warmup):
 
     dev = torch.device("cuda:0")
     p = workloads.make_inputs(w)
-    t = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in p.items()}
+    t = _upload(p, w, dev)
     D, Aux, Acc = _outputs(w, ge, dev)
     stream = torch.cuda.current_stream(dev)
     args = _device_args(w, t, D, Aux, Acc, stream, ge)
+    run = _launcher(w, ge)
     for _ in range(warmup):
-        rc = ge.gemm_epi_run_ext(*args)
+        rc = run(*args)
         if rc:
             raise RuntimeError(ge.gemm_epi_status_string(rc))
-    wall_ms, ev_ms, stats = _timed_launches(lambda i: ge.gemm_epi_run_ext(*args), steps, stream)
+    wall_ms, ev_ms, stats = _timed_launches(lambda i: run(*args), steps, stream)
     rc, plan = _plan(args, ge)
     return {"ms_per_step": wall_ms, "kernel_ms": ev_ms, "launch_ms": stats, "plan": plan}
 
@@ -161,7 +187,7 @@ def bench_gpu_cold(w, steps, warmup):
 
     dev = torch.device("cuda:0")
     p = workloads.make_inputs(w)
-    base = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in p.items()}
+    base = _upload(p, w, dev)
     sets = min(4096, -(-2 * MALL_BYTES // w.hbm_bytes) + 1)
     copies = []
     for _ in range(sets):
@@ -169,9 +195,10 @@ def bench_gpu_cold(w, steps, warmup):
         copies.append((t,) + _outputs(w, ge, dev))
     stream = torch.cuda.current_stream(dev)
     arglist = [_device_args(w, t, D, Aux, Acc, stream, ge) for (t, D, Aux, Acc) in copies]
+    run = _launcher(w, ge)
     for i in range(warmup):
-        ge.gemm_epi_run_ext(*arglist[i % sets])
-    _, ev_ms, stats = _timed_launches(lambda i: ge.gemm_epi_run_ext(*arglist[(i + warmup) % sets]), steps, stream)
+        run(*arglist[i % sets])
+    _, ev_ms, stats = _timed_launches(lambda i: run(*arglist[(i + warmup) % sets]), steps, stream)
     del copies
     return {"copies": sets, "kernel_ms": round(ev_ms, 5), "launch_ms": {k: round(v, 5) for k, v in stats.items()},
             "tflops": round(w.flops / (ev_ms * 1e-3) / 1e12, 2),
@@ -325,7 +352,7 @@ def result_line(w, g, steps, warmup, cpu):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": w.dtype,
         "data": "synthetic",
         "config": {
             "workload": w.name, "L": w.L, "M": w.M, "N": w.N, "K": w.K, "epilogue": w.kind,
@@ -389,10 +416,11 @@ def main():
             g = bench_gpu(other, a.steps, a.warmup)
             line = result_line(other, g, a.steps, a.warmup, None)
             line["cold"] = bench_gpu_cold(other, a.steps, a.warmup)
-            sk = bench_gpu_stream_k(other, a.steps, a.warmup)
+            # the stream-K and unfused compositions take fp16 tensors only
+            sk = bench_gpu_stream_k(other, a.steps, a.warmup) if other.dtype == "f16" else None
             if sk is not None:
                 line["stream_k"] = sk
-            if a.compare_unfused:
+            if a.compare_unfused and other.dtype == "f16":
                 line["unfused_own"] = bench_unfused_own(other, a.steps, a.warmup)
                 line["unfused_library"] = bench_unfused_library(other, a.steps, a.warmup)
             print(json.dumps(line), file=sys.stderr, flush=True)

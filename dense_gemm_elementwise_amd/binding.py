@@ -46,11 +46,15 @@ STATUS = {
     5: "GEMM_EPI_ERR_ALIGN",
     6: "GEMM_EPI_ERR_HIP",
     7: "GEMM_EPI_ERR_WORKSPACE",
+    8: "GEMM_EPI_ERR_DTYPE",
 }
+# element types of the 16-bit tensors (gemm_epi_run_typed)
+DTYPES = {"f16": 0, "bf16": 1}
 
 # every function include/gemm_epi.h declares
-EXPORTS = ("gemm_epi_run", "gemm_epi_run_ext", "gemm_epi_run_ws", "gemm_epi_run_unfused", "gemm_epi_status_string",
-           "gemm_epi_last_hip_error", "gemm_epi_plan", "gemm_epi_plan_ext", "gemm_epi_plan_ws")
+EXPORTS = ("gemm_epi_run", "gemm_epi_run_ext", "gemm_epi_run_typed", "gemm_epi_run_ws", "gemm_epi_run_unfused",
+           "gemm_epi_status_string", "gemm_epi_last_hip_error", "gemm_epi_plan", "gemm_epi_plan_ext",
+           "gemm_epi_plan_ws")
 
 
 class GemmEpiError(RuntimeError):
@@ -78,6 +82,9 @@ def lib():
     L.gemm_epi_run_ext.restype = ctypes.c_int
     L.gemm_epi_run_ext.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_float),
                                    ctypes.c_int, vp, vp, vp, vp]
+    L.gemm_epi_run_typed.restype = ctypes.c_int
+    L.gemm_epi_run_typed.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_float),
+                                     ctypes.c_int, vp, vp, vp, ctypes.c_int, vp]
     L.gemm_epi_run_unfused.restype = ctypes.c_int
     L.gemm_epi_run_unfused.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_float),
                                        ctypes.c_int, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -130,6 +137,16 @@ def gemm_epi_run_ext(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilog
     sc = (ctypes.c_float * 3)(*[float(v) for v in scalars]) if scalars is not None else None
     return lib().gemm_epi_run_ext(int(L), int(M), int(N), int(K), A, B, C, X, row_bias, col_bias, sc,
                                   _kind_id(epilogue_kind), D, Aux, acc_out, stream)
+
+
+def gemm_epi_run_typed(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilogue_kind, D, Aux, acc_out,
+                       dtype, stream) -> int:
+    """Pointer-level call of gemm_epi_run_typed: gemm_epi_run_ext with the
+    element type of the 16-bit tensors ("f16" / "bf16" or the enum value)."""
+    sc = (ctypes.c_float * 3)(*[float(v) for v in scalars]) if scalars is not None else None
+    dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    return lib().gemm_epi_run_typed(int(L), int(M), int(N), int(K), A, B, C, X, row_bias, col_bias, sc,
+                                    _kind_id(epilogue_kind), D, Aux, acc_out, dt, stream)
 
 
 def gemm_epi_run_unfused(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilogue_kind, D, Aux, acc_out,
@@ -203,8 +220,9 @@ def run(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, D, Aux=None,
     """D (and Aux, acc_out) <- fused epilogue of A @ B on torch tensors.
 
     A (L,M,K), B (L,K,N), C, X, D, Aux (L,M,N): contiguous float16 CUDA
-    tensors; row_bias (N,) and col_bias (M,) or (M, 1) float16 for
-    BIAS_ROW_COL; acc_out (L,M,N) float32 for RELU_SCALE_ACC.  s3 is
+    tensors, or all bfloat16 (then the bfloat16 kernels run, through
+    gemm_epi_run_typed); row_bias (N,) and col_bias (M,) or (M, 1) of the
+    same type for BIAS_ROW_COL; acc_out (L,M,N) float32 for RELU_SCALE_ACC.  s3 is
     extra_scalar (AUX_SCALE), x_factor (LINCOMB_X_ACC) or scale
     (RELU_SCALE_ACC).  The kernel is queued on `stream` (a torch.cuda.Stream;
     default: the current stream); with sync=True the call waits for it.
@@ -220,27 +238,28 @@ def run(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, D, Aux=None,
         raise ValueError("A and B must be 3-D: (L,M,K) and (L,K,N)")
     L, M, K = A.shape
     N = B.shape[2]
-    _check_tensor("A", A, (L, M, K))
-    _check_tensor("B", B, (L, K, N))
-    _check_tensor("D", D, (L, M, N))
+    et = torch.bfloat16 if isinstance(A, torch.Tensor) and A.dtype == torch.bfloat16 else torch.float16
+    _check_tensor("A", A, (L, M, K), et)
+    _check_tensor("B", B, (L, K, N), et)
+    _check_tensor("D", D, (L, M, N), et)
     kname = kind if isinstance(kind, str) else {v: k for k, v in KINDS.items()}[int(kind)]
     if kname in READS_C:
         if C is None:
             raise ValueError(f"{kname} reads C")
-        _check_tensor("C", C, (L, M, N))
+        _check_tensor("C", C, (L, M, N), et)
     if kname in READS_X:
         if X is None:
             raise ValueError(f"{kname} reads X")
-        _check_tensor("X", X, (L, M, N))
+        _check_tensor("X", X, (L, M, N), et)
     if kname in READS_BIAS:
         if row_bias is None or col_bias is None:
             raise ValueError(f"{kname} reads row_bias (N,) and col_bias (M,)")
-        _check_tensor("row_bias", row_bias.reshape(-1) if row_bias.dim() == 2 else row_bias, (N,))
-        _check_tensor("col_bias", col_bias.reshape(-1) if col_bias.dim() == 2 else col_bias, (M,))
+        _check_tensor("row_bias", row_bias.reshape(-1) if row_bias.dim() == 2 else row_bias, (N,), et)
+        _check_tensor("col_bias", col_bias.reshape(-1) if col_bias.dim() == 2 else col_bias, (M,), et)
     if kname in HAS_AUX:
         if Aux is None:
             raise ValueError(f"{kname} writes a second output: pass Aux")
-        _check_tensor("Aux", Aux, (L, M, N))
+        _check_tensor("Aux", Aux, (L, M, N), et)
     if kname in HAS_ACC:
         if acc_out is None:
             raise ValueError(f"{kname} writes the fp32 accumulator: pass acc_out")
@@ -257,8 +276,14 @@ def run(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, D, Aux=None,
     skw = stream_k_workspace
     if skw is not None and (skw.device != dev or not skw.is_contiguous()):
         raise ValueError("stream_k_workspace must be a contiguous tensor on the operands' device")
+    if et == torch.bfloat16 and (ws is not None or skw is not None):
+        raise ValueError("the unfused and stream-K compositions take float16 tensors only")
     with torch.cuda.device(dev):
-        if skw is not None:
+        if et == torch.bfloat16:
+            rc = gemm_epi_run_typed(L, M, N, K, A.data_ptr(), B.data_ptr(), _ptr(C), _ptr(X), _ptr(row_bias),
+                                    _ptr(col_bias), (alpha, beta, s3), KINDS[kname], D.data_ptr(), _ptr(Aux),
+                                    _ptr(acc_out), DTYPES["bf16"], s.cuda_stream)
+        elif skw is not None:
             rc = gemm_epi_run_ws(L, M, N, K, A.data_ptr(), B.data_ptr(), _ptr(C), _ptr(X), _ptr(row_bias),
                                  _ptr(col_bias), (alpha, beta, s3), KINDS[kname], D.data_ptr(), _ptr(Aux),
                                  _ptr(acc_out), skw.data_ptr(), skw.numel() * skw.element_size(), s.cuda_stream)

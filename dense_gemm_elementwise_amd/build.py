@@ -1,8 +1,10 @@
 """Builds libgemm_epi.so (the HIP kernels and the C ABI) for gfx950, in-tree.
 
-hipcc compiles the single translation unit csrc/gemm_epi.hip for
---offload-arch=gfx950 only.  Packed-fp32 VALU instructions are switched off
-(-packed-fp32-ops): the epilogue is plain scalar fp32 arithmetic.
+hipcc compiles the translation units csrc/gemm_epi.hip (the C ABI and the
+fp16 kernels) and csrc/gemm_epi_bf16.hip (the bfloat16 kernels) in parallel
+for --offload-arch=gfx950 only, then links them into one shared library.
+Packed-fp32 VALU instructions are switched off (-packed-fp32-ops): the
+epilogue is plain scalar fp32 arithmetic.
 """
 import os
 import shutil
@@ -10,7 +12,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "gemm_epi.hip")
+SRCS = [os.path.join(PKG, "csrc", "gemm_epi.hip"), os.path.join(PKG, "csrc", "gemm_epi_bf16.hip")]
 LIB = os.path.join(PKG, "libgemm_epi.so")
 ARCH = "gfx950"
 
@@ -23,14 +25,26 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Wno-unused-command-line-argument",
-           "-o", LIB + ".tmp", SRC]
+    flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+             "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Wno-unused-command-line-argument"]
+    objs = [LIB + f".{i}.o" for i in range(len(SRCS))]
+    procs = []
+    for src, obj in zip(SRCS, objs):
+        cmd = [hipcc(), *flags, "-c", "-o", obj, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((cmd, subprocess.Popen(cmd)))
+    failed = [cmd for cmd, proc in procs if proc.wait() != 0]
+    if failed:
+        raise subprocess.CalledProcessError(1, failed[0])
+    link = [hipcc(), f"--offload-arch={ARCH}", "-fPIC", "-shared", "-o", LIB + ".tmp", *objs]
     if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+        print(" ".join(link), flush=True)
+    subprocess.run(link, check=True)
+    for obj in objs:
+        os.remove(obj)
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

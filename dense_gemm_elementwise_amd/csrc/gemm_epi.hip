@@ -11,25 +11,13 @@
 
 #include "gemm_epi.h"
 #include "gemm_epi_kernels.hpp"
+#include "gemm_epi_launch.hpp"
 
 using namespace gemm_epi;
 
 namespace {
 
 thread_local int g_last_hip_error = 0;
-
-struct TileCfg {
-    int bm, bn;      // output tile
-    int bk, stages;  // K step per LDS stage, LDS stages in the ring
-    int wgm, wgn;    // wave grid (threads = 64 * wgm * wgn)
-    int mi;          // MFMA block: 32 (32x32x16) or 16 (16x16x32)
-};
-
-// The tile configurations compiled into the library (fast path), and the one
-// general-path configuration.
-constexpr TileCfg kTiles[] = {{256, 256, 64, 2, 4, 2, 16}, {128, 256, 64, 2, 2, 4, 16}, {256, 128, 64, 2, 4, 2, 16},
-                              {128, 128, 64, 3, 2, 2, 32}, {64, 64, 32, 4, 2, 2, 16}};
-constexpr TileCfg kGeneral = {128, 128, 64, 2, 2, 2, 32};
 
 // Relative MFMA efficiency of a tile (bigger tiles reuse each LDS operand
 // read over more MFMAs and amortise the epilogue better).
@@ -122,54 +110,6 @@ bool use_fast_path(int64_t M, int64_t N, int64_t K, const Operands &o, int kind)
     if (M * K * 2 >= lim - 64 || K * N * 2 >= lim - 64) return false;
     return true;
 }
-
-// Calls f(std::integral_constant<int, KIND>) for a public kind (checked by
-// check_args before any call).
-template <typename F>
-hipError_t dispatch_kind(int kind, F &&f)
-{
-    switch (kind) {
-    case GEMM_EPI_LINCOMB: return f(std::integral_constant<int, LINCOMB>{});
-    case GEMM_EPI_AUX_SCALE: return f(std::integral_constant<int, AUX_SCALE>{});
-    case GEMM_EPI_LINCOMB_X_ACC: return f(std::integral_constant<int, LINCOMB_X_ACC>{});
-    case GEMM_EPI_RELU: return f(std::integral_constant<int, RELU>{});
-    case GEMM_EPI_SQUARE: return f(std::integral_constant<int, SQUARE>{});
-    case GEMM_EPI_RELU_SQUARE: return f(std::integral_constant<int, RELU_SQUARE>{});
-    case GEMM_EPI_RELU_AUX_STORE: return f(std::integral_constant<int, RELU_AUX_STORE>{});
-    case GEMM_EPI_RELU_SCALE_ACC: return f(std::integral_constant<int, RELU_SCALE_ACC>{});
-    case GEMM_EPI_BIAS_ROW_COL: return f(std::integral_constant<int, BIAS_ROW_COL>{});
-    case GEMM_EPI_SIGMOID: return f(std::integral_constant<int, SIGMOID>{});
-    case GEMM_EPI_TANH: return f(std::integral_constant<int, TANH>{});
-    case GEMM_EPI_GELU: return f(std::integral_constant<int, GELU>{});
-    case GEMM_EPI_SILU: return f(std::integral_constant<int, SILU>{});
-    case GEMM_EPI_LEAKY_RELU: return f(std::integral_constant<int, LEAKY_RELU>{});
-    default: return f(std::integral_constant<int, HARDSWISH>{});
-    }
-}
-
-template <int BM, int BN, int BK, int NS, int WGM, int WGN, int MI, int KIND, bool VEC, bool SK = false>
-hipError_t launch_one(const Params &p, hipStream_t stream, int grid)
-{
-    hipLaunchKernelGGL((gemm_epi_kernel<BM, BN, BK, NS, WGM, WGN, MI, KIND, VEC, SK>), dim3(grid),
-                       dim3(64 * WGM * WGN), 0, stream, p);
-    return hipGetLastError();
-}
-
-#define GE_LAUNCH(T, KIND, VEC) \
-    launch_one<T.bm, T.bn, T.bk, T.stages, T.wgm, T.wgn, T.mi, KIND, VEC>(p, stream, p.num_tiles)
-
-template <int KIND>
-hipError_t launch_kind(const Params &p, const TileCfg &t, bool vec, hipStream_t stream)
-{
-    if (!vec) return GE_LAUNCH(kGeneral, KIND, false);
-    if (t.bm == kTiles[0].bm && t.bn == kTiles[0].bn) return GE_LAUNCH(kTiles[0], KIND, true);
-    if (t.bm == kTiles[1].bm && t.bn == kTiles[1].bn) return GE_LAUNCH(kTiles[1], KIND, true);
-    if (t.bm == kTiles[2].bm && t.bn == kTiles[2].bn) return GE_LAUNCH(kTiles[2], KIND, true);
-    if (t.bm == kTiles[3].bm && t.bn == kTiles[3].bn) return GE_LAUNCH(kTiles[3], KIND, true);
-    return GE_LAUNCH(kTiles[4], KIND, true);
-}
-
-#undef GE_LAUNCH
 
 // ---- stream-K ---------------------------------------------------------------
 // Tiles with a stream-K build: a workgroup walks a contiguous range of
@@ -282,6 +222,7 @@ const char *gemm_epi_status_string(int status)
     case GEMM_EPI_ERR_ALIGN: return "a tensor pointer is not aligned to its element size";
     case GEMM_EPI_ERR_HIP: return "HIP launch error";
     case GEMM_EPI_ERR_WORKSPACE: return "the workspace is missing or smaller than the call needs";
+    case GEMM_EPI_ERR_DTYPE: return "unknown element type";
     default: return "unknown status";
     }
 }
@@ -320,9 +261,18 @@ int gemm_epi_run_ext(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, 
                      const void *X, const void *row_bias, const void *col_bias, const float *scalars,
                      int epilogue_kind, void *D, void *Aux, void *acc_out, void *stream)
 {
+    return gemm_epi_run_typed(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilogue_kind, D, Aux, acc_out,
+                              GEMM_EPI_F16, stream);
+}
+
+int gemm_epi_run_typed(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                       const void *X, const void *row_bias, const void *col_bias, const float *scalars,
+                       int epilogue_kind, void *D, void *Aux, void *acc_out, int dtype, void *stream)
+{
     const Operands o = {A, B, C, X, row_bias, col_bias, D, Aux, acc_out};
     int rc = check_args(L, M, N, K, o, epilogue_kind);
     if (rc != GEMM_EPI_OK) return rc;
+    if (dtype != GEMM_EPI_F16 && dtype != GEMM_EPI_BF16) return GEMM_EPI_ERR_DTYPE;
     if (!scalars) return GEMM_EPI_ERR_NULL_INPUT;
     const bool vec = use_fast_path(M, N, K, o, epilogue_kind);
     const TileCfg t = choose_tile(L, M, N, vec);
@@ -355,7 +305,10 @@ int gemm_epi_run_ext(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, 
 
     hipStream_t s = (hipStream_t)stream;
     hipError_t err;
-    err = dispatch_kind(epilogue_kind, [&](auto k) { return launch_kind<decltype(k)::value>(p, t, vec, s); });
+    if (dtype == GEMM_EPI_BF16)
+        err = launch_fused_bf16(epilogue_kind, p, t, vec, s);
+    else
+        err = dispatch_kind(epilogue_kind, [&](auto k) { return launch_kind<decltype(k)::value>(p, t, vec, s); });
     if (err != hipSuccess) {
         g_last_hip_error = (int)err;
         return GEMM_EPI_ERR_HIP;

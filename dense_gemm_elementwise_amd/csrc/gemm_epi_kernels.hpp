@@ -47,6 +47,28 @@ namespace gemm_epi {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// 16-bit tensor elements travel as raw bits in _Float16 storage; BF selects
+// how the bits read: IEEE binary16, or bfloat16 (the upper half of an IEEE
+// binary32: widening is a shift, narrowing is the hardware's
+// round-to-nearest-even conversion).
+template <bool BF>
+__device__ __forceinline__ float ld16(_Float16 h)
+{
+    if constexpr (BF)
+        return __builtin_bit_cast(float, (uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+    else
+        return (float)h;
+}
+template <bool BF>
+__device__ __forceinline__ _Float16 st16(float f)
+{
+    if constexpr (BF)
+        return __builtin_bit_cast(_Float16, (__bf16)f);
+    else
+        return (_Float16)f;
+}
 typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -397,7 +419,8 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void *p)
 // vectors); otherwise every global access is element-wise and guarded and
 // LDS is filled through registers.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int NSTAGES, int WGM, int WGN, int MI, int KIND, bool VEC, bool SK = false>
+template <int BM, int BN, int BK, int NSTAGES, int WGM, int WGN, int MI, int KIND, bool VEC, bool SK = false,
+          bool BF = false>
 __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
 {
     constexpr int NW = WGM * WGN;                // waves per workgroup
@@ -603,10 +626,17 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
         for (int i = 0; i < TM; i++)
 #pragma unroll
             for (int j = 0; j < TN; j++) {
-                if constexpr (MI == 32)
+                if constexpr (BF) {
+                    const bf16x8 a8 = __builtin_bit_cast(bf16x8, af[i]), b8 = __builtin_bit_cast(bf16x8, bf[j]);
+                    if constexpr (MI == 32)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, b8, acc[i][j], 0, 0, 0);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, acc[i][j], 0, 0, 0);
+                } else if constexpr (MI == 32) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-                else
+                } else {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+                }
             }
     };
 
@@ -888,15 +918,16 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
                     if constexpr (HAS_X) x4 = xbuf[i & 1][pass][h];
                     if constexpr (HAS_BIAS) {
                         rb4 = rbias[h];
-                        cbv = (float)cbias[i & 1][pass];
+                        cbv = ld16<BF>(cbias[i & 1][pass]);
                     }
                     hvec d4, e4;
 #pragma unroll
                     for (int e = 0; e < CPL; e++) {
                         float d, a = 0.0f;
-                        epi_elem<KIND>(av[e], (float)c4[e], (float)x4[e], (float)rb4[e], cbv, alpha, beta, s, d, a);
-                        d4[e] = (_Float16)d;
-                        e4[e] = (_Float16)a;
+                        epi_elem<KIND>(av[e], ld16<BF>(c4[e]), ld16<BF>(x4[e]), ld16<BF>(rb4[e]), cbv, alpha, beta, s,
+                                       d, a);
+                        d4[e] = st16<BF>(d);
+                        e4[e] = st16<BF>(a);
                     }
                     if constexpr (kind_writes_d(KIND)) *(hvec *)(p.D + o) = d4;
                     if constexpr (kind_has_aux(KIND)) *(hvec *)(p.Aux + o) = e4;
@@ -906,17 +937,17 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
                             *(f32x4 *)(p.acc_out + o + 4 * q) = f32x4{av[4 * q], av[4 * q + 1], av[4 * q + 2], av[4 * q + 3]};
                     }
                 } else {
-                    const float cbv = HAS_BIAS ? (float)p.col_bias[gm] : 0.0f;
+                    const float cbv = HAS_BIAS ? ld16<BF>(p.col_bias[gm]) : 0.0f;
 #pragma unroll
                     for (int e = 0; e < CPL; e++) {
                         if (gn + e >= N) break;
-                        const float c = HAS_C ? (float)p.C[o + e] : 0.0f;
-                        const float x = HAS_X ? (float)p.X[o + e] : 0.0f;
-                        const float rb = HAS_BIAS ? (float)p.row_bias[gn + e] : 0.0f;
+                        const float c = HAS_C ? ld16<BF>(p.C[o + e]) : 0.0f;
+                        const float x = HAS_X ? ld16<BF>(p.X[o + e]) : 0.0f;
+                        const float rb = HAS_BIAS ? ld16<BF>(p.row_bias[gn + e]) : 0.0f;
                         float d, a = 0.0f;
                         epi_elem<KIND>(av[e], c, x, rb, cbv, alpha, beta, s, d, a);
-                        if constexpr (kind_writes_d(KIND)) p.D[o + e] = (_Float16)d;
-                        if constexpr (kind_has_aux(KIND)) p.Aux[o + e] = (_Float16)a;
+                        if constexpr (kind_writes_d(KIND)) p.D[o + e] = st16<BF>(d);
+                        if constexpr (kind_has_aux(KIND)) p.Aux[o + e] = st16<BF>(a);
                         if constexpr (kind_has_acc_out(KIND)) p.acc_out[o + e] = av[e];
                     }
                 }

@@ -1,0 +1,82 @@
+// gemm_epi_launch.hpp -- tile configurations, kernel launchers and the kind
+// dispatch shared by the translation units of libgemm_epi.so (the fp16 one,
+// which also holds the C ABI, and the bfloat16 one).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <type_traits>
+
+#include "gemm_epi.h"
+#include "gemm_epi_kernels.hpp"
+
+namespace gemm_epi {
+
+struct TileCfg {
+    int bm, bn;      // output tile
+    int bk, stages;  // K step per LDS stage, LDS stages in the ring
+    int wgm, wgn;    // wave grid (threads = 64 * wgm * wgn)
+    int mi;          // MFMA block: 32 (32x32x16) or 16 (16x16x32)
+};
+
+// The tile configurations compiled into the library (fast path), and the one
+// general-path configuration.
+inline constexpr TileCfg kTiles[] = {{256, 256, 64, 2, 4, 2, 16}, {128, 256, 64, 2, 2, 4, 16},
+                                     {256, 128, 64, 2, 4, 2, 16}, {128, 128, 64, 3, 2, 2, 32},
+                                     {64, 64, 32, 4, 2, 2, 16}};
+inline constexpr TileCfg kGeneral = {128, 128, 64, 2, 2, 2, 32};
+
+// Calls f(std::integral_constant<int, KIND>) for a public kind (checked by
+// check_args before any call).
+template <typename F>
+hipError_t dispatch_kind(int kind, F &&f)
+{
+    switch (kind) {
+    case GEMM_EPI_LINCOMB: return f(std::integral_constant<int, LINCOMB>{});
+    case GEMM_EPI_AUX_SCALE: return f(std::integral_constant<int, AUX_SCALE>{});
+    case GEMM_EPI_LINCOMB_X_ACC: return f(std::integral_constant<int, LINCOMB_X_ACC>{});
+    case GEMM_EPI_RELU: return f(std::integral_constant<int, RELU>{});
+    case GEMM_EPI_SQUARE: return f(std::integral_constant<int, SQUARE>{});
+    case GEMM_EPI_RELU_SQUARE: return f(std::integral_constant<int, RELU_SQUARE>{});
+    case GEMM_EPI_RELU_AUX_STORE: return f(std::integral_constant<int, RELU_AUX_STORE>{});
+    case GEMM_EPI_RELU_SCALE_ACC: return f(std::integral_constant<int, RELU_SCALE_ACC>{});
+    case GEMM_EPI_BIAS_ROW_COL: return f(std::integral_constant<int, BIAS_ROW_COL>{});
+    case GEMM_EPI_SIGMOID: return f(std::integral_constant<int, SIGMOID>{});
+    case GEMM_EPI_TANH: return f(std::integral_constant<int, TANH>{});
+    case GEMM_EPI_GELU: return f(std::integral_constant<int, GELU>{});
+    case GEMM_EPI_SILU: return f(std::integral_constant<int, SILU>{});
+    case GEMM_EPI_LEAKY_RELU: return f(std::integral_constant<int, LEAKY_RELU>{});
+    default: return f(std::integral_constant<int, HARDSWISH>{});
+    }
+}
+
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, int MI, int KIND, bool VEC, bool SK = false,
+          bool BF = false>
+hipError_t launch_one(const Params &p, hipStream_t stream, int grid)
+{
+    hipLaunchKernelGGL((gemm_epi_kernel<BM, BN, BK, NS, WGM, WGN, MI, KIND, VEC, SK, BF>), dim3(grid),
+                       dim3(64 * WGM * WGN), 0, stream, p);
+    return hipGetLastError();
+}
+
+#define GE_LAUNCH(T, KIND, VEC) \
+    launch_one<T.bm, T.bn, T.bk, T.stages, T.wgm, T.wgn, T.mi, KIND, VEC, false, BF>(p, stream, p.num_tiles)
+
+// The fused kernel of one kind on tile configuration t (the general-path
+// kernel when vec is false); BF: the 16-bit tensors are bfloat16.
+template <int KIND, bool BF = false>
+hipError_t launch_kind(const Params &p, const TileCfg &t, bool vec, hipStream_t stream)
+{
+    if (!vec) return GE_LAUNCH(kGeneral, KIND, false);
+    if (t.bm == kTiles[0].bm && t.bn == kTiles[0].bn) return GE_LAUNCH(kTiles[0], KIND, true);
+    if (t.bm == kTiles[1].bm && t.bn == kTiles[1].bn) return GE_LAUNCH(kTiles[1], KIND, true);
+    if (t.bm == kTiles[2].bm && t.bn == kTiles[2].bn) return GE_LAUNCH(kTiles[2], KIND, true);
+    if (t.bm == kTiles[3].bm && t.bn == kTiles[3].bn) return GE_LAUNCH(kTiles[3], KIND, true);
+    return GE_LAUNCH(kTiles[4], KIND, true);
+}
+
+#undef GE_LAUNCH
+
+// The fused call on bfloat16 tensors (defined in gemm_epi_bf16.hip, a
+// translation unit of its own so the two element types compile in parallel).
+hipError_t launch_fused_bf16(int kind, const Params &p, const TileCfg &t, bool vec, hipStream_t stream);
+
+}  // namespace gemm_epi

@@ -3,8 +3,9 @@
 This module only draws inputs: it holds none of the method's arithmetic (no
 product, no epilogue, no rounding of results).  Both the HIP path and the CPU
 oracle are fed from it, so a workload's inputs are bit-identical on both
-sides.  All tensors are packed row-major host arrays of float16:
-A (L,M,K), B (L,K,N), C and X (L,M,N), row_bias (N,) and col_bias (M,).
+sides.  All tensors are packed row-major host arrays of float16 (for a bfloat16
+workload: uint16 arrays holding bfloat16 bit patterns, numpy having no such
+type): A (L,M,K), B (L,K,N), C and X (L,M,N), row_bias (N,) and col_bias (M,).
 
 The draws follow the constructions on the pages:
   - "randint_pm2": integers uniform in {-2..2}, drawn A, then B, then C from
@@ -18,6 +19,8 @@ The draws follow the constructions on the pages:
   - "normal": N(0, 1) drawn in float32 from a generator seeded 2025, then
     rounded to float16, in the order A, B, C, X (the pages do not show how the
     Alpha-Beta example fills its tensors).
+A bfloat16 workload draws the same values with the same generator and
+rounds them to bfloat16 instead (the integer recipes are exact in both).
 For the bias kind (tutorial cell [9]) C is not drawn; the row bias (N,) and
 the column bias (M,) follow A and B from the same generator: N(0, 1) rounded
 to float16 as the page draws them (torch.randn in float16), or integers in
@@ -57,6 +60,7 @@ class Workload:
     seed: int
     exact: bool  # integer-valued inputs: results must be bit-exact
     note: str = field(default="", compare=False)
+    dtype: str = "f16"  # element type of the 16-bit tensors: "f16" or "bf16"
 
     @property
     def flops(self) -> int:
@@ -109,16 +113,48 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in (
     # GELU at the headline size; alpha = 1/64 puts alpha*acc + beta*C (acc has
     # standard deviation sqrt(K) = 90.5) where the activation is not flat
     Workload("gelu_8192", 1, 8192, 8192, 8192, "GELU", 1.0 / 64, 1.0, 0.0, "normal", 2025, False),
+    # bfloat16 operands and outputs (the Custom Epilogue Example's "Data Type
+    # Support"): the tutorial's 1024^3 case (integers, exact) and the headline
+    Workload("aux_scale_bf16_1024", 1, 1024, 1024, 1024, "AUX_SCALE", 1.0, 2.0, 0.5, "randint_pm2", 2025, True,
+             dtype="bf16"),
+    Workload("x_acc_bf16_8192", 1, 8192, 8192, 8192, "LINCOMB_X_ACC", 2.0, 1.0, 3.0, "normal", 2025, False,
+             dtype="bf16"),
 )}
 
 # The workload the headline throughput is quoted on.
 HEADLINE = "x_acc_8192"
 
 
-def draw(init: str, seed: int, L: int, M: int, N: int, K: int, with_x: bool, kind: str = "LINCOMB"):
+def to_bf16_bits(t) -> np.ndarray:
+    """A float32 (or exactly convertible) torch tensor rounded to bfloat16,
+    to nearest with ties to even, as a uint16 numpy array of bit patterns."""
+    return t.to(torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_bits_to_float(bits: np.ndarray) -> np.ndarray:
+    """uint16 bfloat16 bit patterns -> float32 values (exact)."""
+    return (np.ascontiguousarray(bits).astype(np.uint32) << 16).view(np.float32)
+
+
+def draw(init: str, seed: int, L: int, M: int, N: int, K: int, with_x: bool, kind: str = "LINCOMB",
+         dtype: str = "f16"):
     """Draws the inputs of one problem with the named recipe, in the order
     A, B, then C (and X) or, for the bias kind, the row and column biases.
-    Returns a list of float16 numpy arrays in that order."""
+    Returns a list of float16 numpy arrays in that order (uint16 bfloat16
+    bit patterns when dtype is "bf16")."""
+    if dtype == "bf16":
+        # the same values, drawn in float32 from the same generator
+        if init == "randint_pm2":
+            g = torch.Generator().manual_seed(seed)
+            shapes = [(L, M, K), (L, K, N)] + ([] if kind in READS_BIAS else [(L, M, N)] * (2 if with_x else 1))
+            out = [to_bf16_bits(torch.randint(-2, 3, s, generator=g, dtype=torch.float32)) for s in shapes]
+            if kind in READS_BIAS:
+                out += [to_bf16_bits(torch.randn(s, generator=g, dtype=torch.float32)) for s in ((N,), (M,))]
+            return out
+        if init in ("normal", "small_int"):
+            f = draw(init, seed, L, M, N, K, with_x, kind, dtype="f32")
+            return [to_bf16_bits(torch.from_numpy(a)) for a in f]
+        raise ValueError(f"recipe {init!r} has no bfloat16 form")
     bias = kind in READS_BIAS
     shapes = [(L, M, K), (L, K, N)]
     if not bias:
@@ -137,15 +173,17 @@ def draw(init: str, seed: int, L: int, M: int, N: int, K: int, with_x: bool, kin
             out += [np.ceil(rs.uniform(-4, 4, size=s).astype(np.float16)) for s in ((N,), (M,))]
     elif init == "normal":
         g = torch.Generator().manual_seed(seed)
-        out = [torch.randn(s, generator=g, dtype=torch.float32).to(torch.float16).numpy() for s in shapes]
+        cast = (lambda t: t.numpy()) if dtype == "f32" else (lambda t: t.to(torch.float16).numpy())
+        out = [cast(torch.randn(s, generator=g, dtype=torch.float32)) for s in shapes]
         if bias:
-            out += [torch.randn(s, generator=g, dtype=torch.float32).to(torch.float16).numpy() for s in ((N,), (M,))]
+            out += [cast(torch.randn(s, generator=g, dtype=torch.float32)) for s in ((N,), (M,))]
     elif init == "small_int":
         # integers uniform in {-3..3}; used by the tail and kind sweeps
         g = torch.Generator().manual_seed(seed)
-        out = [torch.randint(-3, 4, s, generator=g, dtype=torch.float16).numpy() for s in shapes]
+        tdt = torch.float32 if dtype == "f32" else torch.float16
+        out = [torch.randint(-3, 4, s, generator=g, dtype=tdt).numpy() for s in shapes]
         if bias:
-            out += [torch.randint(-3, 4, s, generator=g, dtype=torch.float16).numpy() for s in ((N,), (M,))]
+            out += [torch.randint(-3, 4, s, generator=g, dtype=tdt).numpy() for s in ((N,), (M,))]
     else:
         raise ValueError(f"unknown init recipe {init!r}")
     return [np.ascontiguousarray(a) for a in out]
@@ -161,9 +199,9 @@ def _as_dict(arrs, kind):
 def make_inputs(w: Workload) -> Dict[str, Optional[np.ndarray]]:
     """Inputs of a named workload: dict with A, B, C, X, row_bias, col_bias
     (None where the kind does not read them)."""
-    return _as_dict(draw(w.init, w.seed, w.L, w.M, w.N, w.K, w.kind in READS_X, w.kind), w.kind)
+    return _as_dict(draw(w.init, w.seed, w.L, w.M, w.N, w.K, w.kind in READS_X, w.kind, w.dtype), w.kind)
 
 
-def make_problem(L, M, N, K, kind, init="small_int", seed=0):
+def make_problem(L, M, N, K, kind, init="small_int", seed=0, dtype="f16"):
     """Inputs for an arbitrary shape (tests), as make_inputs returns them."""
-    return _as_dict(draw(init, seed, L, M, N, K, kind in READS_X, kind), kind)
+    return _as_dict(draw(init, seed, L, M, N, K, kind in READS_X, kind, dtype), kind)

@@ -121,9 +121,21 @@ typedef enum {
     GEMM_EPI_ERR_ALIGN = 5,       /* an fp16 pointer is not 2-byte aligned, or acc_out is not 4-byte
                                      aligned */
     GEMM_EPI_ERR_HIP = 6,         /* the launch failed; see gemm_epi_last_hip_error() */
-    GEMM_EPI_ERR_WORKSPACE = 7    /* the workspace is NULL or smaller than the call needs
+    GEMM_EPI_ERR_WORKSPACE = 7,   /* the workspace is NULL or smaller than the call needs
                                      (gemm_epi_run_unfused, gemm_epi_run_ws) */
+    GEMM_EPI_ERR_DTYPE = 8        /* unknown element type (gemm_epi_run_typed) */
 } gemm_epi_status;
+
+/*
+ * Element types of the 16-bit tensors (A, B, C, X, row_bias, col_bias, D,
+ * Aux), for gemm_epi_run_typed: the Custom Epilogue Example's "Data Type
+ * Support" lists FP16 and BF16 among the input types (A, B) and the output
+ * types (C, D).  Accumulation and the epilogue stay fp32; acc_out stays fp32.
+ */
+typedef enum {
+    GEMM_EPI_F16 = 0,  /* IEEE 754 binary16 */
+    GEMM_EPI_BF16 = 1  /* bfloat16: 1 sign, 8 exponent and 7 fraction bits (the upper half of a binary32) */
+} gemm_epi_dtype;
 
 /*
  * gemm_epi_run -- launch the fused GEMM + epilogue on `stream`.
@@ -187,6 +199,21 @@ int gemm_epi_run(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, cons
 int gemm_epi_run_ext(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
                      const void *X, const void *row_bias, const void *col_bias, const float *scalars,
                      int epilogue_kind, void *D, void *Aux, void *acc_out, void *stream);
+
+/*
+ * gemm_epi_run_typed -- gemm_epi_run_ext with the element type of the 16-bit
+ * tensors as an argument: dtype is GEMM_EPI_F16 (then the call is exactly
+ * gemm_epi_run_ext) or GEMM_EPI_BF16, in which case A, B, C, X, row_bias,
+ * col_bias, D and Aux all hold bfloat16 values with the same shapes, layouts
+ * and alignment rules.  bfloat16 products are exact in fp32, the accumulator
+ * and the epilogue are fp32 as for fp16, and every bfloat16 output is
+ * rounded once, to nearest with ties to even.  The tile choice
+ * (gemm_epi_plan_ext) does not depend on dtype.  Status codes as
+ * gemm_epi_run_ext, plus GEMM_EPI_ERR_DTYPE for another dtype value.
+ */
+int gemm_epi_run_typed(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                       const void *X, const void *row_bias, const void *col_bias, const float *scalars,
+                       int epilogue_kind, void *D, void *Aux, void *acc_out, int dtype, void *stream);
 
 /*
  * gemm_epi_run_unfused -- the same operation as gemm_epi_run_ext, NOT fused:

@@ -32,7 +32,8 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert set(names) == {"gemm_epi_run", "gemm_epi_run_ext", "gemm_epi_run_ws", "gemm_epi_run_unfused",
+    assert set(names) == {"gemm_epi_run", "gemm_epi_run_ext", "gemm_epi_run_typed", "gemm_epi_run_ws",
+                          "gemm_epi_run_unfused",
                           "gemm_epi_status_string", "gemm_epi_last_hip_error", "gemm_epi_plan", "gemm_epi_plan_ext",
                           "gemm_epi_plan_ws"}
     raw = ctypes.CDLL(binding.LIB_PATH)
@@ -47,10 +48,12 @@ def test_enum_values_match_header():
         assert re.search(rf"GEMM_EPI_{name}\s*=\s*{val}\b", text), name
     for val, name in binding.STATUS.items():
         assert re.search(rf"{name}\s*=\s*{val}\b", text), name
+    for name, val in binding.DTYPES.items():
+        assert re.search(rf"GEMM_EPI_{name.upper()}\s*=\s*{val}\b", text), name
 
 
 def test_status_strings():
-    for code in range(8):
+    for code in range(9):
         s = ge.gemm_epi_status_string(code)
         assert isinstance(s, str) and s
     assert ge.gemm_epi_status_string(0) == "ok"
@@ -121,6 +124,19 @@ def test_ext_operand_checks():
     assert plan_ext(kind=bias, C=None, rb=P16, cb=P16)[0] == 0   # the bias kind does not read C
     assert plan_ext(kind=acc, Aux=P16, acc=P16)[0] == 0
     assert plan_ext(kind=ge.KINDS["RELU_AUX_STORE"], Aux=P16)[0] == 0
+
+
+def test_typed_entry_point_checks():
+    def typed(dtype, **kw):
+        a = dict(A=P16, B=P16, C=P16, X=P16, rb=P16, cb=P16, D=P16, Aux=P16, acc=P16)
+        a.update(kw)
+        return ge.gemm_epi_run_typed(1, 8, 8, 8, a["A"], a["B"], a["C"], a["X"], a["rb"], a["cb"], SC, 0, a["D"],
+                                     a["Aux"], a["acc"], dtype, None)
+    assert typed(2) == 8 and typed(-1) == 8            # unknown element type
+    assert typed("bf16", A=None) == 2                  # the argument checks come first
+    assert typed("bf16", D=None) == 3
+    assert typed("bf16", C=P1) == 5
+    assert ge.gemm_epi_status_string(8) == "unknown element type"
 
 
 def test_unfused_workspace_checks():
@@ -217,6 +233,8 @@ def test_plan_tiles_for_the_workloads():
         "bias_row_col_8192": (256, 256, 1024),
         "lincomb_deep_k_256x256x65536": (64, 64, 16),
         "gelu_8192": (256, 256, 1024),
+        "aux_scale_bf16_1024": (64, 64, 256),     # the tile choice does not depend on the element type
+        "x_acc_bf16_8192": (256, 256, 1024),
     }
     want.update({f"{a.lower()}_256": (64, 64, 16) for a in workloads.ACTIVATIONS})
     assert set(want) == set(workloads.WORKLOADS)
