@@ -144,11 +144,14 @@ struct Params {
 // ---------------------------------------------------------------------------
 // Activations, fp32, written from the mathematics (no library call).  Their
 // error is a few fp32 units in the last place or about 1e-6 relative, far
-// below the fp16 output's 2^-11.
+// below the fp16 output's 2^-11.  Quotients use the hardware reciprocal
+// (v_rcp_f32, 1 ulp) instead of the correctly rounded division, a sequence of
+// about ten instructions that made the GELU epilogue VALU-bound.
 // ---------------------------------------------------------------------------
 // e^x = 2^(x log2 e) on the hardware base-2 exponential (v_exp_f32)
 __device__ __forceinline__ float act_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
-__device__ __forceinline__ float act_sigmoid(float x) { return 1.0f / (1.0f + act_exp(-x)); }
+__device__ __forceinline__ float act_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float act_sigmoid(float x) { return act_rcp(1.0f + act_exp(-x)); }
 // tanh: for |x| < 1/4 its Maclaurin series to x^9 (truncation below 1e-8
 // relative); otherwise (1 - e^-2|x|) / (1 + e^-2|x|) with the sign of x, where
 // e^-2|x| <= 0.61 so nothing cancels
@@ -165,7 +168,7 @@ __device__ __forceinline__ float act_tanh(float x)
         return __builtin_fmaf(x * x2, p, x);
     }
     const float e = act_exp(-2.0f * ax);
-    return __builtin_copysignf((1.0f - e) / (1.0f + e), x);
+    return __builtin_copysignf((1.0f - e) * act_rcp(1.0f + e), x);
 }
 // gelu(x) = x Phi(x), Phi(x) = erfc(-x / sqrt 2) / 2, in the form that keeps
 // relative accuracy in the left tail: with z = |x| / sqrt 2,
@@ -178,7 +181,7 @@ __device__ __forceinline__ float act_erfc_pos(float z)
     constexpr float c[9] = {-2.037919330e-04f, 2.859725058e-01f, 2.504409850e-01f, 3.914754093e-01f,
                             -2.268847674e-01f, 7.775521874e-01f, -6.962806582e-01f, 2.504747510e-01f,
                             -3.254655749e-02f};
-    const float t = 2.0f / (2.0f + z);
+    const float t = 2.0f * act_rcp(2.0f + z);
     float p = c[8];
 #pragma unroll
     for (int k = 7; k >= 0; k--) p = __builtin_fmaf(p, t, c[k]);
@@ -190,11 +193,11 @@ __device__ __forceinline__ float act_gelu(float x)
     const float ec = act_erfc_pos(__builtin_fabsf(x) * 0.707106781186547524f);
     return x >= 0.0f ? x * (1.0f - 0.5f * ec) : x * (0.5f * ec);
 }
-__device__ __forceinline__ float act_silu(float x) { return x / (1.0f + act_exp(-x)); }
+__device__ __forceinline__ float act_silu(float x) { return x * act_rcp(1.0f + act_exp(-x)); }
 __device__ __forceinline__ float act_hardswish(float x)
 {
 #pragma clang fp contract(off)
-    return x * __builtin_fminf(__builtin_fmaxf(x + 3.0f, 0.0f), 6.0f) / 6.0f;
+    return x * __builtin_fminf(__builtin_fmaxf(x + 3.0f, 0.0f), 6.0f) * (1.0f / 6.0f);
 }
 
 template <int KIND>
@@ -838,9 +841,14 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     const float alpha = p.alpha, beta = p.beta, s = p.s;
     const int64_t mn_base = (int64_t)l * M * N;
     auto lane_col = [&](int h) { return CPL * (lane & 15) + h * EPI_HALF; };
-    hvec cbuf[2][CP][EPI_GROUPS];
-    hvec xbuf[2][XP][EPI_GROUPS];
-    _Float16 cbias[2][BP];
+    // a kind whose only elementwise input is C loads every slab's C at once
+    // (the fragment registers are free by now): more loads in flight
+    constexpr bool PRELOAD = VEC && HAS_C && !HAS_X && !HAS_BIAS;
+    constexpr int NB = PRELOAD ? TM : 2;
+    hvec cbuf[NB][CP][EPI_GROUPS];
+    hvec xbuf[NB][XP][EPI_GROUPS];
+    _Float16 cbias[NB][BP];
+    auto slot = [](int i) { return PRELOAD ? i : (i & 1); };
     hvec rbias[EPI_GROUPS];
     auto epi_prefetch = [&](int i, hvec (&cb)[CP][EPI_GROUPS], hvec (&xb)[XP][EPI_GROUPS], _Float16 (&colb)[BP]) {
 #pragma unroll
@@ -870,7 +878,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
                 rbias[h] = (scol < WN && gn < N) ? *(const hvec *)(p.row_bias + gn) : hvec{};
             }
         }
-        epi_prefetch(0, cbuf[0], xbuf[0], cbias[0]);
+        if constexpr (PRELOAD) {
+#pragma unroll
+            for (int i = 0; i < TM; i++) epi_prefetch(i, cbuf[i], xbuf[i], cbias[i]);
+        } else {
+            epi_prefetch(0, cbuf[0], xbuf[0], cbias[0]);
+        }
     }
     barrier_lds();  // every wave is done with the main loop's LDS, which the epilogue reuses
 
@@ -890,7 +903,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
             }
         wave_lds_sync();  // each wave reads back only its own slab
         if constexpr (VEC) {
-            if (i + 1 < TM) epi_prefetch(i + 1, cbuf[(i + 1) & 1], xbuf[(i + 1) & 1], cbias[(i + 1) & 1]);
+            if (!PRELOAD && i + 1 < TM)
+                epi_prefetch(i + 1, cbuf[(i + 1) & 1], xbuf[(i + 1) & 1], cbias[(i + 1) & 1]);
         }
 #pragma unroll
         for (int pass = 0; pass < EPI_PASSES; pass++) {
@@ -914,11 +928,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
                     if (gn >= N) continue;  // N % 8 == 0: a lane's column group is all in or all out
                     hvec c4 = {}, x4 = {}, rb4 = {};
                     float cbv = 0.0f;
-                    if constexpr (HAS_C) c4 = cbuf[i & 1][pass][h];
-                    if constexpr (HAS_X) x4 = xbuf[i & 1][pass][h];
+                    if constexpr (HAS_C) c4 = cbuf[slot(i)][pass][h];
+                    if constexpr (HAS_X) x4 = xbuf[slot(i)][pass][h];
                     if constexpr (HAS_BIAS) {
                         rb4 = rbias[h];
-                        cbv = ld16<BF>(cbias[i & 1][pass]);
+                        cbv = ld16<BF>(cbias[slot(i)][pass]);
                     }
                     hvec d4, e4;
 #pragma unroll
