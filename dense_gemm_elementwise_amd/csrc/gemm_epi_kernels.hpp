@@ -841,28 +841,34 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     const float alpha = p.alpha, beta = p.beta, s = p.s;
     const int64_t mn_base = (int64_t)l * M * N;
     auto lane_col = [&](int h) { return CPL * (lane & 15) + h * EPI_HALF; };
-    // a kind whose only elementwise input is C loads every slab's C at once
-    // (the fragment registers are free by now): more loads in flight
-    constexpr bool PRELOAD = VEC && HAS_C && !HAS_X && !HAS_BIAS;
-    constexpr int NB = PRELOAD ? TM : 2;
-    hvec cbuf[NB][CP][EPI_GROUPS];
-    hvec xbuf[NB][XP][EPI_GROUPS];
-    _Float16 cbias[NB][BP];
-    auto slot = [](int i) { return PRELOAD ? i : (i & 1); };
+    // C of every slab is loaded at once when the epilogue starts (the operand
+    // fragment registers are free by then): more loads in flight.  X and the
+    // column bias go one slab ahead.
+    constexpr bool PRE_C = VEC && HAS_C;
+    constexpr int NBC = PRE_C ? TM : 2;
+    hvec cbuf[NBC][CP][EPI_GROUPS];
+    hvec xbuf[2][XP][EPI_GROUPS];
+    _Float16 cbias[2][BP];
+    auto cslot = [](int i) { return PRE_C ? i : (i & 1); };
     hvec rbias[EPI_GROUPS];
-    auto epi_prefetch = [&](int i, hvec (&cb)[CP][EPI_GROUPS], hvec (&xb)[XP][EPI_GROUPS], _Float16 (&colb)[BP]) {
+    // loads slab i's C (with_c) and its X and column bias (with_x)
+    auto epi_prefetch = [&](int i, hvec (&cb)[CP][EPI_GROUPS], hvec (&xb)[XP][EPI_GROUPS], _Float16 (&colb)[BP],
+                            bool with_c, bool with_x) {
 #pragma unroll
         for (int pass = 0; pass < EPI_PASSES; pass++) {
             const int gm = m0 + wm * WM + i * SLAB + pass * 4 + (lane >> 4);
-            if constexpr (HAS_BIAS) colb[pass] = gm < M ? p.col_bias[gm] : (_Float16)0.0f;
+            if constexpr (HAS_BIAS)
+                if (with_x) colb[pass] = gm < M ? p.col_bias[gm] : (_Float16)0.0f;
 #pragma unroll
             for (int h = 0; h < EPI_GROUPS; h++) {
                 const int scol = lane_col(h);
                 const int gn = n0 + wn * WN + scol;
                 if (scol < WN && gm < M && gn < N) {
                     const int64_t o = mn_base + (int64_t)gm * N + gn;
-                    if constexpr (HAS_C) cb[pass][h] = *(const hvec *)(p.C + o);
-                    if constexpr (HAS_X) xb[pass][h] = *(const hvec *)(p.X + o);
+                    if constexpr (HAS_C)
+                        if (with_c) cb[pass][h] = *(const hvec *)(p.C + o);
+                    if constexpr (HAS_X)
+                        if (with_x) xb[pass][h] = *(const hvec *)(p.X + o);
                 }
             }
         }
@@ -878,11 +884,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
                 rbias[h] = (scol < WN && gn < N) ? *(const hvec *)(p.row_bias + gn) : hvec{};
             }
         }
-        if constexpr (PRELOAD) {
+        epi_prefetch(0, cbuf[0], xbuf[0], cbias[0], true, true);
+        if constexpr (PRE_C) {
 #pragma unroll
-            for (int i = 0; i < TM; i++) epi_prefetch(i, cbuf[i], xbuf[i], cbias[i]);
-        } else {
-            epi_prefetch(0, cbuf[0], xbuf[0], cbias[0]);
+            for (int i = 1; i < TM; i++) epi_prefetch(i, cbuf[i], xbuf[1], cbias[1], true, false);
         }
     }
     barrier_lds();  // every wave is done with the main loop's LDS, which the epilogue reuses
@@ -903,8 +908,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
             }
         wave_lds_sync();  // each wave reads back only its own slab
         if constexpr (VEC) {
-            if (!PRELOAD && i + 1 < TM)
-                epi_prefetch(i + 1, cbuf[(i + 1) & 1], xbuf[(i + 1) & 1], cbias[(i + 1) & 1]);
+            if (i + 1 < TM)
+                epi_prefetch(i + 1, cbuf[cslot(i + 1)], xbuf[(i + 1) & 1], cbias[(i + 1) & 1], !PRE_C, true);
         }
 #pragma unroll
         for (int pass = 0; pass < EPI_PASSES; pass++) {
@@ -928,11 +933,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
                     if (gn >= N) continue;  // N % 8 == 0: a lane's column group is all in or all out
                     hvec c4 = {}, x4 = {}, rb4 = {};
                     float cbv = 0.0f;
-                    if constexpr (HAS_C) c4 = cbuf[slot(i)][pass][h];
-                    if constexpr (HAS_X) x4 = xbuf[slot(i)][pass][h];
+                    if constexpr (HAS_C) c4 = cbuf[cslot(i)][pass][h];
+                    if constexpr (HAS_X) x4 = xbuf[i & 1][pass][h];
                     if constexpr (HAS_BIAS) {
                         rb4 = rbias[h];
-                        cbv = ld16<BF>(cbias[slot(i)][pass]);
+                        cbv = ld16<BF>(cbias[i & 1][pass]);
                     }
                     hvec d4, e4;
 #pragma unroll
