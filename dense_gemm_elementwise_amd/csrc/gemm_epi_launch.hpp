@@ -18,10 +18,13 @@ struct TileCfg {
 };
 
 // The tile configurations compiled into the library (fast path), and the one
-// general-path configuration.
+// general-path configuration.  The 64 x 64 tile (small problems, one wave of
+// workgroups or less) takes BK = 64: its stages are latency-bound, so half as
+// many of them is what counts (1024^3: 12.0 -> 9.7 us against BK = 32; more
+// stages in the ring did not help).
 inline constexpr TileCfg kTiles[] = {{256, 256, 64, 2, 4, 2, 16}, {128, 256, 64, 2, 2, 4, 16},
                                      {256, 128, 64, 2, 4, 2, 16}, {128, 128, 64, 3, 2, 2, 32},
-                                     {64, 64, 32, 4, 2, 2, 16}};
+                                     {64, 64, 64, 4, 2, 2, 16}};
 inline constexpr TileCfg kGeneral = {128, 128, 64, 2, 2, 2, 32};
 
 // Calls f(std::integral_constant<int, KIND>) for a public kind (checked by
