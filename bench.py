@@ -28,7 +28,8 @@ if ROOT not in sys.path:
 
 PEAK_FP16_TFLOPS = 2516.6  # MI355X dense fp16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
-KERNEL_SOURCES = ("dense_gemm_elementwise_amd/csrc/gemm_epi_kernels.hpp", "dense_gemm_elementwise_amd/csrc/gemm_epi.hip")
+KERNEL_SOURCES = ("dense_gemm_elementwise_amd/csrc/gemm_epi_kernels.hpp", "dense_gemm_elementwise_amd/csrc/gemm_epi.hip",
+                  "dense_gemm_elementwise_amd/csrc/gemm_epi_launch.hpp", "dense_gemm_elementwise_amd/csrc/gemm_epi_bf16.hip")
 
 
 def kernel_source_hash():
