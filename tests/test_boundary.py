@@ -275,3 +275,16 @@ def test_workload_draws_follow_the_pages():
     rs = np.random.RandomState(1234)
     first = np.ceil(rs.uniform(-4, 4, size=(1, 128, 128)).astype(np.float16))
     assert np.array_equal(first.view(np.uint16), c[0].view(np.uint16))
+
+
+def test_c_program_builds_against_the_header(tmp_path):
+    """The C ABI compiles from plain C (gcc, C11, -Wall -Wextra) and links
+    against libgemm_epi.so: tests/c_abi/c_abi_check.c."""
+    import subprocess
+    import sys
+    sys.path.insert(0, ROOT)
+    from tests.c_abi import build as c_abi_build
+    out = str(tmp_path / "c_abi_check")
+    r = subprocess.run(c_abi_build.command(out), capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    assert "warning" not in r.stderr, r.stderr

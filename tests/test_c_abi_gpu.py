@@ -1,0 +1,20 @@
+"""The C ABI from plain C on the GPU: tests/c_abi/c_abi_check (built by
+__graft_entry__.build()) calls gemm_epi_run_typed for fp16 and bf16 tensors
+on integer inputs, fast and general kernels, and compares every output bit
+for bit with the CPU oracle; it also checks that an argument error comes
+back as a status code.  It runs as a child process."""
+import os
+import subprocess
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+EXE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi", "c_abi_check")
+
+
+def test_c_program_against_the_oracle():
+    assert os.path.exists(EXE), f"{EXE} is missing: run __graft_entry__.build() first"
+    r = subprocess.run([EXE], capture_output=True, text=True, timeout=120)
+    print(r.stdout, r.stderr, flush=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.count("PASS kind=") == 8 and "PASS: 0 failing case(s)" in r.stdout
