@@ -22,12 +22,16 @@
  * (all epilogue tensors share one major order, as the "Constraints" section
  * of the Custom Epilogue Example requires).  Offsets are 64-bit.
  *
- * Arithmetic: fp16 inputs, fp32 accumulation (the tutorial's
- * accumulator_type=torch.float32; "--acc_dtype Float32" on the example's
- * command line), epilogue in fp32 ("--epi_dtype Float32") from the unrounded
- * accumulator, scalars in fp32 (the example's 'float' scalars), each output
- * converted once to fp16 with round-to-nearest-even (overflow gives inf).
- * The order of the K summation is not specified.
+ * Arithmetic: fp16 inputs (or bfloat16, through gemm_epi_run_typed), fp32
+ * accumulation (the tutorial's accumulator_type=torch.float32;
+ * "--acc_dtype Float32" on the example's command line), epilogue in fp32
+ * ("--epi_dtype Float32") from the unrounded accumulator, scalars in fp32
+ * (the example's 'float' scalars), each output converted once to fp16 (or
+ * bfloat16) with round-to-nearest-even (overflow gives inf).  The order of
+ * the K summation is not specified; the epilogue's roundings are:
+ * alpha*acc + beta*C is fma(alpha, acc, beta*C), + s*X one more fma, every
+ * other operation rounded on its own, so every entry point gives the same
+ * bits for the same accumulator.
  */
 #ifndef GEMM_EPI_H
 #define GEMM_EPI_H
