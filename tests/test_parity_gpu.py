@@ -422,3 +422,36 @@ def test_large_operand_uses_general_kernel_with_64bit_offsets():
     ref = oracle.gemm_epi_points(A.numpy(), B.numpy(), C.numpy(), kind="LINCOMB", alpha=1.0, beta=1.0,
                                  l=l, i=i, j=j)
     assert_bit_exact(D.cpu().numpy()[l, i, j], ref["D"], "large operand rows")
+
+
+# ---------------------------------------------------------------------------
+# Closed forms on the GPU output alone (no oracle): A = I makes acc = B
+# exactly, A = 0 makes acc = +0, so each epilogue reduces to elementwise
+# arithmetic on B and C that numpy rounds the same way (one rounding of an
+# exact value: the small-integer inputs keep every intermediate exact).
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("kind,alpha,beta,s3", [("LINCOMB", 1.0, 2.0, 0.0), ("AUX_SCALE", 3.0, 2.0, 0.5),
+                                                ("RELU_SQUARE", 0.5, 1.0, 0.0), ("LINCOMB_X_ACC", 2.0, 1.0, 3.0)])
+@pytest.mark.parametrize("a_form", ["identity", "zero"])
+def test_closed_forms_on_gpu_output(kind, alpha, beta, s3, a_form):
+    L, M, N = 2, 136, 264
+    K = M
+    log(f"[parity] closed form A={a_form} kind={kind}")
+    p = workloads.make_problem(L, M, N, K, kind, init="small_int", seed=9)
+    p["A"] = (np.broadcast_to(np.eye(M, dtype=np.float16), (L, M, M)) if a_form == "identity"
+              else np.zeros((L, M, K), np.float16)).copy()
+    got = gpu_run(p, kind, alpha, beta, s3)
+    acc = p["B"].astype(np.float64) if a_form == "identity" else np.zeros((L, M, N))
+    c = p["C"].astype(np.float64)
+    lin = alpha * acc + beta * c
+    if kind == "LINCOMB":
+        want = {"D": lin}
+    elif kind == "AUX_SCALE":
+        want = {"Aux": lin, "D": s3 * lin}
+    elif kind == "RELU_SQUARE":
+        d = np.maximum(lin, 0.0)
+        want = {"D": d, "Aux": d * d}
+    else:
+        want = {"Aux": acc, "D": lin + s3 * p["X"].astype(np.float64)}
+    for name, w in want.items():
+        assert_bit_exact(got[name], w.astype(np.float16), f"closed form A={a_form} {kind} {name}")
