@@ -348,8 +348,13 @@ TAIL_SHAPES = [
 # shapes whose tile choice is 128 x 128 and 256 x 128 (the others are reached above)
 TILE_SHAPES = [(1, 768, 2816, 72), (1, 2304, 2048, 40), (1, 2400, 1032, 24)]
 
+# the 256 x 256 tile with 1, 2, 3 and 5 k stages of 64, the last one ragged,
+# and ragged M and N: its prologue and the DMA waits near the end of K
+BIG_TILE_SHAPES = [(1, 4000, 4000, 8), (1, 4000, 4000, 24), (1, 4000, 4000, 40), (1, 4000, 4000, 72),
+                   (1, 4000, 4000, 104), (1, 4000, 4000, 136), (1, 3000, 5000, 264)]
 
-@pytest.mark.parametrize("shape", TAIL_SHAPES + TILE_SHAPES)
+
+@pytest.mark.parametrize("shape", TAIL_SHAPES + TILE_SHAPES + BIG_TILE_SHAPES)
 def test_tails_bit_exact(shape):
     L, M, N, K = shape
     kind = "AUX_SCALE"
