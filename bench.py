@@ -324,6 +324,20 @@ def omp_threads():
     return len(os.sched_getaffinity(0))
 
 
+def measured_mfma_busy(workload_name):
+    """The share of SIMD cycles with the MFMA unit busy (rocprofv3's MfmaUtil)
+    from the committed profile summary, if it was taken on the current kernel
+    source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_src_sha256") != kernel_source_hash() or "mfma_util_pct" not in rec:
+        return None
+    return round(rec["mfma_util_pct"] / 100.0, 4)
+
+
 def roofline(w, kernel_ms):
     """The bound of this workload's kernel (the larger of its MFMA time and
     its algorithmic-bytes time at peak) and what the measured launch
@@ -337,7 +351,7 @@ def roofline(w, kernel_ms):
         achieved, peak, unit, bound = w.hbm_bytes / t / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
     return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name),
-            "attainable_frac": round(max(t_mfma, t_hbm) / t, 4)}
+            "attainable_frac": round(max(t_mfma, t_hbm) / t, 4), "mfma_busy": measured_mfma_busy(w.name)}
 
 
 def result_line(w, g, steps, warmup, cpu):
