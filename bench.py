@@ -146,7 +146,7 @@ def bench_gpu(w, steps, warmup):
 
 
 def bench_gpu_stream_k(w, steps, warmup):
-    """The same workload through gemm_epi_run_ws, which splits K across
+    """The same workload through gemm_epi_run_ws_typed, which splits K across
     workgroups (stream-K) when the problem has too few tiles; None when no
     split is planned for it."""
     import torch
@@ -155,7 +155,8 @@ def bench_gpu_stream_k(w, steps, warmup):
 
     dev = torch.device("cuda:0")
     p = workloads.make_inputs(w)
-    t = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in p.items()}
+    t = _upload(p, w, dev)
+    dt = ge.DTYPES[w.dtype]
     D, Aux, Acc = _outputs(w, ge, dev)
     stream = torch.cuda.current_stream(dev)
     args = _device_args(w, t, D, Aux, Acc, stream, ge)
@@ -163,12 +164,12 @@ def bench_gpu_stream_k(w, steps, warmup):
     if rc or plan["workspace_bytes"] == 0:
         return None
     ws = torch.zeros(plan["workspace_bytes"], dtype=torch.uint8, device=dev)
-    wargs = args[:15] + (ws.data_ptr(), plan["workspace_bytes"], args[15])
+    wargs = args[:15] + (ws.data_ptr(), plan["workspace_bytes"], dt, args[15])
     for _ in range(warmup):
-        rc = ge.gemm_epi_run_ws(*wargs)
+        rc = ge.gemm_epi_run_ws_typed(*wargs)
         if rc:
             raise RuntimeError(ge.gemm_epi_status_string(rc))
-    _, ev_ms, stats = _timed_launches(lambda i: ge.gemm_epi_run_ws(*wargs), steps, stream)
+    _, ev_ms, stats = _timed_launches(lambda i: ge.gemm_epi_run_ws_typed(*wargs), steps, stream)
     return {"tile": [plan["bm"], plan["bn"], plan["bk"]], "workgroups": plan["workgroups"],
             "workspace_bytes": plan["workspace_bytes"], "kernel_ms": round(ev_ms, 5),
             "launch_ms": {k: round(v, 5) for k, v in stats.items()},
@@ -208,7 +209,7 @@ def bench_gpu_cold(w, steps, warmup):
 
 def bench_unfused_own(w, steps, warmup):
     """Context, not the metric: the same workload through this library's own
-    unfused composition (gemm_epi_run_unfused: the GEMM writes the fp32
+    unfused composition (gemm_epi_run_unfused_typed: the GEMM writes the fp32
     accumulator to HBM, a second launch applies the epilogue).  Same
     results as the fused kernel; the difference is the fusion's saving."""
     import torch
@@ -217,17 +218,18 @@ def bench_unfused_own(w, steps, warmup):
 
     dev = torch.device("cuda:0")
     p = workloads.make_inputs(w)
-    t = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in p.items()}
+    t = _upload(p, w, dev)
+    dt = ge.DTYPES[w.dtype]
     D, Aux, Acc = _outputs(w, ge, dev)
     ws = torch.empty(w.L * w.M * w.N, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     args = _device_args(w, t, D, Aux, Acc, stream, ge)
-    uargs = args[:15] + (ws.data_ptr(), ws.numel() * 4, args[15])
+    uargs = args[:15] + (ws.data_ptr(), ws.numel() * 4, dt, args[15])
     for _ in range(warmup):
-        rc = ge.gemm_epi_run_unfused(*uargs)
+        rc = ge.gemm_epi_run_unfused_typed(*uargs)
         if rc:
             raise RuntimeError(ge.gemm_epi_status_string(rc))
-    _, ev_ms, stats = _timed_launches(lambda i: ge.gemm_epi_run_unfused(*uargs), steps, stream)
+    _, ev_ms, stats = _timed_launches(lambda i: ge.gemm_epi_run_unfused_typed(*uargs), steps, stream)
     return {"what": "own GEMM kernel writing the fp32 accumulator + own elementwise epilogue kernel",
             "ms_per_step": round(ev_ms, 5), "tflops": round(w.flops / (ev_ms * 1e-3) / 1e12, 2)}
 
@@ -237,13 +239,14 @@ def bench_unfused_library(w, steps, warmup):
     vendor library -- torch.matmul (hipBLASLt, fp16 output) followed by the
     epilogue as separate torch elementwise kernels -- on the same inputs.
     This is the three-kernel composition the fusion replaces; its
-    intermediate Y = A @ B is rounded to fp16 before the epilogue."""
+    intermediate Y = A @ B is rounded to the 16-bit element type before the
+    epilogue."""
     import torch
     from dense_gemm_elementwise_amd import workloads
 
     dev = torch.device("cuda:0")
     p = workloads.make_inputs(w)
-    t = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in p.items()}
+    t = _upload(p, w, dev)
     A, B, C, X = t["A"], t["B"], t["C"], t["X"]
     rb, cb = t["row_bias"], t["col_bias"]
     a, b, s3 = w.alpha, w.beta, w.s3
@@ -431,11 +434,10 @@ def main():
             g = bench_gpu(other, a.steps, a.warmup)
             line = result_line(other, g, a.steps, a.warmup, None)
             line["cold"] = bench_gpu_cold(other, a.steps, a.warmup)
-            # the stream-K and unfused compositions take fp16 tensors only
-            sk = bench_gpu_stream_k(other, a.steps, a.warmup) if other.dtype == "f16" else None
+            sk = bench_gpu_stream_k(other, a.steps, a.warmup)
             if sk is not None:
                 line["stream_k"] = sk
-            if a.compare_unfused and other.dtype == "f16":
+            if a.compare_unfused:
                 line["unfused_own"] = bench_unfused_own(other, a.steps, a.warmup)
                 line["unfused_library"] = bench_unfused_library(other, a.steps, a.warmup)
             print(json.dumps(line), file=sys.stderr, flush=True)

@@ -53,7 +53,7 @@ DTYPES = {"f16": 0, "bf16": 1}
 
 # every function include/gemm_epi.h declares
 EXPORTS = ("gemm_epi_run", "gemm_epi_run_ext", "gemm_epi_run_typed", "gemm_epi_run_ws", "gemm_epi_run_unfused",
-           "gemm_epi_status_string", "gemm_epi_last_hip_error", "gemm_epi_plan", "gemm_epi_plan_ext",
+           "gemm_epi_run_ws_typed", "gemm_epi_run_unfused_typed", "gemm_epi_status_string", "gemm_epi_last_hip_error", "gemm_epi_plan", "gemm_epi_plan_ext",
            "gemm_epi_plan_ws")
 
 
@@ -91,6 +91,13 @@ def lib():
     L.gemm_epi_run_ws.restype = ctypes.c_int
     L.gemm_epi_run_ws.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_float),
                                   ctypes.c_int, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.gemm_epi_run_unfused_typed.restype = ctypes.c_int
+    L.gemm_epi_run_unfused_typed.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp,
+                                             ctypes.POINTER(ctypes.c_float), ctypes.c_int, vp, vp, vp, vp,
+                                             ctypes.c_size_t, ctypes.c_int, vp]
+    L.gemm_epi_run_ws_typed.restype = ctypes.c_int
+    L.gemm_epi_run_ws_typed.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_float),
+                                        ctypes.c_int, vp, vp, vp, vp, ctypes.c_size_t, ctypes.c_int, vp]
     L.gemm_epi_plan_ws.restype = ctypes.c_int
     L.gemm_epi_plan_ws.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
                                    ctypes.POINTER(i64)]
@@ -144,9 +151,8 @@ def gemm_epi_run_typed(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epil
     """Pointer-level call of gemm_epi_run_typed: gemm_epi_run_ext with the
     element type of the 16-bit tensors ("f16" / "bf16" or the enum value)."""
     sc = (ctypes.c_float * 3)(*[float(v) for v in scalars]) if scalars is not None else None
-    dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
     return lib().gemm_epi_run_typed(int(L), int(M), int(N), int(K), A, B, C, X, row_bias, col_bias, sc,
-                                    _kind_id(epilogue_kind), D, Aux, acc_out, dt, stream)
+                                    _kind_id(epilogue_kind), D, Aux, acc_out, _dtype_id(dtype), stream)
 
 
 def gemm_epi_run_unfused(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilogue_kind, D, Aux, acc_out,
@@ -167,6 +173,31 @@ def gemm_epi_run_ws(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilogu
     sc = (ctypes.c_float * 3)(*[float(v) for v in scalars]) if scalars is not None else None
     return lib().gemm_epi_run_ws(int(L), int(M), int(N), int(K), A, B, C, X, row_bias, col_bias, sc,
                                  _kind_id(epilogue_kind), D, Aux, acc_out, workspace, int(workspace_bytes), stream)
+
+
+def _dtype_id(dtype):
+    return DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+
+
+def gemm_epi_run_unfused_typed(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilogue_kind, D, Aux,
+                               acc_out, workspace, workspace_bytes, dtype, stream) -> int:
+    """Pointer-level call of gemm_epi_run_unfused_typed: gemm_epi_run_unfused
+    with the element type of the 16-bit tensors ("f16" / "bf16" or the enum
+    value)."""
+    sc = (ctypes.c_float * 3)(*[float(v) for v in scalars]) if scalars is not None else None
+    return lib().gemm_epi_run_unfused_typed(int(L), int(M), int(N), int(K), A, B, C, X, row_bias, col_bias, sc,
+                                            _kind_id(epilogue_kind), D, Aux, acc_out, workspace,
+                                            int(workspace_bytes), _dtype_id(dtype), stream)
+
+
+def gemm_epi_run_ws_typed(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilogue_kind, D, Aux, acc_out,
+                          workspace, workspace_bytes, dtype, stream) -> int:
+    """Pointer-level call of gemm_epi_run_ws_typed: gemm_epi_run_ws with the
+    element type of the 16-bit tensors ("f16" / "bf16" or the enum value)."""
+    sc = (ctypes.c_float * 3)(*[float(v) for v in scalars]) if scalars is not None else None
+    return lib().gemm_epi_run_ws_typed(int(L), int(M), int(N), int(K), A, B, C, X, row_bias, col_bias, sc,
+                                       _kind_id(epilogue_kind), D, Aux, acc_out, workspace, int(workspace_bytes),
+                                       _dtype_id(dtype), stream)
 
 
 def gemm_epi_plan_ws(L, M, N, K, A, B, C, X, row_bias, col_bias, epilogue_kind, D, Aux, acc_out):
@@ -220,8 +251,8 @@ def run(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, D, Aux=None,
     """D (and Aux, acc_out) <- fused epilogue of A @ B on torch tensors.
 
     A (L,M,K), B (L,K,N), C, X, D, Aux (L,M,N): contiguous float16 CUDA
-    tensors, or all bfloat16 (then the bfloat16 kernels run, through
-    gemm_epi_run_typed); row_bias (N,) and col_bias (M,) or (M, 1) of the
+    tensors, or all bfloat16 (then the bfloat16 kernels run; every
+    composition below takes either type); row_bias (N,) and col_bias (M,) or (M, 1) of the
     same type for BIAS_ROW_COL; acc_out (L,M,N) float32 for RELU_SCALE_ACC.  s3 is
     extra_scalar (AUX_SCALE), x_factor (LINCOMB_X_ACC) or scale
     (RELU_SCALE_ACC).  The kernel is queued on `stream` (a torch.cuda.Stream;
@@ -276,25 +307,16 @@ def run(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, D, Aux=None,
     skw = stream_k_workspace
     if skw is not None and (skw.device != dev or not skw.is_contiguous()):
         raise ValueError("stream_k_workspace must be a contiguous tensor on the operands' device")
-    if et == torch.bfloat16 and (ws is not None or skw is not None):
-        raise ValueError("the unfused and stream-K compositions take float16 tensors only")
+    dt = DTYPES["bf16"] if et == torch.bfloat16 else DTYPES["f16"]
+    ops = (L, M, N, K, A.data_ptr(), B.data_ptr(), _ptr(C), _ptr(X), _ptr(row_bias), _ptr(col_bias),
+           (alpha, beta, s3), KINDS[kname], D.data_ptr(), _ptr(Aux), _ptr(acc_out))
     with torch.cuda.device(dev):
-        if et == torch.bfloat16:
-            rc = gemm_epi_run_typed(L, M, N, K, A.data_ptr(), B.data_ptr(), _ptr(C), _ptr(X), _ptr(row_bias),
-                                    _ptr(col_bias), (alpha, beta, s3), KINDS[kname], D.data_ptr(), _ptr(Aux),
-                                    _ptr(acc_out), DTYPES["bf16"], s.cuda_stream)
-        elif skw is not None:
-            rc = gemm_epi_run_ws(L, M, N, K, A.data_ptr(), B.data_ptr(), _ptr(C), _ptr(X), _ptr(row_bias),
-                                 _ptr(col_bias), (alpha, beta, s3), KINDS[kname], D.data_ptr(), _ptr(Aux),
-                                 _ptr(acc_out), skw.data_ptr(), skw.numel() * skw.element_size(), s.cuda_stream)
-        elif ws is None:
-            rc = gemm_epi_run_ext(L, M, N, K, A.data_ptr(), B.data_ptr(), _ptr(C), _ptr(X), _ptr(row_bias),
-                                  _ptr(col_bias), (alpha, beta, s3), KINDS[kname], D.data_ptr(), _ptr(Aux),
-                                  _ptr(acc_out), s.cuda_stream)
+        if skw is not None:
+            rc = gemm_epi_run_ws_typed(*ops, skw.data_ptr(), skw.numel() * skw.element_size(), dt, s.cuda_stream)
+        elif ws is not None:
+            rc = gemm_epi_run_unfused_typed(*ops, ws.data_ptr(), ws.numel() * 4, dt, s.cuda_stream)
         else:
-            rc = gemm_epi_run_unfused(L, M, N, K, A.data_ptr(), B.data_ptr(), _ptr(C), _ptr(X), _ptr(row_bias),
-                                      _ptr(col_bias), (alpha, beta, s3), KINDS[kname], D.data_ptr(), _ptr(Aux),
-                                      _ptr(acc_out), ws.data_ptr(), ws.numel() * 4, s.cuda_stream)
+            rc = gemm_epi_run_typed(*ops, dt, s.cuda_stream)
     if rc != 0:
         msg = gemm_epi_status_string(rc)
         if rc == 6:

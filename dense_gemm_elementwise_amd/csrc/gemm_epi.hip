@@ -113,9 +113,8 @@ bool use_fast_path(int64_t M, int64_t N, int64_t K, const Operands &o, int kind)
 
 // ---- stream-K ---------------------------------------------------------------
 // Tiles with a stream-K build: a workgroup walks a contiguous range of
-// (tile, k stage) units, so a few tiles can keep every CU busy.  (The
-// 8-wave 256 x 256 tile has no registers to spare for the range loop.)
-constexpr TileCfg kSkTiles[] = {{128, 128, 64, 3, 2, 2, 32}};
+// (tile, k stage) units, so a few tiles can keep every CU busy.
+constexpr TileCfg kSkTiles[] = {kSkTile};
 
 struct SkPlan {
     bool on = false;
@@ -183,26 +182,25 @@ SkPlan plan_stream_k(int64_t L, int64_t M, int64_t N, int64_t K, bool vec)
     return best;
 }
 
-template <int KIND>
-hipError_t launch_kind_sk(Params p, const SkPlan &sk, void *workspace, hipStream_t stream)
+// The stream-K split of a call: units per workgroup and the workspace's
+// partial-sum slots and per-tile counters.
+void set_sk_params(Params &p, const SkPlan &sk, void *workspace)
 {
     p.sk_q = sk.units / sk.groups;
     p.sk_r = sk.units % sk.groups;
     p.partials = (float *)workspace;
     p.counters = (int *)((char *)workspace + sk_partials_bytes(sk.t, sk.groups));
-    constexpr TileCfg T = kSkTiles[0];
-    return launch_one<T.bm, T.bn, T.bk, T.stages, T.wgm, T.wgn, T.mi, KIND, true, true>(p, stream, sk.groups);
 }
 
 // The elementwise stage of the unfused composition.
-template <int KIND>
+template <int KIND, bool BF>
 hipError_t launch_epilogue(const EpiParams &q, bool vec, hipStream_t stream)
 {
     const int64_t blocks = q.rows < 8192 ? q.rows : 8192;
     if (vec)
-        hipLaunchKernelGGL((epilogue_kernel<KIND, true>), dim3((unsigned)blocks), dim3(256), 0, stream, q);
+        hipLaunchKernelGGL((epilogue_kernel<KIND, true, BF>), dim3((unsigned)blocks), dim3(256), 0, stream, q);
     else
-        hipLaunchKernelGGL((epilogue_kernel<KIND, false>), dim3((unsigned)blocks), dim3(256), 0, stream, q);
+        hipLaunchKernelGGL((epilogue_kernel<KIND, false, BF>), dim3((unsigned)blocks), dim3(256), 0, stream, q);
     return hipGetLastError();
 }
 
@@ -321,9 +319,19 @@ int gemm_epi_run_unfused(int64_t L, int64_t M, int64_t N, int64_t K, const void 
                          int epilogue_kind, void *D, void *Aux, void *acc_out, void *workspace,
                          size_t workspace_bytes, void *stream)
 {
+    return gemm_epi_run_unfused_typed(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilogue_kind, D, Aux,
+                                      acc_out, workspace, workspace_bytes, GEMM_EPI_F16, stream);
+}
+
+int gemm_epi_run_unfused_typed(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                               const void *C, const void *X, const void *row_bias, const void *col_bias,
+                               const float *scalars, int epilogue_kind, void *D, void *Aux, void *acc_out,
+                               void *workspace, size_t workspace_bytes, int dtype, void *stream)
+{
     const Operands o = {A, B, C, X, row_bias, col_bias, D, Aux, acc_out};
     int rc = check_args(L, M, N, K, o, epilogue_kind);
     if (rc != GEMM_EPI_OK) return rc;
+    if (dtype != GEMM_EPI_F16 && dtype != GEMM_EPI_BF16) return GEMM_EPI_ERR_DTYPE;
     if (!scalars) return GEMM_EPI_ERR_NULL_INPUT;
     // the accumulator goes to acc_out when the kind returns it, else to the workspace
     float *acc = (float *)(kind_has_acc_out(epilogue_kind) ? acc_out : workspace);
@@ -352,7 +360,8 @@ int gemm_epi_run_unfused(int64_t L, int64_t M, int64_t N, int64_t K, const void 
     p.group_m = L > 1 ? 2 : 8;
     p.alpha = 1.0f;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t err = launch_kind<ACC_STORE>(p, t, vec1, s);
+    const bool bf = dtype == GEMM_EPI_BF16;
+    hipError_t err = bf ? launch_acc_store_bf16(p, t, vec1, s) : launch_kind<ACC_STORE>(p, t, vec1, s);
 
     // stage 2: the epilogue, elementwise, from the accumulator in HBM
     if (err == hipSuccess) {
@@ -375,7 +384,12 @@ int gemm_epi_run_unfused(int64_t L, int64_t M, int64_t N, int64_t K, const void 
         if (kind_reads_x(epilogue_kind)) vec2 = vec2 && aligned(X, 8);
         if (kind_reads_bias(epilogue_kind)) vec2 = vec2 && aligned(row_bias, 8);
         if (kind_has_aux(epilogue_kind)) vec2 = vec2 && aligned(Aux, 8);
-        err = dispatch_kind(epilogue_kind, [&](auto k) { return launch_epilogue<decltype(k)::value>(q, vec2, s); });
+        if (bf)
+            err = dispatch_kind(epilogue_kind,
+                                [&](auto k) { return launch_epilogue<decltype(k)::value, true>(q, vec2, s); });
+        else
+            err = dispatch_kind(epilogue_kind,
+                                [&](auto k) { return launch_epilogue<decltype(k)::value, false>(q, vec2, s); });
     }
     if (err != hipSuccess) {
         g_last_hip_error = (int)err;
@@ -418,15 +432,25 @@ int gemm_epi_run_ws(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, c
                     const void *X, const void *row_bias, const void *col_bias, const float *scalars, int epilogue_kind,
                     void *D, void *Aux, void *acc_out, void *workspace, size_t workspace_bytes, void *stream)
 {
+    return gemm_epi_run_ws_typed(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilogue_kind, D, Aux, acc_out,
+                                 workspace, workspace_bytes, GEMM_EPI_F16, stream);
+}
+
+int gemm_epi_run_ws_typed(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                          const void *X, const void *row_bias, const void *col_bias, const float *scalars,
+                          int epilogue_kind, void *D, void *Aux, void *acc_out, void *workspace,
+                          size_t workspace_bytes, int dtype, void *stream)
+{
     const Operands o = {A, B, C, X, row_bias, col_bias, D, Aux, acc_out};
     int rc = check_args(L, M, N, K, o, epilogue_kind);
     if (rc != GEMM_EPI_OK) return rc;
+    if (dtype != GEMM_EPI_F16 && dtype != GEMM_EPI_BF16) return GEMM_EPI_ERR_DTYPE;
     if (!scalars) return GEMM_EPI_ERR_NULL_INPUT;
     const bool vec = use_fast_path(M, N, K, o, epilogue_kind);
     const SkPlan sk = plan_stream_k(L, M, N, K, vec);
     if (!sk.on)
-        return gemm_epi_run_ext(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilogue_kind, D, Aux,
-                                acc_out, stream);
+        return gemm_epi_run_typed(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilogue_kind, D, Aux,
+                                  acc_out, dtype, stream);
     if (!workspace || workspace_bytes < sk.workspace) return GEMM_EPI_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return GEMM_EPI_ERR_ALIGN;
 
@@ -450,9 +474,14 @@ int gemm_epi_run_ws(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, c
     p.alpha = scalars[0];
     p.beta = scalars[1];
     p.s = scalars[2];
+    set_sk_params(p, sk, workspace);
     hipStream_t s = (hipStream_t)stream;
     hipError_t err;
-    err = dispatch_kind(epilogue_kind, [&](auto k) { return launch_kind_sk<decltype(k)::value>(p, sk, workspace, s); });
+    if (dtype == GEMM_EPI_BF16)
+        err = launch_sk_bf16(epilogue_kind, p, sk.groups, s);
+    else
+        err = dispatch_kind(epilogue_kind,
+                            [&](auto k) { return launch_kind_sk<decltype(k)::value>(p, sk.groups, s); });
     if (err != hipSuccess) {
         g_last_hip_error = (int)err;
         return GEMM_EPI_ERR_HIP;

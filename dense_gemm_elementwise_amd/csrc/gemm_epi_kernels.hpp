@@ -148,10 +148,24 @@ struct Params {
 // (v_rcp_f32, 1 ulp) instead of the correctly rounded division, a sequence of
 // about ten instructions that made the GELU epilogue VALU-bound.
 // ---------------------------------------------------------------------------
-// e^x = 2^(x log2 e) on the hardware base-2 exponential (v_exp_f32)
+// e^x = 2^(x log2 e) on the hardware base-2 exponential (v_exp_f32).  It
+// returns no subnormals, so a factor that may fall below 2^-126 is formed
+// as a product of two halves, e^x = e^(x/2) e^(x/2): the multiply rounds
+// once into the subnormal range (the kernels run with fp32 subnormals
+// enabled), which the bfloat16 outputs can hold down to 2^-133.
 __device__ __forceinline__ float act_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
 __device__ __forceinline__ float act_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
-__device__ __forceinline__ float act_sigmoid(float x) { return act_rcp(1.0f + act_exp(-x)); }
+// sigmoid(x) = 1 / (1 + e^-x) for x >= 0 and e^x / (1 + e^x) for x < 0, with
+// e^-|x| = v v, v = e^(-|x|/2): nothing overflows, and far left the result is
+// e^x itself, subnormal included
+__device__ __forceinline__ float act_sigmoid(float x)
+{
+#pragma clang fp contract(off)
+    const float v = act_exp(-0.5f * __builtin_fabsf(x));
+    const float e = v * v;
+    const float r = act_rcp(1.0f + e);
+    return x >= 0.0f ? r : e * r;
+}
 // tanh: for |x| < 1/4 its Maclaurin series to x^9 (truncation below 1e-8
 // relative); otherwise (1 - e^-2|x|) / (1 + e^-2|x|) with the sign of x, where
 // e^-2|x| <= 0.61 so nothing cancels
@@ -174,26 +188,33 @@ __device__ __forceinline__ float act_tanh(float x)
 // relative accuracy in the left tail: with z = |x| / sqrt 2,
 // x >= 0: x (1 - erfc(z) / 2); x < 0: x erfc(z) / 2.  erfc(z) = e^{-z^2} P(t),
 // t = 2 / (2 + z), P a degree-8 polynomial fitted to the scaled
-// complementary error function by fit_erfc.py (relative error 7e-8)
-__device__ __forceinline__ float act_erfc_pos(float z)
+// complementary error function by fit_erfc.py (relative error 7e-8).
+// e^{-z^2} = h h with h = e^{-z^2/2}, multiplied in last: past x = -13.2 the
+// result is subnormal in fp32
+__device__ __forceinline__ float act_gelu(float x)
 {
 #pragma clang fp contract(off)
     constexpr float c[9] = {-2.037919330e-04f, 2.859725058e-01f, 2.504409850e-01f, 3.914754093e-01f,
                             -2.268847674e-01f, 7.775521874e-01f, -6.962806582e-01f, 2.504747510e-01f,
                             -3.254655749e-02f};
+    const float z = __builtin_fabsf(x) * 0.707106781186547524f;
     const float t = 2.0f * act_rcp(2.0f + z);
     float p = c[8];
 #pragma unroll
     for (int k = 7; k >= 0; k--) p = __builtin_fmaf(p, t, c[k]);
-    return p * act_exp(-(z * z));
+    const float h = act_exp(-0.5f * (z * z));
+    return x >= 0.0f ? x * (1.0f - 0.5f * ((p * h) * h)) : (((0.5f * x) * p) * h) * h;
 }
-__device__ __forceinline__ float act_gelu(float x)
+// silu(x) = x sigmoid(x); for x < 0, x e^x / (1 + e^x) with the product
+// x e^x formed as (x v) v, v = e^(x/2)
+__device__ __forceinline__ float act_silu(float x)
 {
 #pragma clang fp contract(off)
-    const float ec = act_erfc_pos(__builtin_fabsf(x) * 0.707106781186547524f);
-    return x >= 0.0f ? x * (1.0f - 0.5f * ec) : x * (0.5f * ec);
+    const float v = act_exp(-0.5f * __builtin_fabsf(x));
+    const float e = v * v;
+    const float r = act_rcp(1.0f + e);
+    return x >= 0.0f ? x * r : ((x * v) * v) * r;
 }
-__device__ __forceinline__ float act_silu(float x) { return x * act_rcp(1.0f + act_exp(-x)); }
 __device__ __forceinline__ float act_hardswish(float x)
 {
 #pragma clang fp contract(off)
@@ -1018,7 +1039,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
 // read); its results equal the fused kernel's bit for bit.  One row of one
 // batch entry per iteration of a block, so a lane knows its row and column
 // without a division; VEC: 4 consecutive columns per lane (N % 4 == 0,
-// 16-byte aligned accumulator, 8-byte aligned fp16 tensors).
+// 16-byte aligned accumulator, 8-byte aligned 16-bit tensors).  BF: the
+// 16-bit tensors are bfloat16.
 // ---------------------------------------------------------------------------
 struct EpiParams {
     const float *acc;  // (L, M, N) fp32 accumulator
@@ -1033,14 +1055,14 @@ struct EpiParams {
     float alpha, beta, s;
 };
 
-template <int KIND, bool VEC>
+template <int KIND, bool VEC, bool BF = false>
 __global__ __launch_bounds__(256) void epilogue_kernel(EpiParams q)
 {
     const float alpha = q.alpha, beta = q.beta, s = q.s;
     for (int64_t row = blockIdx.x; row < q.rows; row += gridDim.x) {
         const int m = (int)(row % q.M);
         const int64_t base = row * q.N;
-        const float cbv = kind_reads_bias(KIND) ? (float)q.col_bias[m] : 0.0f;
+        const float cbv = kind_reads_bias(KIND) ? ld16<BF>(q.col_bias[m]) : 0.0f;
         if constexpr (VEC) {
             for (int n = 4 * threadIdx.x; n < q.N; n += 4 * blockDim.x) {
                 const int64_t o = base + n;
@@ -1053,9 +1075,10 @@ __global__ __launch_bounds__(256) void epilogue_kernel(EpiParams q)
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     float d, a = 0.0f;
-                    epi_elem<KIND>(a4[e], (float)c4[e], (float)x4[e], (float)rb4[e], cbv, alpha, beta, s, d, a);
-                    d4[e] = (_Float16)d;
-                    e4[e] = (_Float16)a;
+                    epi_elem<KIND>(a4[e], ld16<BF>(c4[e]), ld16<BF>(x4[e]), ld16<BF>(rb4[e]), cbv, alpha, beta, s, d,
+                                   a);
+                    d4[e] = st16<BF>(d);
+                    e4[e] = st16<BF>(a);
                 }
                 *(half4 *)(q.D + o) = d4;
                 if constexpr (kind_has_aux(KIND)) *(half4 *)(q.Aux + o) = e4;
@@ -1063,13 +1086,13 @@ __global__ __launch_bounds__(256) void epilogue_kernel(EpiParams q)
         } else {
             for (int n = threadIdx.x; n < q.N; n += blockDim.x) {
                 const int64_t o = base + n;
-                const float c = kind_reads_c(KIND) ? (float)q.C[o] : 0.0f;
-                const float x = kind_reads_x(KIND) ? (float)q.X[o] : 0.0f;
-                const float rb = kind_reads_bias(KIND) ? (float)q.row_bias[n] : 0.0f;
+                const float c = kind_reads_c(KIND) ? ld16<BF>(q.C[o]) : 0.0f;
+                const float x = kind_reads_x(KIND) ? ld16<BF>(q.X[o]) : 0.0f;
+                const float rb = kind_reads_bias(KIND) ? ld16<BF>(q.row_bias[n]) : 0.0f;
                 float d, a = 0.0f;
                 epi_elem<KIND>(q.acc[o], c, x, rb, cbv, alpha, beta, s, d, a);
-                q.D[o] = (_Float16)d;
-                if constexpr (kind_has_aux(KIND)) q.Aux[o] = (_Float16)a;
+                q.D[o] = st16<BF>(d);
+                if constexpr (kind_has_aux(KIND)) q.Aux[o] = st16<BF>(a);
             }
         }
     }

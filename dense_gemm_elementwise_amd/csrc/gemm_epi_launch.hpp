@@ -78,8 +78,23 @@ hipError_t launch_kind(const Params &p, const TileCfg &t, bool vec, hipStream_t 
 
 #undef GE_LAUNCH
 
-// The fused call on bfloat16 tensors (defined in gemm_epi_bf16.hip, a
-// translation unit of its own so the two element types compile in parallel).
+// The stream-K build (the fused kernel walking a contiguous range of
+// (tile, k stage) units per workgroup) exists for this tile only: the 8-wave
+// 256 x 256 tile has no registers to spare for the range loop.
+inline constexpr TileCfg kSkTile = {128, 128, 64, 3, 2, 2, 32};
+
+template <int KIND, bool BF = false>
+hipError_t launch_kind_sk(const Params &p, int groups, hipStream_t stream)
+{
+    constexpr TileCfg T = kSkTile;
+    return launch_one<T.bm, T.bn, T.bk, T.stages, T.wgm, T.wgn, T.mi, KIND, true, true, BF>(p, stream, groups);
+}
+
+// The bfloat16 kernels are defined in gemm_epi_bf16.hip, a translation unit
+// of its own so that the two element types compile in parallel: the fused
+// call, its stream-K build, and the GEMM stage of the unfused composition.
 hipError_t launch_fused_bf16(int kind, const Params &p, const TileCfg &t, bool vec, hipStream_t stream);
+hipError_t launch_sk_bf16(int kind, const Params &p, int groups, hipStream_t stream);
+hipError_t launch_acc_store_bf16(const Params &p, const TileCfg &t, bool vec, hipStream_t stream);
 
 }  // namespace gemm_epi

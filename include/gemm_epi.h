@@ -127,12 +127,12 @@ typedef enum {
     GEMM_EPI_ERR_HIP = 6,         /* the launch failed; see gemm_epi_last_hip_error() */
     GEMM_EPI_ERR_WORKSPACE = 7,   /* the workspace is NULL or smaller than the call needs
                                      (gemm_epi_run_unfused, gemm_epi_run_ws) */
-    GEMM_EPI_ERR_DTYPE = 8        /* unknown element type (gemm_epi_run_typed) */
+    GEMM_EPI_ERR_DTYPE = 8        /* unknown element type (the *_typed entry points) */
 } gemm_epi_status;
 
 /*
  * Element types of the 16-bit tensors (A, B, C, X, row_bias, col_bias, D,
- * Aux), for gemm_epi_run_typed: the Custom Epilogue Example's "Data Type
+ * Aux), for the *_typed entry points: the Custom Epilogue Example's "Data Type
  * Support" lists FP16 and BF16 among the input types (A, B) and the output
  * types (C, D).  Accumulation and the epilogue stay fp32; acc_out stays fp32.
  */
@@ -247,6 +247,19 @@ int gemm_epi_run_unfused(int64_t L, int64_t M, int64_t N, int64_t K, const void 
                          size_t workspace_bytes, void *stream);
 
 /*
+ * gemm_epi_run_unfused_typed -- gemm_epi_run_unfused with the element type
+ * of the 16-bit tensors as an argument, as in gemm_epi_run_typed (the
+ * workspace stays fp32).  With GEMM_EPI_F16 it is exactly
+ * gemm_epi_run_unfused; with GEMM_EPI_BF16 its outputs equal those of
+ * gemm_epi_run_typed with GEMM_EPI_BF16 bit for bit.  Status codes as
+ * gemm_epi_run_unfused, plus GEMM_EPI_ERR_DTYPE.
+ */
+int gemm_epi_run_unfused_typed(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                               const void *C, const void *X, const void *row_bias, const void *col_bias,
+                               const float *scalars, int epilogue_kind, void *D, void *Aux, void *acc_out,
+                               void *workspace, size_t workspace_bytes, int dtype, void *stream);
+
+/*
  * gemm_epi_run_ws -- gemm_epi_run_ext that may split the K range of tiles
  * across workgroups (stream-K scheduling, the Python examples article's
  * "Basic GEMM" swizzling option) when the problem has too few tiles to keep
@@ -273,6 +286,18 @@ int gemm_epi_run_unfused(int64_t L, int64_t M, int64_t N, int64_t K, const void 
 int gemm_epi_run_ws(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
                     const void *X, const void *row_bias, const void *col_bias, const float *scalars, int epilogue_kind,
                     void *D, void *Aux, void *acc_out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gemm_epi_run_ws_typed -- gemm_epi_run_ws with the element type of the
+ * 16-bit tensors as an argument, as in gemm_epi_run_typed.  The split
+ * (gemm_epi_plan_ws) and the workspace do not depend on dtype; where no
+ * split is planned the call is exactly gemm_epi_run_typed.  Status codes as
+ * gemm_epi_run_ws, plus GEMM_EPI_ERR_DTYPE.
+ */
+int gemm_epi_run_ws_typed(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                          const void *X, const void *row_bias, const void *col_bias, const float *scalars,
+                          int epilogue_kind, void *D, void *Aux, void *acc_out, void *workspace,
+                          size_t workspace_bytes, int dtype, void *stream);
 
 /* gemm_epi_plan_ext for gemm_epi_run_ws: out[0..5] as gemm_epi_plan (out[4] is
  * the number of workgroups, the split's workgroup count when it splits), and

@@ -1,6 +1,7 @@
 """bfloat16 tensors on the GPU (gemm_epi_run_typed with GEMM_EPI_BF16, reached
-through run() with torch.bfloat16 tensors), against the oracle's bfloat16
-path.
+through run() with torch.bfloat16 tensors; the unfused and stream-K
+compositions through gemm_epi_run_unfused_typed and gemm_epi_run_ws_typed),
+against the oracle's bfloat16 path.
 
 Bar: integer-valued inputs make every product and partial sum exact, so the
 only rounding is the final bfloat16 store, on both sides: every output is
@@ -49,7 +50,9 @@ def bits(t):
     return t.cpu().view(torch.int16).numpy().view(np.uint16)
 
 
-def gpu_run_bf16(p, kind, alpha, beta, s3, offset=0):
+def gpu_run_bf16(p, kind, alpha, beta, s3, offset=0, **compose):
+    """One call through run(); compose may name unfused_workspace or
+    stream_k_workspace to run that composition instead of the fused call."""
     t = to_dev_bf16(p, offset)
     L, M, K = p["A"].shape
     N = p["B"].shape[2]
@@ -57,7 +60,7 @@ def gpu_run_bf16(p, kind, alpha, beta, s3, offset=0):
     Aux = alloc_bf16(L, M, N, offset) if kind in ge.HAS_AUX else None
     acc = alloc_bf16(L, M, N, offset, torch.float32) if kind in ge.HAS_ACC else None
     ge.run(t["A"], t["B"], t["C"], t["X"], kind=kind, alpha=alpha, beta=beta, s3=s3, D=D, Aux=Aux,
-           row_bias=t.get("row_bias"), col_bias=t.get("col_bias"), acc_out=acc)
+           row_bias=t.get("row_bias"), col_bias=t.get("col_bias"), acc_out=acc, **compose)
     out = {"D": bits(D)}
     if Aux is not None:
         out["Aux"] = bits(Aux)
@@ -71,8 +74,13 @@ def ulp_bf16(x):
     return 2.0 ** (np.floor(np.log2(np.maximum(ax, 2.0 ** -126))) - 7)
 
 
-def check_bf16(p, kind, a, b, s, exact, offset=0, what=""):
-    got = gpu_run_bf16(p, kind, a, b, s, offset)
+def check_bf16(p, kind, a, b, s, exact, offset=0, what="", **compose):
+    got = gpu_run_bf16(p, kind, a, b, s, offset, **compose)
+    compare_bf16(got, p, kind, a, b, s, exact, what)
+    return got
+
+
+def compare_bf16(got, p, kind, a, b, s, exact, what):
     ref = oracle.gemm_epi(p["A"], p["B"], p["C"], p["X"], kind=kind, alpha=a, beta=b, s3=s,
                           row_bias=p.get("row_bias"), col_bias=p.get("col_bias"), want64=True, dtype="bf16")
     for name in ("D", "Aux"):
@@ -153,3 +161,73 @@ def test_x_acc_bf16_8192_sampled_and_properties():
                                  l=l, i=i, j=j, dtype="bf16")
     assert_close(oracle.bf16_decode(bits(D)[l, i, j]), ref["D64"], "x_acc_bf16_8192 D")
     assert_close(oracle.bf16_decode(bits(Y)[l, i, j]), ref["Aux64"], "x_acc_bf16_8192 Y")
+
+
+# ---- the unfused and stream-K compositions on bfloat16 tensors ----------------
+
+@pytest.mark.parametrize("kind", workloads.KINDS)
+@pytest.mark.parametrize("shape,offset", [((2, 200, 136, 264), 0),    # vector paths
+                                          ((2, 200, 136, 264), 1),    # misaligned: element-wise paths
+                                          ((3, 77, 45, 61), 0)])      # K, N not multiples of 8 (N % 4 != 0)
+def test_unfused_bf16_equals_fused_and_oracle(kind, shape, offset):
+    """gemm_epi_run_unfused_typed: the same accumulator and the same fp32
+    epilogue arithmetic as the fused kernel, so the same bits; on integer
+    inputs also the oracle's."""
+    L, M, N, K = shape
+    a, b, s = KIND_SCALARS[kind]
+    log(f"[bf16 unfused] kind={kind} shape={shape} offset={offset}")
+    p = workloads.make_problem(L, M, N, K, kind, init="small_int", seed=M + N * K, dtype="bf16")
+    ws = torch.full((L * M * N + offset,), float("nan"), dtype=torch.float32, device=DEV)[offset:]
+    unfused = check_bf16(p, kind, a, b, s, exact=True, offset=offset, what=f"bf16 unfused {kind} {shape}",
+                         unfused_workspace=ws)
+    fused = gpu_run_bf16(p, kind, a, b, s, offset)
+    for name in fused:
+        assert np.array_equal(np.asarray(fused[name]).view(np.uint8), np.asarray(unfused[name]).view(np.uint8)), \
+            f"bf16 {kind} {name}: fused != unfused"
+
+
+# few tiles and a long K, so that the planner splits K across workgroups
+BF16_SPLIT = [((1, 200, 304, 12000), workloads.KINDS),
+              ((1, 256, 256, 16384), ["AUX_SCALE", "LINCOMB_X_ACC", "RELU_SCALE_ACC", "BIAS_ROW_COL", "GELU"])]
+
+
+@pytest.mark.parametrize("shape,kind", [(sh, k) for sh, kinds in BF16_SPLIT for k in kinds])
+def test_stream_k_bf16_integer(shape, kind):
+    """gemm_epi_run_ws_typed with a split: every partial sum is exact on
+    integer inputs, so the outputs equal the oracle's (activations within one
+    bfloat16 ulp), on two calls that share the workspace, whose counters
+    must be back at zero after each."""
+    from test_stream_k_gpu import counters_are_zero, plan, workspace
+    L, M, N, K = shape
+    a, b, s = KIND_SCALARS[kind]
+    cfg = plan(shape, kind)
+    log(f"[bf16 stream-k] kind={kind} shape={shape} workgroups={cfg['workgroups']}")
+    ws = workspace(cfg)
+    p = workloads.make_problem(L, M, N, K, kind, init="small_int", seed=L + M + 3 * N + K, dtype="bf16")
+    for call in range(2):
+        got = gpu_run_bf16(p, kind, a, b, s, stream_k_workspace=ws)
+        compare_bf16(got, p, kind, a, b, s, True, f"bf16 stream-k call {call} {kind} {shape}")
+        assert counters_are_zero(ws, cfg)
+
+
+@pytest.mark.parametrize("act", workloads.ACTIVATIONS)
+def test_every_bf16_input(act):
+    """acc = t exactly for every bfloat16 t with 2^-60 <= |t| <= 120, and 0
+    (A's first column holds t, B's first row is ones, the rest zeros): the
+    activations over their whole range, including the left tails whose
+    results are bfloat16 subnormals (sigmoid and SiLU below x = -87, GELU
+    below x = -13.2)."""
+    patterns = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16)
+    v = oracle.bf16_decode(patterns)
+    keep = np.isfinite(v) & (np.abs(v) <= 120.0) & ((np.abs(v) >= 2.0 ** -60) | (v == 0))
+    t = patterns[keep]
+    M, N, K = t.size, 8, 8
+    A = np.zeros((1, M, K), np.uint16)
+    A[0, :, 0] = t
+    B = np.zeros((1, K, N), np.uint16)
+    B[0, 0, :] = 0x3F80  # 1.0
+    C = np.zeros((1, M, N), np.uint16)
+    p = {"A": A, "B": B, "C": C, "X": None, "row_bias": None, "col_bias": None}
+    s3 = 0.125 if act == "LEAKY_RELU" else 0.0
+    log(f"[bf16] sweep {act}: {M} inputs")
+    check_bf16(p, act, 1.0, 0.0, s3, exact=True, what=f"bf16 sweep {act}")

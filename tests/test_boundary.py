@@ -33,7 +33,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     names = declared_functions()
     assert set(names) == {"gemm_epi_run", "gemm_epi_run_ext", "gemm_epi_run_typed", "gemm_epi_run_ws",
-                          "gemm_epi_run_unfused",
+                          "gemm_epi_run_unfused", "gemm_epi_run_ws_typed", "gemm_epi_run_unfused_typed",
                           "gemm_epi_status_string", "gemm_epi_last_hip_error", "gemm_epi_plan", "gemm_epi_plan_ext",
                           "gemm_epi_plan_ws"}
     raw = ctypes.CDLL(binding.LIB_PATH)
@@ -137,6 +137,33 @@ def test_typed_entry_point_checks():
     assert typed("bf16", D=None) == 3
     assert typed("bf16", C=P1) == 5
     assert ge.gemm_epi_status_string(8) == "unknown element type"
+
+
+def test_typed_composition_checks():
+    """gemm_epi_run_ws_typed and gemm_epi_run_unfused_typed check the element
+    type after the operands and before anything else (no launch here)."""
+    def ws_typed(dtype, **kw):
+        a = dict(A=P16, D=P16, ws=P16, ws_bytes=1 << 30)
+        a.update(kw)
+        return ge.gemm_epi_run_ws_typed(1, 256, 256, 65536, a["A"], P16, P16, None, None, None, SC, 0, a["D"],
+                                        None, None, a["ws"], a["ws_bytes"], dtype, None)
+
+    def unfused_typed(dtype, **kw):
+        a = dict(A=P16, D=P16, ws=P16, ws_bytes=8 * 8 * 4)
+        a.update(kw)
+        return ge.gemm_epi_run_unfused_typed(1, 8, 8, 8, a["A"], P16, P16, None, None, None, SC, 0, a["D"], None,
+                                             None, a["ws"], a["ws_bytes"], dtype, None)
+    for f in (ws_typed, unfused_typed):
+        assert f(2) == 8 and f(-1) == 8                # unknown element type
+        assert f("bf16", A=None) == 2                  # the argument checks come first
+        assert f("bf16", D=None) == 3
+        assert f(7, A=P1) == 5
+    # the workspace checks follow the element type's
+    assert ws_typed("bf16", ws=None) == 7
+    assert ws_typed("bf16", ws_bytes=16) == 7
+    assert ws_typed("bf16", ws=P2) == 5
+    assert unfused_typed("bf16", ws=None) == 7
+    assert unfused_typed("bf16", ws_bytes=8 * 8 * 4 - 1) == 7
 
 
 def test_unfused_workspace_checks():
