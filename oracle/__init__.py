@@ -70,6 +70,9 @@ def lib():
     L.oracle_gemm_epi_typed.restype = ctypes.c_int
     L.oracle_gemm_epi_typed.argtypes = [i64, i64, i64, i64, u16p, u16p, u16p, u16p, u16p, u16p, f32p, ctypes.c_int,
                                         u16p, u16p, f32p, f64p, f64p, f64p, ctypes.c_int]
+    L.oracle_gemm_epi_f32e.restype = ctypes.c_int
+    L.oracle_gemm_epi_f32e.argtypes = [i64, i64, i64, i64, u16p, u16p, f32p, f32p, f32p, f32p, f32p, ctypes.c_int,
+                                       f32p, f32p, f32p, f64p, f64p, f64p, ctypes.c_int]
     L.oracle_gemm_epi_points_typed.restype = ctypes.c_int
     L.oracle_gemm_epi_points_typed.argtypes = [i64, i64, i64, i64, u16p, u16p, u16p, u16p, u16p, u16p, f32p,
                                                ctypes.c_int, i64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -206,6 +209,47 @@ def gemm_epi(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, row_bia
         out["Acc64"] = Acc64
         if Aux64 is not None:
             out["Aux64"] = Aux64
+    return out
+
+
+def gemm_epi_f32e(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, row_bias=None, col_bias=None,
+                  want64=False, ab_dtype="f16"):
+    """gemm_epi with fp32 epilogue tensors: A, B 16-bit of type ab_dtype
+    ("f16": float16 arrays or uint16 bits; "bf16": uint16 bits); C, X,
+    row_bias, col_bias float32 arrays; D and Aux returned as float32 (one
+    round-to-nearest-even from the unrounded double)."""
+    A, B = _bits(A, ab_dtype), _bits(B, ab_dtype)
+    f32 = (lambda a: None if a is None else np.ascontiguousarray(a, dtype=np.float32))
+    C, X = f32(C), f32(X)
+    L, M, N, K = _shapes(A, B, C)
+    rb = f32(np.asarray(row_bias).reshape(-1)) if row_bias is not None else None
+    cb = f32(np.asarray(col_bias).reshape(-1)) if col_bias is not None else None
+    if rb is not None and rb.size != N:
+        raise ValueError(f"row_bias must have N = {N} entries")
+    if cb is not None and cb.size != M:
+        raise ValueError(f"col_bias must have M = {M} entries")
+    sc = np.array([alpha, beta, s3], np.float32)
+    D = np.empty((L, M, N), np.float32)
+    Aux = np.empty((L, M, N), np.float32) if kind in HAS_AUX else None
+    Acc = np.empty((L, M, N), np.float32) if kind in HAS_ACC else None
+    D64 = np.empty((L, M, N), np.float64) if want64 else None
+    Aux64 = np.empty((L, M, N), np.float64) if (want64 and kind in HAS_AUX) else None
+    Acc64 = np.empty((L, M, N), np.float64) if want64 else None
+    rc = lib().oracle_gemm_epi_f32e(L, M, N, K, _ptr(A), _ptr(B), _ptr(C), _ptr(X), _ptr(rb), _ptr(cb), _ptr(sc),
+                                    KINDS[kind], _ptr(D), _ptr(Aux), _ptr(Acc), _ptr(D64), _ptr(Aux64), _ptr(Acc64),
+                                    DTYPES[ab_dtype])
+    if rc:
+        raise ValueError(f"oracle_gemm_epi_f32e rejected the call (code {rc})")
+    out = {"D": D}
+    if Aux is not None:
+        out["Aux"] = Aux
+    if Acc is not None:
+        out["Acc"] = Acc
+    if want64:
+        out["D64"] = D64
+        if Aux64 is not None:
+            out["Aux64"] = Aux64
+        out["Acc64"] = Acc64
     return out
 
 

@@ -398,6 +398,97 @@ int oracle_gemm_epi_typed(int64_t L, int64_t M, int64_t N, int64_t K, const uint
     return 0;
 }
 
+/*
+ * fp32 epilogue tensors (the Custom Epilogue Example's "Data Type Support"
+ * lists FP32 among the C and D types, with FP16 or BF16 A and B and an FP32
+ * accumulator).  A and B are 16-bit of type ab_dtype (ORACLE_DTYPE_F16 or
+ * ORACLE_DTYPE_BF16); C, X, RB, CB are IEEE binary32, widened exactly to
+ * double; D and Aux are binary32, each rounded once from the unrounded double
+ * (C's conversion from double to float rounds to nearest, ties to even, and
+ * gives +-inf past the largest finite float).  Everything else as
+ * oracle_gemm_epi_typed, whose product and epilogue this repeats.
+ */
+int oracle_gemm_epi_f32e(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
+                         const float *C, const float *X, const float *RB, const float *CB, const float *scalars,
+                         int kind, float *D, float *Aux, float *Acc, double *D64, double *Aux64, double *Acc64,
+                         int ab_dtype)
+{
+    if (L < 1 || M < 1 || N < 1 || K < 1)
+        return 1;
+    if (!A || !B || !scalars)
+        return 2;
+    if (!oracle_kind_valid(kind))
+        return 4;
+    if ((oracle_kind_reads_c(kind) && !C) || (oracle_kind_reads_x(kind) && !X) ||
+        (oracle_kind_reads_bias(kind) && (!RB || !CB)))
+        return 2;
+    if (!D || (oracle_kind_has_aux(kind) && !Aux) || (oracle_kind_has_acc_out(kind) && !Acc))
+        return 3;
+    if (ab_dtype != ORACLE_DTYPE_F16 && ab_dtype != ORACLE_DTYPE_BF16)
+        return 8;
+    const decode_fn dec = ab_dtype == ORACLE_DTYPE_BF16 ? oracle_bf16_decode : oracle_f16_decode;
+    const double alpha = scalars[0], beta = scalars[1], s = scalars[2];
+    double *Bd = (double *)malloc(sizeof(double) * (size_t)K * (size_t)N);
+    if (!Bd)
+        return 7;
+    for (int64_t l = 0; l < L; l++) {
+        const uint16_t *Al = A + l * M * K;
+        const uint16_t *Bl = B + l * K * N;
+        for (int64_t q = 0; q < K * N; q++)
+            Bd[q] = dec(Bl[q]);
+        int fail = 0;
+#pragma omp parallel
+        {
+            double *acc = (double *)malloc(sizeof(double) * (size_t)N);
+            if (!acc) {
+#pragma omp atomic write
+                fail = 1;
+            }
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t i = 0; i < M; i++) {
+                if (!acc)
+                    continue;
+                for (int64_t j = 0; j < N; j++)
+                    acc[j] = 0.0;
+                for (int64_t k = 0; k < K; k++) {
+                    const double a = dec(Al[i * K + k]);
+                    const double *brow = Bd + k * N;
+                    for (int64_t j = 0; j < N; j++)
+                        acc[j] = acc[j] + a * brow[j];
+                }
+                const int64_t row = (l * M + i) * N;
+                const double cb = oracle_kind_reads_bias(kind) ? (double)CB[i] : 0.0;
+                for (int64_t j = 0; j < N; j++) {
+                    double c = oracle_kind_reads_c(kind) ? (double)C[row + j] : 0.0;
+                    double x = oracle_kind_reads_x(kind) ? (double)X[row + j] : 0.0;
+                    double rb = oracle_kind_reads_bias(kind) ? (double)RB[j] : 0.0;
+                    double d = 0.0, aux = 0.0;
+                    epilogue(kind, acc[j], c, x, rb, cb, alpha, beta, s, &d, &aux);
+                    D[row + j] = (float)d;
+                    if (D64)
+                        D64[row + j] = d;
+                    if (oracle_kind_has_aux(kind)) {
+                        Aux[row + j] = (float)aux;
+                        if (Aux64)
+                            Aux64[row + j] = aux;
+                    }
+                    if (oracle_kind_has_acc_out(kind))
+                        Acc[row + j] = (float)acc[j];
+                    if (Acc64)
+                        Acc64[row + j] = acc[j];
+                }
+            }
+            free(acc);
+        }
+        if (fail) {
+            free(Bd);
+            return 7;
+        }
+    }
+    free(Bd);
+    return 0;
+}
+
 /* fp16 tensors (the boundary's default element type). */
 int oracle_gemm_epi_ext(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
                         const uint16_t *C, const uint16_t *X, const uint16_t *RB, const uint16_t *CB,
