@@ -49,12 +49,12 @@ STATUS = {
     8: "GEMM_EPI_ERR_DTYPE",
 }
 # element types of the 16-bit tensors (gemm_epi_run_typed)
-DTYPES = {"f16": 0, "bf16": 1}
+DTYPES = {"f16": 0, "bf16": 1, "f32": 2}
 
 # every function include/gemm_epi.h declares
-EXPORTS = ("gemm_epi_run", "gemm_epi_run_ext", "gemm_epi_run_typed", "gemm_epi_run_ws", "gemm_epi_run_unfused",
-           "gemm_epi_run_ws_typed", "gemm_epi_run_unfused_typed", "gemm_epi_status_string", "gemm_epi_last_hip_error", "gemm_epi_plan", "gemm_epi_plan_ext",
-           "gemm_epi_plan_ws")
+EXPORTS = ("gemm_epi_run", "gemm_epi_run_ext", "gemm_epi_run_typed", "gemm_epi_run_mixed", "gemm_epi_run_ws",
+           "gemm_epi_run_unfused", "gemm_epi_run_ws_typed", "gemm_epi_run_unfused_typed", "gemm_epi_status_string",
+           "gemm_epi_last_hip_error", "gemm_epi_plan", "gemm_epi_plan_ext", "gemm_epi_plan_ws")
 
 
 class GemmEpiError(RuntimeError):
@@ -85,6 +85,9 @@ def lib():
     L.gemm_epi_run_typed.restype = ctypes.c_int
     L.gemm_epi_run_typed.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_float),
                                      ctypes.c_int, vp, vp, vp, ctypes.c_int, vp]
+    L.gemm_epi_run_mixed.restype = ctypes.c_int
+    L.gemm_epi_run_mixed.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_float),
+                                     ctypes.c_int, vp, vp, vp, ctypes.c_int, ctypes.c_int, vp]
     L.gemm_epi_run_unfused.restype = ctypes.c_int
     L.gemm_epi_run_unfused.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_float),
                                        ctypes.c_int, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -112,6 +115,10 @@ def lib():
                                     ctypes.POINTER(i64)]
     _lib = L
     return L
+
+
+def _dtype_id(dtype):
+    return DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
 
 
 def _kind_id(kind):
@@ -155,6 +162,17 @@ def gemm_epi_run_typed(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epil
                                     _kind_id(epilogue_kind), D, Aux, acc_out, _dtype_id(dtype), stream)
 
 
+def gemm_epi_run_mixed(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilogue_kind, D, Aux, acc_out,
+                       ab_dtype, epi_dtype, stream) -> int:
+    """Pointer-level call of gemm_epi_run_mixed: the element type of A and B
+    ("f16" / "bf16") and that of the epilogue tensors ("f32", or the same as
+    A and B) given separately."""
+    sc = (ctypes.c_float * 3)(*[float(v) for v in scalars]) if scalars is not None else None
+    return lib().gemm_epi_run_mixed(int(L), int(M), int(N), int(K), A, B, C, X, row_bias, col_bias, sc,
+                                    _kind_id(epilogue_kind), D, Aux, acc_out, _dtype_id(ab_dtype),
+                                    _dtype_id(epi_dtype), stream)
+
+
 def gemm_epi_run_unfused(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilogue_kind, D, Aux, acc_out,
                          workspace, workspace_bytes, stream) -> int:
     """Pointer-level call of gemm_epi_run_unfused: the same operation in two
@@ -173,10 +191,6 @@ def gemm_epi_run_ws(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilogu
     sc = (ctypes.c_float * 3)(*[float(v) for v in scalars]) if scalars is not None else None
     return lib().gemm_epi_run_ws(int(L), int(M), int(N), int(K), A, B, C, X, row_bias, col_bias, sc,
                                  _kind_id(epilogue_kind), D, Aux, acc_out, workspace, int(workspace_bytes), stream)
-
-
-def _dtype_id(dtype):
-    return DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
 
 
 def gemm_epi_run_unfused_typed(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilogue_kind, D, Aux,
@@ -252,7 +266,9 @@ def run(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, D, Aux=None,
 
     A (L,M,K), B (L,K,N), C, X, D, Aux (L,M,N): contiguous float16 CUDA
     tensors, or all bfloat16 (then the bfloat16 kernels run; every
-    composition below takes either type); row_bias (N,) and col_bias (M,) or (M, 1) of the
+    composition below takes either type); or A, B float16 / bfloat16 with
+    C, X, D, Aux and the biases float32 (gemm_epi_run_mixed, fused call
+    only); row_bias (N,) and col_bias (M,) or (M, 1) of the
     same type for BIAS_ROW_COL; acc_out (L,M,N) float32 for RELU_SCALE_ACC.  s3 is
     extra_scalar (AUX_SCALE), x_factor (LINCOMB_X_ACC) or scale
     (RELU_SCALE_ACC).  The kernel is queued on `stream` (a torch.cuda.Stream;
@@ -269,9 +285,11 @@ def run(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, D, Aux=None,
         raise ValueError("A and B must be 3-D: (L,M,K) and (L,K,N)")
     L, M, K = A.shape
     N = B.shape[2]
-    et = torch.bfloat16 if isinstance(A, torch.Tensor) and A.dtype == torch.bfloat16 else torch.float16
-    _check_tensor("A", A, (L, M, K), et)
-    _check_tensor("B", B, (L, K, N), et)
+    at = torch.bfloat16 if isinstance(A, torch.Tensor) and A.dtype == torch.bfloat16 else torch.float16
+    # the epilogue tensors are of A's type, or all float32
+    et = torch.float32 if isinstance(D, torch.Tensor) and D.dtype == torch.float32 else at
+    _check_tensor("A", A, (L, M, K), at)
+    _check_tensor("B", B, (L, K, N), at)
     _check_tensor("D", D, (L, M, N), et)
     kname = kind if isinstance(kind, str) else {v: k for k, v in KINDS.items()}[int(kind)]
     if kname in READS_C:
@@ -307,7 +325,9 @@ def run(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, D, Aux=None,
     skw = stream_k_workspace
     if skw is not None and (skw.device != dev or not skw.is_contiguous()):
         raise ValueError("stream_k_workspace must be a contiguous tensor on the operands' device")
-    dt = DTYPES["bf16"] if et == torch.bfloat16 else DTYPES["f16"]
+    dt = DTYPES["bf16"] if at == torch.bfloat16 else DTYPES["f16"]
+    if et == torch.float32 and (ws is not None or skw is not None):
+        raise ValueError("the unfused and stream-K compositions take 16-bit epilogue tensors only")
     ops = (L, M, N, K, A.data_ptr(), B.data_ptr(), _ptr(C), _ptr(X), _ptr(row_bias), _ptr(col_bias),
            (alpha, beta, s3), KINDS[kname], D.data_ptr(), _ptr(Aux), _ptr(acc_out))
     with torch.cuda.device(dev):
@@ -315,6 +335,8 @@ def run(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, D, Aux=None,
             rc = gemm_epi_run_ws_typed(*ops, skw.data_ptr(), skw.numel() * skw.element_size(), dt, s.cuda_stream)
         elif ws is not None:
             rc = gemm_epi_run_unfused_typed(*ops, ws.data_ptr(), ws.numel() * 4, dt, s.cuda_stream)
+        elif et == torch.float32:
+            rc = gemm_epi_run_mixed(*ops, dt, DTYPES["f32"], s.cuda_stream)
         else:
             rc = gemm_epi_run_typed(*ops, dt, s.cuda_stream)
     if rc != 0:

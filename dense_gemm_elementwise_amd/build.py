@@ -1,8 +1,10 @@
 """Builds libgemm_epi.so (the HIP kernels and the C ABI) for gfx950, in-tree.
 
 hipcc compiles the translation units csrc/gemm_epi.hip (the C ABI and the
-fp16 kernels) and csrc/gemm_epi_bf16.hip (the bfloat16 kernels) in parallel
-for --offload-arch=gfx950 only, then links them into one shared library.
+fp16 kernels), csrc/gemm_epi_bf16.hip (the bfloat16 kernels) and
+csrc/gemm_epi_f32e.hip, csrc/gemm_epi_bf16_f32e.hip (fp16 / bfloat16 A and B
+with fp32 epilogue tensors) in parallel for --offload-arch=gfx950 only, then
+links them into one shared library.
 Packed-fp32 VALU instructions are switched off (-packed-fp32-ops): the
 epilogue is plain scalar fp32 arithmetic.
 """
@@ -12,7 +14,8 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", "gemm_epi.hip"), os.path.join(PKG, "csrc", "gemm_epi_bf16.hip")]
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("gemm_epi.hip", "gemm_epi_bf16.hip", "gemm_epi_f32e.hip",
+                                               "gemm_epi_bf16_f32e.hip")]
 LIB = os.path.join(PKG, "libgemm_epi.so")
 ARCH = "gfx950"
 

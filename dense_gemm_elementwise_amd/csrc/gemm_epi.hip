@@ -267,11 +267,27 @@ int gemm_epi_run_typed(int64_t L, int64_t M, int64_t N, int64_t K, const void *A
                        const void *X, const void *row_bias, const void *col_bias, const float *scalars,
                        int epilogue_kind, void *D, void *Aux, void *acc_out, int dtype, void *stream)
 {
+    return gemm_epi_run_mixed(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilogue_kind, D, Aux, acc_out,
+                              dtype, dtype, stream);
+}
+
+int gemm_epi_run_mixed(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                       const void *X, const void *row_bias, const void *col_bias, const float *scalars,
+                       int epilogue_kind, void *D, void *Aux, void *acc_out, int ab_dtype, int epi_dtype,
+                       void *stream)
+{
     const Operands o = {A, B, C, X, row_bias, col_bias, D, Aux, acc_out};
     int rc = check_args(L, M, N, K, o, epilogue_kind);
     if (rc != GEMM_EPI_OK) return rc;
-    if (dtype != GEMM_EPI_F16 && dtype != GEMM_EPI_BF16) return GEMM_EPI_ERR_DTYPE;
+    if (ab_dtype != GEMM_EPI_F16 && ab_dtype != GEMM_EPI_BF16) return GEMM_EPI_ERR_DTYPE;
+    const bool f32e = epi_dtype == GEMM_EPI_F32;
+    if (epi_dtype != ab_dtype && !f32e) return GEMM_EPI_ERR_DTYPE;
     if (!scalars) return GEMM_EPI_ERR_NULL_INPUT;
+    if (f32e) {
+        const void *words[] = {C, X, row_bias, col_bias, D, Aux};
+        for (const void *w : words)
+            if (w && !aligned(w, 4)) return GEMM_EPI_ERR_ALIGN;
+    }
     const bool vec = use_fast_path(M, N, K, o, epilogue_kind);
     const TileCfg t = choose_tile(L, M, N, vec);
     const int64_t tm = (M + t.bm - 1) / t.bm, tn = (N + t.bn - 1) / t.bn;
@@ -281,7 +297,7 @@ int gemm_epi_run_typed(int64_t L, int64_t M, int64_t N, int64_t K, const void *A
     Params p;
     p.A = (const _Float16 *)A;
     p.B = (const _Float16 *)B;
-    p.C = (const _Float16 *)C;
+    p.C = (const _Float16 *)C;  // the kernels read the epilogue tensors as their element type
     p.X = (const _Float16 *)X;
     p.D = (_Float16 *)D;
     p.Aux = (_Float16 *)Aux;
@@ -303,7 +319,10 @@ int gemm_epi_run_typed(int64_t L, int64_t M, int64_t N, int64_t K, const void *A
 
     hipStream_t s = (hipStream_t)stream;
     hipError_t err;
-    if (dtype == GEMM_EPI_BF16)
+    const bool bf = ab_dtype == GEMM_EPI_BF16;
+    if (f32e)
+        err = bf ? launch_fused_bf16_f32e(epilogue_kind, p, t, vec, s) : launch_fused_f16_f32e(epilogue_kind, p, t, vec, s);
+    else if (bf)
         err = launch_fused_bf16(epilogue_kind, p, t, vec, s);
     else
         err = dispatch_kind(epilogue_kind, [&](auto k) { return launch_kind<decltype(k)::value>(p, t, vec, s); });

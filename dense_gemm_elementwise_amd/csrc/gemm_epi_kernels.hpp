@@ -69,6 +69,22 @@ __device__ __forceinline__ _Float16 st16(float f)
     else
         return (_Float16)f;
 }
+
+// Element type of the epilogue tensors (C, X, the biases, D, Aux): the
+// 16-bit type of A and B, or fp32 when F32E (widening is then the identity
+// and narrowing does not round).
+template <bool BF, bool F32E>
+struct EpiElem {
+    using T = _Float16;
+    static __device__ __forceinline__ float ld(T v) { return ld16<BF>(v); }
+    static __device__ __forceinline__ T st(float f) { return st16<BF>(f); }
+};
+template <bool BF>
+struct EpiElem<BF, true> {
+    using T = float;
+    static __device__ __forceinline__ float ld(T v) { return v; }
+    static __device__ __forceinline__ T st(float f) { return f; }
+};
 typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -444,7 +460,7 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void *p)
 // LDS is filled through registers.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int BK, int NSTAGES, int WGM, int WGN, int MI, int KIND, bool VEC, bool SK = false,
-          bool BF = false>
+          bool BF = false, bool F32E = false>
 __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
 {
     constexpr int NW = WGM * WGN;                // waves per workgroup
@@ -850,8 +866,15 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     // into registers one slab ahead, so the loads' latency hides behind the
     // previous slab's work; a lane's columns are the same in every slab, so its
     // row-bias values are loaded once.
-    constexpr int CPL = WN % 128 == 0 && !kind_has_acc_out(KIND) ? 8 : 4;
-    using hvec = typename std::conditional<CPL == 8, half8, half4>::type;
+    // With fp32 epilogue tensors a lane keeps 4 columns: 16-byte vectors again.
+    constexpr int CPL = WN % 128 == 0 && !kind_has_acc_out(KIND) && !F32E ? 8 : 4;
+    using E = EpiElem<BF, F32E>;
+    using et = typename E::T;
+    using hvec = typename std::conditional<F32E, f32x4,
+                                           typename std::conditional<CPL == 8, half8, half4>::type>::type;
+    const et *const pC = (const et *)p.C, *const pX = (const et *)p.X;
+    const et *const prb = (const et *)p.row_bias, *const pcb = (const et *)p.col_bias;
+    et *const pD = (et *)p.D, *const pAux = (et *)p.Aux;
     constexpr int EPI_PASSES = SLAB / 4;
     constexpr int EPI_GROUPS = CPL == 4 && WN >= 128 ? 2 : 1;
     constexpr int EPI_HALF = WN / 2;
@@ -867,31 +890,32 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     // panels (16-batch RELU_SQUARE 215 -> 183 us, 8192^3 LINCOMB_X_ACC -1%).
     // With two elementwise inputs (C and X) the loads are non-temporal too
     // (another -1%); with C alone that measured 5% slower than plain loads.
-    auto ld_epi = [](const _Float16 *q) {
+    auto ld_epi = [](const et *q) {
         if constexpr (HAS_X)
             return __builtin_nontemporal_load((const hvec *)q);
         else
             return *(const hvec *)q;
     };
-    auto st_epi = [](_Float16 *q, hvec v) { __builtin_nontemporal_store(v, (hvec *)q); };
+    auto st_epi = [](et *q, hvec v) { __builtin_nontemporal_store(v, (hvec *)q); };
     // C of every slab is loaded at once when the epilogue starts (the operand
     // fragment registers are free by then): more loads in flight.  X and the
-    // column bias go one slab ahead.
-    constexpr bool PRE_C = VEC && HAS_C;
+    // column bias go one slab ahead, and so does C when it is fp32 (all of it
+    // would take 128 registers).
+    constexpr bool PRE_C = VEC && HAS_C && !F32E;
     constexpr int NBC = PRE_C ? TM : 2;
     hvec cbuf[NBC][CP][EPI_GROUPS];
     hvec xbuf[2][XP][EPI_GROUPS];
-    _Float16 cbias[2][BP];
+    et cbias[2][BP];
     auto cslot = [](int i) { return PRE_C ? i : (i & 1); };
     hvec rbias[EPI_GROUPS];
     // loads slab i's C (with_c) and its X and column bias (with_x)
-    auto epi_prefetch = [&](int i, hvec (&cb)[CP][EPI_GROUPS], hvec (&xb)[XP][EPI_GROUPS], _Float16 (&colb)[BP],
+    auto epi_prefetch = [&](int i, hvec (&cb)[CP][EPI_GROUPS], hvec (&xb)[XP][EPI_GROUPS], et (&colb)[BP],
                             bool with_c, bool with_x) {
 #pragma unroll
         for (int pass = 0; pass < EPI_PASSES; pass++) {
             const int gm = m0 + wm * WM + i * SLAB + pass * 4 + (lane >> 4);
             if constexpr (HAS_BIAS)
-                if (with_x) colb[pass] = gm < M ? p.col_bias[gm] : (_Float16)0.0f;
+                if (with_x) colb[pass] = gm < M ? pcb[gm] : (et)0.0f;
 #pragma unroll
             for (int h = 0; h < EPI_GROUPS; h++) {
                 const int scol = lane_col(h);
@@ -899,9 +923,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
                 if (scol < WN && gm < M && gn < N) {
                     const int64_t o = mn_base + (int64_t)gm * N + gn;
                     if constexpr (HAS_C)
-                        if (with_c) cb[pass][h] = ld_epi(p.C + o);
+                        if (with_c) cb[pass][h] = ld_epi(pC + o);
                     if constexpr (HAS_X)
-                        if (with_x) xb[pass][h] = ld_epi(p.X + o);
+                        if (with_x) xb[pass][h] = ld_epi(pX + o);
                 }
             }
         }
@@ -914,7 +938,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
             for (int h = 0; h < EPI_GROUPS; h++) {
                 const int scol = lane_col(h);
                 const int gn = n0 + wn * WN + scol;
-                rbias[h] = (scol < WN && gn < N) ? *(const hvec *)(p.row_bias + gn) : hvec{};
+                rbias[h] = (scol < WN && gn < N) ? *(const hvec *)(prb + gn) : hvec{};
             }
         }
         epi_prefetch(0, cbuf[0], xbuf[0], cbias[0], true, true);
@@ -970,19 +994,18 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
                     if constexpr (HAS_X) x4 = xbuf[i & 1][pass][h];
                     if constexpr (HAS_BIAS) {
                         rb4 = rbias[h];
-                        cbv = ld16<BF>(cbias[i & 1][pass]);
+                        cbv = E::ld(cbias[i & 1][pass]);
                     }
                     hvec d4, e4;
 #pragma unroll
                     for (int e = 0; e < CPL; e++) {
                         float d, a = 0.0f;
-                        epi_elem<KIND>(av[e], ld16<BF>(c4[e]), ld16<BF>(x4[e]), ld16<BF>(rb4[e]), cbv, alpha, beta, s,
-                                       d, a);
-                        d4[e] = st16<BF>(d);
-                        e4[e] = st16<BF>(a);
+                        epi_elem<KIND>(av[e], E::ld(c4[e]), E::ld(x4[e]), E::ld(rb4[e]), cbv, alpha, beta, s, d, a);
+                        d4[e] = E::st(d);
+                        e4[e] = E::st(a);
                     }
-                    if constexpr (kind_writes_d(KIND)) st_epi(p.D + o, d4);
-                    if constexpr (kind_has_aux(KIND)) st_epi(p.Aux + o, e4);
+                    if constexpr (kind_writes_d(KIND)) st_epi(pD + o, d4);
+                    if constexpr (kind_has_aux(KIND)) st_epi(pAux + o, e4);
                     if constexpr (kind_has_acc_out(KIND)) {
 #pragma unroll
                         for (int q = 0; q < CPL / 4; q++)
@@ -990,17 +1013,17 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
                                                         (f32x4 *)(p.acc_out + o + 4 * q));
                     }
                 } else {
-                    const float cbv = HAS_BIAS ? ld16<BF>(p.col_bias[gm]) : 0.0f;
+                    const float cbv = HAS_BIAS ? E::ld(pcb[gm]) : 0.0f;
 #pragma unroll
                     for (int e = 0; e < CPL; e++) {
                         if (gn + e >= N) break;
-                        const float c = HAS_C ? ld16<BF>(p.C[o + e]) : 0.0f;
-                        const float x = HAS_X ? ld16<BF>(p.X[o + e]) : 0.0f;
-                        const float rb = HAS_BIAS ? ld16<BF>(p.row_bias[gn + e]) : 0.0f;
+                        const float c = HAS_C ? E::ld(pC[o + e]) : 0.0f;
+                        const float x = HAS_X ? E::ld(pX[o + e]) : 0.0f;
+                        const float rb = HAS_BIAS ? E::ld(prb[gn + e]) : 0.0f;
                         float d, a = 0.0f;
                         epi_elem<KIND>(av[e], c, x, rb, cbv, alpha, beta, s, d, a);
-                        if constexpr (kind_writes_d(KIND)) p.D[o + e] = st16<BF>(d);
-                        if constexpr (kind_has_aux(KIND)) p.Aux[o + e] = st16<BF>(a);
+                        if constexpr (kind_writes_d(KIND)) pD[o + e] = E::st(d);
+                        if constexpr (kind_has_aux(KIND)) pAux[o + e] = E::st(a);
                         if constexpr (kind_has_acc_out(KIND)) p.acc_out[o + e] = av[e];
                     }
                 }

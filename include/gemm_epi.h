@@ -122,23 +122,27 @@ typedef enum {
     GEMM_EPI_ERR_NULL_OUTPUT = 3, /* D NULL; Aux NULL for a kind with a second output; acc_out NULL
                                      for RELU_SCALE_ACC */
     GEMM_EPI_ERR_KIND = 4,        /* unknown epilogue kind */
-    GEMM_EPI_ERR_ALIGN = 5,       /* an fp16 pointer is not 2-byte aligned, or acc_out is not 4-byte
-                                     aligned */
+    GEMM_EPI_ERR_ALIGN = 5,       /* a 16-bit tensor is not 2-byte aligned, or acc_out (or an fp32
+                                     epilogue tensor) is not 4-byte aligned */
     GEMM_EPI_ERR_HIP = 6,         /* the launch failed; see gemm_epi_last_hip_error() */
     GEMM_EPI_ERR_WORKSPACE = 7,   /* the workspace is NULL or smaller than the call needs
                                      (gemm_epi_run_unfused, gemm_epi_run_ws) */
-    GEMM_EPI_ERR_DTYPE = 8        /* unknown element type (the *_typed entry points) */
+    GEMM_EPI_ERR_DTYPE = 8        /* unknown element type or combination (the *_typed entry points,
+                                     gemm_epi_run_mixed) */
 } gemm_epi_status;
 
 /*
- * Element types of the 16-bit tensors (A, B, C, X, row_bias, col_bias, D,
- * Aux), for the *_typed entry points: the Custom Epilogue Example's "Data Type
- * Support" lists FP16 and BF16 among the input types (A, B) and the output
- * types (C, D).  Accumulation and the epilogue stay fp32; acc_out stays fp32.
+ * Element types of the tensors (A, B, C, X, row_bias, col_bias, D, Aux), for
+ * the *_typed entry points (one 16-bit type for all of them) and
+ * gemm_epi_run_mixed (fp32 epilogue tensors): the Custom Epilogue Example's
+ * "Data Type Support" lists FP16 and BF16 among the input types (A, B) and
+ * FP32, FP16 and BF16 among the output types (C, D).  Accumulation and the
+ * epilogue stay fp32; acc_out stays fp32.
  */
 typedef enum {
     GEMM_EPI_F16 = 0,  /* IEEE 754 binary16 */
-    GEMM_EPI_BF16 = 1  /* bfloat16: 1 sign, 8 exponent and 7 fraction bits (the upper half of a binary32) */
+    GEMM_EPI_BF16 = 1, /* bfloat16: 1 sign, 8 exponent and 7 fraction bits (the upper half of a binary32) */
+    GEMM_EPI_F32 = 2   /* IEEE 754 binary32 (epilogue tensors only) */
 } gemm_epi_dtype;
 
 /*
@@ -218,6 +222,23 @@ int gemm_epi_run_ext(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, 
 int gemm_epi_run_typed(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
                        const void *X, const void *row_bias, const void *col_bias, const float *scalars,
                        int epilogue_kind, void *D, void *Aux, void *acc_out, int dtype, void *stream);
+
+/*
+ * gemm_epi_run_mixed -- the fused call with separate element types for A, B
+ * (ab_dtype: GEMM_EPI_F16 or GEMM_EPI_BF16) and for the epilogue tensors C, X,
+ * row_bias, col_bias, D and Aux (epi_dtype: GEMM_EPI_F32, or the same type as
+ * ab_dtype, in which case the call is exactly gemm_epi_run_typed).  With fp32
+ * epilogue tensors (the example's FP32 C and D) the same fp32 epilogue runs;
+ * C, X and the biases are read as they are and D, Aux are stored without a
+ * further rounding.  Those tensors must then be 4-byte aligned (16-byte aligned,
+ * with K % 8 == N % 8 == 0 and 16-byte aligned A, B, for the vector kernels);
+ * shapes and layouts are unchanged.  Status codes as gemm_epi_run_ext, plus
+ * GEMM_EPI_ERR_DTYPE for any other combination.
+ */
+int gemm_epi_run_mixed(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                       const void *X, const void *row_bias, const void *col_bias, const float *scalars,
+                       int epilogue_kind, void *D, void *Aux, void *acc_out, int ab_dtype, int epi_dtype,
+                       void *stream);
 
 /*
  * gemm_epi_run_unfused -- the same operation as gemm_epi_run_ext, NOT fused:
