@@ -106,21 +106,32 @@ def _plan(args, ge):
 
 
 def _timed_launches(launch, steps, stream):
-    """Times `steps` launches between two synchronisations.  One HIP event
-    before every launch and one after the last give each launch's duration
-    on the launch stream; the wall clock covers the whole timed region."""
+    """Times `steps` launches between two synchronisations: one HIP event on
+    the launch stream before the first launch and one after the last give
+    the average launch duration (what the roofline uses), and the wall clock
+    covers the whole timed region.  The median and minimum of single
+    launches come from a second pass of `steps` launches with an event
+    before each, after the timed region, so that those events (a few us per
+    launch on short kernels) stay out of it.  launch(i) is called with
+    i = 0 .. 2*steps - 1 across the two passes."""
     import torch
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(steps):
-        ev[i].record(stream)
         launch(i)
-    ev[steps].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    total = e0.elapsed_time(e1)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    for i in range(steps):
+        ev[i].record(stream)
+        launch(steps + i)
+    ev[steps].record(stream)
+    torch.cuda.synchronize()
     per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
-    total = ev[0].elapsed_time(ev[steps])
     return wall * 1e3 / steps, total / steps, {"median": per[steps // 2], "min": per[0], "mean": total / steps}
 
 
@@ -403,7 +414,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # about 50 launches pass before the clock and the caches settle on a fresh process
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=6144)
