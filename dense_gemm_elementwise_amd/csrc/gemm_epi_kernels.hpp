@@ -124,6 +124,9 @@ __host__ __device__ constexpr bool kind_reads_bias(int k) { return k == BIAS_ROW
 __host__ __device__ constexpr bool kind_has_acc_out(int k) { return k == RELU_SCALE_ACC || k == ACC_STORE; }
 __host__ __device__ constexpr bool kind_writes_d(int k) { return k != ACC_STORE; }
 
+// The 16-bit tensors travel as raw bits; C, X, D, Aux and the biases hold
+// fp32 values instead when the kernel is built with F32E (the kernel reads
+// them through its epilogue element type).
 struct Params {
     const _Float16 *A;
     const _Float16 *B;
