@@ -174,3 +174,13 @@ def test_same_accumulator_as_the_16_bit_call():
     ge.run(t["A"], t["B"], t["C"].float(), t["X"].float(), kind="LINCOMB_X_ACC", alpha=2.0, beta=1.0, s3=3.0,
            D=D32, Aux=Y32)
     assert torch.equal(D32.half(), D16) and torch.equal(Y32.half(), Y16)
+
+
+def test_x_acc_8192_every_element():
+    """The Alpha-Beta example's size with fp32 epilogue tensors: Gaussian fp16
+    A, B and fp32 C, X; every D and Y element against the full oracle (fp64,
+    about 14 s on 16 cores) within the Gaussian tolerance, none non-finite."""
+    L, M, N, K = 1, 8192, 8192, 8192
+    log("[f32e] x_acc 8192^3, every element")
+    p = problem(L, M, N, K, "LINCOMB_X_ACC", "f16", seed=2025, init="normal")
+    check(p, "LINCOMB_X_ACC", "f16", 2.0, 1.0, 3.0, exact=False, what="f32e x_acc 8192")
