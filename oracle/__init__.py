@@ -70,6 +70,9 @@ def lib():
     L.oracle_gemm_epi_typed.restype = ctypes.c_int
     L.oracle_gemm_epi_typed.argtypes = [i64, i64, i64, i64, u16p, u16p, u16p, u16p, u16p, u16p, f32p, ctypes.c_int,
                                         u16p, u16p, f32p, f64p, f64p, f64p, ctypes.c_int]
+    L.oracle_gemm_epi_typed2.restype = ctypes.c_int
+    L.oracle_gemm_epi_typed2.argtypes = [i64, i64, i64, i64, u16p, u16p, u16p, u16p, u16p, u16p, f32p, ctypes.c_int,
+                                         u16p, u16p, f32p, f64p, f64p, f64p, ctypes.c_int, ctypes.c_int]
     L.oracle_gemm_epi_f32e.restype = ctypes.c_int
     L.oracle_gemm_epi_f32e.argtypes = [i64, i64, i64, i64, u16p, u16p, f32p, f32p, f32p, f32p, f32p, ctypes.c_int,
                                        f32p, f32p, f32p, f64p, f64p, f64p, ctypes.c_int]
@@ -171,7 +174,7 @@ def _biases(row_bias, col_bias, M, N, dtype="f16"):
 
 
 def gemm_epi(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, row_bias=None, col_bias=None,
-             want64=False, dtype="f16"):
+             want64=False, dtype="f16", epi_dtype=None):
     """Full fused GEMM + epilogue on host arrays.
 
     A (L,M,K), B (L,K,N), C and X (L,M,N): float16 arrays (or uint16 bits);
@@ -179,13 +182,16 @@ def gemm_epi(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, row_bia
     with D (and Aux for kinds with a second output) as float16 arrays, Acc
     (float32) for kinds that return the accumulator, plus D64 / Aux64 / Acc64
     (unrounded float64) when want64 is set.  dtype "bf16": the 16-bit tensors
-    are bfloat16, passed and returned as uint16 bit patterns.
+    are bfloat16, passed and returned as uint16 bit patterns.  epi_dtype
+    (default: dtype) gives C, X, the biases, D and Aux a 16-bit type of their
+    own.
     """
+    epi_dtype = epi_dtype or dtype
     A, B = _bits(A, dtype), _bits(B, dtype)
-    C = _bits(C, dtype) if C is not None else None
-    X = _bits(X, dtype) if X is not None else None
+    C = _bits(C, epi_dtype) if C is not None else None
+    X = _bits(X, epi_dtype) if X is not None else None
     L, M, N, K = _shapes(A, B, C)
-    rb, cb = _biases(row_bias, col_bias, M, N, dtype)
+    rb, cb = _biases(row_bias, col_bias, M, N, epi_dtype)
     sc = np.array([alpha, beta, s3], np.float32)
     D = np.empty((L, M, N), np.uint16)
     Aux = np.empty((L, M, N), np.uint16) if kind in HAS_AUX else None
@@ -193,12 +199,12 @@ def gemm_epi(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, row_bia
     D64 = np.empty((L, M, N), np.float64) if want64 else None
     Aux64 = np.empty((L, M, N), np.float64) if (want64 and kind in HAS_AUX) else None
     Acc64 = np.empty((L, M, N), np.float64) if want64 else None
-    rc = lib().oracle_gemm_epi_typed(L, M, N, K, _ptr(A), _ptr(B), _ptr(C), _ptr(X), _ptr(rb), _ptr(cb), _ptr(sc),
-                                     KINDS[kind], _ptr(D), _ptr(Aux), _ptr(Acc), _ptr(D64), _ptr(Aux64), _ptr(Acc64),
-                                     DTYPES[dtype])
+    rc = lib().oracle_gemm_epi_typed2(L, M, N, K, _ptr(A), _ptr(B), _ptr(C), _ptr(X), _ptr(rb), _ptr(cb), _ptr(sc),
+                                      KINDS[kind], _ptr(D), _ptr(Aux), _ptr(Acc), _ptr(D64), _ptr(Aux64),
+                                      _ptr(Acc64), DTYPES[dtype], DTYPES[epi_dtype])
     if rc:
-        raise ValueError(f"oracle_gemm_epi_typed rejected the call (code {rc})")
-    view = (lambda a: a.view(np.float16)) if dtype == "f16" else (lambda a: a)
+        raise ValueError(f"oracle_gemm_epi_typed2 rejected the call (code {rc})")
+    view = (lambda a: a.view(np.float16)) if epi_dtype == "f16" else (lambda a: a)
     out = {"D": view(D)}
     if Aux is not None:
         out["Aux"] = view(Aux)

@@ -324,18 +324,41 @@ static int check_args(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t
  * invalid arguments.  OpenMP splits the rows; each element's sum is the same
  * whatever the thread count.
  */
+int oracle_gemm_epi_typed2(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
+                           const uint16_t *C, const uint16_t *X, const uint16_t *RB, const uint16_t *CB,
+                           const float *scalars, int kind, uint16_t *D, uint16_t *Aux, float *Acc, double *D64,
+                           double *Aux64, double *Acc64, int ab_dtype, int cd_dtype);
+
 int oracle_gemm_epi_typed(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
                           const uint16_t *C, const uint16_t *X, const uint16_t *RB, const uint16_t *CB,
                           const float *scalars, int kind, uint16_t *D, uint16_t *Aux, float *Acc, double *D64,
                           double *Aux64, double *Acc64, int dtype)
 {
+    return oracle_gemm_epi_typed2(L, M, N, K, A, B, C, X, RB, CB, scalars, kind, D, Aux, Acc, D64, Aux64, Acc64,
+                                  dtype, dtype);
+}
+
+/*
+ * The same with separate 16-bit element types for A, B (ab_dtype) and for
+ * C, X, RB, CB, D, Aux (cd_dtype): the Custom Epilogue Example's "Data Type
+ * Support" lists FP16 and BF16 among both the input types and the output
+ * types.  Each tensor is decoded with its own type's decoder and each output
+ * encoded once with the epilogue type's encoder; nothing else changes.
+ */
+int oracle_gemm_epi_typed2(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
+                           const uint16_t *C, const uint16_t *X, const uint16_t *RB, const uint16_t *CB,
+                           const float *scalars, int kind, uint16_t *D, uint16_t *Aux, float *Acc, double *D64,
+                           double *Aux64, double *Acc64, int ab_dtype, int cd_dtype)
+{
     int rc = check_args(L, M, N, K, A, B, C, X, RB, CB, scalars, kind, D, Aux, Acc);
     if (rc)
         return rc;
-    if (dtype != ORACLE_DTYPE_F16 && dtype != ORACLE_DTYPE_BF16)
+    if ((ab_dtype != ORACLE_DTYPE_F16 && ab_dtype != ORACLE_DTYPE_BF16) ||
+        (cd_dtype != ORACLE_DTYPE_F16 && cd_dtype != ORACLE_DTYPE_BF16))
         return 8;
-    const decode_fn dec = dtype == ORACLE_DTYPE_BF16 ? oracle_bf16_decode : oracle_f16_decode;
-    const encode_fn enc = dtype == ORACLE_DTYPE_BF16 ? oracle_bf16_encode : oracle_f16_encode;
+    const decode_fn dec = ab_dtype == ORACLE_DTYPE_BF16 ? oracle_bf16_decode : oracle_f16_decode;
+    const decode_fn dec_cd = cd_dtype == ORACLE_DTYPE_BF16 ? oracle_bf16_decode : oracle_f16_decode;
+    const encode_fn enc = cd_dtype == ORACLE_DTYPE_BF16 ? oracle_bf16_encode : oracle_f16_encode;
     const double alpha = scalars[0], beta = scalars[1], s = scalars[2];
     double *Bd = (double *)malloc(sizeof(double) * (size_t)K * (size_t)N);
     if (!Bd)
@@ -366,11 +389,11 @@ int oracle_gemm_epi_typed(int64_t L, int64_t M, int64_t N, int64_t K, const uint
                         acc[j] = acc[j] + a * brow[j];
                 }
                 const int64_t row = (l * M + i) * N;
-                const double cb = oracle_kind_reads_bias(kind) ? dec(CB[i]) : 0.0;
+                const double cb = oracle_kind_reads_bias(kind) ? dec_cd(CB[i]) : 0.0;
                 for (int64_t j = 0; j < N; j++) {
-                    double c = oracle_kind_reads_c(kind) ? dec(C[row + j]) : 0.0;
-                    double x = oracle_kind_reads_x(kind) ? dec(X[row + j]) : 0.0;
-                    double rb = oracle_kind_reads_bias(kind) ? dec(RB[j]) : 0.0;
+                    double c = oracle_kind_reads_c(kind) ? dec_cd(C[row + j]) : 0.0;
+                    double x = oracle_kind_reads_x(kind) ? dec_cd(X[row + j]) : 0.0;
+                    double rb = oracle_kind_reads_bias(kind) ? dec_cd(RB[j]) : 0.0;
                     double d = 0.0, aux = 0.0;
                     epilogue(kind, acc[j], c, x, rb, cb, alpha, beta, s, &d, &aux);
                     D[row + j] = enc(d);
