@@ -267,8 +267,8 @@ def run(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, D, Aux=None,
     A (L,M,K), B (L,K,N), C, X, D, Aux (L,M,N): contiguous float16 CUDA
     tensors, or all bfloat16 (then the bfloat16 kernels run; every
     composition below takes either type); or A, B float16 / bfloat16 with
-    C, X, D, Aux and the biases float32 (gemm_epi_run_mixed, fused call
-    only); row_bias (N,) and col_bias (M,) or (M, 1) of the
+    C, X, D, Aux and the biases all float32 or all of the other 16-bit type
+    (gemm_epi_run_mixed, fused call only; D's dtype selects it); row_bias (N,) and col_bias (M,) or (M, 1) of the
     same type for BIAS_ROW_COL; acc_out (L,M,N) float32 for RELU_SCALE_ACC.  s3 is
     extra_scalar (AUX_SCALE), x_factor (LINCOMB_X_ACC) or scale
     (RELU_SCALE_ACC).  The kernel is queued on `stream` (a torch.cuda.Stream;
@@ -286,8 +286,8 @@ def run(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, D, Aux=None,
     L, M, K = A.shape
     N = B.shape[2]
     at = torch.bfloat16 if isinstance(A, torch.Tensor) and A.dtype == torch.bfloat16 else torch.float16
-    # the epilogue tensors are of A's type, or all float32
-    et = torch.float32 if isinstance(D, torch.Tensor) and D.dtype == torch.float32 else at
+    # the epilogue tensors (C, X, biases, D, Aux) share D's type: A's, the other 16-bit type, or float32
+    et = D.dtype if isinstance(D, torch.Tensor) and D.dtype in (torch.float16, torch.bfloat16, torch.float32) else at
     _check_tensor("A", A, (L, M, K), at)
     _check_tensor("B", B, (L, K, N), at)
     _check_tensor("D", D, (L, M, N), et)
@@ -326,8 +326,8 @@ def run(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, D, Aux=None,
     if skw is not None and (skw.device != dev or not skw.is_contiguous()):
         raise ValueError("stream_k_workspace must be a contiguous tensor on the operands' device")
     dt = DTYPES["bf16"] if at == torch.bfloat16 else DTYPES["f16"]
-    if et == torch.float32 and (ws is not None or skw is not None):
-        raise ValueError("the unfused and stream-K compositions take 16-bit epilogue tensors only")
+    if et != at and (ws is not None or skw is not None):
+        raise ValueError("the unfused and stream-K compositions take epilogue tensors of A's type only")
     ops = (L, M, N, K, A.data_ptr(), B.data_ptr(), _ptr(C), _ptr(X), _ptr(row_bias), _ptr(col_bias),
            (alpha, beta, s3), KINDS[kname], D.data_ptr(), _ptr(Aux), _ptr(acc_out))
     with torch.cuda.device(dev):
@@ -335,8 +335,9 @@ def run(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, D, Aux=None,
             rc = gemm_epi_run_ws_typed(*ops, skw.data_ptr(), skw.numel() * skw.element_size(), dt, s.cuda_stream)
         elif ws is not None:
             rc = gemm_epi_run_unfused_typed(*ops, ws.data_ptr(), ws.numel() * 4, dt, s.cuda_stream)
-        elif et == torch.float32:
-            rc = gemm_epi_run_mixed(*ops, dt, DTYPES["f32"], s.cuda_stream)
+        elif et != at:
+            edt = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[et]
+            rc = gemm_epi_run_mixed(*ops, dt, DTYPES[edt], s.cuda_stream)
         else:
             rc = gemm_epi_run_typed(*ops, dt, s.cuda_stream)
     if rc != 0:

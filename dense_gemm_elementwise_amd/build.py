@@ -3,8 +3,10 @@
 hipcc compiles the translation units csrc/gemm_epi.hip (the C ABI and the
 fp16 kernels), csrc/gemm_epi_bf16.hip (the bfloat16 kernels) and
 csrc/gemm_epi_f32e.hip, csrc/gemm_epi_bf16_f32e.hip (fp16 / bfloat16 A and B
-with fp32 epilogue tensors) in parallel for --offload-arch=gfx950 only, then
-links them into one shared library.
+with fp32 epilogue tensors) and csrc/gemm_epi_f16_bf16e.hip,
+csrc/gemm_epi_bf16_f16e.hip (the other 16-bit type for the epilogue tensors)
+in parallel for --offload-arch=gfx950 only, then links them into one shared
+library.
 Packed-fp32 VALU instructions are switched off (-packed-fp32-ops): the
 epilogue is plain scalar fp32 arithmetic.
 """
@@ -15,7 +17,8 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRCS = [os.path.join(PKG, "csrc", f) for f in ("gemm_epi.hip", "gemm_epi_bf16.hip", "gemm_epi_f32e.hip",
-                                               "gemm_epi_bf16_f32e.hip")]
+                                               "gemm_epi_bf16_f32e.hip", "gemm_epi_f16_bf16e.hip",
+                                               "gemm_epi_bf16_f16e.hip")]
 LIB = os.path.join(PKG, "libgemm_epi.so")
 ARCH = "gfx950"
 

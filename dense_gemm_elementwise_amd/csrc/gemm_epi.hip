@@ -281,7 +281,9 @@ int gemm_epi_run_mixed(int64_t L, int64_t M, int64_t N, int64_t K, const void *A
     if (rc != GEMM_EPI_OK) return rc;
     if (ab_dtype != GEMM_EPI_F16 && ab_dtype != GEMM_EPI_BF16) return GEMM_EPI_ERR_DTYPE;
     const bool f32e = epi_dtype == GEMM_EPI_F32;
-    if (epi_dtype != ab_dtype && !f32e) return GEMM_EPI_ERR_DTYPE;
+    if (epi_dtype != ab_dtype && !f32e && epi_dtype != GEMM_EPI_F16 && epi_dtype != GEMM_EPI_BF16)
+        return GEMM_EPI_ERR_DTYPE;
+    const bool other16 = !f32e && epi_dtype != ab_dtype;
     if (!scalars) return GEMM_EPI_ERR_NULL_INPUT;
     if (f32e) {
         const void *words[] = {C, X, row_bias, col_bias, D, Aux};
@@ -322,6 +324,8 @@ int gemm_epi_run_mixed(int64_t L, int64_t M, int64_t N, int64_t K, const void *A
     const bool bf = ab_dtype == GEMM_EPI_BF16;
     if (f32e)
         err = bf ? launch_fused_bf16_f32e(epilogue_kind, p, t, vec, s) : launch_fused_f16_f32e(epilogue_kind, p, t, vec, s);
+    else if (other16)
+        err = bf ? launch_fused_bf16_f16e(epilogue_kind, p, t, vec, s) : launch_fused_f16_bf16e(epilogue_kind, p, t, vec, s);
     else if (bf)
         err = launch_fused_bf16(epilogue_kind, p, t, vec, s);
     else

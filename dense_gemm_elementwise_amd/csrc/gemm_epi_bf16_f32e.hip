@@ -12,7 +12,7 @@ namespace gemm_epi {
 hipError_t launch_fused_bf16_f32e(int kind, const Params &p, const TileCfg &t, bool vec, hipStream_t stream)
 {
     return dispatch_kind(kind,
-                         [&](auto k) { return launch_kind<decltype(k)::value, true, true>(p, t, vec, stream); });
+                         [&](auto k) { return launch_kind<decltype(k)::value, true, EPI_F32>(p, t, vec, stream); });
 }
 
 }  // namespace gemm_epi

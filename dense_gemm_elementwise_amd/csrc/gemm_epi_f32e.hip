@@ -12,7 +12,7 @@ namespace gemm_epi {
 hipError_t launch_fused_f16_f32e(int kind, const Params &p, const TileCfg &t, bool vec, hipStream_t stream)
 {
     return dispatch_kind(kind,
-                         [&](auto k) { return launch_kind<decltype(k)::value, false, true>(p, t, vec, stream); });
+                         [&](auto k) { return launch_kind<decltype(k)::value, false, EPI_F32>(p, t, vec, stream); });
 }
 
 }  // namespace gemm_epi

@@ -70,17 +70,20 @@ __device__ __forceinline__ _Float16 st16(float f)
         return (_Float16)f;
 }
 
-// Element type of the epilogue tensors (C, X, the biases, D, Aux): the
-// 16-bit type of A and B, or fp32 when F32E (widening is then the identity
-// and narrowing does not round).
-template <bool BF, bool F32E>
+// Element type of the epilogue tensors (C, X, the biases, D, Aux), by EPI:
+// EPI_AB the 16-bit type of A and B; EPI_F32 fp32 (widening is then the
+// identity and narrowing does not round); EPI_OTHER16 the other 16-bit type
+// (bfloat16 for fp16 A and B, fp16 for bfloat16 ones).
+enum EpiMode : int { EPI_AB = 0, EPI_F32 = 1, EPI_OTHER16 = 2 };
+template <bool BF, int EPI>
 struct EpiElem {
+    static constexpr bool EBF = EPI == EPI_OTHER16 ? !BF : BF;
     using T = _Float16;
-    static __device__ __forceinline__ float ld(T v) { return ld16<BF>(v); }
-    static __device__ __forceinline__ T st(float f) { return st16<BF>(f); }
+    static __device__ __forceinline__ float ld(T v) { return ld16<EBF>(v); }
+    static __device__ __forceinline__ T st(float f) { return st16<EBF>(f); }
 };
 template <bool BF>
-struct EpiElem<BF, true> {
+struct EpiElem<BF, EPI_F32> {
     using T = float;
     static __device__ __forceinline__ float ld(T v) { return v; }
     static __device__ __forceinline__ T st(float f) { return f; }
@@ -125,8 +128,8 @@ __host__ __device__ constexpr bool kind_has_acc_out(int k) { return k == RELU_SC
 __host__ __device__ constexpr bool kind_writes_d(int k) { return k != ACC_STORE; }
 
 // The 16-bit tensors travel as raw bits; C, X, D, Aux and the biases hold
-// fp32 values instead when the kernel is built with F32E (the kernel reads
-// them through its epilogue element type).
+// fp32 values instead when the kernel is built with EPI_F32 (the kernel
+// reads them through its epilogue element type).
 struct Params {
     const _Float16 *A;
     const _Float16 *B;
@@ -463,7 +466,7 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void *p)
 // LDS is filled through registers.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int BK, int NSTAGES, int WGM, int WGN, int MI, int KIND, bool VEC, bool SK = false,
-          bool BF = false, bool F32E = false>
+          bool BF = false, int EPI = EPI_AB>
 __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
 {
     constexpr int NW = WGM * WGN;                // waves per workgroup
@@ -870,8 +873,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     // previous slab's work; a lane's columns are the same in every slab, so its
     // row-bias values are loaded once.
     // With fp32 epilogue tensors a lane keeps 4 columns: 16-byte vectors again.
+    constexpr bool F32E = EPI == EPI_F32;
     constexpr int CPL = WN % 128 == 0 && !kind_has_acc_out(KIND) && !F32E ? 8 : 4;
-    using E = EpiElem<BF, F32E>;
+    using E = EpiElem<BF, EPI>;
     using et = typename E::T;
     using hvec = typename std::conditional<F32E, f32x4,
                                            typename std::conditional<CPL == 8, half8, half4>::type>::type;

@@ -52,21 +52,21 @@ hipError_t dispatch_kind(int kind, F &&f)
 }
 
 template <int BM, int BN, int BK, int NS, int WGM, int WGN, int MI, int KIND, bool VEC, bool SK = false,
-          bool BF = false, bool F32E = false>
+          bool BF = false, int EPI = EPI_AB>
 hipError_t launch_one(const Params &p, hipStream_t stream, int grid)
 {
-    hipLaunchKernelGGL((gemm_epi_kernel<BM, BN, BK, NS, WGM, WGN, MI, KIND, VEC, SK, BF, F32E>), dim3(grid),
+    hipLaunchKernelGGL((gemm_epi_kernel<BM, BN, BK, NS, WGM, WGN, MI, KIND, VEC, SK, BF, EPI>), dim3(grid),
                        dim3(64 * WGM * WGN), 0, stream, p);
     return hipGetLastError();
 }
 
 #define GE_LAUNCH(T, KIND, VEC) \
-    launch_one<T.bm, T.bn, T.bk, T.stages, T.wgm, T.wgn, T.mi, KIND, VEC, false, BF, F32E>(p, stream, p.num_tiles)
+    launch_one<T.bm, T.bn, T.bk, T.stages, T.wgm, T.wgn, T.mi, KIND, VEC, false, BF, EPI>(p, stream, p.num_tiles)
 
 // The fused kernel of one kind on tile configuration t (the general-path
-// kernel when vec is false); BF: A and B (and the 16-bit epilogue tensors)
-// are bfloat16; F32E: the epilogue tensors are fp32.
-template <int KIND, bool BF = false, bool F32E = false>
+// kernel when vec is false); BF: A and B are bfloat16; EPI: the epilogue
+// tensors' type (EpiMode).
+template <int KIND, bool BF = false, int EPI = EPI_AB>
 hipError_t launch_kind(const Params &p, const TileCfg &t, bool vec, hipStream_t stream)
 {
     if (!vec) return GE_LAUNCH(kGeneral, KIND, false);
@@ -98,8 +98,11 @@ hipError_t launch_fused_bf16(int kind, const Params &p, const TileCfg &t, bool v
 hipError_t launch_sk_bf16(int kind, const Params &p, int groups, hipStream_t stream);
 hipError_t launch_acc_store_bf16(const Params &p, const TileCfg &t, bool vec, hipStream_t stream);
 // The fused call with fp32 epilogue tensors (C, X, the biases, D, Aux), A and
-// B fp16 (gemm_epi_f32e.hip) or bfloat16 (gemm_epi_bf16_f32e.hip).
+// B fp16 (gemm_epi_f32e.hip) or bfloat16 (gemm_epi_bf16_f32e.hip); and with
+// the other 16-bit type for the epilogue tensors (gemm_epi_mixed16.hip).
 hipError_t launch_fused_f16_f32e(int kind, const Params &p, const TileCfg &t, bool vec, hipStream_t stream);
 hipError_t launch_fused_bf16_f32e(int kind, const Params &p, const TileCfg &t, bool vec, hipStream_t stream);
+hipError_t launch_fused_f16_bf16e(int kind, const Params &p, const TileCfg &t, bool vec, hipStream_t stream);
+hipError_t launch_fused_bf16_f16e(int kind, const Params &p, const TileCfg &t, bool vec, hipStream_t stream);
 
 }  // namespace gemm_epi

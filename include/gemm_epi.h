@@ -226,14 +226,16 @@ int gemm_epi_run_typed(int64_t L, int64_t M, int64_t N, int64_t K, const void *A
 /*
  * gemm_epi_run_mixed -- the fused call with separate element types for A, B
  * (ab_dtype: GEMM_EPI_F16 or GEMM_EPI_BF16) and for the epilogue tensors C, X,
- * row_bias, col_bias, D and Aux (epi_dtype: GEMM_EPI_F32, or the same type as
- * ab_dtype, in which case the call is exactly gemm_epi_run_typed).  With fp32
- * epilogue tensors (the example's FP32 C and D) the same fp32 epilogue runs;
- * C, X and the biases are read as they are and D, Aux are stored without a
- * further rounding.  Those tensors must then be 4-byte aligned (16-byte aligned,
- * with K % 8 == N % 8 == 0 and 16-byte aligned A, B, for the vector kernels);
- * shapes and layouts are unchanged.  Status codes as gemm_epi_run_ext, plus
- * GEMM_EPI_ERR_DTYPE for any other combination.
+ * row_bias, col_bias, D and Aux (epi_dtype: GEMM_EPI_F16, GEMM_EPI_BF16 or
+ * GEMM_EPI_F32; equal to ab_dtype, the call is exactly gemm_epi_run_typed).
+ * The example lists FP16 and BF16 as input types and FP32, FP16 and BF16 as
+ * C and D types.  The same fp32 epilogue runs whatever the types: C, X and
+ * the biases are widened exactly, and each 16-bit output is rounded once to
+ * nearest-even; fp32 outputs are stored without a further rounding.  fp32
+ * tensors must be 4-byte aligned (16-byte aligned, with K % 8 == N % 8 == 0
+ * and 16-byte aligned A, B, for the vector kernels); shapes and layouts are
+ * unchanged.  Status codes as gemm_epi_run_ext, plus GEMM_EPI_ERR_DTYPE for
+ * any other combination.
  */
 int gemm_epi_run_mixed(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
                        const void *X, const void *row_bias, const void *col_bias, const float *scalars,

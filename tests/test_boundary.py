@@ -168,21 +168,22 @@ def test_typed_composition_checks():
 
 
 def test_mixed_entry_point_checks():
-    """gemm_epi_run_mixed: A and B fp16 or bf16; epilogue tensors fp32 or A's
-    type; fp32 tensors 4-byte aligned (no launch here)."""
+    """gemm_epi_run_mixed: A and B fp16 or bf16; epilogue tensors fp16, bf16
+    or fp32; fp32 tensors 4-byte aligned (no launch here)."""
     def mixed(ab, epi, **kw):
         a = dict(A=P16, C=P16, D=P16, Aux=P16)
         a.update(kw)
         return ge.gemm_epi_run_mixed(1, 8, 8, 8, a["A"], P16, a["C"], P16, P16, P16, SC, 1, a["D"], a["Aux"], None,
                                      ab, epi, None)
     assert mixed("f32", "f32") == 8            # fp32 A and B are not a combination
-    assert mixed("f16", "bf16") == 8 and mixed("bf16", "f16") == 8
-    assert mixed(5, "f32") == 8 and mixed("f16", 7) == 8
+    assert mixed(5, "f32") == 8 and mixed("f16", 7) == 8 and mixed("bf16", -1) == 8
     assert mixed("f16", "f32", A=None) == 2    # the argument checks come first
     assert mixed("bf16", "f32", Aux=None) == 3
     assert mixed("f16", "f32", C=P2) == 5      # fp32 C only 2-byte aligned
     assert mixed("bf16", "f32", D=P2) == 5
     assert mixed("f16", "f32", D=P1) == 5
+    assert mixed("f16", "bf16", C=P1) == 5     # 16-bit C must be 2-byte aligned
+    assert mixed("bf16", "f16", A=None) == 2
 
 
 def test_unfused_workspace_checks():
