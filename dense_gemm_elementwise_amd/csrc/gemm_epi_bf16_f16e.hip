@@ -11,8 +11,9 @@ namespace gemm_epi {
 
 hipError_t launch_fused_bf16_f16e(int kind, const Params &p, const TileCfg &t, bool vec, hipStream_t stream)
 {
-    return dispatch_kind(kind,
-                         [&](auto k) { return launch_kind<decltype(k)::value, true, EPI_OTHER16>(p, t, vec, stream); });
+    return dispatch_kind(kind, [&](auto k) {
+        return launch_kind<decltype(k)::value, true, EPI_OTHER16>(p, t, vec, stream);
+    });
 }
 
 }  // namespace gemm_epi

@@ -11,8 +11,9 @@ namespace gemm_epi {
 
 hipError_t launch_fused_f16_bf16e(int kind, const Params &p, const TileCfg &t, bool vec, hipStream_t stream)
 {
-    return dispatch_kind(kind,
-                         [&](auto k) { return launch_kind<decltype(k)::value, false, EPI_OTHER16>(p, t, vec, stream); });
+    return dispatch_kind(kind, [&](auto k) {
+        return launch_kind<decltype(k)::value, false, EPI_OTHER16>(p, t, vec, stream);
+    });
 }
 
 }  // namespace gemm_epi
