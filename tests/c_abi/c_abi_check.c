@@ -18,11 +18,15 @@
 
 #include "gemm_epi.h"
 
-/* the oracle's typed entry point (oracle/oracle.c) */
-int oracle_gemm_epi_typed(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
-                          const uint16_t *C, const uint16_t *X, const uint16_t *RB, const uint16_t *CB,
-                          const float *scalars, int kind, uint16_t *D, uint16_t *Aux, float *Acc, double *D64,
-                          double *Aux64, double *Acc64, int dtype);
+/* the oracle's typed entry points (oracle/oracle.c) */
+int oracle_gemm_epi_typed2(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
+                           const uint16_t *C, const uint16_t *X, const uint16_t *RB, const uint16_t *CB,
+                           const float *scalars, int kind, uint16_t *D, uint16_t *Aux, float *Acc, double *D64,
+                           double *Aux64, double *Acc64, int ab_dtype, int cd_dtype);
+int oracle_gemm_epi_f32e(int64_t L, int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
+                         const float *C, const float *X, const float *RB, const float *CB, const float *scalars,
+                         int kind, float *D, float *Aux, float *Acc, double *D64, double *Aux64, double *Acc64,
+                         int ab_dtype);
 
 #define CHECK_HIP(x)                                                                        \
     do {                                                                                    \
@@ -51,13 +55,27 @@ static uint16_t *draw(size_t n, int dtype)
     return h;
 }
 
-static void *upload(const uint16_t *h, size_t n)
+static void *upload_bytes(const void *h, size_t bytes)
 {
     void *d = NULL;
     if (!h) return NULL;
-    CHECK_HIP(hipMalloc(&d, n * 2));
-    CHECK_HIP(hipMemcpy(d, h, n * 2, hipMemcpyHostToDevice));
+    CHECK_HIP(hipMalloc(&d, bytes));
+    CHECK_HIP(hipMemcpy(d, h, bytes, hipMemcpyHostToDevice));
     return d;
+}
+
+static void *upload(const uint16_t *h, size_t n) { return upload_bytes(h, n * 2); }
+
+static float *draw_f32(size_t n) /* the same small integers, as fp32 */
+{
+    float *h = (float *)malloc(n * 4);
+    for (size_t i = 0; i < n; i++) h[i] = (float)next_int();
+    return h;
+}
+
+static const char *type_name(int dtype)
+{
+    return dtype == GEMM_EPI_BF16 ? "bf16" : dtype == GEMM_EPI_F32 ? "f32" : "f16";
 }
 
 static int same_bits(const uint16_t *g, const uint16_t *w, size_t n, const char *what)
@@ -69,24 +87,28 @@ static int same_bits(const uint16_t *g, const uint16_t *w, size_t n, const char 
     return bad == 0;
 }
 
-static int run_case(int kind, int dtype, int64_t L, int64_t M, int64_t N, int64_t K, const float sc[3])
+/* A, B of type dtype; C, X, D, Aux of the 16-bit type epi (gemm_epi_run_mixed) */
+static int run_case(int kind, int dtype, int epi, int64_t L, int64_t M, int64_t N, int64_t K, const float sc[3])
 {
     const int has_aux = kind == GEMM_EPI_AUX_SCALE || kind == GEMM_EPI_LINCOMB_X_ACC || kind == GEMM_EPI_SQUARE ||
                         kind == GEMM_EPI_RELU_SQUARE || kind == GEMM_EPI_RELU_AUX_STORE;
     const int reads_x = kind == GEMM_EPI_LINCOMB_X_ACC;
     const size_t na = (size_t)(L * M * K), nb = (size_t)(L * K * N), nc = (size_t)(L * M * N);
     lcg_state = 0x9E3779B97F4A7C15ULL ^ (uint64_t)(kind * 131 + dtype * 7 + M);
-    uint16_t *A = draw(na, dtype), *B = draw(nb, dtype), *C = draw(nc, dtype);
-    uint16_t *X = reads_x ? draw(nc, dtype) : NULL;
+    uint16_t *A = draw(na, dtype), *B = draw(nb, dtype), *C = draw(nc, epi);
+    uint16_t *X = reads_x ? draw(nc, epi) : NULL;
     void *dA = upload(A, na), *dB = upload(B, nb), *dC = upload(C, nc), *dX = upload(X, nc);
     void *dD = NULL, *dAux = NULL;
     CHECK_HIP(hipMalloc(&dD, nc * 2));
     if (has_aux) CHECK_HIP(hipMalloc(&dAux, nc * 2));
 
     int ok = 1;
-    const int rc = gemm_epi_run_typed(L, M, N, K, dA, dB, dC, dX, NULL, NULL, sc, kind, dD, dAux, NULL, dtype, NULL);
+    const int rc = epi == dtype
+                       ? gemm_epi_run_typed(L, M, N, K, dA, dB, dC, dX, NULL, NULL, sc, kind, dD, dAux, NULL, dtype, NULL)
+                       : gemm_epi_run_mixed(L, M, N, K, dA, dB, dC, dX, NULL, NULL, sc, kind, dD, dAux, NULL, dtype, epi,
+                                            NULL);
     if (rc != GEMM_EPI_OK) {
-        fprintf(stderr, "  gemm_epi_run_typed returned %d (%s)\n", rc, gemm_epi_status_string(rc));
+        fprintf(stderr, "  the call returned %d (%s)\n", rc, gemm_epi_status_string(rc));
         ok = 0;
     } else {
         CHECK_HIP(hipDeviceSynchronize());
@@ -94,8 +116,8 @@ static int run_case(int kind, int dtype, int64_t L, int64_t M, int64_t N, int64_
         uint16_t *Dref = (uint16_t *)malloc(nc * 2), *Auxref = has_aux ? (uint16_t *)malloc(nc * 2) : NULL;
         CHECK_HIP(hipMemcpy(D, dD, nc * 2, hipMemcpyDeviceToHost));
         if (has_aux) CHECK_HIP(hipMemcpy(Aux, dAux, nc * 2, hipMemcpyDeviceToHost));
-        const int orc = oracle_gemm_epi_typed(L, M, N, K, A, B, C, X, NULL, NULL, sc, kind, Dref, Auxref, NULL, NULL,
-                                              NULL, NULL, dtype);
+        const int orc = oracle_gemm_epi_typed2(L, M, N, K, A, B, C, X, NULL, NULL, sc, kind, Dref, Auxref, NULL, NULL,
+                                               NULL, NULL, dtype, epi);
         if (orc != 0) {
             fprintf(stderr, "  the oracle rejected the case (%d)\n", orc);
             ok = 0;
@@ -107,8 +129,70 @@ static int run_case(int kind, int dtype, int64_t L, int64_t M, int64_t N, int64_
         free(Dref);
         free(Auxref);
     }
-    printf("%s kind=%d dtype=%s L=%lld M=%lld N=%lld K=%lld\n", ok ? "PASS" : "FAIL", kind,
-           dtype == GEMM_EPI_BF16 ? "bf16" : "f16", (long long)L, (long long)M, (long long)N, (long long)K);
+    printf("%s kind=%d dtype=%s epi=%s L=%lld M=%lld N=%lld K=%lld\n", ok ? "PASS" : "FAIL", kind, type_name(dtype),
+           type_name(epi), (long long)L, (long long)M, (long long)N, (long long)K);
+    fflush(stdout);
+    hipFree(dA);
+    hipFree(dB);
+    hipFree(dC);
+    hipFree(dX);
+    hipFree(dD);
+    hipFree(dAux);
+    free(A);
+    free(B);
+    free(C);
+    free(X);
+    return ok;
+}
+
+/* A, B of type dtype; C, X, D, Aux fp32 (gemm_epi_run_mixed with GEMM_EPI_F32) */
+static int run_case_f32(int kind, int dtype, int64_t L, int64_t M, int64_t N, int64_t K, const float sc[3])
+{
+    const int has_aux = kind == GEMM_EPI_AUX_SCALE || kind == GEMM_EPI_LINCOMB_X_ACC || kind == GEMM_EPI_SQUARE ||
+                        kind == GEMM_EPI_RELU_SQUARE || kind == GEMM_EPI_RELU_AUX_STORE;
+    const int reads_x = kind == GEMM_EPI_LINCOMB_X_ACC;
+    const size_t na = (size_t)(L * M * K), nb = (size_t)(L * K * N), nc = (size_t)(L * M * N);
+    lcg_state = 0x243F6A8885A308D3ULL ^ (uint64_t)(kind * 131 + dtype * 7 + M);
+    uint16_t *A = draw(na, dtype), *B = draw(nb, dtype);
+    float *C = draw_f32(nc), *X = reads_x ? draw_f32(nc) : NULL;
+    void *dA = upload(A, na), *dB = upload(B, nb), *dC = upload_bytes(C, nc * 4);
+    void *dX = X ? upload_bytes(X, nc * 4) : NULL;
+    void *dD = NULL, *dAux = NULL;
+    CHECK_HIP(hipMalloc(&dD, nc * 4));
+    if (has_aux) CHECK_HIP(hipMalloc(&dAux, nc * 4));
+    int ok = 1;
+    const int rc = gemm_epi_run_mixed(L, M, N, K, dA, dB, dC, dX, NULL, NULL, sc, kind, dD, dAux, NULL, dtype,
+                                      GEMM_EPI_F32, NULL);
+    if (rc != GEMM_EPI_OK) {
+        fprintf(stderr, "  gemm_epi_run_mixed returned %d (%s)\n", rc, gemm_epi_status_string(rc));
+        ok = 0;
+    } else {
+        CHECK_HIP(hipDeviceSynchronize());
+        float *D = (float *)malloc(nc * 4), *Aux = has_aux ? (float *)malloc(nc * 4) : NULL;
+        float *Dref = (float *)malloc(nc * 4), *Auxref = has_aux ? (float *)malloc(nc * 4) : NULL;
+        CHECK_HIP(hipMemcpy(D, dD, nc * 4, hipMemcpyDeviceToHost));
+        if (has_aux) CHECK_HIP(hipMemcpy(Aux, dAux, nc * 4, hipMemcpyDeviceToHost));
+        if (oracle_gemm_epi_f32e(L, M, N, K, A, B, C, X, NULL, NULL, sc, kind, Dref, Auxref, NULL, NULL, NULL, NULL,
+                                 dtype) != 0) {
+            fprintf(stderr, "  the oracle rejected the case\n");
+            ok = 0;
+        } else {
+            /* integer inputs: every value is exact, so the fp32 outputs are equal (+0 and -0 alike) */
+            size_t bad = 0;
+            for (size_t i = 0; i < nc; i++) {
+                if (D[i] != Dref[i]) bad++;
+                if (has_aux && Aux[i] != Auxref[i]) bad++;
+            }
+            if (bad) fprintf(stderr, "  %zu fp32 outputs differ\n", bad);
+            ok = bad == 0;
+        }
+        free(D);
+        free(Aux);
+        free(Dref);
+        free(Auxref);
+    }
+    printf("%s kind=%d dtype=%s epi=f32 L=%lld M=%lld N=%lld K=%lld\n", ok ? "PASS" : "FAIL", kind, type_name(dtype),
+           (long long)L, (long long)M, (long long)N, (long long)K);
     fflush(stdout);
     hipFree(dA);
     hipFree(dB);
@@ -128,11 +212,16 @@ int main(void)
     const float lin[3] = {1.0f, 2.0f, 0.0f}, aux[3] = {1.0f, 2.0f, 0.5f}, xacc[3] = {2.0f, 1.0f, 3.0f};
     int fails = 0;
     for (int dtype = GEMM_EPI_F16; dtype <= GEMM_EPI_BF16; dtype++) {
-        fails += !run_case(GEMM_EPI_LINCOMB, dtype, 1, 256, 512, 128, lin);
-        fails += !run_case(GEMM_EPI_AUX_SCALE, dtype, 2, 200, 136, 264, aux);
-        fails += !run_case(GEMM_EPI_LINCOMB_X_ACC, dtype, 1, 520, 776, 88, xacc);
-        fails += !run_case(GEMM_EPI_RELU_SQUARE, dtype, 3, 77, 45, 61, lin);   /* general kernel: K, N % 8 != 0 */
+        fails += !run_case(GEMM_EPI_LINCOMB, dtype, dtype, 1, 256, 512, 128, lin);
+        fails += !run_case(GEMM_EPI_AUX_SCALE, dtype, dtype, 2, 200, 136, 264, aux);
+        fails += !run_case(GEMM_EPI_LINCOMB_X_ACC, dtype, dtype, 1, 520, 776, 88, xacc);
+        fails += !run_case(GEMM_EPI_RELU_SQUARE, dtype, dtype, 3, 77, 45, 61, lin); /* general kernel: K, N % 8 != 0 */
     }
+    /* the other element-type pairs of gemm_epi_run_mixed */
+    fails += !run_case(GEMM_EPI_AUX_SCALE, GEMM_EPI_F16, GEMM_EPI_BF16, 2, 200, 136, 264, aux);
+    fails += !run_case(GEMM_EPI_LINCOMB_X_ACC, GEMM_EPI_BF16, GEMM_EPI_F16, 1, 520, 776, 88, xacc);
+    fails += !run_case_f32(GEMM_EPI_LINCOMB_X_ACC, GEMM_EPI_F16, 1, 520, 776, 88, xacc);
+    fails += !run_case_f32(GEMM_EPI_RELU_SQUARE, GEMM_EPI_BF16, 3, 77, 45, 61, lin);
     /* an argument error comes back as a status code, before any launch */
     const int bad = gemm_epi_run_typed(1, 8, 8, 8, NULL, NULL, NULL, NULL, NULL, NULL, lin, 0, NULL, NULL, NULL,
                                        GEMM_EPI_F16, NULL);
