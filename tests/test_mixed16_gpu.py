@@ -79,7 +79,8 @@ def check(p, kind, ab, epi, a, b, s, exact, offset=0, what=""):
         got = t.cpu().view(torch.int16).numpy().view(np.uint16)
         want = np.asarray(ref[name]).view(np.uint16)
         g = decode(got, epi)
-        assert np.all(np.isfinite(g)), f"{what} {name}: non-finite"
+        # non-finite only where the oracle's rounded output overflows too (E = D*D can pass fp16's 65504)
+        assert np.all(np.isfinite(g) | ~np.isfinite(decode(want, epi))), f"{what} {name}: non-finite"
         if exact and kind not in ge.ACTIVATIONS:
             bad = np.count_nonzero((got != want) & (((got | want) & 0x7FFF) != 0))
             assert bad == 0, f"{what} {name}: {bad} of {got.size} differ"

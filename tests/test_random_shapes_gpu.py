@@ -1,7 +1,8 @@
 """Seeded random sweep over the shape space: batch 1-3, M, N, K from 1 to
 700 (K up to 2100), every kind, fp16 and bf16 tensors, aligned and
-misaligned pointers (fast and general kernels), the fused call and the
-stream-K entry point.  Integer-valued inputs keep every sum exact, so each
+misaligned pointers (fast and general kernels), the fused call, the
+stream-K entry point, and epilogue tensors of another type than A and B
+(fp32 or the other 16-bit type).  Integer-valued inputs keep every sum exact, so each
 case is bit-exact against the oracle (activation kinds: within one ulp and
 mostly bit-identical, as in the other parity tests).
 """
@@ -76,3 +77,38 @@ def test_random_stream_k_case(seed):
         assert_bit_exact(Aux.cpu().numpy(), ref["Aux"], f"random stream-k {seed} Aux")
     if acc is not None:
         assert np.array_equal(acc.cpu().numpy(), ref["Acc"])
+
+
+def mixed_cases(n=24, seed=20251203):
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        L = int(rng.integers(1, 3))
+        M, N = (int(v) for v in rng.integers(1, 601, 2))
+        K = int(rng.integers(1, 1501))
+        if rng.random() < 0.5:
+            N, K = max(8, N - N % 8), max(8, K - K % 8)
+        kind = workloads.KINDS[int(rng.integers(0, len(workloads.KINDS)))]
+        ab = "bf16" if rng.random() < 0.5 else "f16"
+        epi = "f32" if rng.random() < 0.5 else ("f16" if ab == "bf16" else "bf16")
+        offset = 1 if rng.random() < 0.2 else 0
+        out.append((c, L, M, N, K, kind, ab, epi, offset))
+    return out
+
+
+@pytest.mark.parametrize("case", mixed_cases(),
+                         ids=lambda c: f"m{c[0]}-{c[5]}-{c[6]}to{c[7]}-{c[1]}x{c[2]}x{c[3]}x{c[4]}-off{c[8]}")
+def test_random_mixed_types_case(case):
+    """The same sweep for epilogue tensors of another type than A and B
+    (gemm_epi_run_mixed): fp32, or the other 16-bit type."""
+    c, L, M, N, K, kind, ab, epi, offset = case
+    a, b, s = KIND_SCALARS[kind]
+    log(f"[random mixed] case {c}: L={L} M={M} N={N} K={K} {kind} {ab}->{epi} offset={offset}")
+    if epi == "f32":
+        import test_f32e_gpu as f32e
+        p = f32e.problem(L, M, N, K, kind, ab, seed=3000 + c, init="small_int")
+        f32e.check(p, kind, ab, a, b, s, exact=True, offset=offset, what=f"random mixed case {c}")
+    else:
+        import test_mixed16_gpu as m16
+        p = m16.problem(L, M, N, K, kind, ab, epi, seed=3000 + c, init="small_int")
+        m16.check(p, kind, ab, epi, a, b, s, exact=True, offset=offset, what=f"random mixed case {c}")
