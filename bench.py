@@ -28,6 +28,8 @@ if ROOT not in sys.path:
 
 PEAK_FP16_TFLOPS = 2516.6  # MI355X dense fp16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+# workloads that --all also times with fp32 and bfloat16 epilogue tensors
+EPI_TYPE_WORKLOADS = ("x_acc_8192", "relu_square_16x2048x2048x1024")
 KERNEL_SOURCES = ("dense_gemm_elementwise_amd/csrc/gemm_epi_kernels.hpp", "dense_gemm_elementwise_amd/csrc/gemm_epi.hip",
                   "dense_gemm_elementwise_amd/csrc/gemm_epi_launch.hpp", "dense_gemm_elementwise_amd/csrc/gemm_epi_bf16.hip")
 
@@ -185,6 +187,37 @@ def bench_gpu_stream_k(w, steps, warmup):
             "workspace_bytes": plan["workspace_bytes"], "kernel_ms": round(ev_ms, 5),
             "launch_ms": {k: round(v, 5) for k, v in stats.items()},
             "tflops": round(w.flops / (ev_ms * 1e-3) / 1e12, 2), "roofline": roofline(w, ev_ms)}
+
+
+def bench_gpu_epi_types(w, steps, warmup):
+    """Context: the same fp16 workload with its epilogue tensors (C, X, the
+    biases, D, Aux) in fp32 and in bfloat16 instead (gemm_epi_run_mixed): the
+    workload's C and X converted on the device (exactly to fp32, rounded to
+    bfloat16).  Launch times and TFLOP/s per epilogue type."""
+    import torch
+    import dense_gemm_elementwise_amd as ge
+    from dense_gemm_elementwise_amd import workloads
+
+    if w.dtype != "f16":
+        return None
+    dev = torch.device("cuda:0")
+    t16 = _upload(workloads.make_inputs(w), w, dev)
+    out = {}
+    for name, tt in (("f32", torch.float32), ("bf16", torch.bfloat16)):
+        t = {k: (v.to(tt) if (v is not None and k not in ("A", "B")) else v) for k, v in t16.items()}
+        D = torch.empty((w.L, w.M, w.N), dtype=tt, device=dev)
+        Aux = torch.empty_like(D) if w.kind in ge.HAS_AUX else None
+        Acc = torch.empty((w.L, w.M, w.N), dtype=torch.float32, device=dev) if w.kind in ge.HAS_ACC else None
+        stream = torch.cuda.current_stream(dev)
+        args = _device_args(w, t, D, Aux, Acc, stream, ge)
+        margs = args[:15] + (ge.DTYPES["f16"], ge.DTYPES[name], args[15])
+        for _ in range(warmup):
+            rc = ge.gemm_epi_run_mixed(*margs)
+            if rc:
+                raise RuntimeError(ge.gemm_epi_status_string(rc))
+        _, ev_ms, stats = _timed_launches(lambda i: ge.gemm_epi_run_mixed(*margs), steps, stream)
+        out[name] = {"kernel_ms": round(ev_ms, 5), "tflops": round(w.flops / (ev_ms * 1e-3) / 1e12, 2)}
+    return out
 
 
 MALL_BYTES = 256 << 20  # MI355X Infinity Cache
@@ -449,6 +482,8 @@ def main():
             sk = bench_gpu_stream_k(other, a.steps, a.warmup)
             if sk is not None:
                 line["stream_k"] = sk
+            if other.name in EPI_TYPE_WORKLOADS:
+                line["epi_types"] = bench_gpu_epi_types(other, a.steps, a.warmup)
             if a.compare_unfused:
                 line["unfused_own"] = bench_unfused_own(other, a.steps, a.warmup)
                 line["unfused_library"] = bench_unfused_library(other, a.steps, a.warmup)
@@ -464,6 +499,8 @@ def main():
                "sample": f"first {rows} of {w.M} output rows of {w.name} (all {w.N} columns, K={w.K}), "
                          f"fp64 i-k-j triple loop + epilogue, {dt:.1f} s"}
     line = result_line(w, g, a.steps, a.warmup, cpu)
+    if a.all and w.name in EPI_TYPE_WORKLOADS:
+        line["epi_types"] = bench_gpu_epi_types(w, a.steps, a.warmup)
     if a.compare_unfused:
         line["unfused_own"] = bench_unfused_own(w, a.steps, a.warmup)
         line["unfused_library"] = bench_unfused_library(w, a.steps, a.warmup)
