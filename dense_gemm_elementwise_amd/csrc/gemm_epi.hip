@@ -36,8 +36,9 @@ constexpr int kNumCUs = 256;
 // efficiency): big tiles when the grid fills the chip several times, smaller
 // ones when big tiles would leave compute units idle.  Ties go to the tile
 // that pads the problem least, then to the one whose long side lies along the
-// problem's long side.
-TileCfg choose_tile(int64_t L, int64_t M, int64_t N, bool vec)
+// problem's long side.  The 64 x 64 tile takes its deeper K step when K is
+// long enough to fill its ring.
+TileCfg choose_tile(int64_t L, int64_t M, int64_t N, int64_t K, bool vec)
 {
     if (!vec) return kGeneral;
     TileCfg best = kTiles[0];
@@ -60,6 +61,7 @@ TileCfg choose_tile(int64_t L, int64_t M, int64_t N, bool vec)
             best = t;
         }
     }
+    if (best.bm == kSmallDeep.bm && best.bn == kSmallDeep.bn && K >= kSmallDeepMinK) return kSmallDeep;
     return best;
 }
 
@@ -147,7 +149,7 @@ SkPlan plan_stream_k(int64_t L, int64_t M, int64_t N, int64_t K, bool vec)
     constexpr double kStageSeconds = 0.76e-6, kOperandBytesPerSecond = 5.5e12;
     SkPlan best;
     if (!vec) return best;
-    const TileCfg dp = choose_tile(L, M, N, vec);
+    const TileCfg dp = choose_tile(L, M, N, K, vec);
     const int64_t dp_tiles = L * ((M + dp.bm - 1) / dp.bm) * ((N + dp.bn - 1) / dp.bn);
     const double dp_cost = (double)((dp_tiles + kNumCUs - 1) / kNumCUs) * ((K + dp.bk - 1) / dp.bk) * dp.bk *
                            dp.bm * dp.bn / tile_efficiency(dp.bm, dp.bn);
@@ -235,7 +237,7 @@ int gemm_epi_plan_ext(int64_t L, int64_t M, int64_t N, int64_t K, const void *A,
     int rc = check_args(L, M, N, K, o, epilogue_kind);
     if (rc != GEMM_EPI_OK) return rc;
     const bool vec = use_fast_path(M, N, K, o, epilogue_kind);
-    const TileCfg t = choose_tile(L, M, N, vec);
+    const TileCfg t = choose_tile(L, M, N, K, vec);
     const int64_t tiles = L * ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
     if (tiles > INT32_MAX) return GEMM_EPI_ERR_SHAPE;
     if (out) {
@@ -291,7 +293,7 @@ int gemm_epi_run_mixed(int64_t L, int64_t M, int64_t N, int64_t K, const void *A
             if (w && !aligned(w, 4)) return GEMM_EPI_ERR_ALIGN;
     }
     const bool vec = use_fast_path(M, N, K, o, epilogue_kind);
-    const TileCfg t = choose_tile(L, M, N, vec);
+    const TileCfg t = choose_tile(L, M, N, K, vec);
     const int64_t tm = (M + t.bm - 1) / t.bm, tn = (N + t.bn - 1) / t.bn;
     const int64_t tiles = L * tm * tn;
     if (tiles > INT32_MAX) return GEMM_EPI_ERR_SHAPE;
@@ -366,7 +368,7 @@ int gemm_epi_run_unfused_typed(int64_t L, int64_t M, int64_t N, int64_t K, const
     // stage 1: the GEMM, writing only the fp32 accumulator
     const Operands o1 = {A, B, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, acc};
     const bool vec1 = use_fast_path(M, N, K, o1, ACC_STORE);
-    const TileCfg t = choose_tile(L, M, N, vec1);
+    const TileCfg t = choose_tile(L, M, N, K, vec1);
     const int64_t tm = (M + t.bm - 1) / t.bm, tn = (N + t.bn - 1) / t.bn;
     const int64_t tiles = L * tm * tn;
     if (tiles > INT32_MAX) return GEMM_EPI_ERR_SHAPE;

@@ -356,11 +356,14 @@ __device__ __forceinline__ int sk_slot(const Params &p, int w, int t, int nk_til
 // each pair moves to its own chunk.  Swizzles that also mix the row's low bit
 // into the chunk conflict 2-way on gfx950 for this read, with 128-byte and
 // with 64-byte rows and for both MFMA shapes (measured with the LDS
-// bank-conflict counter).
+// bank-conflict counter).  256-byte rows each span all 64 banks, so there
+// the low bit has to go in as well: 16 rows, 16 chunks.
 template <int A_CHUNKS>
 __device__ __forceinline__ int swz_a(int row)
 {
-    if constexpr (A_CHUNKS == 8)
+    if constexpr (A_CHUNKS == 16)
+        return ((row >> 1) & 7) | ((row & 1) << 3);  // 256-byte rows
+    else if constexpr (A_CHUNKS == 8)
         return (row >> 1) & 7;  // 128-byte rows
     else
         return (row >> 1) & 3;  // 64-byte rows
@@ -369,7 +372,10 @@ __device__ __forceinline__ int swz_a(int row)
 // The B transpose reads differ by MFMA shape.  MI = 32: the 32 lanes served
 // together read 4 consecutive k-rows x 4 consecutive chunks.  MI = 16: they
 // read k-rows r..r+3 and r+8..r+11 x 2 consecutive chunks, so the swizzle also
-// separates k-rows 8 apart.
+// separates k-rows 8 apart.  With 8-chunk (128-byte) k-rows, even and odd
+// k-rows fall in opposite halves of the 64 banks, and the four k-rows of one
+// parity (bits 1 and 3 of the k-row) take the four chunk pairs: a 2-way
+// conflict left by 2 * (krow & 3) cost 32% of the 64 x 64 tile's LDS cycles.
 template <int B_CHUNKS, int MI>
 __device__ __forceinline__ int swz_b(int krow)
 {
@@ -377,6 +383,8 @@ __device__ __forceinline__ int swz_b(int krow)
         return (0xCA60 >> ((krow & 3) * 4)) & 15;          // 0, 6, 10, 12 for krow % 4 = 0..3
     else if constexpr (B_CHUNKS >= 16)
         return 2 * ((krow & 3) | (((krow >> 3) & 1) << 2));  // 0, 2, .., 14 over krow % 4 and bit 3
+    else if constexpr (MI == 16)
+        return 2 * (((krow >> 1) & 1) | (((krow >> 3) & 1) << 1));  // 8-chunk rows: 0, 2, 4, 6
     else
         return 2 * (krow & 3);                              // 8-chunk rows: 0, 2, 4, 6
 }
@@ -477,7 +485,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     constexpr int NACC = MI == 32 ? 16 : 4;      // accumulator registers per block
     using acc_t = typename std::conditional<MI == 32, f32x16, f32x4>::type;
     static_assert(TM >= 1 && TN >= 1, "tile too small");
-    static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
+    static_assert(BK == 32 || BK == 64 || BK == 128, "BK must be 32, 64 or 128");
     static_assert(NSTAGES >= 2, "at least two stages");
     constexpr int A_ROW = BK * 2;     // bytes per A row in LDS
     constexpr int A_CHUNKS = BK / 8;  // 16-byte chunks per A row

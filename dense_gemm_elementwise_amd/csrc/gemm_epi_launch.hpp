@@ -19,12 +19,16 @@ struct TileCfg {
 
 // The tile configurations compiled into the library (fast path), and the one
 // general-path configuration.  The 64 x 64 tile (small problems, one wave of
-// workgroups or less) takes BK = 64: its stages are latency-bound, so half as
-// many of them is what counts (1024^3: 12.0 -> 9.7 us against BK = 32; more
-// stages in the ring did not help).
+// workgroups or less) has latency-bound stages, so fewer, deeper ones are
+// what counts: BK = 64 (1024^3: 12.0 -> 9.7 us against BK = 32; more stages
+// in the ring did not help), and BK = 128 (kSmallDeep) once K >= 512, where
+// it is 1-8% faster again; below that the ring holds fewer than four stages
+// and BK = 128 is 2-5% slower.
 inline constexpr TileCfg kTiles[] = {{256, 256, 64, 2, 4, 2, 16}, {128, 256, 64, 2, 2, 4, 16},
                                      {256, 128, 64, 2, 4, 2, 16}, {128, 128, 64, 3, 2, 2, 32},
                                      {64, 64, 64, 4, 2, 2, 16}};
+inline constexpr TileCfg kSmallDeep = {64, 64, 128, 4, 2, 2, 16};
+inline constexpr int64_t kSmallDeepMinK = 512;
 inline constexpr TileCfg kGeneral = {128, 128, 64, 2, 2, 2, 32};
 
 // Calls f(std::integral_constant<int, KIND>) for a public kind (checked by
@@ -74,6 +78,7 @@ hipError_t launch_kind(const Params &p, const TileCfg &t, bool vec, hipStream_t 
     if (t.bm == kTiles[1].bm && t.bn == kTiles[1].bn) return GE_LAUNCH(kTiles[1], KIND, true);
     if (t.bm == kTiles[2].bm && t.bn == kTiles[2].bn) return GE_LAUNCH(kTiles[2], KIND, true);
     if (t.bm == kTiles[3].bm && t.bn == kTiles[3].bn) return GE_LAUNCH(kTiles[3], KIND, true);
+    if (t.bk == kSmallDeep.bk) return GE_LAUNCH(kSmallDeep, KIND, true);
     return GE_LAUNCH(kTiles[4], KIND, true);
 }
 

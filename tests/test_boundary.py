@@ -268,30 +268,43 @@ def test_plan_fast_and_general_paths():
 
 def test_plan_tiles_for_the_workloads():
     want = {
-        "aux_scale_128": (64, 64, 4),
-        "aux_scale_1024": (64, 64, 256),
-        "lincomb_2400x3232x4096": (128, 256, 19 * 13),
-        "x_acc_8192": (256, 256, 1024),
-        "relu_square_16x2048x2048x1024": (256, 256, 1024),
-        "relu_aux_store_1024": (64, 64, 256),
-        "relu_scale_acc_1024": (64, 64, 256),
-        "bias_row_col_1024": (64, 64, 256),
-        "relu_scale_acc_8192": (256, 256, 1024),
-        "bias_row_col_8192": (256, 256, 1024),
-        "lincomb_deep_k_256x256x65536": (64, 64, 16),
-        "gelu_8192": (256, 256, 1024),
-        "aux_scale_bf16_1024": (64, 64, 256),     # the tile choice does not depend on the element type
-        "x_acc_bf16_8192": (256, 256, 1024),
+        "aux_scale_128": (64, 64, 64, 4),
+        "aux_scale_1024": (64, 64, 128, 256),
+        "lincomb_2400x3232x4096": (128, 256, 64, 19 * 13),
+        "x_acc_8192": (256, 256, 64, 1024),
+        "relu_square_16x2048x2048x1024": (256, 256, 64, 1024),
+        "relu_aux_store_1024": (64, 64, 128, 256),
+        "relu_scale_acc_1024": (64, 64, 128, 256),
+        "bias_row_col_1024": (64, 64, 128, 256),
+        "relu_scale_acc_8192": (256, 256, 64, 1024),
+        "bias_row_col_8192": (256, 256, 64, 1024),
+        "lincomb_deep_k_256x256x65536": (64, 64, 128, 16),
+        "gelu_8192": (256, 256, 64, 1024),
+        "aux_scale_bf16_1024": (64, 64, 128, 256),     # the tile choice does not depend on the element type
+        "x_acc_bf16_8192": (256, 256, 64, 1024),
     }
-    want.update({f"{a.lower()}_256": (64, 64, 16) for a in workloads.ACTIVATIONS})
+    want.update({f"{a.lower()}_256": (64, 64, 64, 16) for a in workloads.ACTIVATIONS})
     assert set(want) == set(workloads.WORKLOADS)
-    for name, (bm, bn, wgs) in want.items():
+    for name, (bm, bn, bk, wgs) in want.items():
         w = workloads.WORKLOADS[name]
         rc, cfg = ge.gemm_epi_plan_ext(w.L, w.M, w.N, w.K, P16, P16, P16, P16, P16, P16, ge.KINDS[w.kind], P16, P16,
                                        P16)
         assert rc == 0, name
-        assert (cfg["bm"], cfg["bn"], cfg["workgroups"]) == (bm, bn, wgs), (name, cfg)
+        assert (cfg["bm"], cfg["bn"], cfg["bk"], cfg["workgroups"]) == (bm, bn, bk, wgs), (name, cfg)
         assert cfg["vec"] == 1
+
+
+def test_small_tile_k_step_follows_k():
+    """The 64 x 64 tile steps K by 64 below K = 512 and by 128 from there on;
+    the other tiles and the general kernel do not depend on K."""
+    for K, bk in ((8, 64), (256, 64), (504, 64), (512, 128), (520, 128), (8192, 128)):
+        rc, cfg = ge.gemm_epi_plan(1, 1024, 1024, K, P16, P16, P16, None, 0, P16, None)
+        assert rc == 0 and (cfg["bm"], cfg["bn"], cfg["bk"], cfg["vec"]) == (64, 64, bk, 1), (K, cfg)
+    for K in (256, 512, 4096):
+        rc, cfg = ge.gemm_epi_plan(1, 8192, 8192, K, P16, P16, P16, None, 0, P16, None)
+        assert rc == 0 and (cfg["bm"], cfg["bn"], cfg["bk"]) == (256, 256, 64), (K, cfg)
+        rc, cfg = ge.gemm_epi_plan(1, 1024, 1024, K + 2, P16, P16, P16, None, 0, P16, None)
+        assert rc == 0 and cfg["vec"] == 0 and cfg["bk"] == 64, (K, cfg)
 
 
 def test_python_wrapper_rejects_bad_tensors():

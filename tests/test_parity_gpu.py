@@ -353,8 +353,14 @@ TILE_SHAPES = [(1, 768, 2816, 72), (1, 2304, 2048, 40), (1, 2400, 1032, 24)]
 BIG_TILE_SHAPES = [(1, 4000, 4000, 8), (1, 4000, 4000, 24), (1, 4000, 4000, 40), (1, 4000, 4000, 72),
                    (1, 4000, 4000, 104), (1, 4000, 4000, 136), (1, 3000, 5000, 264)]
 
+# the 64 x 64 tile with its 128-deep K step (K >= 512): 4 full stages, a
+# ragged last stage of 8 and of 120, more stages than the ring holds, ragged
+# M and N, batches
+DEEP_SMALL_SHAPES = [(1, 64, 64, 512), (1, 1000, 1000, 520), (1, 777, 1000, 1016), (2, 300, 520, 2056),
+                     (3, 200, 136, 1160)]
 
-@pytest.mark.parametrize("shape", TAIL_SHAPES + TILE_SHAPES + BIG_TILE_SHAPES)
+
+@pytest.mark.parametrize("shape", TAIL_SHAPES + TILE_SHAPES + BIG_TILE_SHAPES + DEEP_SMALL_SHAPES)
 def test_tails_bit_exact(shape):
     L, M, N, K = shape
     kind = "AUX_SCALE"
@@ -373,8 +379,8 @@ def test_every_tile_configuration_is_exercised():
         rc, cfg = ge.gemm_epi_plan(L, M, N, K, P, P, P, P, 1, P, P)
         assert rc == 0
         if cfg["vec"]:
-            seen.add((cfg["bm"], cfg["bn"]))
-    assert seen == {(256, 256), (128, 256), (256, 128), (128, 128), (64, 64)}, seen
+            seen.add((cfg["bm"], cfg["bn"], cfg["bk"]))
+    assert seen == {(256, 256, 64), (128, 256, 64), (256, 128, 64), (128, 128, 64), (64, 64, 64), (64, 64, 128)}, seen
 
 
 def test_identity_and_zero_closed_forms_on_gpu():
