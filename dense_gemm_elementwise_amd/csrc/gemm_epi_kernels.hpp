@@ -871,7 +871,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     // The wave tile is handled one MFMA row-block (SLAB rows) at a time.  In a
     // slab, pass p covers rows 4p..4p+3; lane owns row 4p + lane/16 and CPL
     // consecutive columns from CPL*(lane%16) (+ a second group at WN/2 for a
-    // 128-wide tile read 4 columns per lane).  CPL = 8 where the wave tile is
+    // 128-wide tile read 4 columns per lane).  A 32-wide wave tile has 8
+    // lanes per row and twice the rows per pass (lane_row below): with 16,
+    // half the lanes would idle (64 x 64 tile: 4-13% faster launches).  CPL = 8 where the wave tile is
     // 128 wide: 16-byte loads and stores, half the vector memory instructions
     // of 4 columns per lane (measured 5% faster on the 16-batch products).  A
     // kind with the fp32 accumulator output keeps 4 columns per lane: with 8,
@@ -890,7 +892,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     const et *const pC = (const et *)p.C, *const pX = (const et *)p.X;
     const et *const prb = (const et *)p.row_bias, *const pcb = (const et *)p.col_bias;
     et *const pD = (et *)p.D, *const pAux = (et *)p.Aux;
-    constexpr int EPI_PASSES = SLAB / 4;
+    // A pass covers 64 / LPR slab rows with LPR lanes per row.  For WN = 32
+    // (LPR = 8) the two 8-lane halves of a 16-lane group take rows 8 apart,
+    // which lie in opposite halves of the LDS banks (8 * EPI_LD = 288 words).
+    constexpr int LPR = WN / CPL >= 16 ? 16 : WN / CPL;
+    static_assert(LPR == 16 || (LPR == 8 && SLAB == 16), "epilogue lane mapping");
+    constexpr int EPI_PASSES = SLAB * LPR / 64;
     constexpr int EPI_GROUPS = CPL == 4 && WN >= 128 ? 2 : 1;
     constexpr int EPI_HALF = WN / 2;
     constexpr bool HAS_C = kind_reads_c(KIND);
@@ -899,7 +906,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     constexpr int CP = HAS_C ? EPI_PASSES : 1, XP = HAS_X ? EPI_PASSES : 1, BP = HAS_BIAS ? EPI_PASSES : 1;
     const float alpha = p.alpha, beta = p.beta, s = p.s;
     const int64_t mn_base = (int64_t)l * M * N;
-    auto lane_col = [&](int h) { return CPL * (lane & 15) + h * EPI_HALF; };
+    auto lane_col = [&](int h) { return CPL * (lane % LPR) + h * EPI_HALF; };
+    auto lane_row = [&](int pass) { return pass * 4 + (lane >> 4) + (LPR == 8 ? 8 * ((lane >> 3) & 1) : 0); };
     // Outputs are stored non-temporally (each is written once and never read
     // back here): they stream to HBM without taking L2 lines from the operand
     // panels (16-batch RELU_SQUARE 215 -> 183 us, 8192^3 LINCOMB_X_ACC -1%).
@@ -928,7 +936,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
                             bool with_c, bool with_x) {
 #pragma unroll
         for (int pass = 0; pass < EPI_PASSES; pass++) {
-            const int gm = m0 + wm * WM + i * SLAB + pass * 4 + (lane >> 4);
+            const int gm = m0 + wm * WM + i * SLAB + lane_row(pass);
             if constexpr (HAS_BIAS)
                 if (with_x) colb[pass] = gm < M ? pcb[gm] : (et)0.0f;
 #pragma unroll
@@ -985,7 +993,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
         }
 #pragma unroll
         for (int pass = 0; pass < EPI_PASSES; pass++) {
-            const int srow = pass * 4 + (lane >> 4);
+            const int srow = lane_row(pass);
             const int gm = m0 + wm * WM + i * SLAB + srow;
 #pragma unroll
             for (int h = 0; h < EPI_GROUPS; h++) {
