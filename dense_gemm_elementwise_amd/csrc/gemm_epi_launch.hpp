@@ -25,9 +25,11 @@ struct TileCfg {
 // it is 1-8% faster again; below that the ring holds fewer than four stages
 // and BK = 128 is 2-5% slower.  Eight waves of 16 x 32 (two per SIMD, where
 // one such workgroup is all a compute unit gets) hide more of that latency
-// than four of 32 x 32: 3% at 1024^3, 6% on 256^3.
+// than four of 32 x 32: 3% at 1024^3, 6% on 256^3.  The 128 x 128 tile
+// likewise runs eight waves of 32 x 64 (2-3% on mid-size grids); its
+// stream-K build keeps four (eight were 2-13% slower there).
 inline constexpr TileCfg kTiles[] = {{256, 256, 64, 2, 4, 2, 16}, {128, 256, 64, 2, 2, 4, 16},
-                                     {256, 128, 64, 2, 4, 2, 16}, {128, 128, 64, 3, 2, 2, 32},
+                                     {256, 128, 64, 2, 4, 2, 16}, {128, 128, 64, 3, 4, 2, 32},
                                      {64, 64, 64, 4, 4, 2, 16}};
 inline constexpr TileCfg kSmallDeep = {64, 64, 128, 4, 4, 2, 16};
 inline constexpr int64_t kSmallDeepMinK = 512;
