@@ -37,7 +37,8 @@ constexpr int kNumCUs = 256;
 // ones when big tiles would leave compute units idle.  Ties go to the tile
 // that pads the problem least, then to the one whose long side lies along the
 // problem's long side.  The 64 x 64 tile takes its deeper K step when K is
-// long enough to fill its ring.
+// long enough to fill its ring, with the shorter ring when the grid has more
+// tiles than compute units.
 TileCfg choose_tile(int64_t L, int64_t M, int64_t N, int64_t K, bool vec)
 {
     if (!vec) return kGeneral;
@@ -61,7 +62,10 @@ TileCfg choose_tile(int64_t L, int64_t M, int64_t N, int64_t K, bool vec)
             best = t;
         }
     }
-    if (best.bm == kSmallDeep.bm && best.bn == kSmallDeep.bn && K >= kSmallDeepMinK) return kSmallDeep;
+    if (best.bm == kSmallDeep.bm && best.bn == kSmallDeep.bn && K >= kSmallDeepMinK) {
+        const int64_t tiles = L * ((M + best.bm - 1) / best.bm) * ((N + best.bn - 1) / best.bn);
+        return tiles > kNumCUs ? kSmallDeepWide : kSmallDeep;
+    }
     return best;
 }
 
