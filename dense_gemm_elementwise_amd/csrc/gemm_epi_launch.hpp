@@ -21,9 +21,9 @@ struct TileCfg {
 // general-path configuration.  The 64 x 64 tile (small problems, one wave of
 // workgroups or less) has latency-bound stages, so fewer, deeper ones are
 // what counts: BK = 64 (1024^3: 12.0 -> 9.7 us against BK = 32; more stages
-// in the ring did not help), and BK = 128 (kSmallDeep) once K >= 512, where
-// it is 1-8% faster again; below that the ring holds fewer than four stages
-// and BK = 128 is 2-5% slower.  Eight waves of 16 x 32 (two per SIMD, where
+// in the ring did not help), and BK = 128 (kSmallDeep) once K >= 256, where
+// it is 1-8% faster again (with four waves of 32 x 32 the break-even was
+// K = 512; the eight waves below moved it to 256).  Eight waves of 16 x 32 (two per SIMD, where
 // one such workgroup is all a compute unit gets) hide more of that latency
 // than four of 32 x 32: 3% at 1024^3, 6% on 256^3.  The 128 x 128 tile
 // likewise runs eight waves of 32 x 64 (2-3% on mid-size grids); its
@@ -37,7 +37,7 @@ inline constexpr TileCfg kSmallDeep = {64, 64, 128, 4, 4, 2, 16};
 // are compute units (1280^2 grids, 400 tiles: 24% faster) and costs where a
 // unit holds only one (192 tiles: 16% slower; 16 tiles: 39%).
 inline constexpr TileCfg kSmallDeepWide = {64, 64, 128, 2, 4, 2, 16};
-inline constexpr int64_t kSmallDeepMinK = 512;
+inline constexpr int64_t kSmallDeepMinK = 256;
 inline constexpr TileCfg kGeneral = {128, 128, 64, 2, 2, 2, 32};
 
 // Calls f(std::integral_constant<int, KIND>) for a public kind (checked by

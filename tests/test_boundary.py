@@ -252,7 +252,7 @@ def test_misaligned_pointers():
 
 def test_plan_fast_and_general_paths():
     rc, cfg = ge.gemm_epi_plan(1, 256, 256, 256, P16, P16, P16, None, 0, P16, None)
-    assert rc == 0 and cfg["vec"] == 1 and cfg["threads"] in (256, 512) and cfg["bk"] in (32, 64)
+    assert rc == 0 and cfg["vec"] == 1 and cfg["threads"] in (256, 512) and cfg["bk"] in (32, 64, 128)
     # K or N not a multiple of 8, or a pointer not 16-byte aligned -> general kernel
     for args in ((1, 256, 256, 250), (1, 256, 250, 256)):
         rc, cfg = ge.gemm_epi_plan(*args, P16, P16, P16, None, 0, P16, None)
@@ -283,7 +283,7 @@ def test_plan_tiles_for_the_workloads():
         "aux_scale_bf16_1024": (64, 64, 128, 256),     # the tile choice does not depend on the element type
         "x_acc_bf16_8192": (256, 256, 64, 1024),
     }
-    want.update({f"{a.lower()}_256": (64, 64, 64, 16) for a in workloads.ACTIVATIONS})
+    want.update({f"{a.lower()}_256": (64, 64, 128, 16) for a in workloads.ACTIVATIONS})
     assert set(want) == set(workloads.WORKLOADS)
     for name, (bm, bn, bk, wgs) in want.items():
         w = workloads.WORKLOADS[name]
@@ -295,9 +295,9 @@ def test_plan_tiles_for_the_workloads():
 
 
 def test_small_tile_k_step_follows_k():
-    """The 64 x 64 tile steps K by 64 below K = 512 and by 128 from there on;
+    """The 64 x 64 tile steps K by 64 below K = 256 and by 128 from there on;
     the other tiles and the general kernel do not depend on K."""
-    for K, bk in ((8, 64), (256, 64), (504, 64), (512, 128), (520, 128), (8192, 128)):
+    for K, bk in ((8, 64), (128, 64), (248, 64), (256, 128), (520, 128), (8192, 128)):
         rc, cfg = ge.gemm_epi_plan(1, 1024, 1024, K, P16, P16, P16, None, 0, P16, None)
         assert rc == 0 and (cfg["bm"], cfg["bn"], cfg["bk"], cfg["vec"]) == (64, 64, bk, 1), (K, cfg)
     for K in (256, 512, 4096):

@@ -353,11 +353,11 @@ TILE_SHAPES = [(1, 768, 2816, 72), (1, 2304, 2048, 40), (1, 2400, 1032, 24)]
 BIG_TILE_SHAPES = [(1, 4000, 4000, 8), (1, 4000, 4000, 24), (1, 4000, 4000, 40), (1, 4000, 4000, 72),
                    (1, 4000, 4000, 104), (1, 4000, 4000, 136), (1, 3000, 5000, 264)]
 
-# the 64 x 64 tile with its 128-deep K step (K >= 512): 4 full stages, a
+# the 64 x 64 tile with its 128-deep K step (K >= 256): 4 full stages, a
 # ragged last stage of 8 and of 120, more stages than the ring holds, ragged
 # M and N, batches; the last two have more tiles than compute units (2-stage
 # ring)
-DEEP_SMALL_SHAPES = [(1, 64, 64, 512), (1, 1000, 1000, 520), (1, 777, 1000, 1016), (2, 300, 520, 2056),
+DEEP_SMALL_SHAPES = [(1, 64, 64, 256), (1, 64, 64, 512), (1, 1000, 1000, 520), (1, 777, 1000, 1016), (2, 300, 520, 2056),
                      (3, 200, 136, 1160), (1, 1280, 1280, 648), (2, 1000, 600, 1032)]
 
 
