@@ -109,7 +109,8 @@ PAIRS = [("f16", "bf16"), ("bf16", "f16")]
                                           ((2, 200, 136, 264), 1),    # misaligned: general kernel
                                           ((3, 77, 45, 61), 0),       # K, N not multiples of 8: general
                                           ((1, 520, 776, 88), 0),     # vector kernel, 256 x 256 tiles
-                                          ((2, 300, 520, 648), 0)])   # 64 x 64 x 128 tile (K >= 256), ragged last stage
+                                          ((2, 300, 520, 648), 0),    # 64 x 64 x 128 tile (K >= 256), ragged last stage
+                                          ((1, 300, 520, 136), 0)])   # 64 x 64 x 64 tile (K < 256), ragged last stage
 def test_every_kind_integer_inputs(kind, ab, epi, shape, offset):
     L, M, N, K = shape
     a, b, s = KIND_SCALARS[kind]
