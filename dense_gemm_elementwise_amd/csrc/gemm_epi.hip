@@ -69,6 +69,15 @@ TileCfg choose_tile(int64_t L, int64_t M, int64_t N, int64_t K, bool vec)
     return best;
 }
 
+// Epilogue tensors of another type than A and B (fp32, or the other 16-bit
+// type) take the 256 x 128 (or 128 x 256) tile where the choice is 256 x 256:
+// their wider epilogue does not fit the 256 x 256 tile's registers.
+TileCfg tile_for_mixed(const TileCfg &t, int64_t M, int64_t N)
+{
+    if (t.bm != kTiles[0].bm || t.bn != kTiles[0].bn) return t;
+    return M >= N ? kTiles[2] : kTiles[1];
+}
+
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 // Host-side operand set of one call (the pointers gemm_epi_run_ext takes).
@@ -297,7 +306,8 @@ int gemm_epi_run_mixed(int64_t L, int64_t M, int64_t N, int64_t K, const void *A
             if (w && !aligned(w, 4)) return GEMM_EPI_ERR_ALIGN;
     }
     const bool vec = use_fast_path(M, N, K, o, epilogue_kind);
-    const TileCfg t = choose_tile(L, M, N, K, vec);
+    TileCfg t = choose_tile(L, M, N, K, vec);
+    if (f32e || other16) t = tile_for_mixed(t, M, N);
     const int64_t tm = (M + t.bm - 1) / t.bm, tn = (N + t.bn - 1) / t.bn;
     const int64_t tiles = L * tm * tn;
     if (tiles > INT32_MAX) return GEMM_EPI_ERR_SHAPE;

@@ -469,6 +469,228 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void *p)
 }
 
 // ---------------------------------------------------------------------------
+// Main loop of the 4-wave 256 x 256 tile: one wave per SIMD, each owning a
+// 128 x 128 accumulator tile (64 blocks of v_mfma_f32_16x16x32, 256 fp32
+// values per lane) held in the accumulation registers (AGPRs).  Against
+// eight waves of 64 x 128 it reads a third fewer LDS bytes per MFMA (the
+// operand bytes of a wave tile grow with its perimeter, the MFMAs with its
+// area), which is what bounds the 8-wave loop.
+//
+// With one wave per SIMD nothing else covers a stall, so the instruction
+// stream is fixed by hand:
+//  * K is walked in 32-wide stages through a ring of W4_NS slots; stage t+1
+//    is published by one barrier at the start of k step t, and the slot of
+//    stage t, which every wave has read into registers by then, is refilled
+//    with stage t + W4_NS right after it: the DMA has W4_NS - 1 k steps
+//    (about 3k cycles) to land.
+//  * A slots sit in one 64 KB region and B slots in the next, so every LDS
+//    read is one base register plus an immediate offset (16-bit offsets).
+//  * Each k step issues its 64 MFMAs with one memory instruction after every
+//    second one: the 24 operand reads of the next k step (8 A ds_read_b128,
+//    16 B ds_read_b64_tr_b16) and this wave's 8 DMAs of the stage W4_NS
+//    ahead.  The order is pinned with scheduling barriers.
+//  * The MFMAs are inline asm with "+a" accumulator operands: with the
+//    builtins the register allocator moved accumulators between the AGPR
+//    and VGPR files inside the loop.  The hardware does not interlock an
+//    MFMA result against a later non-MFMA reader and the compiler cannot see
+//    inside the asm, so wait states are inserted by hand after the loop.
+// ---------------------------------------------------------------------------
+constexpr int W4_BK = 32;
+constexpr int W4_NS = 4;
+constexpr int W4_A_SLOT = 256 * W4_BK * 2;  // 16 KB: 256 rows x 64 bytes
+constexpr int W4_B_SLOT = W4_BK * 256 * 2;  // 16 KB: 32 k-rows x 512 bytes
+constexpr int W4_B_BASE = W4_NS * W4_A_SLOT;
+constexpr int W4_LDS = W4_NS * (W4_A_SLOT + W4_B_SLOT);
+
+template <bool BF>
+__device__ __forceinline__ void mfma16_agpr(f32x4 &acc, const half8 &a, const half8 &b)
+{
+    if constexpr (BF)
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    else
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Orders every accumulator write before it against every access after it
+// (each asm takes one row of accumulator blocks as in-out operands, in
+// program order) and covers the last write with wait states: MFMAs in inline
+// asm are opaque to the compiler's hazard recognizer, so the gap between a
+// VALU write and an MFMA read, and between an MFMA result and an ordinary
+// read, is inserted here.
+__device__ __forceinline__ void agpr_fence(f32x4 (&acc)[8][8])
+{
+#pragma unroll
+    for (int i = 0; i < 7; i++)
+        asm volatile("" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
+                     "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc[7][0]), "+a"(acc[7][1]), "+a"(acc[7][2]), "+a"(acc[7][3]), "+a"(acc[7][4]),
+                   "+a"(acc[7][5]), "+a"(acc[7][6]), "+a"(acc[7][7]));
+}
+
+template <bool BF>
+__device__ __forceinline__ void mainloop_w4(f32x4 (&acc)[8][8], const _Float16 *Al, const _Float16 *Bl, int M,
+                                            int N, int K, int m0, int n0, int kb, int nk, char *smem)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    constexpr uint32_t kParked = 0x7FFFFFF0u;
+    const uint32_t smem_lds = lds_addr_of(smem);
+
+    // DMA: 16 KB of A and 16 KB of B per stage, 1 KB per wave instruction,
+    // 4 + 4 instructions per wave.  A block q of wave w: rows 16 (4q + w) ..
+    // + 15, lane -> row + lane / 4, physical chunk lane % 4.  B block: two
+    // k-rows of 32 chunks.
+    uint32_t a_voff[4], b_voff[4];
+    int a_kcol[4];  // first k column of the lane's A chunk, for the stage that crosses K
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const int row = (q * 4 + wave) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ swz_a<4>(row);
+        const int gm = m0 + row;
+        a_kcol[q] = c * 8;
+        a_voff[q] = gm < M ? (uint32_t)(gm * K + c * 8) * 2u : kParked;
+        const int lin = (q * 4 + wave) * 64 + lane;
+        const int krow = lin >> 5;
+        const int cb = (lin & 31) ^ swz_b<32, 16>(krow);
+        const int gn = n0 + cb * 8;
+        b_voff[q] = gn < N ? (uint32_t)(krow * N + gn) * 2u : kParked;
+    }
+    // One DMA instruction of the stage at k column k0 into ring slot `slot`:
+    // op 0..3 = A, 4..7 = B.  Past the last stage the ring is still fed, with
+    // a zero-record descriptor (the buffer unit writes zeros into the free
+    // slot and touches no memory), so every k step issues the same number of
+    // DMAs and one vmcnt value serves every wait.  Only the last stage can
+    // cross K (A columns past K are the next row's: parked).
+    const uint32_t lds_w = (uint32_t)__builtin_amdgcn_readfirstlane((int)(smem_lds + wave * 1024));
+    auto dma_op = [&](int op, int slot, int k0, const i32x4 &ra, const i32x4 &rb) {
+        if (op < 4) {
+            int voff = (int)a_voff[op];
+            if (k0 + W4_BK > K) voff = k0 + a_kcol[op] < K ? voff : (int)kParked;
+            dma16(ra, lds_w + slot * W4_A_SLOT + op * 4096, voff);
+        } else {
+            dma16(rb, lds_w + W4_B_BASE + slot * W4_B_SLOT + (op - 4) * 4096, (int)b_voff[op - 4]);
+        }
+    };
+    auto rsrc_a = [&](int s) {  // stage s (s >= nk: no records)
+        const int k0 = (kb + s) * W4_BK;
+        return make_rsrc(Al + k0, s < nk ? (uint32_t)(((int64_t)M * K - k0) * 2) : 0u);
+    };
+    auto rsrc_b = [&](int s) {
+        const int k0 = (kb + s) * W4_BK;
+        return make_rsrc(Bl + (int64_t)k0 * N, s < nk ? (uint32_t)((int64_t)(K - k0) * N * 2) : 0u);
+    };
+
+    // Operand reads.  A block i: lane (li + 16 lg) reads row wm*128 + 16 i + li,
+    // k columns 8 lg..8 lg+7 (one ds_read_b128); the swizzle depends on row
+    // bits 1-2 only, so block i is block 0 + i KB.  B block j: two
+    // ds_read_b64_tr_b16, lane 4e + r of 16-lane group g pointing at k-row
+    // 8 g + 4 h + e, columns 4 r..4 r+3 of the block; h moves 4 k-rows
+    // (+2 KB, same swizzle), j has its own address.
+    const int li = lane & 15, lg = lane >> 4, lq = lane & 15;
+    const int a_row = wm * 128 + li;
+    const char *a_rd = smem + a_row * 64 + ((lg ^ swz_a<4>(a_row)) * 16);
+    const char *b_rd[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const int n = wn * 128 + j * 16 + 4 * (lq & 3);
+        const int krow = 8 * lg + (lq >> 2);
+        b_rd[j] = smem + W4_B_BASE + krow * 512 + (((n >> 3) ^ swz_b<32, 16>(krow)) * 16) + (n & 7) * 2;
+    }
+    auto read_a = [&](int slot, int i) {
+        return *(const half8 *)(a_rd + slot * W4_A_SLOT + i * 1024);
+    };
+    auto read_b = [&](int slot, int j, int h) {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+            (GE_LDS(fp16x4_t) *)(b_rd[j] + slot * W4_B_SLOT + h * 2048));
+    };
+
+    half8 fa[2][8], fb[2][8];
+    fp16x4_t fbh[8][2];
+
+    // One k step: MFMAs on the fragments in buffer P (stage slot S), operand
+    // reads of slot (S+1) % NS into buffer P^1, DMA of stage `sd` into slot S.
+    // On the last step the reads fetch a slot nobody writes any more into
+    // registers nobody uses: every branch stays outside the pinned sequence.
+    auto kstep = [&](auto S_, auto P_, int sd) {
+        constexpr int S = decltype(S_)::value, P = decltype(P_)::value;
+        constexpr int SN = (S + 1) % W4_NS;
+        const i32x4 ra = rsrc_a(sd), rb = rsrc_b(sd);
+        const int k0dma = (kb + sd) * W4_BK;
+#pragma unroll
+        for (int m = 0; m < 64; m++) {
+            mfma16_agpr<BF>(acc[m >> 3][m & 7], fa[P][m >> 3], fb[P][m & 7]);
+            if ((m & 1) == 0) {
+                const int op = m >> 1, g = op >> 2, r = op & 3;
+                if (r == 0)
+                    fa[P ^ 1][g] = read_a(SN, g);
+                else if (r == 1)
+                    fbh[g][0] = read_b(SN, g, 0);
+                else if (r == 2)
+                    fbh[g][1] = read_b(SN, g, 1);
+                else
+                    dma_op(g, S, k0dma, ra, rb);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const half4 lo = __builtin_bit_cast(half4, fbh[j][0]), hi = __builtin_bit_cast(half4, fbh[j][1]);
+            fb[P ^ 1][j] = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+    };
+
+    // prologue: stages 0..NS-1 in flight (zero-record past nk), stage 0
+    // published and read into buffer 0
+#pragma unroll
+    for (int s = 0; s < W4_NS; s++) {
+        const i32x4 ra = rsrc_a(s), rb = rsrc_b(s);
+        const int k0 = (kb + s) * W4_BK;
+#pragma unroll
+        for (int op = 0; op < 8; op++) dma_op(op, s, k0, ra, rb);
+    }
+    wait_vmcnt<(W4_NS - 1) * 8>();
+    barrier_lds();
+#pragma unroll
+    for (int i = 0; i < 8; i++) fa[0][i] = read_a(0, i);
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        fbh[j][0] = read_b(0, j, 0);
+        fbh[j][1] = read_b(0, j, 1);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const half4 lo = __builtin_bit_cast(half4, fbh[j][0]), hi = __builtin_bit_cast(half4, fbh[j][1]);
+        fb[0][j] = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    agpr_fence(acc);  // the accumulators' zeroing (VALU) before the first MFMA reads them
+
+    // Step t: its own DMA of stage t+1 has landed (the NS-2 stages after it
+    // may still be in flight), then the barrier publishes stage t+1 and frees
+    // slot t; the last step has nothing to publish.  Steps go in groups of
+    // NS, so that slots and register buffers are compile-time.
+    static_assert(W4_NS == 4, "the k-step unrolling assumes a 4-slot ring of even length");
+    auto step = [&](auto D_, int t) {
+        constexpr int d = decltype(D_)::value;
+        if (t + 1 < nk) {
+            wait_vmcnt<(W4_NS - 2) * 8>();
+            barrier_lds();
+        }
+        kstep(std::integral_constant<int, d>{}, std::integral_constant<int, d & 1>{}, t + W4_NS);
+    };
+#pragma unroll 1
+    for (int t = 0; t < nk; t += W4_NS) {
+        step(std::integral_constant<int, 0>{}, t);
+        if (t + 1 < nk) step(std::integral_constant<int, 1>{}, t + 1);
+        if (t + 2 < nk) step(std::integral_constant<int, 2>{}, t + 2);
+        if (t + 3 < nk) step(std::integral_constant<int, 3>{}, t + 3);
+    }
+    agpr_fence(acc);  // the last MFMAs' results before the epilogue reads them
+}
+
+// ---------------------------------------------------------------------------
 // The kernel.  VEC = fast path (16-byte global->LDS DMA, 8-byte epilogue
 // vectors); otherwise every global access is element-wise and guarded and
 // LDS is filled through registers.
@@ -503,6 +725,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     constexpr int EPI_BYTES = NW * SLAB * EPI_LD * 4;
     constexpr int SMEM = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
     static_assert(SMEM <= 160 * 1024, "LDS budget");
+    // the 4-wave 256 x 256 configuration runs the hand-scheduled main loop
+    constexpr bool W4 = NW == 4 && BM == 256 && BN == 256 && BK == W4_BK && NSTAGES == W4_NS && MI == 16 && VEC &&
+                        !SK;
+    static_assert(!W4 || MAIN_BYTES == W4_LDS, "4-wave ring layout");
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
     const int tid = threadIdx.x;
@@ -534,6 +760,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
 
     const int nk = ke - kb;  // k stages in this segment
 
+    if constexpr (W4) {
+        mainloop_w4<BF>(acc, Al, Bl, M, N, K, m0, n0, kb, nk, smem);
+    } else {
     // ---- global -> LDS --------------------------------------------------
     // One wave instruction fills 1 KB: 1024 / A_ROW rows of A, or
     // 1024 / B_ROW k-rows of B.  DMA_PER_STAGE = this thread's DMA
@@ -807,6 +1036,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
         }
     }
 
+    }  // main loop (W4 or general)
+
     // ---- stream-K: partial sums of a split tile -------------------------------
     if constexpr (SK) {
         if (kb != 0 || ke != nk_tile) {
@@ -876,15 +1107,17 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     // half the lanes would idle (64 x 64 tile: 4-13% faster launches).  CPL = 8 where the wave tile is
     // 128 wide: 16-byte loads and stores, half the vector memory instructions
     // of 4 columns per lane (measured 5% faster on the 16-batch products).  A
-    // kind with the fp32 accumulator output keeps 4 columns per lane: with 8,
-    // each 16-byte fp32 store instruction would fill only half of every cache
-    // line it touches (measured 6% slower).  C / X (and the column bias) of a slab are loaded
+    // kind with the fp32 accumulator output keeps 4 columns per lane on the
+    // 8-wave tiles: with 8, each 16-byte fp32 store instruction would fill
+    // only half of every cache line it touches (measured 6% slower).  On the
+    // 4-wave tile it takes 8 as well: with 4 its epilogue runs out of VGPRs
+    // and spills.  C / X (and the column bias) of a slab are loaded
     // into registers one slab ahead, so the loads' latency hides behind the
     // previous slab's work; a lane's columns are the same in every slab, so its
     // row-bias values are loaded once.
     // With fp32 epilogue tensors a lane keeps 4 columns: 16-byte vectors again.
     constexpr bool F32E = EPI == EPI_F32;
-    constexpr int CPL = WN % 128 == 0 && !kind_has_acc_out(KIND) && !F32E ? 8 : 4;
+    constexpr int CPL = WN % 128 == 0 && (!kind_has_acc_out(KIND) || W4) && !F32E ? 8 : 4;
     using E = EpiElem<BF, EPI>;
     using et = typename E::T;
     using hvec = typename std::conditional<F32E, f32x4,
@@ -922,14 +1155,19 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     auto st_epi = [](et *q, hvec v) { __builtin_nontemporal_store(v, (hvec *)q); };
     // C of every slab is loaded at once when the epilogue starts (the operand
     // fragment registers are free by then): more loads in flight.  X and the
-    // column bias go one slab ahead, and so does C when it is fp32 (all of it
-    // would take 128 registers).
-    constexpr bool PRE_C = VEC && HAS_C && !F32E;
-    constexpr int NBC = PRE_C ? TM : 2;
+    // column bias go EPD slabs ahead, and so does C when it is fp32 (all of it
+    // would take 128 registers) or when the wave tile has 8 slabs (the 4-wave
+    // tile: 128 registers again).  EPD is 1 on the 8-wave tiles, whose two
+    // waves per SIMD overlap each other's loads; the 4-wave tile, one wave per
+    // SIMD, keeps 3 slabs of C and X in flight.
+    constexpr bool PRE_C = VEC && HAS_C && !F32E && TM <= 4;
+    constexpr int EPD = W4 ? 3 : 1;
+    constexpr int NBX = EPD + 1;
+    constexpr int NBC = PRE_C ? TM : NBX;
     hvec cbuf[NBC][CP][EPI_GROUPS];
-    hvec xbuf[2][XP][EPI_GROUPS];
-    et cbias[2][BP];
-    auto cslot = [](int i) { return PRE_C ? i : (i & 1); };
+    hvec xbuf[NBX][XP][EPI_GROUPS];
+    et cbias[NBX][BP];
+    auto cslot = [](int i) { return PRE_C ? i : i % NBX; };
     hvec rbias[EPI_GROUPS];
     // loads slab i's C (with_c) and its X and column bias (with_x)
     auto epi_prefetch = [&](int i, hvec (&cb)[CP][EPI_GROUPS], hvec (&xb)[XP][EPI_GROUPS], et (&colb)[BP],
@@ -964,10 +1202,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
                 rbias[h] = (scol < WN && gn < N) ? *(const hvec *)(prb + gn) : hvec{};
             }
         }
-        epi_prefetch(0, cbuf[0], xbuf[0], cbias[0], true, true);
+#pragma unroll
+        for (int i = 0; i < EPD && i < TM; i++) epi_prefetch(i, cbuf[cslot(i)], xbuf[i], cbias[i], true, true);
         if constexpr (PRE_C) {
 #pragma unroll
-            for (int i = 1; i < TM; i++) epi_prefetch(i, cbuf[i], xbuf[1], cbias[1], true, false);
+            for (int i = EPD; i < TM; i++) epi_prefetch(i, cbuf[i], xbuf[EPD], cbias[EPD], true, false);
         }
     }
     barrier_lds();  // every wave is done with the main loop's LDS, which the epilogue reuses
@@ -988,8 +1227,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
             }
         wave_lds_sync();  // each wave reads back only its own slab
         if constexpr (VEC) {
-            if (i + 1 < TM)
-                epi_prefetch(i + 1, cbuf[cslot(i + 1)], xbuf[(i + 1) & 1], cbias[(i + 1) & 1], !PRE_C, true);
+            if (i + EPD < TM)
+                epi_prefetch(i + EPD, cbuf[cslot(i + EPD)], xbuf[(i + EPD) % NBX], cbias[(i + EPD) % NBX], !PRE_C,
+                             true);
         }
 #pragma unroll
         for (int pass = 0; pass < EPI_PASSES; pass++) {
@@ -1014,10 +1254,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
                     hvec c4 = {}, x4 = {}, rb4 = {};
                     float cbv = 0.0f;
                     if constexpr (HAS_C) c4 = cbuf[cslot(i)][pass][h];
-                    if constexpr (HAS_X) x4 = xbuf[i & 1][pass][h];
+                    if constexpr (HAS_X) x4 = xbuf[i % NBX][pass][h];
                     if constexpr (HAS_BIAS) {
                         rb4 = rbias[h];
-                        cbv = E::ld(cbias[i & 1][pass]);
+                        cbv = E::ld(cbias[i % NBX][pass]);
                     }
                     hvec d4, e4;
 #pragma unroll
@@ -1053,6 +1293,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
             }
         }
         wave_lds_sync();  // slab reads done before the next block row overwrites it
+        // 4-wave tile: keep the next block row's accumulator reads (AGPR ->
+        // VGPR) from being hoisted above this one, which runs out of VGPRs
+        if constexpr (W4) __builtin_amdgcn_sched_barrier(0);
     }
     };  // segment
 

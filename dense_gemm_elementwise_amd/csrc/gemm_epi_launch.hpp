@@ -18,7 +18,9 @@ struct TileCfg {
 };
 
 // The tile configurations compiled into the library (fast path), and the one
-// general-path configuration.  The 64 x 64 tile (small problems, one wave of
+// general-path configuration.  The 256 x 256 tile runs four waves of 128 x 128
+// on the hand-scheduled main loop (mainloop_w4: accumulators in AGPRs, BK = 32
+// stages in a 4-slot ring).  The 64 x 64 tile (small problems, one wave of
 // workgroups or less) has latency-bound stages, so fewer, deeper ones are
 // what counts: BK = 64 (1024^3: 12.0 -> 9.7 us against BK = 32; more stages
 // in the ring did not help), and BK = 128 (kSmallDeep) once K >= 256, where
@@ -28,7 +30,7 @@ struct TileCfg {
 // than four of 32 x 32: 3% at 1024^3, 6% on 256^3.  The 128 x 128 tile
 // likewise runs eight waves of 32 x 64 (2-3% on mid-size grids); its
 // stream-K build keeps four (eight were 2-13% slower there).
-inline constexpr TileCfg kTiles[] = {{256, 256, 64, 2, 4, 2, 16}, {128, 256, 64, 2, 2, 4, 16},
+inline constexpr TileCfg kTiles[] = {{256, 256, 32, 4, 2, 2, 16}, {128, 256, 64, 2, 2, 4, 16},
                                      {256, 128, 64, 2, 4, 2, 16}, {128, 128, 64, 3, 4, 2, 32},
                                      {64, 64, 64, 4, 4, 2, 16}};
 inline constexpr TileCfg kSmallDeep = {64, 64, 128, 4, 4, 2, 16};
@@ -83,7 +85,10 @@ template <int KIND, bool BF = false, int EPI = EPI_AB>
 hipError_t launch_kind(const Params &p, const TileCfg &t, bool vec, hipStream_t stream)
 {
     if (!vec) return GE_LAUNCH(kGeneral, KIND, false);
-    if (t.bm == kTiles[0].bm && t.bn == kTiles[0].bn) return GE_LAUNCH(kTiles[0], KIND, true);
+    // the 256 x 256 tile is built for epilogue tensors of the type of A and B
+    // only (the host gives the others 256 x 128 or 128 x 256)
+    if constexpr (EPI == EPI_AB)
+        if (t.bm == kTiles[0].bm && t.bn == kTiles[0].bn) return GE_LAUNCH(kTiles[0], KIND, true);
     if (t.bm == kTiles[1].bm && t.bn == kTiles[1].bn) return GE_LAUNCH(kTiles[1], KIND, true);
     if (t.bm == kTiles[2].bm && t.bn == kTiles[2].bn) return GE_LAUNCH(kTiles[2], KIND, true);
     if (t.bm == kTiles[3].bm && t.bn == kTiles[3].bn) return GE_LAUNCH(kTiles[3], KIND, true);

@@ -271,17 +271,17 @@ def test_plan_tiles_for_the_workloads():
         "aux_scale_128": (64, 64, 64, 4),
         "aux_scale_1024": (64, 64, 128, 256),
         "lincomb_2400x3232x4096": (128, 256, 64, 19 * 13),
-        "x_acc_8192": (256, 256, 64, 1024),
-        "relu_square_16x2048x2048x1024": (256, 256, 64, 1024),
+        "x_acc_8192": (256, 256, 32, 1024),
+        "relu_square_16x2048x2048x1024": (256, 256, 32, 1024),
         "relu_aux_store_1024": (64, 64, 128, 256),
         "relu_scale_acc_1024": (64, 64, 128, 256),
         "bias_row_col_1024": (64, 64, 128, 256),
-        "relu_scale_acc_8192": (256, 256, 64, 1024),
-        "bias_row_col_8192": (256, 256, 64, 1024),
+        "relu_scale_acc_8192": (256, 256, 32, 1024),
+        "bias_row_col_8192": (256, 256, 32, 1024),
         "lincomb_deep_k_256x256x65536": (64, 64, 128, 16),
-        "gelu_8192": (256, 256, 64, 1024),
+        "gelu_8192": (256, 256, 32, 1024),
         "aux_scale_bf16_1024": (64, 64, 128, 256),     # the tile choice does not depend on the element type
-        "x_acc_bf16_8192": (256, 256, 64, 1024),
+        "x_acc_bf16_8192": (256, 256, 32, 1024),
     }
     want.update({f"{a.lower()}_256": (64, 64, 128, 16) for a in workloads.ACTIVATIONS})
     assert set(want) == set(workloads.WORKLOADS)
@@ -302,7 +302,7 @@ def test_small_tile_k_step_follows_k():
         assert rc == 0 and (cfg["bm"], cfg["bn"], cfg["bk"], cfg["vec"]) == (64, 64, bk, 1), (K, cfg)
     for K in (256, 512, 4096):
         rc, cfg = ge.gemm_epi_plan(1, 8192, 8192, K, P16, P16, P16, None, 0, P16, None)
-        assert rc == 0 and (cfg["bm"], cfg["bn"], cfg["bk"]) == (256, 256, 64), (K, cfg)
+        assert rc == 0 and (cfg["bm"], cfg["bn"], cfg["bk"], cfg["threads"]) == (256, 256, 32, 256), (K, cfg)
         rc, cfg = ge.gemm_epi_plan(1, 1024, 1024, K + 2, P16, P16, P16, None, 0, P16, None)
         assert rc == 0 and cfg["vec"] == 0 and cfg["bk"] == 64, (K, cfg)
 

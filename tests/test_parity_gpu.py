@@ -348,10 +348,12 @@ TAIL_SHAPES = [
 # shapes whose tile choice is 128 x 128 and 256 x 128 (the others are reached above)
 TILE_SHAPES = [(1, 768, 2816, 72), (1, 2304, 2048, 40), (1, 2400, 1032, 24)]
 
-# the 256 x 256 tile with 1, 2, 3 and 5 k stages of 64, the last one ragged,
-# and ragged M and N: its prologue and the DMA waits near the end of K
-BIG_TILE_SHAPES = [(1, 4000, 4000, 8), (1, 4000, 4000, 24), (1, 4000, 4000, 40), (1, 4000, 4000, 72),
-                   (1, 4000, 4000, 104), (1, 4000, 4000, 136), (1, 3000, 5000, 264)]
+# the 256 x 256 tile (k stages of 32 in a 4-slot ring, steps in groups of 4)
+# with 1 to 9 k stages, full and ragged last ones, and ragged M and N: its
+# prologue, the zero-fed ring past the last stage and the group remainders
+BIG_TILE_SHAPES = [(1, 4000, 4000, 8), (1, 4000, 4000, 24), (1, 4000, 4000, 32), (1, 4000, 4000, 40),
+                   (1, 4000, 4000, 72), (1, 4000, 4000, 104), (1, 4000, 4000, 136), (1, 4000, 4000, 200),
+                   (1, 4000, 4000, 248), (1, 3000, 5000, 256), (1, 3000, 5000, 264)]
 
 # the 64 x 64 tile with its 128-deep K step (K >= 256): 4 full stages, a
 # ragged last stage of 8 and of 120, more stages than the ring holds, ragged
@@ -371,17 +373,22 @@ def test_tails_bit_exact(shape):
 
 
 def test_every_tile_configuration_is_exercised():
-    """The shapes above reach all compiled tile configurations of the fast path."""
+    """The shapes above reach all compiled tile configurations of the fast path.
+    The 64 x 64 x 128 tile has two LDS rings: 4 stages, or 2 when the grid
+    has more tiles than the 256 compute units (the host's rule), so the ring
+    is told apart by the workgroup count."""
     seen = set()
     P = 0x7F0000001000
-    shapes = TAIL_SHAPES + TILE_SHAPES + [(2, 200, 136, 264), (1, 300, 520, 136)] + [
+    shapes = TAIL_SHAPES + TILE_SHAPES + DEEP_SMALL_SHAPES + [(2, 200, 136, 264), (1, 300, 520, 136)] + [
         (w.L, w.M, w.N, w.K) for w in workloads.WORKLOADS.values()]
     for (L, M, N, K) in shapes:
         rc, cfg = ge.gemm_epi_plan(L, M, N, K, P, P, P, P, 1, P, P)
         assert rc == 0
         if cfg["vec"]:
-            seen.add((cfg["bm"], cfg["bn"], cfg["bk"]))
-    assert seen == {(256, 256, 64), (128, 256, 64), (256, 128, 64), (128, 128, 64), (64, 64, 64), (64, 64, 128)}, seen
+            ring = "2-stage" if cfg["bk"] == 128 and cfg["workgroups"] > 256 else ""
+            seen.add((cfg["bm"], cfg["bn"], cfg["bk"], ring))
+    assert seen == {(256, 256, 32, ""), (128, 256, 64, ""), (256, 128, 64, ""), (128, 128, 64, ""), (64, 64, 64, ""),
+                    (64, 64, 128, ""), (64, 64, 128, "2-stage")}, seen
 
 
 def test_identity_and_zero_closed_forms_on_gpu():
