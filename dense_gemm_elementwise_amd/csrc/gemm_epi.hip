@@ -123,6 +123,9 @@ bool use_fast_path(int64_t M, int64_t N, int64_t K, const Operands &o, int kind)
     // 32-bit buffer offsets: one batch entry of A or B must span < 2 GiB
     const int64_t lim = (int64_t)1 << 31;
     if (M * K * 2 >= lim - 64 || K * N * 2 >= lim - 64) return false;
+    // the epilogue addresses one tile's rows (at most 256) of an epilogue
+    // tensor (at most 4-byte elements) below the parked offset 2^31 - 16
+    if (256 * N * 4 >= lim - 64) return false;
     return true;
 }
 

@@ -92,6 +92,7 @@ typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 #define GE_LDS(T) __attribute__((address_space(3))) T
 
@@ -691,6 +692,39 @@ __device__ __forceinline__ void mainloop_w4(f32x4 (&acc)[8][8], const _Float16 *
 }
 
 // ---------------------------------------------------------------------------
+// Range-checked buffer loads and stores of the fast-path epilogue.  A lane
+// whose element lies past the descriptor's record count reads zeros and its
+// store is dropped by the buffer unit, so the epilogue needs no per-lane
+// branch: with branches the compiler's wait-count pass lost track of the
+// loads in flight and waited for all of them before every store.  AUX = 2
+// marks the access non-temporal.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t epi_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+template <typename V, int AUX>
+__device__ __forceinline__ V buf_load(__amdgpu_buffer_rsrc_t r, int off)
+{
+    if constexpr (sizeof(V) == 16)
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
+    else if constexpr (sizeof(V) == 8)
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX));
+    else if constexpr (sizeof(V) == 4)
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX));
+    else
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, AUX));
+}
+template <typename V, int AUX>
+__device__ __forceinline__ void buf_store(V v, __amdgpu_buffer_rsrc_t r, int off)
+{
+    if constexpr (sizeof(V) == 16)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, off, 0, AUX);
+    else
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, v), r, off, 0, AUX);
+}
+
+// ---------------------------------------------------------------------------
 // The kernel.  VEC = fast path (16-byte global->LDS DMA, 8-byte epilogue
 // vectors); otherwise every global access is element-wise and guarded and
 // LDS is filled through registers.
@@ -1146,13 +1180,26 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     // panels (16-batch RELU_SQUARE 215 -> 183 us, 8192^3 LINCOMB_X_ACC -1%).
     // With two elementwise inputs (C and X) the loads are non-temporal too
     // (another -1%); with C alone that measured 5% slower than plain loads.
-    auto ld_epi = [](const et *q) {
-        if constexpr (HAS_X)
-            return __builtin_nontemporal_load((const hvec *)q);
-        else
-            return *(const hvec *)q;
+    //
+    // The fast path addresses the tile's rows of each epilogue tensor through
+    // a buffer descriptor whose record count ends at row min(M, m0 + BM):
+    // rows past M are out of range by construction, and a lane whose columns
+    // lie past N gets the parked offset (N % 8 == 0: a lane's columns are all
+    // in or all out).  The host keeps BM * N * 4 bytes below the parked offset.
+    constexpr int LD_AUX = HAS_X ? 2 : 0;
+    const int rows_here = min(M - m0, BM);
+    const int64_t tbase = mn_base + (int64_t)m0 * N;  // element offset of the tile's first row
+    const uint32_t ebytes = (uint32_t)rows_here * (uint32_t)N * (uint32_t)sizeof(et);
+    const __amdgpu_buffer_rsrc_t rC = epi_rsrc(pC + tbase, ebytes), rX = epi_rsrc(pX + tbase, ebytes);
+    const __amdgpu_buffer_rsrc_t rD = epi_rsrc(pD + tbase, ebytes), rAux = epi_rsrc(pAux + tbase, ebytes);
+    const __amdgpu_buffer_rsrc_t rAcc = epi_rsrc(p.acc_out + tbase, (uint32_t)rows_here * (uint32_t)N * 4u);
+    // byte offset of (slab i, pass, column group h) within the tile's rows, or parked
+    auto epi_off = [&](int i, int pass, int h, int es) {
+        const int gn = n0 + wn * WN + lane_col(h);
+        const int off = ((wm * WM + i * SLAB + lane_row(pass)) * N + gn) * es;
+        const int out = -(int)(gn >= N);  // all ones past N (a mask, not a branch)
+        return (off & ~out) | ((int)0x7FFFFFF0 & out);
     };
-    auto st_epi = [](et *q, hvec v) { __builtin_nontemporal_store(v, (hvec *)q); };
     // C of every slab is loaded at once when the epilogue starts (the operand
     // fragment registers are free by then): more loads in flight.  X and the
     // column bias go EPD slabs ahead, and so does C when it is fp32 (all of it
@@ -1169,25 +1216,23 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     et cbias[NBX][BP];
     auto cslot = [](int i) { return PRE_C ? i : i % NBX; };
     hvec rbias[EPI_GROUPS];
+    const __amdgpu_buffer_rsrc_t rcb = epi_rsrc(pcb, (uint32_t)M * sizeof(et));
+    const __amdgpu_buffer_rsrc_t rrb = epi_rsrc(prb, (uint32_t)N * sizeof(et));
     // loads slab i's C (with_c) and its X and column bias (with_x)
     auto epi_prefetch = [&](int i, hvec (&cb)[CP][EPI_GROUPS], hvec (&xb)[XP][EPI_GROUPS], et (&colb)[BP],
                             bool with_c, bool with_x) {
 #pragma unroll
         for (int pass = 0; pass < EPI_PASSES; pass++) {
             const int gm = m0 + wm * WM + i * SLAB + lane_row(pass);
-            if constexpr (HAS_BIAS)
-                if (with_x) colb[pass] = gm < M ? pcb[gm] : (et)0.0f;
+            if constexpr (HAS_BIAS)  // one value per row, zero past M
+                if (with_x) colb[pass] = buf_load<et, 0>(rcb, gm * (int)sizeof(et));
 #pragma unroll
             for (int h = 0; h < EPI_GROUPS; h++) {
-                const int scol = lane_col(h);
-                const int gn = n0 + wn * WN + scol;
-                if (scol < WN && gm < M && gn < N) {
-                    const int64_t o = mn_base + (int64_t)gm * N + gn;
-                    if constexpr (HAS_C)
-                        if (with_c) cb[pass][h] = ld_epi(pC + o);
-                    if constexpr (HAS_X)
-                        if (with_x) xb[pass][h] = ld_epi(pX + o);
-                }
+                const int off = epi_off(i, pass, h, (int)sizeof(et));
+                if constexpr (HAS_C)
+                    if (with_c) cb[pass][h] = buf_load<hvec, LD_AUX>(rC, off);
+                if constexpr (HAS_X)
+                    if (with_x) xb[pass][h] = buf_load<hvec, LD_AUX>(rX, off);
             }
         }
     };
@@ -1197,9 +1242,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
         if constexpr (HAS_BIAS) {
 #pragma unroll
             for (int h = 0; h < EPI_GROUPS; h++) {
-                const int scol = lane_col(h);
-                const int gn = n0 + wn * WN + scol;
-                rbias[h] = (scol < WN && gn < N) ? *(const hvec *)(prb + gn) : hvec{};
+                const int gn = n0 + wn * WN + lane_col(h);
+                rbias[h] = buf_load<hvec, 0>(rrb, gn < N ? gn * (int)sizeof(et) : (int)0x7FFFFFF0);
             }
         }
 #pragma unroll
@@ -1247,10 +1291,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
 #pragma unroll
                     for (int e = 0; e < 4; e++) av[4 * q + e] = a4[e];
                 }
-                if (gm >= M) continue;
-                const int64_t o = mn_base + (int64_t)gm * N + gn;
                 if constexpr (VEC) {
-                    if (gn >= N) continue;  // N % 8 == 0: a lane's column group is all in or all out
                     hvec c4 = {}, x4 = {}, rb4 = {};
                     float cbv = 0.0f;
                     if constexpr (HAS_C) c4 = cbuf[cslot(i)][pass][h];
@@ -1267,15 +1308,19 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
                         d4[e] = E::st(d);
                         e4[e] = E::st(a);
                     }
-                    if constexpr (kind_writes_d(KIND)) st_epi(pD + o, d4);
-                    if constexpr (kind_has_aux(KIND)) st_epi(pAux + o, e4);
+                    const int off = epi_off(i, pass, h, (int)sizeof(et));
+                    if constexpr (kind_writes_d(KIND)) buf_store<hvec, 2>(d4, rD, off);
+                    if constexpr (kind_has_aux(KIND)) buf_store<hvec, 2>(e4, rAux, off);
                     if constexpr (kind_has_acc_out(KIND)) {
+                        const int off4 = epi_off(i, pass, h, 4);
 #pragma unroll
                         for (int q = 0; q < CPL / 4; q++)
-                            __builtin_nontemporal_store(f32x4{av[4 * q], av[4 * q + 1], av[4 * q + 2], av[4 * q + 3]},
-                                                        (f32x4 *)(p.acc_out + o + 4 * q));
+                            buf_store<f32x4, 2>(f32x4{av[4 * q], av[4 * q + 1], av[4 * q + 2], av[4 * q + 3]}, rAcc,
+                                                off4 < 0x7FFFFFF0 ? off4 + 16 * q : off4);
                     }
                 } else {
+                    if (gm >= M) continue;
+                    const int64_t o = mn_base + (int64_t)gm * N + gn;
                     const float cbv = HAS_BIAS ? E::ld(pcb[gm]) : 0.0f;
 #pragma unroll
                     for (int e = 0; e < CPL; e++) {
