@@ -424,6 +424,20 @@ __device__ __forceinline__ void dma16(const i32x4 &rsrc, uint32_t lds_addr, int 
         : "s"(m0v), "v"(voffset), "s"(rsrc)
         : "memory", "m0");
 }
+// The same DMA split in two, so that each part can sit in its own gap between
+// MFMAs: m0_set<OFF> writes M0 = base + OFF with one scalar instruction (base
+// uniform, in an SGPR); dma16_issue then loads into LDS at M0.  The M0 write
+// needs one wait state before the load, which the MFMA between them gives;
+// nothing else in the main loop uses M0.
+template <uint32_t OFF>
+__device__ __forceinline__ void m0_set(uint32_t base)
+{
+    asm volatile("s_add_u32 m0, %0, %1" : : "s"(base), "i"(OFF) : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_issue(const i32x4 &rsrc, int voffset)
+{
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voffset), "s"(rsrc) : "memory");
+}
 #pragma clang diagnostic pop
 
 // Waits until at most N of this wave's vector-memory operations are
@@ -479,29 +493,51 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void *p)
 //
 // With one wave per SIMD nothing else covers a stall, so the instruction
 // stream is fixed by hand:
-//  * K is walked in 32-wide stages through a ring of W4_NS slots; stage t+1
-//    is published by one barrier at the start of k step t, and the slot of
-//    stage t, which every wave has read into registers by then, is refilled
-//    with stage t + W4_NS right after it: the DMA has W4_NS - 1 k steps
-//    (about 3k cycles) to land.
-//  * A slots sit in one 64 KB region and B slots in the next, so every LDS
-//    read is one base register plus an immediate offset (16-bit offsets).
+//  * K is walked in k steps of 32.  B arrives in 32-deep stages (32 k-rows
+//    of 512 bytes) through a ring of 4 slots; A in 64-deep chunks (256 rows
+//    of 128 bytes) through a ring of 3 slots.  A DMA instruction moves 1 KB;
+//    its cost goes with the cache lines it touches, so A rows of a full
+//    128-byte line (8 per instruction) cost half of 64-byte rows (16 half
+//    lines), measured as a third of the DMA time of the 32-deep A stages.
+//  * One barrier at the start of k step t publishes what k step t+1 reads
+//    (B stage t+1; A chunk (t+1)/2) and frees what k step t has finished
+//    reading.  Every k step issues 8 DMAs per wave: B stage t+4 into the B
+//    slot of stage t, and half of A chunk (t+5)/2 into the slot of chunk
+//    (t+5)/2 - 3.  Each lands three k steps (about 3k cycles) before it is
+//    read, so one vmcnt value (16: the two newer steps' DMAs) serves every
+//    wait.  Past the last stage the rings are still fed, with zero-record
+//    descriptors, to keep that count.
+//  * A slots sit in [0, 96 KB), B slots in [96 KB, 160 KB); every LDS read is
+//    a base register plus an immediate offset below 64 KB.
 //  * Each k step issues its 64 MFMAs with one memory instruction after every
 //    second one: the 24 operand reads of the next k step (8 A ds_read_b128,
-//    16 B ds_read_b64_tr_b16) and this wave's 8 DMAs of the stage W4_NS
-//    ahead.  The order is pinned with scheduling barriers.
+//    16 B ds_read_b64_tr_b16) and the 8 DMAs.  The order is pinned with
+//    scheduling barriers.  Slots and register buffers repeat every 12 k
+//    steps, which the loop unrolls.
 //  * The MFMAs are inline asm with "+a" accumulator operands: with the
 //    builtins the register allocator moved accumulators between the AGPR
 //    and VGPR files inside the loop.  The hardware does not interlock an
 //    MFMA result against a later non-MFMA reader and the compiler cannot see
-//    inside the asm, so wait states are inserted by hand after the loop.
+//    inside the asm, so wait states are inserted by hand (agpr_fence).
 // ---------------------------------------------------------------------------
-constexpr int W4_BK = 32;
-constexpr int W4_NS = 4;
-constexpr int W4_A_SLOT = 256 * W4_BK * 2;  // 16 KB: 256 rows x 64 bytes
+constexpr int W4_BK = 32;                   // k step, and the B stage depth
+constexpr int W4_NS = 4;                    // B ring slots
+constexpr int W4_NA = 3;                    // A ring slots
+constexpr int W4_A_SLOT = 256 * 64 * 2;     // 32 KB: 256 rows x 128 bytes (64 k)
 constexpr int W4_B_SLOT = W4_BK * 256 * 2;  // 16 KB: 32 k-rows x 512 bytes
-constexpr int W4_B_BASE = W4_NS * W4_A_SLOT;
-constexpr int W4_LDS = W4_NS * (W4_A_SLOT + W4_B_SLOT);
+constexpr int W4_B_BASE = W4_NA * W4_A_SLOT;
+constexpr int W4_LDS = W4_B_BASE + W4_NS * W4_B_SLOT;  // 160 KB
+constexpr int W4_PERIOD = 12;               // k steps after which slots and buffers repeat
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
+}
 
 template <bool BF>
 __device__ __forceinline__ void mfma16_agpr(f32x4 &acc, const half8 &a, const half8 &b)
@@ -539,60 +575,80 @@ __device__ __forceinline__ void mainloop_w4(f32x4 (&acc)[8][8], const _Float16 *
     const int wm = wave >> 1, wn = wave & 1;
     constexpr uint32_t kParked = 0x7FFFFFF0u;
     const uint32_t smem_lds = lds_addr_of(smem);
+    const int kbase = kb * W4_BK;  // first k column of this segment
+    const int nka = (nk + 1) >> 1;  // A chunks
 
-    // DMA: 16 KB of A and 16 KB of B per stage, 1 KB per wave instruction,
-    // 4 + 4 instructions per wave.  A block q of wave w: rows 16 (4q + w) ..
-    // + 15, lane -> row + lane / 4, physical chunk lane % 4.  B block: two
-    // k-rows of 32 chunks.
-    uint32_t a_voff[4], b_voff[4];
-    int a_kcol[4];  // first k column of the lane's A chunk, for the stage that crosses K
+    // DMA offsets.  A half-chunk h (rows 128h..128h+127) is 16 instructions,
+    // 4 per wave: instruction q of wave w fills rows 8 (16h + 4q + w) .. + 7,
+    // lane -> row + lane / 8, physical chunk lane % 8.  B stage: 16
+    // instructions of two 512-byte k-rows, 4 per wave.
+    uint32_t a_voff[2][4], b_voff[4];
+    int a_kcol[2][4];  // first k column of the lane's A chunk, for the chunk that crosses K
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int row = (h * 16 + q * 4 + wave) * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ swz_a<8>(row);
+            const int gm = m0 + row;
+            a_kcol[h][q] = c * 8;
+            a_voff[h][q] = gm < M ? (uint32_t)(gm * K + c * 8) * 2u : kParked;
+        }
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-        const int row = (q * 4 + wave) * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ swz_a<4>(row);
-        const int gm = m0 + row;
-        a_kcol[q] = c * 8;
-        a_voff[q] = gm < M ? (uint32_t)(gm * K + c * 8) * 2u : kParked;
         const int lin = (q * 4 + wave) * 64 + lane;
         const int krow = lin >> 5;
         const int cb = (lin & 31) ^ swz_b<32, 16>(krow);
         const int gn = n0 + cb * 8;
         b_voff[q] = gn < N ? (uint32_t)(krow * N + gn) * 2u : kParked;
     }
-    // One DMA instruction of the stage at k column k0 into ring slot `slot`:
-    // op 0..3 = A, 4..7 = B.  Past the last stage the ring is still fed, with
-    // a zero-record descriptor (the buffer unit writes zeros into the free
-    // slot and touches no memory), so every k step issues the same number of
-    // DMAs and one vmcnt value serves every wait.  Only the last stage can
-    // cross K (A columns past K are the next row's: parked).
     const uint32_t lds_w = (uint32_t)__builtin_amdgcn_readfirstlane((int)(smem_lds + wave * 1024));
-    auto dma_op = [&](int op, int slot, int k0, const i32x4 &ra, const i32x4 &rb) {
-        if (op < 4) {
-            int voff = (int)a_voff[op];
-            if (k0 + W4_BK > K) voff = k0 + a_kcol[op] < K ? voff : (int)kParked;
-            dma16(ra, lds_w + slot * W4_A_SLOT + op * 4096, voff);
-        } else {
-            dma16(rb, lds_w + W4_B_BASE + slot * W4_B_SLOT + (op - 4) * 4096, (int)b_voff[op - 4]);
-        }
-    };
-    auto rsrc_a = [&](int s) {  // stage s (s >= nk: no records)
-        const int k0 = (kb + s) * W4_BK;
-        return make_rsrc(Al + k0, s < nk ? (uint32_t)(((int64_t)M * K - k0) * 2) : 0u);
-    };
+    // descriptors of B stage s and A chunk c (zero records past the end)
     auto rsrc_b = [&](int s) {
-        const int k0 = (kb + s) * W4_BK;
+        const int k0 = kbase + s * W4_BK;
         return make_rsrc(Bl + (int64_t)k0 * N, s < nk ? (uint32_t)((int64_t)(K - k0) * N * 2) : 0u);
     };
+    auto rsrc_a = [&](int c) {
+        const int k0 = kbase + c * 64;
+        return make_rsrc(Al + k0, c < nka ? (uint32_t)(((int64_t)M * K - k0) * 2) : 0u);
+    };
+    // DMA op g of a k step: g < 4: A instruction g of half h of chunk c (k0 its
+    // first column) into A slot sa; g >= 4: B instruction g - 4 into B slot sb.
+    // Only the last chunk can cross K (A columns past K are the next row's:
+    // parked).
+    // A offsets of the last chunk, the only one that can cross K (columns past
+    // K are the next row's: parked)
+    uint32_t a_voff_last[2][4];
+    {
+        const int k0l = kbase + (nka - 1) * 64;
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) a_voff_last[h][q] = k0l + a_kcol[h][q] < K ? a_voff[h][q] : kParked;
+    }
+    // LDS address (M0) of DMA g of a k step: A chunk half h into A slot sa,
+    // B stage into B slot sb
+    auto dma_lds = [](int g, int h, int sa, int sb) {
+        return g < 4 ? (uint32_t)(sa * W4_A_SLOT + (h * 16 + g * 4) * 1024)
+                     : (uint32_t)(W4_B_BASE + sb * W4_B_SLOT + (g - 4) * 4096);
+    };
 
-    // Operand reads.  A block i: lane (li + 16 lg) reads row wm*128 + 16 i + li,
-    // k columns 8 lg..8 lg+7 (one ds_read_b128); the swizzle depends on row
-    // bits 1-2 only, so block i is block 0 + i KB.  B block j: two
-    // ds_read_b64_tr_b16, lane 4e + r of 16-lane group g pointing at k-row
-    // 8 g + 4 h + e, columns 4 r..4 r+3 of the block; h moves 4 k-rows
-    // (+2 KB, same swizzle), j has its own address.
+    // Operand reads.  A block i of k step t: lane (li + 16 lg) reads row
+    // wm*128 + 16 i + li, k columns 8 lg..8 lg+7 of the step's half of the
+    // chunk (logical 16-byte chunk 4 (t & 1) + lg; one ds_read_b128).  The
+    // swizzle depends on row bits 1-3, so block i is block 0 + 2 KB i, and the
+    // step's half flips address bit 6.  B block j: two ds_read_b64_tr_b16,
+    // lane 4e + r of 16-lane group g pointing at k-row 8 g + 4 h + e,
+    // columns 4 r..4 r+3 of the block; h moves 4 k-rows (+2 KB, same
+    // swizzle), j has its own address.
     const int li = lane & 15, lg = lane >> 4, lq = lane & 15;
     const int a_row = wm * 128 + li;
-    const char *a_rd = smem + a_row * 64 + ((lg ^ swz_a<4>(a_row)) * 16);
+    const char *a_rd[W4_NA][2];
+#pragma unroll
+    for (int sl = 0; sl < W4_NA; sl++)
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++)
+            a_rd[sl][kk] = smem + sl * W4_A_SLOT + a_row * 128 + (((kk * 4 + lg) ^ swz_a<8>(a_row)) * 16);
     const char *b_rd[8];
 #pragma unroll
     for (int j = 0; j < 8; j++) {
@@ -600,96 +656,128 @@ __device__ __forceinline__ void mainloop_w4(f32x4 (&acc)[8][8], const _Float16 *
         const int krow = 8 * lg + (lq >> 2);
         b_rd[j] = smem + W4_B_BASE + krow * 512 + (((n >> 3) ^ swz_b<32, 16>(krow)) * 16) + (n & 7) * 2;
     }
-    auto read_a = [&](int slot, int i) {
-        return *(const half8 *)(a_rd + slot * W4_A_SLOT + i * 1024);
-    };
-    auto read_b = [&](int slot, int j, int h) {
+    auto read_a = [&](int sa, int kk, int i) { return *(const half8 *)(a_rd[sa][kk] + i * 2048); };
+    auto read_b = [&](int sb, int j, int h) {
         return __builtin_amdgcn_ds_read_tr16_b64_v4f16(
-            (GE_LDS(fp16x4_t) *)(b_rd[j] + slot * W4_B_SLOT + h * 2048));
+            (GE_LDS(fp16x4_t) *)(b_rd[j] + sb * W4_B_SLOT + h * 2048));
     };
 
     half8 fa[2][8], fb[2][8];
     fp16x4_t fbh[8][2];
+    auto join_b = [&](int P) {
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const half4 lo = __builtin_bit_cast(half4, fbh[j][0]), hi = __builtin_bit_cast(half4, fbh[j][1]);
+            fb[P][j] = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+    };
 
-    // One k step: MFMAs on the fragments in buffer P (stage slot S), operand
-    // reads of slot (S+1) % NS into buffer P^1, DMA of stage `sd` into slot S.
-    // On the last step the reads fetch a slot nobody writes any more into
-    // registers nobody uses: every branch stays outside the pinned sequence.
-    auto kstep = [&](auto S_, auto P_, int sd) {
-        constexpr int S = decltype(S_)::value, P = decltype(P_)::value;
-        constexpr int SN = (S + 1) % W4_NS;
-        const i32x4 ra = rsrc_a(sd), rb = rsrc_b(sd);
-        const int k0dma = (kb + sd) * W4_BK;
+    // One k step t, t % 12 = D (compile time): MFMAs on the fragments in
+    // buffer D % 2; operand reads of step t+1 into the other buffer; the 8
+    // DMAs (B stage t+4, half (t+1) % 2 of A chunk (t+5)/2).  With one wave
+    // per SIMD, only two or three other instructions fit in the shadow of one
+    // MFMA, so the work is spread over the 64 gaps after the MFMAs: the 24
+    // reads in the even gaps 0..46; DMA g takes three odd gaps, 8g+1 (its A
+    // offset), 8g+3 (M0) and 8g+5 (the load).  On the last step the reads
+    // fetch slots nobody writes any more into registers nobody uses: every
+    // branch stays outside the pinned sequence.
+    auto kstep = [&](auto D_, int t) {
+        constexpr int D = decltype(D_)::value;
+        constexpr int P = D & 1;
+        constexpr int SB = D % W4_NS;                  // B slot of step t, refilled with stage t+4
+        constexpr int SBN = (D + 1) % W4_NS;           // B slot of step t+1
+        constexpr int SAN = ((D + 1) >> 1) % W4_NA;    // A slot of step t+1
+        constexpr int KKN = (D + 1) & 1;               // its half of the chunk
+        constexpr int SAD = ((D + 5) >> 1) % W4_NA;    // A slot refilled in this step
+        constexpr int HD = (D + 1) & 1;                // the half refilled
+        const int ca = (t + 5) >> 1;
+        i32x4 ra, rb;  // built in gaps 1 and 33, before their first loads (gaps 5 and 37)
+        bool last_chunk;
+        int dvoff[4];
 #pragma unroll
         for (int m = 0; m < 64; m++) {
             mfma16_agpr<BF>(acc[m >> 3][m & 7], fa[P][m >> 3], fb[P][m & 7]);
             if ((m & 1) == 0) {
-                const int op = m >> 1, g = op >> 2, r = op & 3;
-                if (r == 0)
-                    fa[P ^ 1][g] = read_a(SN, g);
-                else if (r == 1)
-                    fbh[g][0] = read_b(SN, g, 0);
-                else if (r == 2)
-                    fbh[g][1] = read_b(SN, g, 1);
-                else
-                    dma_op(g, S, k0dma, ra, rb);
+                if (m < 48) {
+                    const int op = m >> 1, g = op / 3, r = op % 3;
+                    if (r == 0)
+                        fa[P ^ 1][g] = read_a(SAN, KKN, g);
+                    else
+                        fbh[g][r - 1] = read_b(SBN, g, r - 1);
+                }
+            } else {
+                const int g = m >> 3, ph = (m & 7) >> 1;  // ph 0: offset, 1: M0, 2: load
+                if (m == 1) {
+                    ra = rsrc_a(ca);
+                    last_chunk = ca == nka - 1;
+                }
+                if (m == 33) rb = rsrc_b(t + W4_NS);
+                if (ph == 0 && g < 4) dvoff[g] = (int)(last_chunk ? a_voff_last[HD][g] : a_voff[HD][g]);
+                if (ph == 1)
+                    static_for<8>([&](auto G_) {
+                        constexpr int gg = decltype(G_)::value;
+                        constexpr uint32_t OFF = gg < 4 ? (uint32_t)(SAD * W4_A_SLOT + (HD * 16 + gg * 4) * 1024)
+                                                        : (uint32_t)(W4_B_BASE + SB * W4_B_SLOT + (gg - 4) * 4096);
+                        if (gg == g) m0_set<OFF>(lds_w);
+                    });
+                if (ph == 2) dma16_issue(g < 4 ? ra : rb, g < 4 ? dvoff[g] : (int)b_voff[g - 4]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const half4 lo = __builtin_bit_cast(half4, fbh[j][0]), hi = __builtin_bit_cast(half4, fbh[j][1]);
-            fb[P ^ 1][j] = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
+        join_b(P ^ 1);
     };
 
-    // prologue: stages 0..NS-1 in flight (zero-record past nk), stage 0
-    // published and read into buffer 0
+    // prologue, as virtual steps -5..-1 of the same pattern: A chunk 0 half 0;
+    // then B stages 0..3 with A chunk 0 half 1, chunk 1, chunk 2 half 0
+    {
+        const i32x4 ra0 = rsrc_a(0), ra1 = rsrc_a(1), ra2 = rsrc_a(2);
+        auto a_off = [&](int c, int h, int g) { return (int)(c == nka - 1 ? a_voff_last[h][g] : a_voff[h][g]); };
 #pragma unroll
-    for (int s = 0; s < W4_NS; s++) {
-        const i32x4 ra = rsrc_a(s), rb = rsrc_b(s);
-        const int k0 = (kb + s) * W4_BK;
+        for (int g = 0; g < 4; g++) dma16(ra0, lds_w + dma_lds(g, 0, 0, 0), a_off(0, 0, g));
 #pragma unroll
-        for (int op = 0; op < 8; op++) dma_op(op, s, k0, ra, rb);
+        for (int s = 0; s < W4_NS; s++) {
+            const i32x4 rb = rsrc_b(s);
+            const int ca = (s + 1) >> 1, h = (s + 1) & 1;
+            const i32x4 &ra = ca == 0 ? ra0 : (ca == 1 ? ra1 : ra2);
+#pragma unroll
+            for (int g = 0; g < 8; g++)
+                dma16(g < 4 ? ra : rb, lds_w + dma_lds(g, h, ca, s), g < 4 ? a_off(ca, h, g) : (int)b_voff[g - 4]);
+        }
     }
-    wait_vmcnt<(W4_NS - 1) * 8>();
+    wait_vmcnt<24>();  // B stage 0 and A chunk 0 (the 24 DMAs after them may fly)
     barrier_lds();
 #pragma unroll
-    for (int i = 0; i < 8; i++) fa[0][i] = read_a(0, i);
+    for (int i = 0; i < 8; i++) fa[0][i] = read_a(0, 0, i);
 #pragma unroll
     for (int j = 0; j < 8; j++) {
         fbh[j][0] = read_b(0, j, 0);
         fbh[j][1] = read_b(0, j, 1);
     }
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-        const half4 lo = __builtin_bit_cast(half4, fbh[j][0]), hi = __builtin_bit_cast(half4, fbh[j][1]);
-        fb[0][j] = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
+    join_b(0);
     agpr_fence(acc);  // the accumulators' zeroing (VALU) before the first MFMA reads them
 
-    // Step t: its own DMA of stage t+1 has landed (the NS-2 stages after it
-    // may still be in flight), then the barrier publishes stage t+1 and frees
-    // slot t; the last step has nothing to publish.  Steps go in groups of
-    // NS, so that slots and register buffers are compile-time.
-    static_assert(W4_NS == 4, "the k-step unrolling assumes a 4-slot ring of even length");
+    // Step t: the DMAs of step t-3 have landed (the 16 of the two newer steps
+    // may still be in flight), then the barrier publishes what step t+1 reads
+    // and frees what step t has read; the last step has nothing to publish.
     auto step = [&](auto D_, int t) {
-        constexpr int d = decltype(D_)::value;
         if (t + 1 < nk) {
-            wait_vmcnt<(W4_NS - 2) * 8>();
+            wait_vmcnt<16>();
             barrier_lds();
         }
-        kstep(std::integral_constant<int, d>{}, std::integral_constant<int, d & 1>{}, t + W4_NS);
+        kstep(D_, t);
     };
 #pragma unroll 1
-    for (int t = 0; t < nk; t += W4_NS) {
+    for (int t = 0; t < nk; t += W4_PERIOD) {
         step(std::integral_constant<int, 0>{}, t);
-        if (t + 1 < nk) step(std::integral_constant<int, 1>{}, t + 1);
-        if (t + 2 < nk) step(std::integral_constant<int, 2>{}, t + 2);
-        if (t + 3 < nk) step(std::integral_constant<int, 3>{}, t + 3);
+#define GE_W4_STEP(d) \
+        if (t + d < nk) step(std::integral_constant<int, d>{}, t + d);
+        GE_W4_STEP(1) GE_W4_STEP(2) GE_W4_STEP(3) GE_W4_STEP(4) GE_W4_STEP(5) GE_W4_STEP(6)
+        GE_W4_STEP(7) GE_W4_STEP(8) GE_W4_STEP(9) GE_W4_STEP(10) GE_W4_STEP(11)
+#undef GE_W4_STEP
     }
     agpr_fence(acc);  // the last MFMAs' results before the epilogue reads them
 }
+
 
 // ---------------------------------------------------------------------------
 // Range-checked buffer loads and stores of the fast-path epilogue.  A lane
@@ -757,12 +845,13 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     constexpr int SLAB = MI;
     constexpr int EPI_LD = WN + (MI == 32 ? 8 : 4);
     constexpr int EPI_BYTES = NW * SLAB * EPI_LD * 4;
-    constexpr int SMEM = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
-    static_assert(SMEM <= 160 * 1024, "LDS budget");
     // the 4-wave 256 x 256 configuration runs the hand-scheduled main loop
     constexpr bool W4 = NW == 4 && BM == 256 && BN == 256 && BK == W4_BK && NSTAGES == W4_NS && MI == 16 && VEC &&
                         !SK;
-    static_assert(!W4 || MAIN_BYTES == W4_LDS, "4-wave ring layout");
+    constexpr int SMEM0 = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
+    constexpr int SMEM = W4 ? (W4_LDS > EPI_BYTES ? W4_LDS : EPI_BYTES) : SMEM0;
+    static_assert(SMEM <= 160 * 1024, "LDS budget");
+
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
     const int tid = threadIdx.x;
