@@ -57,7 +57,8 @@ EXPORTS = ("gemm_epi_run", "gemm_epi_run_ext", "gemm_epi_run_typed", "gemm_epi_r
            "gemm_epi_last_hip_error", "gemm_epi_plan", "gemm_epi_plan_ext", "gemm_epi_plan_ws")
 
 
-class GemmEpiError(RuntimeError):
+class GemmEpiError(ValueError):
+    """A nonzero status of the C ABI, with its status string."""
     def __init__(self, status, message):
         super().__init__(f"{STATUS.get(status, status)}: {message}")
         self.status = status

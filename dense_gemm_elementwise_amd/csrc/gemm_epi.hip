@@ -139,8 +139,16 @@ struct SkPlan {
     TileCfg t{};
     int groups = 0;
     int64_t tiles = 0, units = 0;
-    size_t workspace = 0;  // bytes: partial slots, then one counter per tile
+    size_t workspace = 0;  // bytes: the counter block, then the partial slots
 };
+
+// Workspace layout of a split, the same for every plan: one int32 counter
+// per tile at offset 0, in a block of fixed capacity (a split covers at most
+// kSkMaxTiles tiles), then 2 partial-sum slots per workgroup.  A workspace
+// that is reused for a shape with another workgroup count therefore finds
+// its counters where the previous call left them at zero.
+constexpr int64_t kSkMaxTiles = 4096;
+constexpr size_t kSkCounterBytes = (size_t)kSkMaxTiles * 4;
 
 size_t sk_partials_bytes(const TileCfg &t, int groups) { return (size_t)2 * groups * t.bm * t.bn * 4; }
 
@@ -159,7 +167,7 @@ size_t sk_partials_bytes(const TileCfg &t, int groups) { return (size_t)2 * grou
 // measured on 512..1024-square tiles with K of 8192..65536.  Fewer
 // workgroups mean more k stages each but fewer partial sums per tile, so the
 // count is searched.  A split is taken only when it wins clearly (by 15%).
-SkPlan plan_stream_k(int64_t L, int64_t M, int64_t N, int64_t K, bool vec)
+SkPlan plan_stream_k(int64_t L, int64_t M, int64_t N, int64_t K, bool vec, int max_groups = kNumCUs)
 {
     constexpr double kFixedStages = 8.5, kPerContributorStages = 1.6;
     constexpr double kStageSeconds = 0.76e-6, kOperandBytesPerSecond = 5.5e12;
@@ -174,9 +182,10 @@ SkPlan plan_stream_k(int64_t L, int64_t M, int64_t N, int64_t K, bool vec)
         const int64_t tiles = L * ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
         const int64_t nk = (K + t.bk - 1) / t.bk;
         const int64_t units = tiles * nk;
-        if (tiles > INT32_MAX || units < 2) continue;
+        if (tiles > kSkMaxTiles || units < 2) continue;
         const double stage = (double)t.bk * t.bm * t.bn / tile_efficiency(t.bm, t.bn);
         for (int groups = kNumCUs; groups >= 1; groups /= 2) {
+            if (groups > max_groups) continue;
             if (groups > units) continue;
             const int64_t per = (units + groups - 1) / groups;
             const bool split = per < nk || units % groups != 0 || (units / groups) % nk != 0;
@@ -193,7 +202,7 @@ SkPlan plan_stream_k(int64_t L, int64_t M, int64_t N, int64_t K, bool vec)
                 best.groups = groups;
                 best.tiles = tiles;
                 best.units = units;
-                best.workspace = sk_partials_bytes(t, groups) + (size_t)tiles * 4;
+                best.workspace = kSkCounterBytes + sk_partials_bytes(t, groups);
             }
         }
     }
@@ -206,8 +215,8 @@ void set_sk_params(Params &p, const SkPlan &sk, void *workspace)
 {
     p.sk_q = sk.units / sk.groups;
     p.sk_r = sk.units % sk.groups;
-    p.partials = (float *)workspace;
-    p.counters = (int *)((char *)workspace + sk_partials_bytes(sk.t, sk.groups));
+    p.counters = (int *)workspace;
+    p.partials = (float *)((char *)workspace + kSkCounterBytes);
 }
 
 // The elementwise stage of the unfused composition.
@@ -215,11 +224,9 @@ template <int KIND, bool BF>
 hipError_t launch_epilogue(const EpiParams &q, bool vec, hipStream_t stream)
 {
     const int64_t blocks = q.rows < 8192 ? q.rows : 8192;
-    if (vec)
-        hipLaunchKernelGGL((epilogue_kernel<KIND, true, BF>), dim3((unsigned)blocks), dim3(256), 0, stream, q);
-    else
-        hipLaunchKernelGGL((epilogue_kernel<KIND, false, BF>), dim3((unsigned)blocks), dim3(256), 0, stream, q);
-    return hipGetLastError();
+    void *args[] = {(void *)&q};
+    const void *fn = vec ? (const void *)&epilogue_kernel<KIND, true, BF> : (const void *)&epilogue_kernel<KIND, false, BF>;
+    return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, 0, stream);
 }
 
 }  // namespace

@@ -70,9 +70,12 @@ template <int BM, int BN, int BK, int NS, int WGM, int WGN, int MI, int KIND, bo
           bool BF = false, int EPI = EPI_AB>
 hipError_t launch_one(const Params &p, hipStream_t stream, int grid)
 {
-    hipLaunchKernelGGL((gemm_epi_kernel<BM, BN, BK, NS, WGM, WGN, MI, KIND, VEC, SK, BF, EPI>), dim3(grid),
-                       dim3(64 * WGM * WGN), 0, stream, p);
-    return hipGetLastError();
+    // hipLaunchKernel reports this launch's own status (hipGetLastError would
+    // also report, and clear, an error an earlier unrelated call left)
+    Params arg = p;
+    void *args[] = {(void *)&arg};
+    return hipLaunchKernel((const void *)&gemm_epi_kernel<BM, BN, BK, NS, WGM, WGN, MI, KIND, VEC, SK, BF, EPI>,
+                           dim3(grid), dim3(64 * WGM * WGN), args, 0, stream);
 }
 
 #define GE_LAUNCH(T, KIND, VEC) \
@@ -119,7 +122,8 @@ hipError_t launch_sk_bf16(int kind, const Params &p, int groups, hipStream_t str
 hipError_t launch_acc_store_bf16(const Params &p, const TileCfg &t, bool vec, hipStream_t stream);
 // The fused call with fp32 epilogue tensors (C, X, the biases, D, Aux), A and
 // B fp16 (gemm_epi_f32e.hip) or bfloat16 (gemm_epi_bf16_f32e.hip); and with
-// the other 16-bit type for the epilogue tensors (gemm_epi_mixed16.hip).
+// the other 16-bit type for the epilogue tensors (gemm_epi_f16_bf16e.hip,
+// gemm_epi_bf16_f16e.hip).
 hipError_t launch_fused_f16_f32e(int kind, const Params &p, const TileCfg &t, bool vec, hipStream_t stream);
 hipError_t launch_fused_bf16_f32e(int kind, const Params &p, const TileCfg &t, bool vec, hipStream_t stream);
 hipError_t launch_fused_f16_bf16e(int kind, const Params &p, const TileCfg &t, bool vec, hipStream_t stream);

@@ -296,7 +296,11 @@ int gemm_epi_run_unfused_typed(int64_t L, int64_t M, int64_t N, int64_t K, const
  *                    gemm_epi_plan_ws reports in out[6] (0 when no split is
  *                    planned: NULL is then accepted); owned by the caller.  It
  *                    must be zero-filled before its first use (e.g. one
- *                    hipMemset); every call leaves it ready for the next.
+ *                    hipMemset); every call leaves it ready for the next,
+ *                    whatever the shape: the per-tile counters sit in a
+ *                    block of fixed size at its start (16 KiB, one int32 per
+ *                    tile of a split; at most 4096 tiles are split), the
+ *                    partial sums after it.
  *   workspace_bytes  its size in bytes.
  *
  * Calls that share one workspace must not overlap in time (two streams

@@ -204,13 +204,14 @@ def test_stream_k_plan_and_workspace_checks():
     # few tiles, long K: split over 128 x 128 tiles.  The workgroup count is
     # searched: a shorter K per workgroup against more partial sums per tile
     # (for 256 x 256 x 65536, 128 workgroups measured fastest of 16..256).  The
-    # workspace holds two partial slots per workgroup plus a counter per tile.
+    # workspace holds a fixed 16 KiB counter block (one int32 per tile, at most
+    # 4096 split tiles) and then two partial slots per workgroup.
     rc, cfg = plan_ws(1, 256, 256, 65536)
     assert rc == 0 and (cfg["bm"], cfg["bn"], cfg["workgroups"]) == (128, 128, 128)
-    assert cfg["workspace_bytes"] == 2 * 128 * 128 * 128 * 4 + 4 * 4
+    assert cfg["workspace_bytes"] == 16384 + 2 * 128 * 128 * 128 * 4
     rc, cfg = plan_ws(1, 256, 256, 16384)
     assert rc == 0 and (cfg["bm"], cfg["bn"], cfg["workgroups"]) == (128, 128, 64)
-    assert cfg["workspace_bytes"] == 2 * 64 * 128 * 128 * 4 + 4 * 4
+    assert cfg["workspace_bytes"] == 16384 + 2 * 64 * 128 * 128 * 4
     for shape in ((1, 200, 304, 12000), (2, 128, 384, 8192), (1, 512, 512, 8192)):
         rc, cfg = plan_ws(*shape)
         assert rc == 0 and cfg["workspace_bytes"] > 0, shape
@@ -224,7 +225,7 @@ def test_stream_k_plan_and_workspace_checks():
         assert rc == rc0 == 0 and cfg["workspace_bytes"] == 0
         assert all(cfg[k] == cfg0[k] for k in cfg0), shape
     # a split call without (enough) workspace is refused before any launch
-    need = 2 * 64 * 128 * 128 * 4 + 4 * 4
+    need = 16384 + 2 * 64 * 128 * 128 * 4
     args = (1, 256, 256, 16384, P16, P16, P16, None, None, None, SC, 0, P16, None, None)
     assert ge.gemm_epi_run_ws(*args, None, need, None) == 7
     assert ge.gemm_epi_run_ws(*args, P16, need - 1, None) == 7
@@ -348,3 +349,13 @@ def test_c_program_builds_against_the_header(tmp_path):
     r = subprocess.run(c_abi_build.command(out), capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     assert "warning" not in r.stderr, r.stderr
+
+
+def test_status_errors_are_value_errors_with_the_status_string():
+    """A nonzero status surfaces from the Python wrapper as a ValueError
+    carrying the library's status string (the wrapper the boundary
+    specifies; the tutorial's failing calls raise)."""
+    assert issubclass(ge.GemmEpiError, ValueError)
+    e = ge.GemmEpiError(7, ge.gemm_epi_status_string(7))
+    assert isinstance(e, ValueError) and e.status == 7
+    assert "GEMM_EPI_ERR_WORKSPACE" in str(e) and ge.gemm_epi_status_string(7) in str(e)

@@ -55,9 +55,13 @@ def workspace(cfg):
     return torch.zeros(cfg["workspace_bytes"], dtype=torch.uint8, device="cuda:0")
 
 
+# the per-tile counters sit at the start of the workspace, in a block of fixed
+# size whatever the plan (include/gemm_epi.h, gemm_epi_run_ws)
+SK_COUNTER_BYTES = 16384
+
+
 def counters_are_zero(ws, cfg):
-    tiles_bytes = cfg["workspace_bytes"] - 2 * cfg["workgroups"] * cfg["bm"] * cfg["bn"] * 4
-    return bool((ws[-tiles_bytes:] == 0).all())
+    return bool((ws[:SK_COUNTER_BYTES] == 0).all())
 
 
 # shapes with few tiles and a long K (the planner splits them): ragged M and N
@@ -140,3 +144,24 @@ def test_deep_k_workload():
     ref = oracle_full(p, w.kind, w.alpha, w.beta, w.s3, want64=True)
     got = run_ws(p, w.kind, w.alpha, w.beta, w.s3, ws)[0]
     assert_close(got["D"], ref["D64"], "deep-K D")
+
+
+def test_one_workspace_serves_plans_with_different_workgroup_counts():
+    """A workspace reused across shapes whose splits use different workgroup
+    counts (so different partial-slot areas): each call must find its
+    counters at zero and stay bit-exact against the oracle."""
+    kind = "AUX_SCALE"
+    a, b, s = KIND_SCALARS[kind]
+    shapes = [(1, 512, 512, 8192), (1, 256, 256, 16384), (1, 512, 512, 8192)]
+    cfgs = [plan(sh, kind) for sh in shapes]
+    assert len({c["workgroups"] for c in cfgs}) > 1, cfgs
+    ws = torch.zeros(max(c["workspace_bytes"] for c in cfgs), dtype=torch.uint8, device="cuda:0")
+    for sh, cfg in zip(shapes, cfgs):
+        L, M, N, K = sh
+        log(f"[stream-k] shared workspace shape={sh} workgroups={cfg['workgroups']}")
+        p = workloads.make_problem(L, M, N, K, kind, init="small_int", seed=M + K)
+        ref = oracle_ref(p, kind, a, b, s, exact=True)
+        got = run_ws(p, kind, a, b, s, ws)[0]
+        assert counters_are_zero(ws, cfg)
+        for name in got:
+            assert_output(got[name], ref, name, kind, True, f"shared workspace {sh} {name}")
