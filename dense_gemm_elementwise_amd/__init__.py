@@ -9,11 +9,11 @@ include/gemm_epi.h); this package only marshals arguments.
 from .binding import (ACTIVATIONS, DTYPES, EXPORTS, HAS_ACC, HAS_AUX, KINDS, READS_BIAS, READS_C, READS_X,
                       GemmEpiError, gemm_epi_last_hip_error, gemm_epi_plan, gemm_epi_plan_ext, gemm_epi_plan_ws,
                       gemm_epi_run, gemm_epi_run_ext, gemm_epi_run_mixed, gemm_epi_run_typed, gemm_epi_run_unfused,
-                      gemm_epi_run_unfused_typed, gemm_epi_run_ws, gemm_epi_run_ws_typed, gemm_epi_status_string, lib,
-                      run)
+                      gemm_epi_run_unfused_typed, gemm_epi_run_ws, gemm_epi_run_ws_static, gemm_epi_run_ws_typed,
+                      gemm_epi_status_string, lib, run)
 
 __all__ = ["run", "gemm_epi_run", "gemm_epi_run_ext", "gemm_epi_run_typed", "gemm_epi_run_mixed",
-           "gemm_epi_run_unfused", "gemm_epi_run_unfused_typed", "gemm_epi_run_ws", "gemm_epi_run_ws_typed",
+           "gemm_epi_run_unfused", "gemm_epi_run_unfused_typed", "gemm_epi_run_ws", "gemm_epi_run_ws_typed", "gemm_epi_run_ws_static",
            "gemm_epi_plan_ws", "gemm_epi_plan", "gemm_epi_plan_ext", "gemm_epi_status_string",
            "gemm_epi_last_hip_error", "lib", "KINDS", "HAS_AUX", "READS_X", "READS_C", "READS_BIAS", "HAS_ACC",
            "GemmEpiError", "EXPORTS", "ACTIVATIONS", "DTYPES"]

@@ -54,7 +54,8 @@ DTYPES = {"f16": 0, "bf16": 1, "f32": 2}
 # every function include/gemm_epi.h declares
 EXPORTS = ("gemm_epi_run", "gemm_epi_run_ext", "gemm_epi_run_typed", "gemm_epi_run_mixed", "gemm_epi_run_ws",
            "gemm_epi_run_unfused", "gemm_epi_run_ws_typed", "gemm_epi_run_unfused_typed", "gemm_epi_status_string",
-           "gemm_epi_last_hip_error", "gemm_epi_plan", "gemm_epi_plan_ext", "gemm_epi_plan_ws")
+           "gemm_epi_last_hip_error", "gemm_epi_plan", "gemm_epi_plan_ext", "gemm_epi_plan_ws",
+           "gemm_epi_run_ws_static")
 
 
 class GemmEpiError(ValueError):
@@ -102,6 +103,9 @@ def lib():
     L.gemm_epi_run_ws_typed.restype = ctypes.c_int
     L.gemm_epi_run_ws_typed.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_float),
                                         ctypes.c_int, vp, vp, vp, vp, ctypes.c_size_t, ctypes.c_int, vp]
+    L.gemm_epi_run_ws_static.restype = ctypes.c_int
+    L.gemm_epi_run_ws_static.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_float),
+                                         ctypes.c_int, vp, vp, vp, ctypes.c_int, vp]
     L.gemm_epi_plan_ws.restype = ctypes.c_int
     L.gemm_epi_plan_ws.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
                                    ctypes.POINTER(i64)]
@@ -213,6 +217,16 @@ def gemm_epi_run_ws_typed(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, e
     return lib().gemm_epi_run_ws_typed(int(L), int(M), int(N), int(K), A, B, C, X, row_bias, col_bias, sc,
                                        _kind_id(epilogue_kind), D, Aux, acc_out, workspace, int(workspace_bytes),
                                        _dtype_id(dtype), stream)
+
+
+def gemm_epi_run_ws_static(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilogue_kind, D, Aux, acc_out,
+                           dtype, stream) -> int:
+    """Pointer-level call of gemm_epi_run_ws_static: gemm_epi_run_ws_typed
+    with its split's scratch in the library's per-device static array (no
+    workspace argument; allocates nothing)."""
+    sc = (ctypes.c_float * 3)(*[float(v) for v in scalars]) if scalars is not None else None
+    return lib().gemm_epi_run_ws_static(int(L), int(M), int(N), int(K), A, B, C, X, row_bias, col_bias, sc,
+                                        _kind_id(epilogue_kind), D, Aux, acc_out, _dtype_id(dtype), stream)
 
 
 def gemm_epi_plan_ws(L, M, N, K, A, B, C, X, row_bias, col_bias, epilogue_kind, D, Aux, acc_out):

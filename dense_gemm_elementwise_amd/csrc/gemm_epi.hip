@@ -6,6 +6,7 @@
 // queues work and the checks run without a GPU.
 #include <hip/hip_runtime.h>
 #include <algorithm>
+#include <mutex>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -138,7 +139,7 @@ struct SkPlan {
     bool on = false;
     TileCfg t{};
     int groups = 0;
-    int64_t tiles = 0, units = 0;
+    int64_t tiles = 0, units = 0, K = 0;
     size_t workspace = 0;  // bytes: the counter block, then the partial slots
 };
 
@@ -203,6 +204,7 @@ SkPlan plan_stream_k(int64_t L, int64_t M, int64_t N, int64_t K, bool vec, int m
                 best.tiles = tiles;
                 best.units = units;
                 best.workspace = kSkCounterBytes + sk_partials_bytes(t, groups);
+                best.K = K;
             }
         }
     }
@@ -227,6 +229,92 @@ hipError_t launch_epilogue(const EpiParams &q, bool vec, hipStream_t stream)
     void *args[] = {(void *)&q};
     const void *fn = vec ? (const void *)&epilogue_kernel<KIND, true, BF> : (const void *)&epilogue_kernel<KIND, false, BF>;
     return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, 0, stream);
+}
+
+// Launches the planned stream-K split of a checked call on `workspace`
+// (counters at offset 0, zero between calls; partial sums after them).
+int launch_split(int64_t L, int64_t M, int64_t N, const Operands &o, const float *scalars, int kind,
+                 const SkPlan &sk, void *workspace, int dtype, hipStream_t s)
+{
+    Params p = {};
+    p.A = (const _Float16 *)o.A;
+    p.B = (const _Float16 *)o.B;
+    p.C = (const _Float16 *)o.C;
+    p.X = (const _Float16 *)o.X;
+    p.D = (_Float16 *)o.D;
+    p.Aux = (_Float16 *)o.Aux;
+    p.row_bias = (const _Float16 *)o.row_bias;
+    p.col_bias = (const _Float16 *)o.col_bias;
+    p.acc_out = (float *)o.acc_out;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)sk.K;
+    p.tiles_m = (int)((M + sk.t.bm - 1) / sk.t.bm);
+    p.tiles_n = (int)((N + sk.t.bn - 1) / sk.t.bn);
+    p.num_tiles = (int)sk.tiles;
+    p.group_m = L > 1 ? 2 : 8;
+    p.alpha = scalars[0];
+    p.beta = scalars[1];
+    p.s = scalars[2];
+    set_sk_params(p, sk, workspace);
+    hipError_t err;
+    if (dtype == GEMM_EPI_BF16)
+        err = launch_sk_bf16(kind, p, sk.groups, s);
+    else
+        err = dispatch_kind(kind, [&](auto k) { return launch_kind_sk<decltype(k)::value>(p, sk.groups, s); });
+    if (err != hipSuccess) {
+        g_last_hip_error = (int)err;
+        return GEMM_EPI_ERR_HIP;
+    }
+    return GEMM_EPI_OK;
+}
+
+// ---- the scratch-free stream-K call (gemm_epi_run_ws_static) ----------------
+// For callers that cannot allocate (code under HIP graph capture, tight
+// serving loops, harnesses that forbid hipMalloc): the split's counters and
+// partial sums live in this file-scope device array, one copy per GPU, held
+// until the process ends.  Its splits use at most kStaticMaxGroups
+// workgroups, whose two partial slots each fill it.  In host code `scratch`
+// is only a stand-in for the symbol: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+constexpr int kStaticMaxGroups = 128;
+constexpr size_t kStaticScratchBytes = kSkCounterBytes + (size_t)2 * kStaticMaxGroups * 128 * 128 * 4;  // 16 MiB + 16 KiB
+static_assert(kSkTile.bm == 128 && kSkTile.bn == 128, "scratch sized for the 128 x 128 split tile");
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+__global__ void zero_words(int *p, int n)
+{
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+// The current device's scratch address.  On a device's first call it is
+// looked up and its counter block cleared by a kernel on the caller's stream
+// (ahead of the split in stream order; a kernel, not a memset node, so that a
+// graph captured around the call replays correctly).
+hipError_t device_scratch(hipStream_t stream, void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        int *words = (int *)ptr;
+        int n = (int)(kSkCounterBytes / 4);
+        void *args[] = {(void *)&words, (void *)&n};
+        e = hipLaunchKernel((const void *)&zero_words, dim3(16), dim3(256), args, 0, stream);
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace
@@ -502,40 +590,31 @@ int gemm_epi_run_ws_typed(int64_t L, int64_t M, int64_t N, int64_t K, const void
                                   acc_out, dtype, stream);
     if (!workspace || workspace_bytes < sk.workspace) return GEMM_EPI_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return GEMM_EPI_ERR_ALIGN;
+    return launch_split(L, M, N, o, scalars, epilogue_kind, sk, workspace, dtype, (hipStream_t)stream);
+}
 
-    Params p = {};
-    p.A = (const _Float16 *)A;
-    p.B = (const _Float16 *)B;
-    p.C = (const _Float16 *)C;
-    p.X = (const _Float16 *)X;
-    p.D = (_Float16 *)D;
-    p.Aux = (_Float16 *)Aux;
-    p.row_bias = (const _Float16 *)row_bias;
-    p.col_bias = (const _Float16 *)col_bias;
-    p.acc_out = (float *)acc_out;
-    p.M = (int)M;
-    p.N = (int)N;
-    p.K = (int)K;
-    p.tiles_m = (int)((M + sk.t.bm - 1) / sk.t.bm);
-    p.tiles_n = (int)((N + sk.t.bn - 1) / sk.t.bn);
-    p.num_tiles = (int)sk.tiles;
-    p.group_m = L > 1 ? 2 : 8;
-    p.alpha = scalars[0];
-    p.beta = scalars[1];
-    p.s = scalars[2];
-    set_sk_params(p, sk, workspace);
-    hipStream_t s = (hipStream_t)stream;
-    hipError_t err;
-    if (dtype == GEMM_EPI_BF16)
-        err = launch_sk_bf16(epilogue_kind, p, sk.groups, s);
-    else
-        err = dispatch_kind(epilogue_kind,
-                            [&](auto k) { return launch_kind_sk<decltype(k)::value>(p, sk.groups, s); });
+int gemm_epi_run_ws_static(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                           const void *X, const void *row_bias, const void *col_bias, const float *scalars,
+                           int epilogue_kind, void *D, void *Aux, void *acc_out, int dtype, void *stream)
+{
+    const Operands o = {A, B, C, X, row_bias, col_bias, D, Aux, acc_out};
+    int rc = check_args(L, M, N, K, o, epilogue_kind);
+    if (rc != GEMM_EPI_OK) return rc;
+    if (dtype != GEMM_EPI_F16 && dtype != GEMM_EPI_BF16) return GEMM_EPI_ERR_DTYPE;
+    if (!scalars) return GEMM_EPI_ERR_NULL_INPUT;
+    const bool vec = use_fast_path(M, N, K, o, epilogue_kind);
+    const SkPlan sk = plan_stream_k(L, M, N, K, vec, kStaticMaxGroups);
+    if (!sk.on)
+        return gemm_epi_run_typed(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilogue_kind, D, Aux,
+                                  acc_out, dtype, stream);
+    if (sk.workspace > kStaticScratchBytes) return GEMM_EPI_ERR_WORKSPACE;  // the plan cap makes this unreachable
+    void *ws = nullptr;
+    const hipError_t err = device_scratch((hipStream_t)stream, &ws);
     if (err != hipSuccess) {
         g_last_hip_error = (int)err;
         return GEMM_EPI_ERR_HIP;
     }
-    return GEMM_EPI_OK;
+    return launch_split(L, M, N, o, scalars, epilogue_kind, sk, ws, dtype, (hipStream_t)stream);
 }
 
 int gemm_epi_run(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,

@@ -326,6 +326,29 @@ int gemm_epi_run_ws_typed(int64_t L, int64_t M, int64_t N, int64_t K, const void
                           int epilogue_kind, void *D, void *Aux, void *acc_out, void *workspace,
                           size_t workspace_bytes, int dtype, void *stream);
 
+/*
+ * gemm_epi_run_ws_static -- gemm_epi_run_ws_typed without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * split's counters and partial sums live in a device array inside the
+ * library: 16 MiB + 16 KiB on each GPU the library runs on, held until the
+ * process ends.  The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); on a device's first call it looks up the
+ * array's address and clears its counter block with a kernel on `stream`.
+ * Its splits use at most 128 workgroups (so its plan can differ from
+ * gemm_epi_plan_ws's, which allows 256; results are the same on integer
+ * inputs and within the fp32 summation order otherwise); where no split
+ * pays the call is exactly gemm_epi_run_typed.  Every call on one GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (two streams, two
+ * threads) race.  `stream` must belong to the calling thread's current
+ * device.  Status codes as gemm_epi_run_ws_typed; GEMM_EPI_ERR_WORKSPACE if a
+ * split would not fit the array; GEMM_EPI_ERR_HIP if the array cannot be
+ * located (for example the current device's index is 64 or more).
+ */
+int gemm_epi_run_ws_static(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                           const void *X, const void *row_bias, const void *col_bias, const float *scalars,
+                           int epilogue_kind, void *D, void *Aux, void *acc_out, int dtype, void *stream);
+
 /* gemm_epi_plan_ext for gemm_epi_run_ws: out[0..5] as gemm_epi_plan (out[4] is
  * the number of workgroups, the split's workgroup count when it splits), and
  * out[6] the workspace bytes the call needs (0: no split). */

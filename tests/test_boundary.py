@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function():
                           "gemm_epi_run_unfused", "gemm_epi_run_ws_typed", "gemm_epi_run_unfused_typed",
                           "gemm_epi_run_mixed",
                           "gemm_epi_status_string", "gemm_epi_last_hip_error", "gemm_epi_plan", "gemm_epi_plan_ext",
-                          "gemm_epi_plan_ws"}
+                          "gemm_epi_plan_ws", "gemm_epi_run_ws_static"}
     raw = ctypes.CDLL(binding.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
