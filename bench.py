@@ -1,14 +1,18 @@
 """Throughput of the fused fp16 GEMM + epilogue on one MI355X.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload x_acc_8192]
-                    [--no-cpu-baseline] [--all] [--compare-unfused]
+                    [--no-cpu-baseline] [--no-configs] [--all] [--compare-unfused]
 
 A step is one call of the fused kernel (one gemm_epi_run_ext) on the workload,
 with every input already resident in HBM.  The timed region is K steps on one
 stream, bracketed by torch.cuda.synchronize(); HIP events recorded on that
 same stream give the average launch duration that the roofline uses.
-Prints ONE JSON line (the headline workload); --all also reports the other
-workloads, one JSON line each on stderr.
+Prints ONE JSON line (the headline workload).  Unless --no-configs (or
+--workload) is given, the line's "configs" entry also reports the other four
+configurations (128^3, 1024^3, 2400 x 3232 x 4096, the 16-batch case), each
+timed the same way just before the headline: kernel us, TFLOP/s, roofline
+and the epilogue's HBM GB/s.  --all also reports every other workload, one
+JSON line each on stderr.
 
 The CPU baseline is the oracle as it stands (plain fp64 triple loop),
 timed on a bounded slice of the same workload on this host's cores.
@@ -364,6 +368,30 @@ def bench_cpu_oracle(w, rows):
     return flops / dt / 1e12, dt, rows
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def config_summary(w, steps, warmup):
+    """One of the other report configurations, timed like the headline:
+    mean launch, TFLOP/s, its roofline and the epilogue's HBM bytes per
+    second (warm: the inputs were just used)."""
+    g = bench_gpu(w, steps, warmup)
+    ms = g["kernel_ms"]
+    return {"kernel_us": round(ms * 1e3, 2), "tflops": round(w.flops / (ms * 1e-3) / 1e12, 2),
+            "roofline": roofline(w, ms), "epilogue_gbs_warm": round(w.epilogue_bytes / (ms * 1e-3) / 1e9, 1),
+            "tile": [g["plan"]["bm"], g["plan"]["bn"], g["plan"]["bk"]], "workgroups": g["plan"]["workgroups"],
+            "shape": [w.L, w.M, w.N, w.K], "epilogue": w.kind}
+
+
 def omp_threads():
     env = os.environ.get("OMP_NUM_THREADS")
     if env and env.isdigit():
@@ -451,6 +479,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other four report configurations (timed before the headline by default)")
     ap.add_argument("--cpu-rows", type=int, default=6144)
     ap.add_argument("--all", action="store_true")
     ap.add_argument("--compare-unfused", action="store_true",
@@ -489,6 +519,13 @@ def main():
                 line["unfused_library"] = bench_unfused_library(other, a.steps, a.warmup)
             print(json.dumps(line), file=sys.stderr, flush=True)
 
+    # The other report configurations first (their launches also bring the
+    # GPU to its working clock before the headline is timed).
+    configs = None
+    if not a.no_configs and a.workload is None:
+        configs = {c: config_summary(workloads.WORKLOADS[c], max(a.steps, 20), max(a.warmup, 20))
+                   for c in workloads.CONFIGS if c != name}
+
     g = bench_gpu(w, a.steps, a.warmup)
     cpu = None
     if not a.no_cpu_baseline:
@@ -496,9 +533,12 @@ def main():
         os.environ["OMP_NUM_THREADS"] = str(threads)
         v, dt, rows = bench_cpu_oracle(w, a.cpu_rows)
         cpu = {"value": round(v, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+               "cpu_model": cpu_model(),
                "sample": f"first {rows} of {w.M} output rows of {w.name} (all {w.N} columns, K={w.K}), "
                          f"fp64 i-k-j triple loop + epilogue, {dt:.1f} s"}
     line = result_line(w, g, a.steps, a.warmup, cpu)
+    if configs is not None:
+        line["configs"] = configs
     if a.all and w.name in EPI_TYPE_WORKLOADS:
         line["epi_types"] = bench_gpu_epi_types(w, a.steps, a.warmup)
     if a.compare_unfused:

@@ -123,6 +123,11 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in (
 
 # The workload the headline throughput is quoted on.
 HEADLINE = "x_acc_8192"
+# The five configurations the throughput is reported on, in order: 128^3 and
+# 1024^3 (tutorial cell [2]), the Python article's 2400 x 3232 x 4096, the
+# headline, and the 16-batch multi-output case.
+CONFIGS = ("aux_scale_128", "aux_scale_1024", "lincomb_2400x3232x4096", "x_acc_8192",
+           "relu_square_16x2048x2048x1024")
 
 
 def to_bf16_bits(t) -> np.ndarray:

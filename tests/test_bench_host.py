@@ -67,3 +67,13 @@ def test_more_than_one_gpu_is_refused():
                        text=True, cwd=ROOT, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_report_configurations_and_cpu_model():
+    """The default line reports the five configurations (the headline plus
+    four in "configs"), and the CPU baseline names the host's CPU model."""
+    from dense_gemm_elementwise_amd import workloads
+    assert len(workloads.CONFIGS) == 5 and workloads.HEADLINE in workloads.CONFIGS
+    assert all(c in workloads.WORKLOADS for c in workloads.CONFIGS)
+    m = bench.cpu_model()
+    assert m is None or (isinstance(m, str) and m)
