@@ -76,7 +76,7 @@ TileCfg choose_tile(int64_t L, int64_t M, int64_t N, int64_t K, bool vec)
 TileCfg tile_for_mixed(const TileCfg &t, int64_t M, int64_t N)
 {
     if (t.bm != kTiles[0].bm || t.bn != kTiles[0].bn) return t;
-    return M >= N ? kTiles[2] : kTiles[1];
+    return M >= N ? kTile256x128W8 : kTile128x256W8;
 }
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }

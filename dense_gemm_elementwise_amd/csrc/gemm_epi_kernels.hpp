@@ -520,14 +520,41 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void *p)
 //    MFMA result against a later non-MFMA reader and the compiler cannot see
 //    inside the asm, so wait states are inserted by hand (agpr_fence).
 // ---------------------------------------------------------------------------
-constexpr int W4_BK = 32;                   // k step, and the B stage depth
-constexpr int W4_NS = 4;                    // B ring slots
-constexpr int W4_NA = 3;                    // A ring slots
-constexpr int W4_A_SLOT = 256 * 64 * 2;     // 32 KB: 256 rows x 128 bytes (64 k)
-constexpr int W4_B_SLOT = W4_BK * 256 * 2;  // 16 KB: 32 k-rows x 512 bytes
-constexpr int W4_B_BASE = W4_NA * W4_A_SLOT;
-constexpr int W4_LDS = W4_B_BASE + W4_NS * W4_B_SLOT;  // 160 KB
-constexpr int W4_PERIOD = 12;               // k steps after which slots and buffers repeat
+constexpr int W4_BK = 32;      // k step, and the B stage depth
+constexpr int W4_NS = 4;       // B ring slots
+constexpr int W4_NA = 3;       // A ring slots
+constexpr int W4_PERIOD = 12;  // k steps after which slots and buffers repeat
+
+// The tiles the 4-wave main loop runs: 256 x 256, 128 x 256 and 256 x 128,
+// four waves in a 2 x 2 grid, each owning a (BM/2) x (BN/2) tile of
+// TM x TN 16 x 16 accumulator blocks.
+template <int BM, int BN>
+struct W4Cfg {
+    static_assert((BM == 256 || BM == 128) && (BN == 256 || BN == 128) && BM + BN >= 384, "4-wave tile");
+    static constexpr int TM = BM / 32, TN = BN / 32;
+    static constexpr int A_SLOT = BM * 128;        // a 64-deep A chunk: BM rows of 128 bytes
+    static constexpr int B_ROW = BN * 2;           // bytes per B k-row
+    static constexpr int B_CHUNKS = BN / 8;        // 16-byte chunks per B k-row
+    static constexpr int B_SLOT = W4_BK * B_ROW;   // a 32-deep B stage
+    static constexpr int B_BASE = W4_NA * A_SLOT;
+    static constexpr int LDS = B_BASE + W4_NS * B_SLOT;
+    static constexpr int NA = BM / 64;             // A DMAs per wave and k step (half a chunk)
+    static constexpr int NB = BN / 64;             // B DMAs per wave and k step (one stage)
+    static constexpr int ND = NA + NB;
+    static constexpr int NMF = TM * TN;            // MFMAs per wave and k step
+    static constexpr int NR = TM + 2 * TN;         // operand reads per wave and k step
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(NMF >= 2 * ND + 2 && NMF >= NR, "the gap schedule needs room");
+};
+
+template <bool W4, int BM, int BN>
+constexpr int w4_lds()
+{
+    if constexpr (W4)
+        return W4Cfg<BM, BN>::LDS;
+    else
+        return 0;
+}
 
 // f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled
 template <int N, int I = 0, typename F>
@@ -554,51 +581,67 @@ __device__ __forceinline__ void mfma16_agpr(f32x4 &acc, const half8 &a, const ha
 // asm are opaque to the compiler's hazard recognizer, so the gap between a
 // VALU write and an MFMA read, and between an MFMA result and an ordinary
 // read, is inserted here.
-__device__ __forceinline__ void agpr_fence(f32x4 (&acc)[8][8])
+template <int TM, int TN>
+__device__ __forceinline__ void agpr_fence(f32x4 (&acc)[TM][TN])
 {
+    static_assert(TN == 4 || TN == 8, "rows of 4 or 8 blocks");
 #pragma unroll
-    for (int i = 0; i < 7; i++)
-        asm volatile("" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
-                     "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-                 : "+a"(acc[7][0]), "+a"(acc[7][1]), "+a"(acc[7][2]), "+a"(acc[7][3]), "+a"(acc[7][4]),
-                   "+a"(acc[7][5]), "+a"(acc[7][6]), "+a"(acc[7][7]));
+    for (int i = 0; i < TM; i++) {
+        if constexpr (TN == 8) {
+            if (i + 1 < TM)
+                asm volatile("" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]),
+                             "+a"(acc[i][4]), "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
+            else
+                asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                             : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]),
+                               "+a"(acc[i][4]), "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
+        } else {
+            if (i + 1 < TM)
+                asm volatile("" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]));
+            else
+                asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                             : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]));
+        }
+    }
 }
 
-template <bool BF>
-__device__ __forceinline__ void mainloop_w4(f32x4 (&acc)[8][8], const _Float16 *Al, const _Float16 *Bl, int M,
-                                            int N, int K, int m0, int n0, int kb, int nk, char *smem)
+template <int BM, int BN, bool BF>
+__device__ __forceinline__ void mainloop_w4(f32x4 (&acc)[BM / 32][BN / 32], const _Float16 *Al, const _Float16 *Bl,
+                                            int M, int N, int K, int m0, int n0, int kb, int nk, char *smem)
 {
+    using C = W4Cfg<BM, BN>;
+    constexpr int TM = C::TM, TN = C::TN, NA = C::NA, NB = C::NB, ND = C::ND, NMF = C::NMF, NR = C::NR;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     constexpr uint32_t kParked = 0x7FFFFFF0u;
     const uint32_t smem_lds = lds_addr_of(smem);
-    const int kbase = kb * W4_BK;  // first k column of this segment
+    const int kbase = kb * W4_BK;   // first k column of this segment
     const int nka = (nk + 1) >> 1;  // A chunks
 
-    // DMA offsets.  A half-chunk h (rows 128h..128h+127) is 16 instructions,
-    // 4 per wave: instruction q of wave w fills rows 8 (16h + 4q + w) .. + 7,
-    // lane -> row + lane / 8, physical chunk lane % 8.  B stage: 16
-    // instructions of two 512-byte k-rows, 4 per wave.
-    uint32_t a_voff[2][4], b_voff[4];
-    int a_kcol[2][4];  // first k column of the lane's A chunk, for the chunk that crosses K
+    // DMA offsets.  A half-chunk h (rows BM/2 h .. BM/2 h + BM/2 - 1) is BM/16
+    // instructions, NA per wave: instruction q of wave w fills rows
+    // 8 (BM/16 h + 4q + w) .. + 7, lane -> row + lane / 8, physical chunk
+    // lane % 8.  B stage: BN/16 instructions of 1 KB, NB per wave (block
+    // 4q + w).
+    uint32_t a_voff[2][NA], b_voff[NB];
+    int a_kcol[2][NA];  // first k column of the lane's A chunk, for the chunk that crosses K
 #pragma unroll
     for (int h = 0; h < 2; h++)
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
-            const int row = (h * 16 + q * 4 + wave) * 8 + (lane >> 3);
+        for (int q = 0; q < NA; q++) {
+            const int row = (h * (BM / 16) + q * 4 + wave) * 8 + (lane >> 3);
             const int c = (lane & 7) ^ swz_a<8>(row);
             const int gm = m0 + row;
             a_kcol[h][q] = c * 8;
             a_voff[h][q] = gm < M ? (uint32_t)(gm * K + c * 8) * 2u : kParked;
         }
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
+    for (int q = 0; q < NB; q++) {
         const int lin = (q * 4 + wave) * 64 + lane;
-        const int krow = lin >> 5;
-        const int cb = (lin & 31) ^ swz_b<32, 16>(krow);
+        const int krow = lin / C::B_CHUNKS;
+        const int cb = (lin % C::B_CHUNKS) ^ swz_b<C::B_CHUNKS, 16>(krow);
         const int gn = n0 + cb * 8;
         b_voff[q] = gn < N ? (uint32_t)(krow * N + gn) * 2u : kParked;
     }
@@ -612,75 +655,93 @@ __device__ __forceinline__ void mainloop_w4(f32x4 (&acc)[8][8], const _Float16 *
         const int k0 = kbase + c * 64;
         return make_rsrc(Al + k0, c < nka ? (uint32_t)(((int64_t)M * K - k0) * 2) : 0u);
     };
-    // DMA op g of a k step: g < 4: A instruction g of half h of chunk c (k0 its
-    // first column) into A slot sa; g >= 4: B instruction g - 4 into B slot sb.
-    // Only the last chunk can cross K (A columns past K are the next row's:
-    // parked).
     // A offsets of the last chunk, the only one that can cross K (columns past
     // K are the next row's: parked)
-    uint32_t a_voff_last[2][4];
+    uint32_t a_voff_last[2][NA];
     {
         const int k0l = kbase + (nka - 1) * 64;
 #pragma unroll
         for (int h = 0; h < 2; h++)
 #pragma unroll
-            for (int q = 0; q < 4; q++) a_voff_last[h][q] = k0l + a_kcol[h][q] < K ? a_voff[h][q] : kParked;
+            for (int q = 0; q < NA; q++) a_voff_last[h][q] = k0l + a_kcol[h][q] < K ? a_voff[h][q] : kParked;
     }
-    // LDS address (M0) of DMA g of a k step: A chunk half h into A slot sa,
-    // B stage into B slot sb
+    // LDS address (M0, less this wave's 1 KB) of DMA g of a k step: g < NA:
+    // A instruction g of chunk half h into A slot sa; else B instruction g - NA
+    // into B slot sb
     auto dma_lds = [](int g, int h, int sa, int sb) {
-        return g < 4 ? (uint32_t)(sa * W4_A_SLOT + (h * 16 + g * 4) * 1024)
-                     : (uint32_t)(W4_B_BASE + sb * W4_B_SLOT + (g - 4) * 4096);
+        return g < NA ? (uint32_t)(sa * C::A_SLOT + (h * (BM / 16) + g * 4) * 1024)
+                      : (uint32_t)(C::B_BASE + sb * C::B_SLOT + (g - NA) * 4096);
     };
 
     // Operand reads.  A block i of k step t: lane (li + 16 lg) reads row
-    // wm*128 + 16 i + li, k columns 8 lg..8 lg+7 of the step's half of the
+    // wm*BM/2 + 16 i + li, k columns 8 lg..8 lg+7 of the step's half of the
     // chunk (logical 16-byte chunk 4 (t & 1) + lg; one ds_read_b128).  The
     // swizzle depends on row bits 1-3, so block i is block 0 + 2 KB i, and the
     // step's half flips address bit 6.  B block j: two ds_read_b64_tr_b16,
     // lane 4e + r of 16-lane group g pointing at k-row 8 g + 4 h + e,
-    // columns 4 r..4 r+3 of the block; h moves 4 k-rows (+2 KB, same
-    // swizzle), j has its own address.
+    // columns 4 r..4 r+3 of the block; h moves 4 k-rows (same swizzle), j has
+    // its own address.
     const int li = lane & 15, lg = lane >> 4, lq = lane & 15;
-    const int a_row = wm * 128 + li;
+    const int a_row = wm * (BM / 2) + li;
     const char *a_rd[W4_NA][2];
 #pragma unroll
     for (int sl = 0; sl < W4_NA; sl++)
 #pragma unroll
         for (int kk = 0; kk < 2; kk++)
-            a_rd[sl][kk] = smem + sl * W4_A_SLOT + a_row * 128 + (((kk * 4 + lg) ^ swz_a<8>(a_row)) * 16);
-    const char *b_rd[8];
+            a_rd[sl][kk] = smem + sl * C::A_SLOT + a_row * 128 + (((kk * 4 + lg) ^ swz_a<8>(a_row)) * 16);
+    const char *b_rd[TN];
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-        const int n = wn * 128 + j * 16 + 4 * (lq & 3);
+    for (int j = 0; j < TN; j++) {
+        const int n = wn * (BN / 2) + j * 16 + 4 * (lq & 3);
         const int krow = 8 * lg + (lq >> 2);
-        b_rd[j] = smem + W4_B_BASE + krow * 512 + (((n >> 3) ^ swz_b<32, 16>(krow)) * 16) + (n & 7) * 2;
+        b_rd[j] = smem + C::B_BASE + krow * C::B_ROW + (((n >> 3) ^ swz_b<C::B_CHUNKS, 16>(krow)) * 16) +
+                  (n & 7) * 2;
     }
     auto read_a = [&](int sa, int kk, int i) { return *(const half8 *)(a_rd[sa][kk] + i * 2048); };
     auto read_b = [&](int sb, int j, int h) {
         return __builtin_amdgcn_ds_read_tr16_b64_v4f16(
-            (GE_LDS(fp16x4_t) *)(b_rd[j] + sb * W4_B_SLOT + h * 2048));
+            (GE_LDS(fp16x4_t) *)(b_rd[j] + sb * C::B_SLOT + h * 4 * C::B_ROW));
     };
 
-    half8 fa[2][8], fb[2][8];
-    fp16x4_t fbh[8][2];
+    half8 fa[2][TM], fb[2][TN];
+    fp16x4_t fbh[TN][2];
     auto join_b = [&](int P) {
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
+        for (int j = 0; j < TN; j++) {
             const half4 lo = __builtin_bit_cast(half4, fbh[j][0]), hi = __builtin_bit_cast(half4, fbh[j][1]);
             fb[P][j] = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
     };
+    // operand read r of a k step: A block, or half h of a B block; the first
+    // 3 min(TM, TN) interleave A, B h0, B h1, the rest follow in order
+    constexpr int MN = TM < TN ? TM : TN;
+    // (all indices compile-time, so that the fragments stay in registers)
+    auto do_read = [&](auto R_, auto P_, int sa, int kk, int sb) {
+        constexpr int r = decltype(R_)::value, P = decltype(P_)::value;
+        if constexpr (r < 3 * MN) {
+            constexpr int g = r / 3, k = r % 3;
+            if constexpr (k == 0)
+                fa[P][g] = read_a(sa, kk, g);
+            else
+                fbh[g][k - 1] = read_b(sb, g, k - 1);
+        } else if constexpr (TM > TN) {
+            fa[P][MN + r - 3 * MN] = read_a(sa, kk, MN + r - 3 * MN);
+        } else {
+            constexpr int x = r - 3 * MN;
+            fbh[MN + x / 2][x % 2] = read_b(sb, MN + x / 2, x % 2);
+        }
+    };
 
     // One k step t, t % 12 = D (compile time): MFMAs on the fragments in
-    // buffer D % 2; operand reads of step t+1 into the other buffer; the 8
+    // buffer D % 2; operand reads of step t+1 into the other buffer; the ND
     // DMAs (B stage t+4, half (t+1) % 2 of A chunk (t+5)/2).  With one wave
     // per SIMD, only two or three other instructions fit in the shadow of one
-    // MFMA, so the work is spread over the 64 gaps after the MFMAs: the 24
-    // reads in the even gaps 0..46; DMA g takes three odd gaps, 8g+1 (its A
-    // offset), 8g+3 (M0) and 8g+5 (the load).  On the last step the reads
-    // fetch slots nobody writes any more into registers nobody uses: every
-    // branch stays outside the pinned sequence.
+    // MFMA, so the work is spread over the NMF gaps after the MFMAs: read r in
+    // gap r NMF / NR; DMA d in three gaps from d NMF / ND on (its A offset,
+    // M0, the load; the MFMA between M0 and the load gives the wait state
+    // the load needs).  On the last step the reads fetch slots nobody writes
+    // any more into registers nobody uses: every branch stays outside the
+    // pinned sequence.
     auto kstep = [&](auto D_, int t) {
         constexpr int D = decltype(D_)::value;
         constexpr int P = D & 1;
@@ -691,39 +752,41 @@ __device__ __forceinline__ void mainloop_w4(f32x4 (&acc)[8][8], const _Float16 *
         constexpr int SAD = ((D + 5) >> 1) % W4_NA;    // A slot refilled in this step
         constexpr int HD = (D + 1) & 1;                // the half refilled
         const int ca = (t + 5) >> 1;
-        i32x4 ra, rb;  // built in gaps 1 and 33, before their first loads (gaps 5 and 37)
+        i32x4 ra, rb;  // built in the gaps of the first A and the first B DMA
         bool last_chunk;
-        int dvoff[4];
-#pragma unroll
-        for (int m = 0; m < 64; m++) {
-            mfma16_agpr<BF>(acc[m >> 3][m & 7], fa[P][m >> 3], fb[P][m & 7]);
-            if ((m & 1) == 0) {
-                if (m < 48) {
-                    const int op = m >> 1, g = op / 3, r = op % 3;
-                    if (r == 0)
-                        fa[P ^ 1][g] = read_a(SAN, KKN, g);
+        int dvoff[NA];
+        // (static_for, not a pragma: a loop the unroller declines would index
+        // the accumulators at run time and move them to scratch memory)
+        static_for<NMF>([&](auto M_) {
+            constexpr int m = decltype(M_)::value;
+            mfma16_agpr<BF>(acc[m / TN][m % TN], fa[P][m / TN], fb[P][m % TN]);
+            static_for<NR>([&](auto R_) {
+                constexpr int r = decltype(R_)::value;
+                if (r * NMF / NR == m) do_read(R_, std::integral_constant<int, P ^ 1>{}, SAN, KKN, SBN);
+            });
+            static_for<ND>([&](auto G_) {
+                constexpr int g = decltype(G_)::value;
+                constexpr int g0 = g * NMF / ND;
+                if (m == g0) {
+                    if constexpr (g == 0) {
+                        ra = rsrc_a(ca);
+                        last_chunk = ca == nka - 1;
+                    }
+                    if constexpr (g == NA) rb = rsrc_b(t + W4_NS);
+                    if constexpr (g < NA) dvoff[g] = (int)(last_chunk ? a_voff_last[HD][g] : a_voff[HD][g]);
+                } else if (m == g0 + 1) {
+                    constexpr uint32_t OFF = g < NA ? (uint32_t)(SAD * C::A_SLOT + (HD * (BM / 16) + g * 4) * 1024)
+                                                    : (uint32_t)(C::B_BASE + SB * C::B_SLOT + (g - NA) * 4096);
+                    m0_set<OFF>(lds_w);
+                } else if (m == g0 + 2) {
+                    if constexpr (g < NA)
+                        dma16_issue(ra, dvoff[g]);
                     else
-                        fbh[g][r - 1] = read_b(SBN, g, r - 1);
+                        dma16_issue(rb, (int)b_voff[g - NA]);
                 }
-            } else {
-                const int g = m >> 3, ph = (m & 7) >> 1;  // ph 0: offset, 1: M0, 2: load
-                if (m == 1) {
-                    ra = rsrc_a(ca);
-                    last_chunk = ca == nka - 1;
-                }
-                if (m == 33) rb = rsrc_b(t + W4_NS);
-                if (ph == 0 && g < 4) dvoff[g] = (int)(last_chunk ? a_voff_last[HD][g] : a_voff[HD][g]);
-                if (ph == 1)
-                    static_for<8>([&](auto G_) {
-                        constexpr int gg = decltype(G_)::value;
-                        constexpr uint32_t OFF = gg < 4 ? (uint32_t)(SAD * W4_A_SLOT + (HD * 16 + gg * 4) * 1024)
-                                                        : (uint32_t)(W4_B_BASE + SB * W4_B_SLOT + (gg - 4) * 4096);
-                        if (gg == g) m0_set<OFF>(lds_w);
-                    });
-                if (ph == 2) dma16_issue(g < 4 ? ra : rb, g < 4 ? dvoff[g] : (int)b_voff[g - 4]);
-            }
+            });
             __builtin_amdgcn_sched_barrier(0);
-        }
+        });
         join_b(P ^ 1);
     };
 
@@ -733,35 +796,29 @@ __device__ __forceinline__ void mainloop_w4(f32x4 (&acc)[8][8], const _Float16 *
         const i32x4 ra0 = rsrc_a(0), ra1 = rsrc_a(1), ra2 = rsrc_a(2);
         auto a_off = [&](int c, int h, int g) { return (int)(c == nka - 1 ? a_voff_last[h][g] : a_voff[h][g]); };
 #pragma unroll
-        for (int g = 0; g < 4; g++) dma16(ra0, lds_w + dma_lds(g, 0, 0, 0), a_off(0, 0, g));
+        for (int g = 0; g < NA; g++) dma16(ra0, lds_w + dma_lds(g, 0, 0, 0), a_off(0, 0, g));
 #pragma unroll
         for (int s = 0; s < W4_NS; s++) {
             const i32x4 rb = rsrc_b(s);
             const int ca = (s + 1) >> 1, h = (s + 1) & 1;
             const i32x4 &ra = ca == 0 ? ra0 : (ca == 1 ? ra1 : ra2);
 #pragma unroll
-            for (int g = 0; g < 8; g++)
-                dma16(g < 4 ? ra : rb, lds_w + dma_lds(g, h, ca, s), g < 4 ? a_off(ca, h, g) : (int)b_voff[g - 4]);
+            for (int g = 0; g < ND; g++)
+                dma16(g < NA ? ra : rb, lds_w + dma_lds(g, h, ca, s), g < NA ? a_off(ca, h, g) : (int)b_voff[g - NA]);
         }
     }
-    wait_vmcnt<24>();  // B stage 0 and A chunk 0 (the 24 DMAs after them may fly)
+    wait_vmcnt<3 * ND>();  // B stage 0 and A chunk 0 (the DMAs of the three newer steps may fly)
     barrier_lds();
-#pragma unroll
-    for (int i = 0; i < 8; i++) fa[0][i] = read_a(0, 0, i);
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-        fbh[j][0] = read_b(0, j, 0);
-        fbh[j][1] = read_b(0, j, 1);
-    }
+    static_for<NR>([&](auto R_) { do_read(R_, std::integral_constant<int, 0>{}, 0, 0, 0); });
     join_b(0);
     agpr_fence(acc);  // the accumulators' zeroing (VALU) before the first MFMA reads them
 
-    // Step t: the DMAs of step t-3 have landed (the 16 of the two newer steps
+    // Step t: the DMAs of step t-3 have landed (those of the two newer steps
     // may still be in flight), then the barrier publishes what step t+1 reads
     // and frees what step t has read; the last step has nothing to publish.
     auto step = [&](auto D_, int t) {
         if (t + 1 < nk) {
-            wait_vmcnt<16>();
+            wait_vmcnt<2 * ND>();
             barrier_lds();
         }
         kstep(D_, t);
@@ -846,8 +903,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     constexpr int EPI_LD = WN + (MI == 32 ? 8 : 4);
     constexpr int EPI_BYTES = NW * SLAB * EPI_LD * 4;
     // the 4-wave 256 x 256 configuration runs the hand-scheduled main loop
-    constexpr bool W4 = NW == 4 && BM == 256 && BN == 256 && BK == W4_BK && NSTAGES == W4_NS && MI == 16 && VEC &&
-                        !SK;
+    constexpr bool W4 = NW == 4 && BM + BN >= 384 && BK == W4_BK && NSTAGES == W4_NS && MI == 16 && VEC && !SK;
+    constexpr int W4_LDS = w4_lds<W4, BM, BN>();
     constexpr int SMEM0 = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
     constexpr int SMEM = W4 ? (W4_LDS > EPI_BYTES ? W4_LDS : EPI_BYTES) : SMEM0;
     static_assert(SMEM <= 160 * 1024, "LDS budget");
@@ -884,7 +941,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     const int nk = ke - kb;  // k stages in this segment
 
     if constexpr (W4) {
-        mainloop_w4<BF>(acc, Al, Bl, M, N, K, m0, n0, kb, nk, smem);
+        mainloop_w4<BM, BN, BF>(acc, Al, Bl, M, N, K, m0, n0, kb, nk, smem);
     } else {
     // ---- global -> LDS --------------------------------------------------
     // One wave instruction fills 1 KB: 1024 / A_ROW rows of A, or

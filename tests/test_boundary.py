@@ -271,7 +271,7 @@ def test_plan_tiles_for_the_workloads():
     want = {
         "aux_scale_128": (64, 64, 64, 4),
         "aux_scale_1024": (64, 64, 128, 256),
-        "lincomb_2400x3232x4096": (128, 256, 64, 19 * 13),
+        "lincomb_2400x3232x4096": (128, 256, 32, 19 * 13),
         "x_acc_8192": (256, 256, 32, 1024),
         "relu_square_16x2048x2048x1024": (256, 256, 32, 1024),
         "relu_aux_store_1024": (64, 64, 128, 256),

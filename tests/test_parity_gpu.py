@@ -363,7 +363,13 @@ DEEP_SMALL_SHAPES = [(1, 64, 64, 256), (1, 64, 64, 512), (1, 1000, 1000, 520), (
                      (3, 200, 136, 1160), (1, 1280, 1280, 648), (2, 1000, 600, 1032)]
 
 
-@pytest.mark.parametrize("shape", TAIL_SHAPES + TILE_SHAPES + BIG_TILE_SHAPES + DEEP_SMALL_SHAPES)
+# the 4-wave 128 x 256 and 256 x 128 tiles: 1 to 32 k stages, ragged last
+# stages, ragged M and N
+MID_TILE_SHAPES = [(1, 3000, 2000, 520), (1, 1500, 4000, 1000), (1, 2000, 3000, 264), (1, 1500, 4000, 8),
+                   (1, 3000, 2000, 136), (2, 1100, 2600, 96)]
+
+
+@pytest.mark.parametrize("shape", TAIL_SHAPES + TILE_SHAPES + BIG_TILE_SHAPES + DEEP_SMALL_SHAPES + MID_TILE_SHAPES)
 def test_tails_bit_exact(shape):
     L, M, N, K = shape
     kind = "AUX_SCALE"
@@ -387,7 +393,7 @@ def test_every_tile_configuration_is_exercised():
         if cfg["vec"]:
             ring = "2-stage" if cfg["bk"] == 128 and cfg["workgroups"] > 256 else ""
             seen.add((cfg["bm"], cfg["bn"], cfg["bk"], ring))
-    assert seen == {(256, 256, 32, ""), (128, 256, 64, ""), (256, 128, 64, ""), (128, 128, 64, ""), (64, 64, 64, ""),
+    assert seen == {(256, 256, 32, ""), (128, 256, 32, ""), (256, 128, 32, ""), (128, 128, 64, ""), (64, 64, 64, ""),
                     (64, 64, 128, ""), (64, 64, 128, "2-stage")}, seen
 
 
