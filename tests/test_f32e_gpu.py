@@ -139,6 +139,7 @@ def check(p, kind, ab, a, b, s, exact, offset=0, what=""):
                                           ((3, 77, 45, 61), 0),       # K, N not multiples of 8: general
                                           ((1, 520, 776, 88), 0),     # vector kernel, 256 x 256 tiles
                                           ((2, 300, 520, 648), 0),    # 64 x 64 x 128 tile (K >= 256), ragged last stage
+                                          ((1, 1280, 1280, 648), 0),  # the same with the 2-stage ring (400 tiles)
                                           ((1, 300, 520, 136), 0)])   # 64 x 64 x 64 tile (K < 256), ragged last stage
 def test_every_kind_integer_inputs(kind, ab, shape, offset):
     L, M, N, K = shape
