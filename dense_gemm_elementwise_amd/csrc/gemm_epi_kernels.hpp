@@ -484,12 +484,14 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void *p)
 }
 
 // ---------------------------------------------------------------------------
-// Main loop of the 4-wave 256 x 256 tile: one wave per SIMD, each owning a
-// 128 x 128 accumulator tile (64 blocks of v_mfma_f32_16x16x32, 256 fp32
-// values per lane) held in the accumulation registers (AGPRs).  Against
-// eight waves of 64 x 128 it reads a third fewer LDS bytes per MFMA (the
+// Main loop of the 4-wave tiles (256 x 256, 128 x 256, 256 x 128): one wave
+// per SIMD, each owning a (BM/2) x (BN/2) accumulator tile held in the
+// accumulation registers (AGPRs; for 256 x 256, 64 blocks of
+// v_mfma_f32_16x16x32 and 256 fp32 values per lane).  Against eight waves of
+// 64 x 128 the 256 x 256 tile reads a third fewer LDS bytes per MFMA (the
 // operand bytes of a wave tile grow with its perimeter, the MFMAs with its
-// area), which is what bounds the 8-wave loop.
+// area), which is what bounds the 8-wave loop.  The figures below are those
+// of the 256 x 256 tile.
 //
 // With one wave per SIMD nothing else covers a stall, so the instruction
 // stream is fixed by hand:
@@ -509,11 +511,13 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void *p)
 //    descriptors, to keep that count.
 //  * A slots sit in [0, 96 KB), B slots in [96 KB, 160 KB); every LDS read is
 //    a base register plus an immediate offset below 64 KB.
-//  * Each k step issues its 64 MFMAs with one memory instruction after every
-//    second one: the 24 operand reads of the next k step (8 A ds_read_b128,
-//    16 B ds_read_b64_tr_b16) and the 8 DMAs.  The order is pinned with
-//    scheduling barriers.  Slots and register buffers repeat every 12 k
-//    steps, which the loop unrolls.
+//  * Each k step spreads its memory work over the gaps between its 64
+//    MFMAs (about two instructions fit in the shadow of one): the 24 operand
+//    reads of the next k step (8 A ds_read_b128, 16 B ds_read_b64_tr_b16),
+//    evenly, and each of the 8 DMAs in three parts (descriptor, M0, issue)
+//    in three consecutive gaps.  The order is pinned with scheduling
+//    barriers.  Slots and register buffers repeat every 12 k steps, which
+//    the loop unrolls.
 //  * The MFMAs are inline asm with "+a" accumulator operands: with the
 //    builtins the register allocator moved accumulators between the AGPR
 //    and VGPR files inside the loop.  The hardware does not interlock an
@@ -1151,26 +1155,6 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
             }
     };
 
-    // Instruction order of one k step (the 64 x 128 wave tile only; measured
-    // neutral or worse on smaller wave tiles): two MFMAs, then each of the
-    // next k step's fragment reads paired with one MFMA, then the rest of the
-    // MFMAs.  Left to itself the compiler issues the reads after most of the
-    // MFMAs, so the next k step's first MFMAs and the stage barrier's wait for
-    // outstanding LDS reads stall on their latency (measured 4.8% slower at
-    // 8192^3 than this order).
-    constexpr int NREAD = ML_TM + 2 * ML_TN, NMFMA = ML_TM * ML_TN;
-    auto sched_ks = [&]() {
-        if constexpr (NMFMA >= 32 && NMFMA >= NREAD + 2) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-#pragma unroll
-            for (int i = 0; i < NREAD; i++) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NREAD - 2, 0);
-        }
-    };
-
     // Waits until this thread's DMA for the stage about to be published has
     // landed, when `newer` later stages (a compile-time count) may still be in
     // flight behind it; near the end of K fewer were issued, and it waits for
@@ -1216,7 +1200,6 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
         for (int kk = 0; kk + 1 < KSTEPS; kk++) {
             read_frags(cur, kk + 1, fa[(p0 + kk + 1) & 1], fb[(p0 + kk + 1) & 1]);
             mfmas(fa[(p0 + kk) & 1], fb[(p0 + kk) & 1]);
-            sched_ks();
         }
         wait_stage(newer_steady{}, kt + NSTAGES <= nk);  // stage kt+1 landed (this thread's part)
         if constexpr (!VEC) __syncthreads();
@@ -1224,7 +1207,6 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
         if (kt + NSTAGES < nk) load_stage(cur, (kb + kt + NSTAGES) * BK);
         read_frags(nxt, 0, fa[(p0 + KSTEPS) & 1], fb[(p0 + KSTEPS) & 1]);
         mfmas(fa[(p0 + KSTEPS - 1) & 1], fb[(p0 + KSTEPS - 1) & 1]);
-        sched_ks();
     };
     auto last_stage = [&](int cur, auto P) {
         constexpr int p0 = decltype(P)::value;
