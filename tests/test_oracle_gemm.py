@@ -222,7 +222,13 @@ def test_random_fp16_tiny_against_exact(shape, kind):
     bound of a rounding boundary."""
     L, M, N, K = shape
     p = workloads.make_problem(L, M, N, K, kind, init="normal", seed=sum(shape) * 31 + len(kind))
-    alpha, beta, s3 = 1.5, -0.75, 2.0
+    check_tiny_against_exact(p, kind, 1.5, -0.75, 2.0)
+
+
+def check_tiny_against_exact(p, kind, alpha, beta, s3):
+    """The oracle on problem p against exact rational arithmetic, as described
+    in test_random_fp16_tiny_against_exact."""
+    L, M, N, K = p["A"].shape[0], p["A"].shape[1], p["B"].shape[2], p["A"].shape[2]
     out = run_oracle(p, kind, alpha, beta, s3, want64=True)
     exD, exAux, exAcc = exact_outputs(p["A"], p["B"], p["C"], p["X"], kind, alpha, beta, s3,
                                       p["row_bias"], p["col_bias"])
@@ -255,6 +261,23 @@ def test_random_fp16_tiny_against_exact(shape, kind):
             want = exact_rne_f32(e)
             if exact_rne_f32(e - b) == exact_rne_f32(e + b) == want:
                 assert float(out["Acc"][idx]) == want, idx
+
+
+@pytest.mark.parametrize("chunk", range(10))
+def test_random_tiny_sweep_against_exact(chunk):
+    """1,200 seeded random cases (120 per chunk): shapes L in 1..2, M, N in
+    1..5, K in 1..9, every exactly checkable kind, Gaussian fp16 inputs and
+    scalars drawn from small dyadic and non-dyadic sets, each against exact
+    rational arithmetic."""
+    rng = np.random.default_rng(20261203 + chunk)
+    kinds = list(workloads.EXACT_KINDS)
+    scal = [0.0, 1.0, -1.0, 0.5, 2.0, -0.75, 1.5, 0.1, 3.0]
+    for case in range(120):
+        L, M, N, K = int(rng.integers(1, 3)), int(rng.integers(1, 6)), int(rng.integers(1, 6)), int(rng.integers(1, 10))
+        kind = kinds[(chunk * 120 + case) % len(kinds)]
+        p = workloads.make_problem(L, M, N, K, kind, init="normal", seed=int(rng.integers(0, 2**31)))
+        alpha, beta, s3 = (float(rng.choice(scal)) for _ in range(3))
+        check_tiny_against_exact(p, kind, alpha, beta, s3)
 
 
 # ---------------------------------------------------------------------------
