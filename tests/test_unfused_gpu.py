@@ -17,7 +17,7 @@ import oracle
 import dense_gemm_elementwise_amd as ge
 from dense_gemm_elementwise_amd import workloads
 
-from test_parity_gpu import KIND_SCALARS, alloc_out, assert_bit_exact, assert_output, log, oracle_full, oracle_ref, to_dev
+from test_parity_gpu import KIND_SCALARS, alloc_out, assert_bit_exact, assert_close, assert_output, log, oracle_full, oracle_ref, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -71,5 +71,10 @@ def test_unfused_equals_fused_gaussian(kind):
     log(f"[unfused] gaussian kind={kind}")
     p = workloads.make_problem(L, M, N, K, kind, init="normal", seed=29)
     fused, unfused = run_both(p, kind, a, b, s)
+    ref = oracle_ref(p, kind, a, b, s, exact=False)
     for name in fused:
         assert np.array_equal(fused[name].view(np.uint8), unfused[name].view(np.uint8)), f"{kind} {name}"
+        if name == "Acc":
+            assert_close(unfused[name], ref["Acc64"], f"unfused gaussian {kind} acc_out")
+        else:
+            assert_output(unfused[name], ref, name, kind, False, f"unfused gaussian {kind} {name}")
