@@ -881,6 +881,24 @@ __device__ __forceinline__ void buf_store(V v, __amdgpu_buffer_rsrc_t r, int off
 // vectors); otherwise every global access is element-wise and guarded and
 // LDS is filled through registers.
 // ---------------------------------------------------------------------------
+// The 16 bytes at byte offset b (0 or 2) of the 20 bytes lo:x.
+__device__ __forceinline__ i32x4 realign16(const i32x4 &lo, int x, uint32_t b)
+{
+    const uint32_t d[5] = {(uint32_t)lo[0], (uint32_t)lo[1], (uint32_t)lo[2], (uint32_t)lo[3], (uint32_t)x};
+    i32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; i++) r[i] = (int)__builtin_amdgcn_alignbyte(d[i + 1], d[i], b);
+    return r;
+}
+// Keeps the first n 16-bit elements of v (none if n <= 0), zeroes the rest.
+__device__ __forceinline__ i32x4 keep_first(i32x4 v, int n)
+{
+#pragma unroll
+    for (int d = 0; d < 4; d++)
+        v[d] &= (int)((2 * d < n ? 0x0000FFFFu : 0u) | (2 * d + 1 < n ? 0xFFFF0000u : 0u));
+    return v;
+}
+
 template <int BM, int BN, int BK, int NSTAGES, int WGM, int WGN, int MI, int KIND, bool VEC, bool SK = false,
           bool BF = false, int EPI = EPI_AB>
 __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
@@ -1031,6 +1049,102 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
         }
     }
 
+    // General path (K or N not a multiple of 8, or an unaligned tensor):
+    // global -> registers -> LDS, into the same swizzled layout.  Each thread
+    // stages G_A + G_B 16-byte chunks a stage.  An operand of less than
+    // 2 GiB is read with a 16-byte buffer load from the 4-byte aligned address
+    // at or below the chunk and one more 4-byte load, and the chunk, at any
+    // even byte offset, is cut out of
+    // that window in registers (elements past K or N, and rows past M or K,
+    // are zeroed); a larger operand is read element by element.  In the main
+    // loop the loads of stage t+2 are issued before stage t's MFMAs and
+    // written to LDS after its last MFMAs are issued, into the slot the
+    // barrier before them freed, so that their latency hides behind a stage
+    // of MFMAs and their realignment runs beside the MFMAs.
+    constexpr int G_A = VEC ? 1 : A_BLKS / NW, G_B = VEC ? 1 : B_BLKS / NW;
+    i32x4 g_lo[G_A + G_B];
+    int g_hi[G_A + G_B];
+    const uint32_t a_mis = (uint32_t)((uintptr_t)Al & 15), b_mis = (uint32_t)((uintptr_t)Bl & 15);
+    const bool a_buf = (int64_t)M * K * 2 + 1024 < ((int64_t)1 << 31);
+    const bool b_buf = (int64_t)K * N * 2 + 1024 < ((int64_t)1 << 31);
+    const __amdgpu_buffer_rsrc_t g_ra =
+        epi_rsrc((const char *)Al - a_mis, a_buf ? (uint32_t)((a_mis + (int64_t)M * K * 2 + 15) & ~15) : 0u);
+    const __amdgpu_buffer_rsrc_t g_rb =
+        epi_rsrc((const char *)Bl - b_mis, b_buf ? (uint32_t)((b_mis + (int64_t)K * N * 2 + 15) & ~15) : 0u);
+    // chunk q of this thread: A row and k chunk, or B k-row and column chunk
+    auto a_chunk = [&](int q, int &row, int &pchunk, int &c) {
+        row = (q * NW + wave) * A_ROWS_PER_BLK + lane / A_CHUNKS;
+        pchunk = lane % A_CHUNKS;
+        c = pchunk ^ swz_a<A_CHUNKS>(row);
+    };
+    auto b_chunk = [&](int q, int &krow, int &pchunk, int &c) {
+        const int lin = (q * NW + wave) * 64 + lane;
+        krow = lin / B_CHUNKS;
+        pchunk = lin % B_CHUNKS;
+        c = pchunk ^ swz_b<B_CHUNKS, MI>(krow);
+    };
+    auto g_issue = [&](int k0) {
+#pragma unroll
+        for (int q = 0; q < G_A; q++) {
+            int row, pchunk, c;
+            a_chunk(q, row, pchunk, c);
+            const int gm = m0 + row, gk = k0 + c * 8;
+            if (a_buf) {
+                const uint32_t byte = a_mis + (uint32_t)(((int64_t)gm * K + gk) * 2);
+                const int off = gm < M ? (int)(byte & ~3u) : 0x7FFFFFE0;
+                g_lo[q] = buf_load<i32x4, 0>(g_ra, off);
+                g_hi[q] = buf_load<int, 0>(g_ra, off + 16);
+            } else {
+                half8 v;
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    v[e] = (gm < M && gk + e < K) ? Al[(int64_t)gm * K + gk + e] : (_Float16)0.0f;
+                g_lo[q] = __builtin_bit_cast(i32x4, v);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < G_B; q++) {
+            int krow, pchunk, c;
+            b_chunk(q, krow, pchunk, c);
+            const int gk = k0 + krow, gn = n0 + c * 8;
+            if (b_buf) {
+                const uint32_t byte = b_mis + (uint32_t)(((int64_t)gk * N + gn) * 2);
+                const int off = gk < K ? (int)(byte & ~3u) : 0x7FFFFFE0;
+                g_lo[G_A + q] = buf_load<i32x4, 0>(g_rb, off);
+                g_hi[G_A + q] = buf_load<int, 0>(g_rb, off + 16);
+            } else {
+                half8 v;
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    v[e] = (gk < K && gn + e < N) ? Bl[(int64_t)gk * N + gn + e] : (_Float16)0.0f;
+                g_lo[G_A + q] = __builtin_bit_cast(i32x4, v);
+            }
+        }
+    };
+    auto g_commit = [&](int stage, int k0) {
+        const int a_off = stage * STAGE;
+        const int b_off = a_off + A_STAGE;
+#pragma unroll
+        for (int q = 0; q < G_A; q++) {
+            int row, pchunk, c;
+            a_chunk(q, row, pchunk, c);
+            const int gm = m0 + row, gk = k0 + c * 8;
+            i32x4 v = g_lo[q];
+            if (a_buf) v = realign16(g_lo[q], g_hi[q], (a_mis + (uint32_t)(((int64_t)gm * K + gk) * 2)) & 3u);
+            *(i32x4 *)(smem + a_off + row * A_ROW + pchunk * 16) = keep_first(v, gm < M ? K - gk : 0);
+        }
+#pragma unroll
+        for (int q = 0; q < G_B; q++) {
+            int krow, pchunk, c;
+            b_chunk(q, krow, pchunk, c);
+            const int gk = k0 + krow, gn = n0 + c * 8;
+            i32x4 v = g_lo[G_A + q];
+            if (b_buf)
+                v = realign16(g_lo[G_A + q], g_hi[G_A + q], (b_mis + (uint32_t)(((int64_t)gk * N + gn) * 2)) & 3u);
+            *(i32x4 *)(smem + b_off + krow * B_ROW + pchunk * 16) = keep_first(v, gk < K ? N - gn : 0);
+        }
+    };
+
     auto load_stage = [&](int stage, int k0) {
         const int a_off = stage * STAGE;
         const int b_off = a_off + A_STAGE;
@@ -1053,38 +1167,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
 #pragma unroll
             for (int q = 0; q < B_DMA; q++) dma16(rb, b_lds + q * NW * 1024, (int)b_voff[q]);
         } else {
-            // element-wise guarded loads through registers, same LDS layout
-#pragma unroll 1
-            for (int q = 0; q < A_BLKS / NW; q++) {
-                const int blk = q * NW + wave;
-                const int row = blk * A_ROWS_PER_BLK + lane / A_CHUNKS;
-                const int pchunk = lane % A_CHUNKS;
-                const int c = pchunk ^ swz_a<A_CHUNKS>(row);
-                const int gm = m0 + row;
-                half8 v;
-#pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    const int gk = k0 + c * 8 + e;
-                    v[e] = (gm < M && gk < K) ? Al[(int64_t)gm * K + gk] : (_Float16)0.0f;
-                }
-                *(half8 *)(smem + a_off + row * A_ROW + pchunk * 16) = v;
-            }
-#pragma unroll 1
-            for (int q = 0; q < B_BLKS / NW; q++) {
-                const int blk = q * NW + wave;
-                const int lin = blk * 64 + lane;
-                const int krow = lin / B_CHUNKS;
-                const int pchunk = lin % B_CHUNKS;
-                const int c = pchunk ^ swz_b<B_CHUNKS, MI>(krow);
-                const int gk = k0 + krow;
-                half8 v;
-#pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    const int gn = n0 + c * 8 + e;
-                    v[e] = (gk < K && gn < N) ? Bl[(int64_t)gk * N + gn] : (_Float16)0.0f;
-                }
-                *(half8 *)(smem + b_off + krow * B_ROW + pchunk * 16) = v;
-            }
+            g_issue(k0);
+            g_commit(stage, k0);
         }
     };
 
@@ -1196,6 +1280,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     // stage (barrier) and starts reading it before its own last MFMAs.
     auto stage_with_next = [&](int kt, int cur, int nxt, auto P) {
         constexpr int p0 = decltype(P)::value;
+        if constexpr (!VEC)
+            if (kt + NSTAGES < nk) g_issue((kb + kt + NSTAGES) * BK);
 #pragma unroll
         for (int kk = 0; kk + 1 < KSTEPS; kk++) {
             read_frags(cur, kk + 1, fa[(p0 + kk + 1) & 1], fb[(p0 + kk + 1) & 1]);
@@ -1204,9 +1290,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
         wait_stage(newer_steady{}, kt + NSTAGES <= nk);  // stage kt+1 landed (this thread's part)
         if constexpr (!VEC) __syncthreads();
         barrier_lds();  // everyone's part landed; stage kt's slot is free
-        if (kt + NSTAGES < nk) load_stage(cur, (kb + kt + NSTAGES) * BK);
+        if constexpr (VEC)
+            if (kt + NSTAGES < nk) load_stage(cur, (kb + kt + NSTAGES) * BK);
         read_frags(nxt, 0, fa[(p0 + KSTEPS) & 1], fb[(p0 + KSTEPS) & 1]);
         mfmas(fa[(p0 + KSTEPS - 1) & 1], fb[(p0 + KSTEPS - 1) & 1]);
+        if constexpr (!VEC)
+            if (kt + NSTAGES < nk) g_commit(cur, (kb + kt + NSTAGES) * BK);
     };
     auto last_stage = [&](int cur, auto P) {
         constexpr int p0 = decltype(P)::value;
