@@ -90,13 +90,16 @@ def _upload(p, w, dev):
     return {k: one(v) for k, v in p.items()}
 
 
-def _launcher(w, ge):
-    """The entry point for workload w: gemm_epi_run_ext, or gemm_epi_run_typed
-    with the workload's element type (same arguments plus dtype)."""
+def _launcher(w, ge, args):
+    """The call of workload w with arguments `args` (those of gemm_epi_run_ext),
+    converted to ctypes once: gemm_epi_run_ext, or gemm_epi_run_typed with
+    the workload's element type.  Host cost per call on MI355X: about 3.8 us
+    against 4.4 us converting the arguments on every call, and 3.4 us for any
+    HIP launch API from C++; it bounds the launch rate of the smallest
+    workloads."""
     if w.dtype == "f16":
-        return ge.gemm_epi_run_ext
-    dt = ge.DTYPES[w.dtype]
-    return lambda *a: ge.gemm_epi_run_typed(*a[:-1], dt, a[-1])
+        return ge.prepared("gemm_epi_run_ext", *args)
+    return ge.prepared("gemm_epi_run_typed", *args[:-1], ge.DTYPES[w.dtype], args[-1])
 
 
 def _outputs(w, ge, dev):
@@ -152,12 +155,12 @@ def bench_gpu(w, steps, warmup):
     D, Aux, Acc = _outputs(w, ge, dev)
     stream = torch.cuda.current_stream(dev)
     args = _device_args(w, t, D, Aux, Acc, stream, ge)
-    run = _launcher(w, ge)
+    run = _launcher(w, ge, args)
     for _ in range(warmup):
-        rc = run(*args)
+        rc = run()
         if rc:
             raise RuntimeError(ge.gemm_epi_status_string(rc))
-    wall_ms, ev_ms, stats = _timed_launches(lambda i: run(*args), steps, stream)
+    wall_ms, ev_ms, stats = _timed_launches(lambda i: run(), steps, stream)
     rc, plan = _plan(args, ge)
     return {"ms_per_step": wall_ms, "kernel_ms": ev_ms, "launch_ms": stats, "plan": plan}
 
@@ -244,11 +247,10 @@ def bench_gpu_cold(w, steps, warmup):
         t = {k: (v.clone() if v is not None else None) for k, v in base.items()}
         copies.append((t,) + _outputs(w, ge, dev))
     stream = torch.cuda.current_stream(dev)
-    arglist = [_device_args(w, t, D, Aux, Acc, stream, ge) for (t, D, Aux, Acc) in copies]
-    run = _launcher(w, ge)
+    calls = [_launcher(w, ge, _device_args(w, t, D, Aux, Acc, stream, ge)) for (t, D, Aux, Acc) in copies]
     for i in range(warmup):
-        run(*arglist[i % sets])
-    _, ev_ms, stats = _timed_launches(lambda i: run(*arglist[(i + warmup) % sets]), steps, stream)
+        calls[i % sets]()
+    _, ev_ms, stats = _timed_launches(lambda i: calls[(i + warmup) % sets](), steps, stream)
     del copies
     return {"copies": sets, "kernel_ms": round(ev_ms, 5), "launch_ms": {k: round(v, 5) for k, v in stats.items()},
             "tflops": round(w.flops / (ev_ms * 1e-3) / 1e12, 2),

@@ -10,9 +10,9 @@ from .binding import (ACTIVATIONS, DTYPES, EXPORTS, HAS_ACC, HAS_AUX, KINDS, REA
                       GemmEpiError, gemm_epi_last_hip_error, gemm_epi_plan, gemm_epi_plan_ext, gemm_epi_plan_ws,
                       gemm_epi_run, gemm_epi_run_ext, gemm_epi_run_mixed, gemm_epi_run_typed, gemm_epi_run_unfused,
                       gemm_epi_run_unfused_typed, gemm_epi_run_ws, gemm_epi_run_ws_static, gemm_epi_run_ws_typed,
-                      gemm_epi_status_string, lib, run)
+                      gemm_epi_status_string, lib, prepared, run)
 
-__all__ = ["run", "gemm_epi_run", "gemm_epi_run_ext", "gemm_epi_run_typed", "gemm_epi_run_mixed",
+__all__ = ["run", "prepared", "gemm_epi_run", "gemm_epi_run_ext", "gemm_epi_run_typed", "gemm_epi_run_mixed",
            "gemm_epi_run_unfused", "gemm_epi_run_unfused_typed", "gemm_epi_run_ws", "gemm_epi_run_ws_typed", "gemm_epi_run_ws_static",
            "gemm_epi_plan_ws", "gemm_epi_plan", "gemm_epi_plan_ext", "gemm_epi_status_string",
            "gemm_epi_last_hip_error", "lib", "KINDS", "HAS_AUX", "READS_X", "READS_C", "READS_BIAS", "HAS_ACC",

@@ -158,6 +158,34 @@ def gemm_epi_run_ext(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilog
                                   _kind_id(epilogue_kind), D, Aux, acc_out, stream)
 
 
+def prepared(entry, *args):
+    """A call of C-ABI entry point `entry` (a name from EXPORTS) that repeats
+    with the same arguments, converted to ctypes once: for loops that issue
+    the same call many times (timing, serving).  Arguments as for the
+    pointer-level wrapper of that entry point: sizes, device addresses (int or
+    None), the scalars as a sequence, the kind and element types as names or
+    enum values, the stream as an address.  Returns a function of no
+    arguments that makes the call and returns its status code."""
+    if entry not in EXPORTS or not entry.startswith("gemm_epi_run"):
+        raise ValueError(f"not a run entry point: {entry}")
+    f = getattr(lib(), entry)
+    if len(args) != len(f.argtypes):
+        raise ValueError(f"{entry} takes {len(f.argtypes)} arguments, got {len(args)}")
+    conv = []
+    ints = 0  # the first int argument of a run entry point is the kind, any later ones element types
+    for t, a in zip(f.argtypes, args):
+        if a is None:
+            conv.append(None)
+        elif t is ctypes.POINTER(ctypes.c_float):
+            conv.append((ctypes.c_float * len(a))(*[float(v) for v in a]))
+        elif t is ctypes.c_int:
+            conv.append(t(_kind_id(a) if ints == 0 else _dtype_id(a)))
+            ints += 1
+        else:
+            conv.append(t(a))
+    return lambda: f(*conv)
+
+
 def gemm_epi_run_typed(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilogue_kind, D, Aux, acc_out,
                        dtype, stream) -> int:
     """Pointer-level call of gemm_epi_run_typed: gemm_epi_run_ext with the

@@ -359,3 +359,19 @@ def test_status_errors_are_value_errors_with_the_status_string():
     e = ge.GemmEpiError(7, ge.gemm_epi_status_string(7))
     assert isinstance(e, ValueError) and e.status == 7
     assert "GEMM_EPI_ERR_WORKSPACE" in str(e) and ge.gemm_epi_status_string(7) in str(e)
+
+
+def test_prepared_call_checks_its_entry_point_and_arguments():
+    """prepared() converts the arguments once; it accepts only the run entry
+    points and their exact argument count (no call is made here)."""
+    args = (1, 64, 64, 64, P16, P16, P16, None, None, None, (1.0, 0.5, 2.0), "AUX_SCALE", P16, P16, None, None)
+    call = ge.prepared("gemm_epi_run_ext", *args)
+    assert callable(call)
+    typed = ge.prepared("gemm_epi_run_typed", *args[:-1], "bf16", None)
+    assert callable(typed)
+    with pytest.raises(ValueError):
+        ge.prepared("gemm_epi_plan_ext", *args)
+    with pytest.raises(ValueError):
+        ge.prepared("no_such_entry", *args)
+    with pytest.raises(ValueError):
+        ge.prepared("gemm_epi_run_ext", *args[:-1])

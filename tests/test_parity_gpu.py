@@ -480,3 +480,32 @@ def test_closed_forms_on_gpu_output(kind, alpha, beta, s3, a_form):
         want = {"Aux": acc, "D": lin + s3 * p["X"].astype(np.float64)}
     for name, w in want.items():
         assert_bit_exact(got[name], w.astype(np.float16), f"closed form A={a_form} {kind} {name}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prepared_call_matches_the_oracle(dtype):
+    """ge.prepared: the same C-ABI call with its arguments converted once,
+    repeated; every repetition bit-exact against the oracle."""
+    L, M, N, K = 2, 200, 136, 264
+    kind = "AUX_SCALE"
+    a, b, s3 = KIND_SCALARS[kind]
+    log(f"[prepared] {dtype}")
+    p = workloads.make_problem(L, M, N, K, kind, init="small_int", seed=321, dtype=dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+
+    def dev(v):
+        return torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).view(tdt).to(DEV)
+    A, B, C = dev(p["A"]), dev(p["B"]), dev(p["C"])
+    D = torch.full((L, M, N), float("nan"), dtype=tdt, device=DEV)
+    Aux = torch.full((L, M, N), float("nan"), dtype=tdt, device=DEV)
+    stream = torch.cuda.current_stream()
+    call = ge.prepared("gemm_epi_run_typed", L, M, N, K, A.data_ptr(), B.data_ptr(), C.data_ptr(), None, None,
+                       None, (a, b, s3), kind, D.data_ptr(), Aux.data_ptr(), None, dtype, stream.cuda_stream)
+    ref = oracle.gemm_epi(p["A"], p["B"], p["C"], None, kind=kind, alpha=a, beta=b, s3=s3, dtype=dtype)
+    for _ in range(3):
+        D.fill_(float("nan"))
+        Aux.fill_(float("nan"))
+        assert call() == 0
+        torch.cuda.synchronize()
+        assert_bit_exact(D.cpu().view(torch.int16).numpy().view(np.uint16), ref["D"], "prepared D")
+        assert_bit_exact(Aux.cpu().view(torch.int16).numpy().view(np.uint16), ref["Aux"], "prepared Aux")
