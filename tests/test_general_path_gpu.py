@@ -21,7 +21,7 @@ import oracle
 import dense_gemm_elementwise_amd as ge
 from dense_gemm_elementwise_amd import workloads
 
-from test_parity_gpu import DEV, KIND_SCALARS, assert_bit_exact, log, oracle_full
+from test_parity_gpu import DEV, KIND_SCALARS, assert_bit_exact, assert_within_ulp, log, oracle_full
 
 pytestmark = pytest.mark.gpu
 
@@ -44,10 +44,16 @@ def run_placed(p, kind, offs, dtype=torch.float16):
     X = place(p["X"], offs[2], dtype) if p["X"] is not None else None
     D = torch.empty(L * M * N + offs[3], dtype=dtype, device=DEV)[offs[3]:].view(L, M, N)
     Aux = torch.empty(L * M * N + offs[3], dtype=dtype, device=DEV)[offs[3]:].view(L, M, N) if kind in ge.HAS_AUX else None
-    ge.run(A, B, C, X, kind=kind, alpha=a, beta=b, s3=s, D=D, Aux=Aux)
+    rb = place(p["row_bias"], offs[2], dtype) if p.get("row_bias") is not None else None
+    cb = place(p["col_bias"], offs[2], dtype) if p.get("col_bias") is not None else None
+    acc = (torch.empty(L * M * N + offs[3], dtype=torch.float32, device=DEV)[offs[3]:].view(L, M, N)
+           if kind in ge.HAS_ACC else None)
+    ge.run(A, B, C, X, kind=kind, alpha=a, beta=b, s3=s, D=D, Aux=Aux, row_bias=rb, col_bias=cb, acc_out=acc)
     out = {"D": D.cpu().view(torch.int16).numpy()}
     if Aux is not None:
         out["Aux"] = Aux.cpu().view(torch.int16).numpy()
+    if acc is not None:
+        out["Acc"] = acc.cpu().numpy()
     return out
 
 
@@ -95,3 +101,38 @@ def test_bf16_offsets_and_residues():
     got = run_placed(p, kind, (3, 6, 1, 5), torch.bfloat16)
     ref = oracle.gemm_epi(p["A"], p["B"], p["C"], p["X"], kind=kind, alpha=a, beta=b, s3=s3, dtype="bf16")
     assert_bit_exact(got["D"].view(np.uint16), ref["D"], "general bf16 D")
+
+
+def general_cases(n=40, seed=20261203):
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        L = int(rng.integers(1, 3))
+        M, N = (int(v) for v in rng.integers(1, 601, 2))
+        K = int(rng.integers(1, 1201))
+        kind = workloads.KINDS[int(rng.integers(0, len(workloads.KINDS)))]
+        offs = tuple(int(v) for v in rng.integers(0, 8, 4))
+        out.append((c, L, M, N, K, kind, offs))
+    return out
+
+
+@pytest.mark.parametrize("case", general_cases(), ids=lambda c: f"g{c[0]}-{c[5]}-{c[1]}x{c[2]}x{c[3]}x{c[4]}-{c[6]}")
+def test_random_general_case(case):
+    """Seeded random shapes, kinds and independent element offsets of A, B,
+    the epilogue inputs (and biases) and the outputs; bit-exact against the oracle (the
+    activation kinds within one ulp, as in the other parity tests)."""
+    c, L, M, N, K, kind, offs = case
+    log(f"[general random] case {c}: L={L} M={M} N={N} K={K} {kind} offsets={offs}")
+    p = workloads.make_problem(L, M, N, K, kind, init="small_int", seed=2000 + c)
+    got = run_placed(p, kind, offs)
+    exact = kind not in ge.ACTIVATIONS
+    ref = oracle_full(p, kind, *KIND_SCALARS[kind], want64=not exact)
+    for name in got:
+        if name == "Acc":  # integer inputs: every fp32 partial sum is exact
+            assert np.array_equal(got[name], ref["Acc"]), f"general random {c} acc_out"
+            continue
+        g = got[name].view(np.float16)
+        if exact:
+            assert_bit_exact(g, ref[name], f"general random {c} {name}")
+        else:
+            assert_within_ulp(g, ref[name + "64"], ref[name], f"general random {c} {name}")
