@@ -484,7 +484,7 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void *p)
 }
 
 // ---------------------------------------------------------------------------
-// Main loop of the 4-wave tiles (256 x 256, 128 x 256, 256 x 128): one wave
+// Main loop of the 4-wave tiles (256 x 256, 128 x 256, 256 x 128, 128 x 128): one wave
 // per SIMD, each owning a (BM/2) x (BN/2) accumulator tile held in the
 // accumulation registers (AGPRs; for 256 x 256, 64 blocks of
 // v_mfma_f32_16x16x32 and 256 fp32 values per lane).  Against eight waves of
@@ -532,12 +532,12 @@ constexpr int W4_PERIOD = 12;  // k steps after which slots and buffers repeat
 // k split of the 64 x 64 x 128 tile's main loop (the kernel says how)
 inline constexpr int KS_SPLIT = 4, KS_WGM = 1, KS_WGN = 2;
 
-// The tiles the 4-wave main loop runs: 256 x 256, 128 x 256 and 256 x 128,
-// four waves in a 2 x 2 grid, each owning a (BM/2) x (BN/2) tile of
-// TM x TN 16 x 16 accumulator blocks.
+// The tiles the 4-wave main loop runs: 256 x 256, 128 x 256, 256 x 128 and
+// 128 x 128, four waves in a 2 x 2 grid, each owning a (BM/2) x (BN/2) tile
+// of TM x TN 16 x 16 accumulator blocks.
 template <int BM, int BN>
 struct W4Cfg {
-    static_assert((BM == 256 || BM == 128) && (BN == 256 || BN == 128) && BM + BN >= 384, "4-wave tile");
+    static_assert((BM == 256 || BM == 128) && (BN == 256 || BN == 128), "4-wave tile");
     static constexpr int TM = BM / 32, TN = BN / 32;
     static constexpr int A_SLOT = BM * 128;        // a 64-deep A chunk: BM rows of 128 bytes
     static constexpr int B_ROW = BN * 2;           // bytes per B k-row
@@ -742,13 +742,14 @@ __device__ __forceinline__ void mainloop_w4(f32x4 (&acc)[BM / 32][BN / 32], cons
     // One k step t, t % 12 = D (compile time): MFMAs on the fragments in
     // buffer D % 2; operand reads of step t+1 into the other buffer; the ND
     // DMAs (B stage t+4, half (t+1) % 2 of A chunk (t+5)/2).  With one wave
-    // per SIMD, only two or three other instructions fit in the shadow of one
-    // MFMA, so the work is spread over the NMF gaps after the MFMAs: read r in
-    // gap r NMF / NR; DMA d in three gaps from d NMF / ND on (its A offset,
-    // M0, the load; the MFMA between M0 and the load gives the wait state
-    // the load needs).  On the last step the reads fetch slots nobody writes
-    // any more into registers nobody uses: every branch stays outside the
-    // pinned sequence.
+    // per SIMD (two on the 128 x 128 tile, from two workgroups), only two or
+    // three other instructions fit in the shadow of one MFMA, so the work is
+    // spread over the NMF gaps after the MFMAs: read r in gap r NMF / NR; DMA
+    // d in three gaps from d NMF / ND on (its A offset, M0, the load; the
+    // MFMA between M0 and the load gives the wait state the load needs).
+    // Near the end the DMAs fetch stages past the end (zero records) and the
+    // last step's reads fetch into registers nobody uses: every branch stays
+    // outside the pinned sequence.
     auto kstep = [&](auto D_, int t) {
         constexpr int D = decltype(D_)::value;
         constexpr int P = D & 1;
@@ -822,12 +823,13 @@ __device__ __forceinline__ void mainloop_w4(f32x4 (&acc)[BM / 32][BN / 32], cons
 
     // Step t: the DMAs of step t-3 have landed (those of the two newer steps
     // may still be in flight), then the barrier publishes what step t+1 reads
-    // and frees what step t has read; the last step has nothing to publish.
+    // and frees the B slot that step t refills, which every wave read (for
+    // step t) in step t-1.  The last step publishes nothing but still needs
+    // the barrier: its DMAs (a stage past the end, zeros) write that slot,
+    // and without it a fast wave zeroes operands a slow wave is still reading.
     auto step = [&](auto D_, int t) {
-        if (t + 1 < nk) {
-            wait_vmcnt<2 * ND>();
-            barrier_lds();
-        }
+        wait_vmcnt<2 * ND>();
+        barrier_lds();
         kstep(D_, t);
     };
 #pragma unroll 1
@@ -839,6 +841,10 @@ __device__ __forceinline__ void mainloop_w4(f32x4 (&acc)[BM / 32][BN / 32], cons
         GE_W4_STEP(7) GE_W4_STEP(8) GE_W4_STEP(9) GE_W4_STEP(10) GE_W4_STEP(11)
 #undef GE_W4_STEP
     }
+    // The DMAs of the last three steps (stages past the end: zero records, but
+    // they still write their ring slots) may be in flight; the epilogue's
+    // slabs reuse A slot 0, so they must have landed before its first write.
+    wait_vmcnt<0>();
     agpr_fence(acc);  // the last MFMAs' results before the epilogue reads them
 }
 
@@ -937,7 +943,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     constexpr int EPI_LD = SLAB_SWZ ? WN : WN + (MI == 32 ? 8 : 4);
     constexpr int EPI_BYTES = NW * SLAB * EPI_LD * 4;
     // the 4-wave 256 x 256 configuration runs the hand-scheduled main loop
-    constexpr bool W4 = NW == 4 && BM + BN >= 384 && BK == W4_BK && NSTAGES == W4_NS && MI == 16 && VEC && !SK;
+    constexpr bool W4 = NW == 4 && BM >= 128 && BN >= 128 && BK == W4_BK && NSTAGES == W4_NS && MI == 16 && VEC && !SK;
     constexpr int W4_LDS = w4_lds<W4, BM, BN>();
     // The 64 x 64 x 128 tile splits the k range of every stage over its waves
     // in the main loop: KS_WGM x KS_WGN spatial groups, KS_SPLIT k groups.

@@ -18,26 +18,31 @@ struct TileCfg {
 };
 
 // The tile configurations compiled into the library (fast path), and the one
-// general-path configuration.  The 256 x 256, 128 x 256 and 256 x 128 tiles run
-// four waves of (BM/2) x (BN/2) on the hand-scheduled main loop (mainloop_w4:
-// accumulators in AGPRs, 32-deep k steps).  The 64 x 64 tile (small problems, one wave of
+// general-path configuration.  The 256 x 256, 128 x 256, 256 x 128 and 128 x 128
+// tiles run four waves of (BM/2) x (BN/2) on the hand-scheduled main loop
+// (mainloop_w4: accumulators in AGPRs, 32-deep k steps); two 128 x 128
+// workgroups fit on a compute unit (80 KiB of LDS each), and against the
+// eight-wave ring it replaced that tile is 18% faster at 2048^3 and 29% at
+// 3072^3, with the same bits.  The 64 x 64 tile (small problems, one wave of
 // workgroups or less) has latency-bound stages, so fewer, deeper ones are
 // what counts: BK = 64 (1024^3: 12.0 -> 9.7 us against BK = 32; more stages
 // in the ring did not help), and BK = 128 (kSmallDeep) once K >= 256, where
 // it is 1-8% faster again (with four waves of 32 x 32 the break-even was
 // K = 512; the eight waves below moved it to 256).  Eight waves of 16 x 32 (two per SIMD, where
 // one such workgroup is all a compute unit gets) hide more of that latency
-// than four of 32 x 32: 3% at 1024^3, 6% on 256^3.  The 128 x 128 tile
-// likewise runs eight waves of 32 x 64 (2-3% on mid-size grids); its
-// stream-K build keeps four (eight were 2-13% slower there).
+// than four of 32 x 32: 3% at 1024^3, 6% on 256^3.  The stream-K build of
+// the 128 x 128 tile keeps four waves of 64 x 64 on the ring (eight were
+// 2-13% slower there).
 inline constexpr TileCfg kTiles[] = {{256, 256, 32, 4, 2, 2, 16}, {128, 256, 32, 4, 2, 2, 16},
-                                     {256, 128, 32, 4, 2, 2, 16}, {128, 128, 64, 3, 4, 2, 32},
+                                     {256, 128, 32, 4, 2, 2, 16}, {128, 128, 32, 4, 2, 2, 16},
                                      {64, 64, 64, 4, 4, 2, 16}};
-// Epilogue tensors of another type than A and B keep the 8-wave forms of the
-// 128 x 256 and 256 x 128 tiles (the host gives them these tiles in place of
-// 256 x 256): their wider epilogue does not fit the 4-wave tiles' registers.
+// Epilogue tensors of another type than A and B keep 8-wave forms of the
+// 128 x 256, 256 x 128 and 128 x 128 tiles (the host gives them these tiles
+// in place of 256 x 256 and the 4-wave 128 x 128): their wider epilogue does
+// not fit the 4-wave tiles' registers.
 inline constexpr TileCfg kTile128x256W8 = {128, 256, 64, 2, 2, 4, 16};
 inline constexpr TileCfg kTile256x128W8 = {256, 128, 64, 2, 4, 2, 16};
+inline constexpr TileCfg kTile128x128W8 = {128, 128, 64, 3, 4, 2, 32};
 inline constexpr TileCfg kSmallDeep = {64, 64, 128, 4, 4, 2, 16};
 // The same with a 2-stage ring (64 KiB of LDS instead of 128): two workgroups
 // fit on a compute unit, which pays once the grid has more tiles than there
@@ -95,17 +100,18 @@ template <int KIND, bool BF = false, int EPI = EPI_AB>
 hipError_t launch_kind(const Params &p, const TileCfg &t, bool vec, hipStream_t stream)
 {
     if (!vec) return GE_LAUNCH(kGeneral, KIND, false);
-    // the 256 x 256 tile is built for epilogue tensors of the type of A and B
-    // only (the host gives the others 256 x 128 or 128 x 256)
+    // the 4-wave tiles are built for epilogue tensors of the type of A and B
+    // only (the host gives the others the 8-wave tiles of the same shape)
     if constexpr (EPI == EPI_AB) {
         if (t.bm == kTiles[0].bm && t.bn == kTiles[0].bn) return GE_LAUNCH(kTiles[0], KIND, true);
         if (t.bm == kTiles[1].bm && t.bn == kTiles[1].bn) return GE_LAUNCH(kTiles[1], KIND, true);
         if (t.bm == kTiles[2].bm && t.bn == kTiles[2].bn) return GE_LAUNCH(kTiles[2], KIND, true);
+        if (t.bm == kTiles[3].bm && t.bn == kTiles[3].bn) return GE_LAUNCH(kTiles[3], KIND, true);
     } else {
         if (t.bm == kTile128x256W8.bm && t.bn == kTile128x256W8.bn) return GE_LAUNCH(kTile128x256W8, KIND, true);
         if (t.bm == kTile256x128W8.bm && t.bn == kTile256x128W8.bn) return GE_LAUNCH(kTile256x128W8, KIND, true);
+        if (t.bm == kTile128x128W8.bm && t.bn == kTile128x128W8.bn) return GE_LAUNCH(kTile128x128W8, KIND, true);
     }
-    if (t.bm == kTiles[3].bm && t.bn == kTiles[3].bn) return GE_LAUNCH(kTiles[3], KIND, true);
     if (t.bk == kSmallDeep.bk && t.stages == kSmallDeepWide.stages) return GE_LAUNCH(kSmallDeepWide, KIND, true);
     if (t.bk == kSmallDeep.bk) return GE_LAUNCH(kSmallDeep, KIND, true);
     return GE_LAUNCH(kTiles[4], KIND, true);

@@ -137,10 +137,11 @@ def check(p, kind, ab, a, b, s, exact, offset=0, what=""):
 @pytest.mark.parametrize("shape,offset", [((2, 200, 136, 264), 0),    # vector kernel, ragged M
                                           ((2, 200, 136, 264), 1),    # misaligned: general kernel
                                           ((3, 77, 45, 61), 0),       # K, N not multiples of 8: general
-                                          ((1, 520, 776, 88), 0),     # vector kernel, 256 x 256 tiles
+                                          ((1, 3112, 3928, 40), 0),   # 256 x 256 tiles (mixed types: 128 x 256)
                                           ((2, 300, 520, 648), 0),    # 64 x 64 x 128 tile (K >= 256), ragged last stage
                                           ((1, 1280, 1280, 648), 0),  # the same with the 2-stage ring (400 tiles)
-                                          ((1, 300, 520, 136), 0)])   # 64 x 64 x 64 tile (K < 256), ragged last stage
+                                          ((1, 300, 520, 136), 0),    # 64 x 64 x 64 tile (K < 256), ragged last stage
+                                          ((1, 1960, 2000, 72), 0)])  # 128 x 128 tiles, ragged M, N
 def test_every_kind_integer_inputs(kind, ab, shape, offset):
     L, M, N, K = shape
     a, b, s = KIND_SCALARS[kind]

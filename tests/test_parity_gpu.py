@@ -319,7 +319,9 @@ KIND_SCALARS.update({a: (2.0 ** -5, 0.5, 0.125 if a == "LEAKY_RELU" else 0.0) fo
 @pytest.mark.parametrize("shape,offset", [((2, 200, 136, 264), 0),    # fast path, ragged M
                                           ((2, 200, 136, 264), 1),    # misaligned -> general kernel
                                           ((3, 77, 45, 61), 0),       # K, N not multiples of 8 -> general
-                                          ((1, 300, 520, 136), 0)])   # fast path, several tiles
+                                          ((1, 300, 520, 136), 0),    # fast path, several tiles
+                                          ((1, 3112, 3928, 40), 0),   # 256 x 256 tiles (mixed types: 128 x 256)
+                                          ((1, 1960, 2000, 72), 0)])  # 128 x 128 tiles, ragged M, N
 def test_every_kind_integer_inputs_bit_exact(kind, shape, offset):
     L, M, N, K = shape
     a, b, s = KIND_SCALARS[kind]
@@ -363,10 +365,11 @@ DEEP_SMALL_SHAPES = [(1, 64, 64, 256), (1, 64, 64, 512), (1, 1000, 1000, 520), (
                      (3, 200, 136, 1160), (1, 1280, 1280, 648), (2, 1000, 600, 1032)]
 
 
-# the 4-wave 128 x 256 and 256 x 128 tiles: 1 to 32 k stages, ragged last
-# stages, ragged M and N
+# the 4-wave 128 x 256, 256 x 128 and 128 x 128 tiles: 1 to 32 k stages,
+# ragged last stages, ragged M and N, batches
 MID_TILE_SHAPES = [(1, 3000, 2000, 520), (1, 1500, 4000, 1000), (1, 2000, 3000, 264), (1, 1500, 4000, 8),
-                   (1, 3000, 2000, 136), (2, 1100, 2600, 96)]
+                   (1, 3000, 2000, 136), (2, 1100, 2600, 96), (1, 2000, 2000, 8), (1, 1800, 2040, 264),
+                   (1, 1900, 2000, 1000), (1, 1960, 2000, 72), (2, 1100, 1304, 136), (1, 2047, 2040, 520)]
 
 
 @pytest.mark.parametrize("shape", TAIL_SHAPES + TILE_SHAPES + BIG_TILE_SHAPES + DEEP_SMALL_SHAPES + MID_TILE_SHAPES)
@@ -393,7 +396,7 @@ def test_every_tile_configuration_is_exercised():
         if cfg["vec"]:
             ring = "2-stage" if cfg["bk"] == 128 and cfg["workgroups"] > 256 else ""
             seen.add((cfg["bm"], cfg["bn"], cfg["bk"], ring))
-    assert seen == {(256, 256, 32, ""), (128, 256, 32, ""), (256, 128, 32, ""), (128, 128, 64, ""), (64, 64, 64, ""),
+    assert seen == {(256, 256, 32, ""), (128, 256, 32, ""), (256, 128, 32, ""), (128, 128, 32, ""), (64, 64, 64, ""),
                     (64, 64, 128, ""), (64, 64, 128, "2-stage")}, seen
 
 
