@@ -144,6 +144,25 @@ def test_tails_bit_exact(shape):
     check_bf16(p, "AUX_SCALE", 1.0, 2.0, 0.5, exact=True, what=f"bf16 tails {shape}")
 
 
+@pytest.mark.parametrize("kind", ["AUX_SCALE", "SQUARE"])
+def test_four_wave_128x128_repeated_short_k(kind):
+    """The bf16 128 x 128 tile with 3 k steps, called many times (the last k
+    step's barrier; see the fp16 test of every 4-wave tile)."""
+    L, M, N, K = 1, 1960, 2000, 72
+    a, b, s = KIND_SCALARS[kind]
+    log(f"[bf16] 4-wave 128x128 short K kind={kind}")
+    p = workloads.make_problem(L, M, N, K, kind, init="small_int", seed=M * N + K, dtype="bf16")
+    want = oracle.gemm_epi(p["A"], p["B"], p["C"], p["X"], kind=kind, alpha=a, beta=b, s3=s, dtype="bf16")
+    t = to_dev_bf16(p)
+    D, Aux = alloc_bf16(L, M, N), alloc_bf16(L, M, N)
+    for rep in range(12):
+        D.fill_(float("nan"))
+        Aux.fill_(float("nan"))
+        ge.run(t["A"], t["B"], t["C"], t["X"], kind=kind, alpha=a, beta=b, s3=s, D=D, Aux=Aux)
+        assert_bit_exact(bits(D), want["D"], f"bf16 {kind} launch {rep} D")
+        assert_bit_exact(bits(Aux), want["Aux"], f"bf16 {kind} launch {rep} Aux")
+
+
 def test_x_acc_bf16_8192_sampled_and_properties():
     w = workloads.WORKLOADS["x_acc_bf16_8192"]
     log(f"[bf16] {w.name}: L={w.L} M={w.M} N={w.N} K={w.K} {w.kind}")

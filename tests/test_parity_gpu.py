@@ -381,6 +381,32 @@ def test_tails_bit_exact(shape):
     check_full(p, kind, 1.0, 2.0, 0.5, exact=True, what=f"tails {shape}")
 
 
+# Short K on every 4-wave tile (2 to 4 k steps), called many times: the last k
+# step refills the B slot that slower waves read their last operands from, and
+# only its barrier keeps the two apart.  Without it the damage was rare (one
+# 16-column block of one wave, in some launches), so each shape repeats.
+FOUR_WAVE_SHORT_K = [(1, 1960, 2000, 72), (1, 1960, 2000, 40), (1, 2000, 3000, 72), (1, 3000, 2000, 104),
+                     (1, 3112, 3928, 72)]
+
+
+@pytest.mark.parametrize("shape", FOUR_WAVE_SHORT_K)
+def test_four_wave_tiles_repeated_short_k(shape):
+    L, M, N, K = shape
+    kind, a, b, s = "AUX_SCALE", 1.0, 2.0, 0.5
+    log(f"[parity] 4-wave short K shape={shape}")
+    p = workloads.make_problem(L, M, N, K, kind, init="small_int", seed=7 * K + M)
+    want = oracle_full(p, kind, a, b, s, want64=False)
+    t = to_dev(p)
+    D = alloc_out(L, M, N)
+    Aux = alloc_out(L, M, N)
+    for rep in range(12):
+        D.fill_(float("nan"))
+        Aux.fill_(float("nan"))
+        ge.run(t["A"], t["B"], t["C"], t["X"], kind=kind, alpha=a, beta=b, s3=s, D=D, Aux=Aux)
+        assert_bit_exact(D.cpu().numpy(), want["D"], f"{shape} launch {rep} D")
+        assert_bit_exact(Aux.cpu().numpy(), want["Aux"], f"{shape} launch {rep} Aux")
+
+
 def test_every_tile_configuration_is_exercised():
     """The shapes above reach all compiled tile configurations of the fast path.
     The 64 x 64 x 128 tile has two LDS rings: 4 stages, or 2 when the grid
