@@ -473,6 +473,52 @@ def copy_calibration(mib, steps):
     print(json.dumps({"copy_calibration_mib": mib, "bytes_read": n * 2, "bytes_written": n * 2, "launches": steps}))
 
 
+# Shapes off the fast path's 16-byte rule (LINCOMB, fp16, Gaussian inputs):
+# (M, N, K, element offset of every tensor from a 256-byte boundary)
+RAGGED_SHAPES = [(4096, 4096, 4095, 0), (4096, 4095, 4096, 0), (4096, 4100, 4096, 0), (4096, 4096, 4096, 1),
+                 (1001, 1001, 1001, 0)]
+
+
+def bench_ragged(steps, warmup):
+    """One JSON line per shape: the general kernel (gemm_epi_run_ext), the
+    same call with its operands staged through a workspace so that the fast
+    kernel runs (gemm_epi_run_ws_typed, the workspace gemm_epi_plan_ws
+    reports), and torch.matmul (hipBLASLt) followed by torch.add; mean launch
+    times from HIP events over `steps` calls after `warmup`."""
+    import torch
+    import dense_gemm_elementwise_amd as ge
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    g = torch.Generator().manual_seed(2025)
+
+    def tensor(shape, off):
+        n = 1
+        for x in shape:
+            n *= x
+        return torch.randn(n + off, generator=g).half().to(dev)[off:].view(shape)
+
+    for (M, N, K, off) in RAGGED_SHAPES:
+        A, B, C, D = tensor((1, M, K), off), tensor((1, K, N), off), tensor((1, M, N), off), tensor((1, M, N), off)
+        P = [t.data_ptr() for t in (A, B, C)]
+        rc, plan = ge.gemm_epi_plan_ws(1, M, N, K, P[0], P[1], P[2], None, None, None, "LINCOMB", D.data_ptr(), None,
+                                       None)
+        if rc:
+            raise RuntimeError(ge.gemm_epi_status_string(rc))
+        ws = torch.zeros(max(plan["workspace_bytes"], 16), dtype=torch.uint8, device=dev)
+        args = (1, M, N, K, P[0], P[1], P[2], None, None, None, (1.0, 1.0, 0.0), "LINCOMB", D.data_ptr(), None, None)
+        general = ge.prepared("gemm_epi_run_ext", *args, stream.cuda_stream)
+        staged = ge.prepared("gemm_epi_run_ws_typed", *args, ws.data_ptr(), ws.numel(), "f16", stream.cuda_stream)
+        line = {"shape": [1, M, N, K], "offset_elems": off, "plan_ws": plan}
+        for name, fn in (("general", general), ("staged", staged), ("torch", lambda: torch.add(torch.matmul(A, B), C))):
+            for _ in range(warmup):
+                fn()
+            _, ev_ms, stats = _timed_launches(lambda i: fn(), steps, stream)
+            line[name + "_us"] = round(ev_ms * 1e3, 1)
+        line["flops"] = 2 * M * N * K
+        print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -490,6 +536,9 @@ def main():
                          "(context, not the metric)")
     ap.add_argument("--copy-kernel", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (calibrates HBM byte counters)")
+    ap.add_argument("--ragged", action="store_true",
+                    help="only time shapes off the fast path's 16-byte rule: general kernel, staged operands, "
+                         "library (one JSON line each)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
@@ -498,6 +547,9 @@ def main():
 
     if a.copy_kernel:
         copy_calibration(a.copy_kernel, a.steps)
+        return
+    if a.ragged:
+        bench_ragged(a.steps, a.warmup)
         return
 
     from dense_gemm_elementwise_amd import workloads

@@ -259,7 +259,7 @@ def gemm_epi_run_ws_static(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, 
 
 def gemm_epi_plan_ws(L, M, N, K, A, B, C, X, row_bias, col_bias, epilogue_kind, D, Aux, acc_out):
     """Host-only plan of gemm_epi_run_ws: (status, dict) with the keys of
-    gemm_epi_plan plus workspace_bytes (0: no split)."""
+    gemm_epi_plan plus workspace_bytes (0: no split and no staging)."""
     out = (ctypes.c_int64 * 7)()
     rc = lib().gemm_epi_plan_ws(int(L), int(M), int(N), int(K), A, B, C, X, row_bias, col_bias,
                                 _kind_id(epilogue_kind), D, Aux, acc_out, out)
@@ -304,7 +304,7 @@ def _ptr(t):
 
 
 def run(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, D, Aux=None, row_bias=None, col_bias=None,
-        acc_out=None, stream=None, sync=True, unfused_workspace=None, stream_k_workspace=None):
+        acc_out=None, stream=None, sync=True, unfused_workspace=None, workspace=None, stream_k_workspace=None):
     """D (and Aux, acc_out) <- fused epilogue of A @ B on torch tensors.
 
     A (L,M,K), B (L,K,N), C, X, D, Aux (L,M,N): contiguous float16 CUDA
@@ -318,10 +318,13 @@ def run(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, D, Aux=None,
     default: the current stream); with sync=True the call waits for it.
     With unfused_workspace (a float32 CUDA tensor of at least L*M*N
     elements) the unfused two-launch composition runs instead of the fused
-    kernel (for comparison; the outputs are the same).  With
-    stream_k_workspace (a zero-initialised CUDA tensor of at least the
-    workspace_bytes gemm_epi_plan_ws reports) the call may split K across
-    workgroups (gemm_epi_run_ws).
+    kernel (for comparison; the outputs are the same).  With workspace (a
+    zero-initialised CUDA tensor of at least the workspace_bytes
+    gemm_epi_plan_ws reports; stream_k_workspace is the same argument under
+    its older name) the call goes through gemm_epi_run_ws: it may split K
+    across workgroups, and operands that miss the fast kernel's layout rules
+    (K or N not a multiple of 8, a tensor not 16-byte aligned) are staged
+    through the workspace so that the fast kernel runs.
     """
     import torch
     if A.dim() != 3 or B.dim() != 3:
@@ -365,12 +368,14 @@ def run(A, B, C=None, X=None, *, kind, alpha=1.0, beta=0.0, s3=0.0, D, Aux=None,
     ws = unfused_workspace
     if ws is not None and (ws.dtype != torch.float32 or ws.device != dev or not ws.is_contiguous()):
         raise ValueError("unfused_workspace must be a contiguous float32 tensor on the operands' device")
-    skw = stream_k_workspace
+    if workspace is not None and stream_k_workspace is not None:
+        raise ValueError("pass workspace or stream_k_workspace (the same argument), not both")
+    skw = workspace if workspace is not None else stream_k_workspace
     if skw is not None and (skw.device != dev or not skw.is_contiguous()):
-        raise ValueError("stream_k_workspace must be a contiguous tensor on the operands' device")
+        raise ValueError("workspace must be a contiguous tensor on the operands' device")
     dt = DTYPES["bf16"] if at == torch.bfloat16 else DTYPES["f16"]
     if et != at and (ws is not None or skw is not None):
-        raise ValueError("the unfused and stream-K compositions take epilogue tensors of A's type only")
+        raise ValueError("the unfused composition and the workspace call take epilogue tensors of A's type only")
     ops = (L, M, N, K, A.data_ptr(), B.data_ptr(), _ptr(C), _ptr(X), _ptr(row_bias), _ptr(col_bias),
            (alpha, beta, s3), KINDS[kname], D.data_ptr(), _ptr(Aux), _ptr(acc_out))
     with torch.cuda.device(dev):

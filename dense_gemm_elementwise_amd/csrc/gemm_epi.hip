@@ -275,6 +275,133 @@ int launch_split(int64_t L, int64_t M, int64_t N, const Operands &o, const float
     return GEMM_EPI_OK;
 }
 
+// ---- staging through the workspace -------------------------------------------
+// Operands that break the fast path's layout rules (K or N not a multiple of
+// 8, or a tensor not 16-byte aligned) are copied into aligned, zero-padded
+// buffers in the workspace, so that the fast kernel runs on them; outputs
+// that break them are written there and copied back.  K % 8 != 0 pads A's
+// rows and B's row count to K8 (the zero products add nothing); N % 8 != 0
+// gives B and every M x N tensor rows of N8 elements.  Otherwise only the
+// misaligned tensors are copied.  The regions start after the stream-K
+// counter block, which staging never touches.
+struct StagePlan {
+    bool on = false;
+    int64_t K = 0, N = 0;  // the fast kernel's K and N
+    bool a = false, b = false, c = false, x = false, rb = false, d = false, aux = false, acc = false;
+    size_t off_a = 0, off_b = 0, off_c = 0, off_x = 0, off_rb = 0, off_d = 0, off_aux = 0, off_acc = 0;
+    size_t bytes = 0;  // workspace bytes the staged call needs
+};
+
+StagePlan plan_staging(int64_t L, int64_t M, int64_t N, int64_t K, const Operands &o, int kind)
+{
+    StagePlan st;
+    const bool kr = K % 8 != 0, nr = N % 8 != 0;
+    st.K = (K + 7) / 8 * 8;
+    st.N = (N + 7) / 8 * 8;
+    st.a = kr || !aligned(o.A, 16);
+    st.b = kr || nr || !aligned(o.B, 16);
+    st.c = kind_reads_c(kind) && (nr || !aligned(o.C, 16));
+    st.x = kind_reads_x(kind) && (nr || !aligned(o.X, 16));
+    st.rb = kind_reads_bias(kind) && (nr || !aligned(o.row_bias, 16));
+    st.d = kind_writes_d(kind) && (nr || !aligned(o.D, 16));
+    st.aux = kind_has_aux(kind) && (nr || !aligned(o.Aux, 16));
+    st.acc = kind_has_acc_out(kind) && (nr || !aligned(o.acc_out, 16));
+    // the staged call must meet the fast path's size rules (16-byte aligned
+    // stand-ins for every pointer)
+    const void *al = (const void *)(uintptr_t)4096;
+    const Operands staged = {al, al, al, al, al, al, al, al, al};
+    if (!use_fast_path(M, st.N, st.K, staged, kind)) return st;
+    size_t off = kSkCounterBytes;
+    auto take = [&](bool on, int64_t elems, int es) {
+        if (!on) return (size_t)0;
+        const size_t at = off;
+        off = (off + (size_t)elems * es + 255) & ~(size_t)255;
+        return at;
+    };
+    st.off_a = take(st.a, L * M * st.K, 2);
+    st.off_b = take(st.b, L * st.K * st.N, 2);
+    st.off_c = take(st.c, L * M * st.N, 2);
+    st.off_x = take(st.x, L * M * st.N, 2);
+    st.off_rb = take(st.rb, st.N, 2);
+    st.off_d = take(st.d, L * M * st.N, 2);
+    st.off_aux = take(st.aux, L * M * st.N, 2);
+    st.off_acc = take(st.acc, L * M * st.N, 4);
+    st.bytes = off;
+    st.on = true;
+    return st;
+}
+
+template <typename T>
+hipError_t launch_stage(bool pad, const void *src, void *dst, int64_t L, int64_t rows, int64_t cols, int64_t prows,
+                        int64_t pcols, hipStream_t stream)
+{
+    StageCopy q = {src, dst, L, rows, cols, prows, pcols};
+    const int64_t n = L * (pad ? prows : rows);
+    const unsigned blocks = (unsigned)(n < 8192 ? n : 8192);
+    void *args[] = {(void *)&q};
+    const void *fn = pad ? (const void *)&stage_pad_kernel<T> : (const void *)&stage_unpad_kernel<T>;
+    return hipLaunchKernel(fn, dim3(blocks), dim3(256), args, 0, stream);
+}
+
+// Runs a checked call through the staging plan: copies in, the fast kernel on
+// the staged operand set, copies out, all on `stream`.
+int launch_staged(int64_t L, int64_t M, int64_t N, int64_t K, const Operands &o, const float *scalars, int kind,
+                  const StagePlan &st, void *workspace, int dtype, hipStream_t s)
+{
+    char *ws = (char *)workspace;
+    auto at = [&](bool on, size_t off, const void *orig) { return on ? (void *)(ws + off) : const_cast<void *>(orig); };
+    Params p = {};
+    p.A = (const _Float16 *)at(st.a, st.off_a, o.A);
+    p.B = (const _Float16 *)at(st.b, st.off_b, o.B);
+    p.C = (const _Float16 *)at(st.c, st.off_c, o.C);
+    p.X = (const _Float16 *)at(st.x, st.off_x, o.X);
+    p.row_bias = (const _Float16 *)at(st.rb, st.off_rb, o.row_bias);
+    p.col_bias = (const _Float16 *)o.col_bias;
+    p.D = (_Float16 *)at(st.d, st.off_d, o.D);
+    p.Aux = (_Float16 *)at(st.aux, st.off_aux, o.Aux);
+    p.acc_out = (float *)at(st.acc, st.off_acc, o.acc_out);
+    const TileCfg t = choose_tile(L, M, st.N, st.K, true);
+    const int64_t tm = (M + t.bm - 1) / t.bm, tn = (st.N + t.bn - 1) / t.bn;
+    const int64_t tiles = L * tm * tn;
+    if (tiles > INT32_MAX) return GEMM_EPI_ERR_SHAPE;
+    p.M = (int)M;
+    p.N = (int)st.N;
+    p.K = (int)st.K;
+    p.tiles_m = (int)tm;
+    p.tiles_n = (int)tn;
+    p.num_tiles = (int)tiles;
+    p.group_m = L > 1 ? 2 : 8;
+    p.alpha = scalars[0];
+    p.beta = scalars[1];
+    p.s = scalars[2];
+
+    hipError_t err = hipSuccess;
+    auto step = [&](hipError_t e) {
+        if (err == hipSuccess) err = e;
+    };
+    if (st.a) step(launch_stage<uint16_t>(true, o.A, (void *)p.A, L, M, K, M, st.K, s));
+    if (st.b && err == hipSuccess) step(launch_stage<uint16_t>(true, o.B, (void *)p.B, L, K, N, st.K, st.N, s));
+    if (st.c && err == hipSuccess) step(launch_stage<uint16_t>(true, o.C, (void *)p.C, L, M, N, M, st.N, s));
+    if (st.x && err == hipSuccess) step(launch_stage<uint16_t>(true, o.X, (void *)p.X, L, M, N, M, st.N, s));
+    if (st.rb && err == hipSuccess)
+        step(launch_stage<uint16_t>(true, o.row_bias, (void *)p.row_bias, 1, 1, N, 1, st.N, s));
+    if (err == hipSuccess) {
+        if (dtype == GEMM_EPI_BF16)
+            step(launch_fused_bf16(kind, p, t, true, s));
+        else
+            step(dispatch_kind(kind, [&](auto k) { return launch_kind<decltype(k)::value>(p, t, true, s); }));
+    }
+    if (st.d && err == hipSuccess) step(launch_stage<uint16_t>(false, p.D, (void *)o.D, L, M, N, M, st.N, s));
+    if (st.aux && err == hipSuccess) step(launch_stage<uint16_t>(false, p.Aux, (void *)o.Aux, L, M, N, M, st.N, s));
+    if (st.acc && err == hipSuccess)
+        step(launch_stage<uint32_t>(false, p.acc_out, (void *)o.acc_out, L, M, N, M, st.N, s));
+    if (err != hipSuccess) {
+        g_last_hip_error = (int)err;
+        return GEMM_EPI_ERR_HIP;
+    }
+    return GEMM_EPI_OK;
+}
+
 // ---- the scratch-free stream-K call (gemm_epi_run_ws_static) ----------------
 // For callers that cannot allocate (code under HIP graph capture, tight
 // serving loops, harnesses that forbid hipMalloc): the split's counters and
@@ -549,6 +676,24 @@ int gemm_epi_plan_ws(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, 
     int rc = check_args(L, M, N, K, o, epilogue_kind);
     if (rc != GEMM_EPI_OK) return rc;
     const bool vec = use_fast_path(M, N, K, o, epilogue_kind);
+    if (!vec) {
+        const StagePlan st = plan_staging(L, M, N, K, o, epilogue_kind);
+        if (st.on) {
+            const TileCfg t = choose_tile(L, M, st.N, st.K, true);
+            const int64_t tiles = L * ((M + t.bm - 1) / t.bm) * ((st.N + t.bn - 1) / t.bn);
+            if (tiles > INT32_MAX) return GEMM_EPI_ERR_SHAPE;
+            if (out) {
+                out[0] = t.bm;
+                out[1] = t.bn;
+                out[2] = t.bk;
+                out[3] = 1;
+                out[4] = tiles;
+                out[5] = 64 * t.wgm * t.wgn;
+                out[6] = (int64_t)st.bytes;
+            }
+            return GEMM_EPI_OK;
+        }
+    }
     const SkPlan sk = plan_stream_k(L, M, N, K, vec);
     if (!sk.on) {
         int64_t o6[6];
@@ -590,6 +735,11 @@ int gemm_epi_run_ws_typed(int64_t L, int64_t M, int64_t N, int64_t K, const void
     if (dtype != GEMM_EPI_F16 && dtype != GEMM_EPI_BF16) return GEMM_EPI_ERR_DTYPE;
     if (!scalars) return GEMM_EPI_ERR_NULL_INPUT;
     const bool vec = use_fast_path(M, N, K, o, epilogue_kind);
+    if (!vec) {
+        const StagePlan st = plan_staging(L, M, N, K, o, epilogue_kind);
+        if (st.on && workspace && workspace_bytes >= st.bytes && aligned(workspace, 16))
+            return launch_staged(L, M, N, K, o, scalars, epilogue_kind, st, workspace, dtype, (hipStream_t)stream);
+    }
     const SkPlan sk = plan_stream_k(L, M, N, K, vec);
     if (!sk.on)
         return gemm_epi_run_typed(L, M, N, K, A, B, C, X, row_bias, col_bias, scalars, epilogue_kind, D, Aux,

@@ -1736,4 +1736,80 @@ __global__ __launch_bounds__(256) void epilogue_kernel(EpiParams q)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Staging copies of the workspace path.  A tensor that breaks the fast
+// path's layout rules (a row length that is not a multiple of 8 elements, or
+// a base address that is not 16-byte aligned) is copied into an aligned
+// buffer whose rows are padded with zeros to a multiple of 8 elements, and an
+// output is written there and copied back afterwards.  Pure copies of raw
+// element bits (T: 2 or 4 bytes) at any element-aligned address, one row of
+// one batch entry per iteration of a block.
+// ---------------------------------------------------------------------------
+struct StageCopy {
+    const void *src;
+    void *dst;
+    int64_t L;
+    int64_t rows, cols;  // the unpadded tensor (L, rows, cols)
+    int64_t prows, pcols;  // the padded one: prows >= rows, pcols >= cols
+};
+
+// Both copies move one element per lane and access, adjacent lanes on
+// adjacent elements, so each wave access covers one contiguous span (128
+// bytes of 2-byte elements) whatever the rows' alignment; four accesses per
+// lane are in flight at a time.
+constexpr int kStageUnroll = 4;
+
+// padded (L, prows, pcols) <- src (L, rows, cols), zeros past rows and cols
+// (q.dst).
+template <typename T>
+__global__ __launch_bounds__(256) void stage_pad_kernel(StageCopy q)
+{
+    const int64_t nrows = q.L * q.prows;
+    for (int64_t row = blockIdx.x; row < nrows; row += gridDim.x) {
+        const int64_t l = row / q.prows, r = row - l * q.prows;
+        const int64_t cols = r < q.rows ? q.cols : 0;  // source elements in this row
+        const T *s = (const T *)q.src + (l * q.rows + (r < q.rows ? r : 0)) * q.cols;
+        T *d = (T *)q.dst + row * q.pcols;
+        for (int64_t c0 = threadIdx.x; c0 < q.pcols; c0 += 256 * kStageUnroll) {
+            T v[kStageUnroll];
+#pragma unroll
+            for (int u = 0; u < kStageUnroll; u++) {
+                const int64_t c = c0 + 256 * u;
+                v[u] = c < cols ? s[c] : (T)0;
+            }
+#pragma unroll
+            for (int u = 0; u < kStageUnroll; u++) {
+                const int64_t c = c0 + 256 * u;
+                if (c < q.pcols) d[c] = v[u];
+            }
+        }
+    }
+}
+
+// dst (L, rows, cols) <- the first rows and cols of padded (L, prows, pcols)
+// (q.src).
+template <typename T>
+__global__ __launch_bounds__(256) void stage_unpad_kernel(StageCopy q)
+{
+    const int64_t nrows = q.L * q.rows;
+    for (int64_t row = blockIdx.x; row < nrows; row += gridDim.x) {
+        const int64_t l = row / q.rows, r = row - l * q.rows;
+        const T *s = (const T *)q.src + (l * q.prows + r) * q.pcols;
+        T *d = (T *)q.dst + row * q.cols;
+        for (int64_t c0 = threadIdx.x; c0 < q.cols; c0 += 256 * kStageUnroll) {
+            T v[kStageUnroll];
+#pragma unroll
+            for (int u = 0; u < kStageUnroll; u++) {
+                const int64_t c = c0 + 256 * u;
+                v[u] = c < q.cols ? s[c] : (T)0;
+            }
+#pragma unroll
+            for (int u = 0; u < kStageUnroll; u++) {
+                const int64_t c = c0 + 256 * u;
+                if (c < q.cols) d[c] = v[u];
+            }
+        }
+    }
+}
+
 }  // namespace gemm_epi

@@ -290,11 +290,22 @@ int gemm_epi_run_unfused_typed(int64_t L, int64_t M, int64_t N, int64_t K, const
  * workspace; the last workgroup to finish its part of the tile adds them up,
  * in k order, and applies the epilogue (the epilogue is not linear, so it
  * only ever sees the full sum).  Where splitting does not pay, the call is
- * exactly gemm_epi_run_ext and the workspace is not touched.
+ * exactly gemm_epi_run_ext and the workspace is not touched, with one
+ * exception.  Operands that miss the fast kernel's layout rules (the 16-byte
+ * alignment rule of the Custom Epilogue Example's "Constraints": K or N not a
+ * multiple of 8, or a tensor not 16-byte aligned) are staged through the
+ * workspace when it is large enough.  The call copies them into aligned
+ * buffers whose rows are padded with zeros, runs the fast kernel on those and
+ * copies padded outputs back, all on `stream` (the zero products leave every
+ * sum unchanged, so the results are gemm_epi_run_ext's, up to the sign of a
+ * zero).  With a smaller workspace, or none, such a call runs
+ * gemm_epi_run_ext's general kernel instead.  Staging never writes the
+ * counter block below.
  *
  *   workspace        device pointer, 16-byte aligned, of at least the size
- *                    gemm_epi_plan_ws reports in out[6] (0 when no split is
- *                    planned: NULL is then accepted); owned by the caller.  It
+ *                    gemm_epi_plan_ws reports in out[6] (0 when neither a
+ *                    split nor staging is planned: NULL is then accepted);
+ *                    owned by the caller.  It
  *                    must be zero-filled before its first use (e.g. one
  *                    hipMemset); every call leaves it ready for the next,
  *                    whatever the shape: the per-tile counters sit in a
@@ -316,9 +327,9 @@ int gemm_epi_run_ws(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, c
 
 /*
  * gemm_epi_run_ws_typed -- gemm_epi_run_ws with the element type of the
- * 16-bit tensors as an argument, as in gemm_epi_run_typed.  The split
- * (gemm_epi_plan_ws) and the workspace do not depend on dtype; where no
- * split is planned the call is exactly gemm_epi_run_typed.  Status codes as
+ * 16-bit tensors as an argument, as in gemm_epi_run_typed.  The split or
+ * staging (gemm_epi_plan_ws) and the workspace do not depend on dtype; where
+ * neither is planned the call is exactly gemm_epi_run_typed.  Status codes as
  * gemm_epi_run_ws, plus GEMM_EPI_ERR_DTYPE.
  */
 int gemm_epi_run_ws_typed(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
@@ -338,7 +349,7 @@ int gemm_epi_run_ws_typed(int64_t L, int64_t M, int64_t N, int64_t K, const void
  * Its splits use at most 128 workgroups (so its plan can differ from
  * gemm_epi_plan_ws's, which allows 256; results are the same on integer
  * inputs and within the fp32 summation order otherwise); where no split
- * pays the call is exactly gemm_epi_run_typed.  Every call on one GPU shares
+ * pays the call is exactly gemm_epi_run_typed (it does not stage operands).  Every call on one GPU shares
  * that GPU's array: calls that overlap in time on one GPU (two streams, two
  * threads) race.  `stream` must belong to the calling thread's current
  * device.  Status codes as gemm_epi_run_ws_typed; GEMM_EPI_ERR_WORKSPACE if a
@@ -351,7 +362,8 @@ int gemm_epi_run_ws_static(int64_t L, int64_t M, int64_t N, int64_t K, const voi
 
 /* gemm_epi_plan_ext for gemm_epi_run_ws: out[0..5] as gemm_epi_plan (out[4] is
  * the number of workgroups, the split's workgroup count when it splits), and
- * out[6] the workspace bytes the call needs (0: no split). */
+ * out[6] the workspace bytes the call needs (0: no split and no staging).  A
+ * call that stages its operands reports the fast kernel's tile, out[3] = 1. */
 int gemm_epi_plan_ws(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
                      const void *X, const void *row_bias, const void *col_bias, int epilogue_kind, const void *D,
                      const void *Aux, const void *acc_out, int64_t out[7]);

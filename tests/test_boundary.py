@@ -375,3 +375,38 @@ def test_prepared_call_checks_its_entry_point_and_arguments():
         ge.prepared("no_such_entry", *args)
     with pytest.raises(ValueError):
         ge.prepared("gemm_epi_run_ext", *args[:-1])
+
+
+def test_plan_ws_stages_operands_that_miss_the_layout_rules():
+    """A shape or pointer off the fast path's 16-byte rule gets the fast kernel
+    on staged copies: the plan reports that kernel's tile (vec 1) and the
+    workspace of the zero-padded copies, each in 256-byte granules after the
+    16 KiB stream-K counter block, which staging leaves alone."""
+    r256 = lambda n: (n + 255) // 256 * 256
+
+    def ws(L, M, N, K, kind, a=P16, b=P16, c=P16, d=P16, aux=None, acc=None, rb=None, cb=None):
+        rc, cfg = ge.gemm_epi_plan_ws(L, M, N, K, a, b, c, None, rb, cb, kind, d, aux, acc)
+        assert rc == 0
+        return cfg
+
+    sq = 4096 * 4096 * 2
+    cfg = ws(1, 4096, 4096, 4095, "LINCOMB")  # K % 8 != 0: A (M x K8) and B (K8 x N)
+    assert (cfg["bm"], cfg["bn"], cfg["bk"], cfg["vec"]) == (256, 256, 32, 1)
+    assert cfg["workspace_bytes"] == 16384 + 2 * sq
+    cfg = ws(1, 4096, 4095, 4096, "LINCOMB")  # N % 8 != 0: B, C and D with rows of N8
+    assert cfg["vec"] == 1 and cfg["workspace_bytes"] == 16384 + 3 * sq
+    cfg = ws(1, 64, 64, 64, "LINCOMB", a=P16 + 2)  # only A misaligned
+    assert cfg["vec"] == 1 and cfg["workspace_bytes"] == 16384 + 64 * 64 * 2
+    cfg = ws(1, 64, 64, 64, "LINCOMB", c=P16 + 6, d=P16 + 2)  # only C and D
+    assert cfg["workspace_bytes"] == 16384 + 2 * 64 * 64 * 2
+    # N = 99 -> 104: B, C, D, Aux (F) and the fp32 accumulator
+    cfg = ws(1, 100, 99, 64, "RELU_SCALE_ACC", aux=P16, acc=P16)
+    assert cfg["workspace_bytes"] == 16384 + r256(64 * 104 * 2) + 3 * r256(100 * 104 * 2) + r256(100 * 104 * 4)
+    # N = 60 -> 64: B, the row bias and D (no C); the column bias needs no copy
+    cfg = ws(1, 64, 60, 64, "BIAS_ROW_COL", c=None, rb=P16, cb=P16 + 2)
+    assert cfg["workspace_bytes"] == 16384 + 64 * 64 * 2 + 256 + 64 * 64 * 2
+    # aligned shapes and pointers stage nothing
+    assert ws(1, 1024, 1024, 1024, "LINCOMB")["workspace_bytes"] == 0
+    # a staged A of 2 GiB or more breaks the fast path's 32-bit offsets: the general kernel, no workspace
+    cfg = ws(1, 1 << 21, 1000, 1001, "LINCOMB")
+    assert cfg["vec"] == 0 and cfg["workspace_bytes"] == 0
