@@ -1,8 +1,8 @@
 /*
  * c_abi_check.c -- the C ABI of libgemm_epi.so used from plain C (no Python,
- * no torch): device buffers from the HIP runtime, one call per case, results
- * compared bit for bit with the CPU oracle (liboracle.so, test
- * infrastructure).
+ * no torch): device buffers from the HIP runtime, one call per case (the
+ * typed, mixed and workspace entry points), results compared bit for bit
+ * with the CPU oracle (liboracle.so, test infrastructure).
  *
  * Inputs are small integers drawn by a seeded linear congruential
  * generator, so every product and partial sum is exact and the final
@@ -87,8 +87,11 @@ static int same_bits(const uint16_t *g, const uint16_t *w, size_t n, const char 
     return bad == 0;
 }
 
-/* A, B of type dtype; C, X, D, Aux of the 16-bit type epi (gemm_epi_run_mixed) */
-static int run_case(int kind, int dtype, int epi, int64_t L, int64_t M, int64_t N, int64_t K, const float sc[3])
+/* A, B of type dtype; C, X, D, Aux of the 16-bit type epi (gemm_epi_run_mixed).  With staged != 0 (epi ==
+ * dtype, a shape off the fast path's 16-byte rule) the call is gemm_epi_run_ws_typed with the workspace
+ * gemm_epi_plan_ws reports, which must stage the operands for the fast kernel. */
+static int run_case(int kind, int dtype, int epi, int64_t L, int64_t M, int64_t N, int64_t K, const float sc[3],
+                    int staged)
 {
     const int has_aux = kind == GEMM_EPI_AUX_SCALE || kind == GEMM_EPI_LINCOMB_X_ACC || kind == GEMM_EPI_SQUARE ||
                         kind == GEMM_EPI_RELU_SQUARE || kind == GEMM_EPI_RELU_AUX_STORE;
@@ -102,11 +105,26 @@ static int run_case(int kind, int dtype, int epi, int64_t L, int64_t M, int64_t 
     CHECK_HIP(hipMalloc(&dD, nc * 2));
     if (has_aux) CHECK_HIP(hipMalloc(&dAux, nc * 2));
 
-    int ok = 1;
-    const int rc = epi == dtype
-                       ? gemm_epi_run_typed(L, M, N, K, dA, dB, dC, dX, NULL, NULL, sc, kind, dD, dAux, NULL, dtype, NULL)
-                       : gemm_epi_run_mixed(L, M, N, K, dA, dB, dC, dX, NULL, NULL, sc, kind, dD, dAux, NULL, dtype, epi,
-                                            NULL);
+    int ok = 1, rc;
+    void *ws = NULL;
+    if (staged) {
+        int64_t plan[7];
+        rc = gemm_epi_plan_ws(L, M, N, K, dA, dB, dC, dX, NULL, NULL, kind, dD, dAux, NULL, plan);
+        if (rc == GEMM_EPI_OK && !(plan[3] == 1 && plan[6] > 16384)) {
+            fprintf(stderr, "  no staging planned (vec %lld, workspace %lld)\n", (long long)plan[3], (long long)plan[6]);
+            ok = 0;
+        }
+        if (rc == GEMM_EPI_OK) {
+            CHECK_HIP(hipMalloc(&ws, (size_t)plan[6]));
+            CHECK_HIP(hipMemset(ws, 0, (size_t)plan[6]));
+            rc = gemm_epi_run_ws_typed(L, M, N, K, dA, dB, dC, dX, NULL, NULL, sc, kind, dD, dAux, NULL, ws,
+                                       (size_t)plan[6], dtype, NULL);
+        }
+    } else {
+        rc = epi == dtype
+                 ? gemm_epi_run_typed(L, M, N, K, dA, dB, dC, dX, NULL, NULL, sc, kind, dD, dAux, NULL, dtype, NULL)
+                 : gemm_epi_run_mixed(L, M, N, K, dA, dB, dC, dX, NULL, NULL, sc, kind, dD, dAux, NULL, dtype, epi, NULL);
+    }
     if (rc != GEMM_EPI_OK) {
         fprintf(stderr, "  the call returned %d (%s)\n", rc, gemm_epi_status_string(rc));
         ok = 0;
@@ -129,9 +147,11 @@ static int run_case(int kind, int dtype, int epi, int64_t L, int64_t M, int64_t 
         free(Dref);
         free(Auxref);
     }
-    printf("%s kind=%d dtype=%s epi=%s L=%lld M=%lld N=%lld K=%lld\n", ok ? "PASS" : "FAIL", kind, type_name(dtype),
-           type_name(epi), (long long)L, (long long)M, (long long)N, (long long)K);
+    printf("%s kind=%d dtype=%s epi=%s L=%lld M=%lld N=%lld K=%lld%s\n", ok ? "PASS" : "FAIL", kind,
+           type_name(dtype), type_name(epi), (long long)L, (long long)M, (long long)N, (long long)K,
+           staged ? " staged" : "");
     fflush(stdout);
+    hipFree(ws);
     hipFree(dA);
     hipFree(dB);
     hipFree(dC);
@@ -212,14 +232,17 @@ int main(void)
     const float lin[3] = {1.0f, 2.0f, 0.0f}, aux[3] = {1.0f, 2.0f, 0.5f}, xacc[3] = {2.0f, 1.0f, 3.0f};
     int fails = 0;
     for (int dtype = GEMM_EPI_F16; dtype <= GEMM_EPI_BF16; dtype++) {
-        fails += !run_case(GEMM_EPI_LINCOMB, dtype, dtype, 1, 256, 512, 128, lin);
-        fails += !run_case(GEMM_EPI_AUX_SCALE, dtype, dtype, 2, 200, 136, 264, aux);
-        fails += !run_case(GEMM_EPI_LINCOMB_X_ACC, dtype, dtype, 1, 520, 776, 88, xacc);
-        fails += !run_case(GEMM_EPI_RELU_SQUARE, dtype, dtype, 3, 77, 45, 61, lin); /* general kernel: K, N % 8 != 0 */
+        fails += !run_case(GEMM_EPI_LINCOMB, dtype, dtype, 1, 256, 512, 128, lin, 0);
+        fails += !run_case(GEMM_EPI_AUX_SCALE, dtype, dtype, 2, 200, 136, 264, aux, 0);
+        fails += !run_case(GEMM_EPI_LINCOMB_X_ACC, dtype, dtype, 1, 520, 776, 88, xacc, 0);
+        fails += !run_case(GEMM_EPI_RELU_SQUARE, dtype, dtype, 3, 77, 45, 61, lin, 0); /* general kernel: K, N % 8 != 0 */
+        /* the same kind of shapes staged through a workspace for the fast kernel */
+        fails += !run_case(GEMM_EPI_RELU_SQUARE, dtype, dtype, 3, 77, 45, 61, lin, 1);
+        fails += !run_case(GEMM_EPI_LINCOMB_X_ACC, dtype, dtype, 1, 300, 517, 139, xacc, 1);
     }
     /* the other element-type pairs of gemm_epi_run_mixed */
-    fails += !run_case(GEMM_EPI_AUX_SCALE, GEMM_EPI_F16, GEMM_EPI_BF16, 2, 200, 136, 264, aux);
-    fails += !run_case(GEMM_EPI_LINCOMB_X_ACC, GEMM_EPI_BF16, GEMM_EPI_F16, 1, 520, 776, 88, xacc);
+    fails += !run_case(GEMM_EPI_AUX_SCALE, GEMM_EPI_F16, GEMM_EPI_BF16, 2, 200, 136, 264, aux, 0);
+    fails += !run_case(GEMM_EPI_LINCOMB_X_ACC, GEMM_EPI_BF16, GEMM_EPI_F16, 1, 520, 776, 88, xacc, 0);
     fails += !run_case_f32(GEMM_EPI_LINCOMB_X_ACC, GEMM_EPI_F16, 1, 520, 776, 88, xacc);
     fails += !run_case_f32(GEMM_EPI_RELU_SQUARE, GEMM_EPI_BF16, 3, 77, 45, 61, lin);
     /* an argument error comes back as a status code, before any launch */

@@ -2,8 +2,10 @@
 __graft_entry__.build()) calls gemm_epi_run_typed for fp16 and bf16 tensors
 and gemm_epi_run_mixed for the other element-type pairs (fp32 or the other
 16-bit type for the epilogue tensors) on integer inputs, fast and general
-kernels, and compares every output bit for bit with the CPU oracle; it also checks that an argument error comes
-back as a status code.  It runs as a child process."""
+kernels, and gemm_epi_run_ws_typed with the workspace gemm_epi_plan_ws
+reports, which stages ragged operands for the fast kernel; it compares every
+output bit for bit with the CPU oracle and checks that an argument error
+comes back as a status code.  It runs as a child process."""
 import os
 import subprocess
 
@@ -18,4 +20,5 @@ def test_c_program_against_the_oracle():
     r = subprocess.run([EXE], capture_output=True, text=True, timeout=120)
     print(r.stdout, r.stderr, flush=True)
     assert r.returncode == 0, r.stdout + r.stderr
-    assert r.stdout.count("PASS kind=") == 12 and "PASS: 0 failing case(s)" in r.stdout
+    assert r.stdout.count("PASS kind=") == 16 and r.stdout.count(" staged\n") == 4
+    assert "PASS: 0 failing case(s)" in r.stdout
