@@ -1,7 +1,8 @@
 """Seeded random sweep over the shape space: batch 1-3, M, N, K from 1 to
 700 (K up to 2100), every kind, fp16 and bf16 tensors, aligned and
 misaligned pointers (fast and general kernels), the fused call, the
-stream-K entry point, and epilogue tensors of another type than A and B
+stream-K entry point and the staging of ragged or misaligned operands
+through its workspace, and epilogue tensors of another type than A and B
 (fp32 or the other 16-bit type).  Integer-valued inputs keep every sum exact, so each
 case is bit-exact against the oracle (activation kinds: within one ulp and
 mostly bit-identical, as in the other parity tests).
@@ -112,3 +113,36 @@ def test_random_mixed_types_case(case):
         import test_mixed16_gpu as m16
         p = m16.problem(L, M, N, K, kind, ab, epi, seed=3000 + c, init="small_int")
         m16.check(p, kind, ab, epi, a, b, s, exact=True, offset=offset, what=f"random mixed case {c}")
+
+
+def staged_cases(n=24, seed=20251203):
+    """Shapes or pointers off the 16-byte rule: K or N not a multiple of 8, or
+    tensors at odd element offsets."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        L = int(rng.integers(1, 4))
+        M, N = (int(v) for v in rng.integers(1, 701, 2))
+        K = int(rng.integers(1, 2101))
+        offs = (0, 0, 0, 0)
+        if rng.random() < 0.4 or (N % 8 == 0 and K % 8 == 0):  # tensors off their 16-byte boundary too
+            offs = tuple(int(v) for v in rng.integers(0, 8, 4))
+            if not any(offs):
+                offs = (1, 0, 0, 0)
+        kind = workloads.KINDS[int(rng.integers(0, len(workloads.KINDS)))]
+        dtype = torch.bfloat16 if rng.random() < 0.3 else torch.float16
+        out.append((c, L, M, N, K, kind, dtype, offs))
+    return out
+
+
+@pytest.mark.parametrize("case", staged_cases(),
+                         ids=lambda c: f"s{c[0]}-{c[5]}-{str(c[6])[6:]}-{c[1]}x{c[2]}x{c[3]}x{c[4]}-{''.join(map(str, c[7]))}")
+def test_random_staged_case(case):
+    """The workspace call staging the operands for the fast kernel."""
+    from test_staged_gpu import compare, run_staged
+    c, L, M, N, K, kind, dtype, offs = case
+    dt = "bf16" if dtype == torch.bfloat16 else "f16"
+    log(f"[random staged] case {c}: L={L} M={M} N={N} K={K} {kind} {dt} offsets={offs}")
+    p = workloads.make_problem(L, M, N, K, kind, init="small_int", seed=3000 + c, dtype=dt)
+    got = run_staged(p, kind, offs, dtype)
+    compare(got, p, kind, True, dtype, f"random staged case {c}")
