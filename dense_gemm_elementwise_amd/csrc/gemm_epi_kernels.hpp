@@ -942,7 +942,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     constexpr bool SLAB_SWZ = WN <= 64;
     constexpr int EPI_LD = SLAB_SWZ ? WN : WN + (MI == 32 ? 8 : 4);
     constexpr int EPI_BYTES = NW * SLAB * EPI_LD * 4;
-    // the 4-wave 256 x 256 configuration runs the hand-scheduled main loop
+    // the 4-wave tiles (256 x 256, 128 x 256, 256 x 128, 128 x 128) run the
+    // hand-scheduled main loop
     constexpr bool W4 = NW == 4 && BM >= 128 && BN >= 128 && BK == W4_BK && NSTAGES == W4_NS && MI == 16 && VEC && !SK;
     constexpr int W4_LDS = w4_lds<W4, BM, BN>();
     // The 64 x 64 x 128 tile splits the k range of every stage over its waves
@@ -1448,8 +1449,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     // kind with the fp32 accumulator output keeps 4 columns per lane on the
     // 8-wave tiles: with 8, each 16-byte fp32 store instruction would fill
     // only half of every cache line it touches (measured 6% slower).  On the
-    // 4-wave tile it takes 8 as well: with 4 its epilogue runs out of VGPRs
-    // and spills.  C / X (and the column bias) of a slab are loaded
+    // 4-wave tiles with 128-wide wave tiles it takes 8 as well: with 4 their
+    // epilogue runs out of VGPRs and spills.  C / X (and the column bias) of a slab are loaded
     // into registers one slab ahead, so the loads' latency hides behind the
     // previous slab's work; a lane's columns are the same in every slab, so its
     // row-bias values are loaded once.
@@ -1508,9 +1509,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     // fragment registers are free by then): more loads in flight.  X and the
     // column bias go EPD slabs ahead, and so does C when it is fp32 (all of it
     // would take 128 registers) or when the wave tile has 8 slabs (the 4-wave
-    // tile: 128 registers again).  EPD is 1 on the 8-wave tiles, whose two
-    // waves per SIMD overlap each other's loads; the 4-wave tile, one wave per
-    // SIMD, keeps 3 slabs of C and X in flight.
+    // tiles 256 rows tall: 128 registers again).  EPD is 1 on the 8-wave
+    // tiles, whose two waves per SIMD overlap each other's loads; the 4-wave
+    // tiles keep 3 slabs of C and X in flight (one wave per SIMD, or two from
+    // two workgroups on 128 x 128).
     constexpr bool PRE_C = VEC && HAS_C && !F32E && TM <= 4;
     constexpr int EPD = W4 ? 3 : 1;
     constexpr int NBX = EPD + 1;
