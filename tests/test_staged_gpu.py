@@ -161,6 +161,24 @@ def test_small_workspace_runs_the_general_kernel():
         compare(got, p, kind, True, torch.float16, f"small workspace {nbytes}")
 
 
+def test_misaligned_workspace_runs_the_general_kernel():
+    """A workspace that is not 16-byte aligned is not used for staging: the
+    general kernel computes the same outputs and the workspace stays zero."""
+    L, M, N, K = 2, 300, 517, 61
+    kind, a, b, s = "AUX_SCALE", 1.0, 2.0, 0.5
+    p = workloads.make_problem(L, M, N, K, kind, init="small_int", seed=6)
+    P = 0x7F0000001000
+    _, cfg = ge.gemm_epi_plan_ws(L, M, N, K, P, P, P, None, None, None, kind, P, P, None)
+    buf = torch.zeros(cfg["workspace_bytes"] + 64, dtype=torch.uint8, device=DEV)
+    ws = buf[8:8 + cfg["workspace_bytes"]]
+    A, B, C = (torch.from_numpy(p[k]).to(DEV) for k in ("A", "B", "C"))
+    D = torch.full((L, M, N), float("nan"), dtype=torch.float16, device=DEV)
+    Aux = torch.full_like(D, float("nan"))
+    ge.run(A, B, C, kind=kind, alpha=a, beta=b, s3=s, D=D, Aux=Aux, workspace=ws)
+    compare({"D": D.cpu().numpy(), "Aux": Aux.cpu().numpy()}, p, kind, True, torch.float16, "misaligned workspace")
+    assert int(torch.count_nonzero(buf)) == 0, "a misaligned workspace was written"
+
+
 def test_staged_and_stream_k_calls_share_a_workspace():
     """Staging leaves the counter block alone, so one zero-filled workspace
     serves stream-K splits and staged calls in any order."""
