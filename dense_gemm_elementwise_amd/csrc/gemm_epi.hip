@@ -280,10 +280,11 @@ int launch_split(int64_t L, int64_t M, int64_t N, const Operands &o, const float
 // 8, or a tensor not 16-byte aligned) are copied into aligned, zero-padded
 // buffers in the workspace, so that the fast kernel runs on them; outputs
 // that break them are written there and copied back.  K % 8 != 0 pads A's
-// rows and B's row count to K8 (the zero products add nothing); N % 8 != 0
-// gives B and every M x N tensor rows of N8 elements.  Otherwise only the
-// misaligned tensors are copied.  The regions start after the stream-K
-// counter block, which staging never touches.
+// rows to K8 with zeros and runs the kernel with K = K8 over B's K rows (its
+// rows past K read as zeros: Params::b_rows); the zero products add nothing.
+// N % 8 != 0 gives B and every M x N tensor rows of N8 elements.  Otherwise
+// only the misaligned tensors are copied.  The regions start after the
+// stream-K counter block, which staging never touches.
 struct StagePlan {
     bool on = false;
     int64_t K = 0, N = 0;  // the fast kernel's K and N
@@ -299,7 +300,7 @@ StagePlan plan_staging(int64_t L, int64_t M, int64_t N, int64_t K, const Operand
     st.K = (K + 7) / 8 * 8;
     st.N = (N + 7) / 8 * 8;
     st.a = kr || !aligned(o.A, 16);
-    st.b = kr || nr || !aligned(o.B, 16);
+    st.b = nr || !aligned(o.B, 16);
     st.c = kind_reads_c(kind) && (nr || !aligned(o.C, 16));
     st.x = kind_reads_x(kind) && (nr || !aligned(o.X, 16));
     st.rb = kind_reads_bias(kind) && (nr || !aligned(o.row_bias, 16));
@@ -319,7 +320,7 @@ StagePlan plan_staging(int64_t L, int64_t M, int64_t N, int64_t K, const Operand
         return at;
     };
     st.off_a = take(st.a, L * M * st.K, 2);
-    st.off_b = take(st.b, L * st.K * st.N, 2);
+    st.off_b = take(st.b, L * K * st.N, 2);
     st.off_c = take(st.c, L * M * st.N, 2);
     st.off_x = take(st.x, L * M * st.N, 2);
     st.off_rb = take(st.rb, st.N, 2);
@@ -367,6 +368,7 @@ int launch_staged(int64_t L, int64_t M, int64_t N, int64_t K, const Operands &o,
     p.M = (int)M;
     p.N = (int)st.N;
     p.K = (int)st.K;
+    p.b_rows = (int)K;  // B (staged or not) keeps its K rows
     p.tiles_m = (int)tm;
     p.tiles_n = (int)tn;
     p.num_tiles = (int)tiles;
@@ -380,7 +382,7 @@ int launch_staged(int64_t L, int64_t M, int64_t N, int64_t K, const Operands &o,
         if (err == hipSuccess) err = e;
     };
     if (st.a) step(launch_stage<uint16_t>(true, o.A, (void *)p.A, L, M, K, M, st.K, s));
-    if (st.b && err == hipSuccess) step(launch_stage<uint16_t>(true, o.B, (void *)p.B, L, K, N, st.K, st.N, s));
+    if (st.b && err == hipSuccess) step(launch_stage<uint16_t>(true, o.B, (void *)p.B, L, K, N, K, st.N, s));
     if (st.c && err == hipSuccess) step(launch_stage<uint16_t>(true, o.C, (void *)p.C, L, M, N, M, st.N, s));
     if (st.x && err == hipSuccess) step(launch_stage<uint16_t>(true, o.X, (void *)p.X, L, M, N, M, st.N, s));
     if (st.rb && err == hipSuccess)
@@ -543,7 +545,7 @@ int gemm_epi_run_mixed(int64_t L, int64_t M, int64_t N, int64_t K, const void *A
     const int64_t tiles = L * tm * tn;
     if (tiles > INT32_MAX) return GEMM_EPI_ERR_SHAPE;
 
-    Params p;
+    Params p = {};
     p.A = (const _Float16 *)A;
     p.B = (const _Float16 *)B;
     p.C = (const _Float16 *)C;  // the kernels read the epilogue tensors as their element type

@@ -142,6 +142,11 @@ struct Params {
     const _Float16 *col_bias;  // M values, shared by the batch entries
     float *acc_out;            // (L, M, N) fp32 accumulator output
     int M, N, K;      // each < 2^31 (checked on the host)
+    // rows of each batch entry of B, and the bound of its k rows, when they
+    // differ from K (0: K).  The staged path pads A's rows to a multiple of 8
+    // with zeros and runs K = that length over an unpadded B: the rows of B
+    // past b_rows read as zeros.  Only the fast path reads it.
+    int b_rows;
     int tiles_m, tiles_n;
     int num_tiles;    // L * tiles_m * tiles_n
     int group_m;      // tile rows per L2 group (>= 1)
@@ -614,7 +619,7 @@ __device__ __forceinline__ void agpr_fence(f32x4 (&acc)[TM][TN])
 
 template <int BM, int BN, bool BF>
 __device__ __forceinline__ void mainloop_w4(f32x4 (&acc)[BM / 32][BN / 32], const _Float16 *Al, const _Float16 *Bl,
-                                            int M, int N, int K, int m0, int n0, int kb, int nk, char *smem)
+                                            int M, int N, int K, int KB, int m0, int n0, int kb, int nk, char *smem)
 {
     using C = W4Cfg<BM, BN>;
     constexpr int TM = C::TM, TN = C::TN, NA = C::NA, NB = C::NB, ND = C::ND, NMF = C::NMF, NR = C::NR;
@@ -656,7 +661,7 @@ __device__ __forceinline__ void mainloop_w4(f32x4 (&acc)[BM / 32][BN / 32], cons
     // descriptors of B stage s and A chunk c (zero records past the end)
     auto rsrc_b = [&](int s) {
         const int k0 = kbase + s * W4_BK;
-        return make_rsrc(Bl + (int64_t)k0 * N, s < nk ? (uint32_t)((int64_t)(K - k0) * N * 2) : 0u);
+        return make_rsrc(Bl + (int64_t)k0 * N, s < nk ? (uint32_t)((int64_t)(KB - k0) * N * 2) : 0u);
     };
     auto rsrc_a = [&](int c) {
         const int k0 = kbase + c * 64;
@@ -971,6 +976,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     const int wm = wave / WGN, wn = wave % WGN;
 
     const int M = p.M, N = p.N, K = p.K;
+    // B's rows per batch entry (the general path keeps K: the host sets b_rows
+    // only for the fast path)
+    const int KB = VEC && p.b_rows > 0 ? p.b_rows : K;
     const int nk_tile = (K + BK - 1) / BK;
     __shared__ int sk_ticket;
 
@@ -982,7 +990,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
                        const int lw) {
     const int m0 = tm * BM, n0 = tn * BN;
     const _Float16 *Al = p.A + (int64_t)l * M * K;
-    const _Float16 *Bl = p.B + (int64_t)l * K * N;
+    const _Float16 *Bl = p.B + (int64_t)l * KB * N;
 
     acc_t acc[TM][TN];
 #pragma unroll
@@ -1011,7 +1019,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
     const int nk = ke - kb;  // k stages in this segment
 
     if constexpr (W4) {
-        mainloop_w4<BM, BN, BF>(acc, Al, Bl, M, N, K, m0, n0, kb, nk, smem);
+        mainloop_w4<BM, BN, BF>(acc, Al, Bl, M, N, K, KB, m0, n0, kb, nk, smem);
     } else {
     // ---- global -> LDS --------------------------------------------------
     // One wave instruction fills 1 KB: 1024 / A_ROW rows of A, or
@@ -1159,7 +1167,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_epi_kernel(Params p)
             const uint32_t a_lds = smem_lds + a_off + wave_u * 1024;
             const uint32_t b_lds = smem_lds + b_off + wave_u * 1024;
             const i32x4 ra = make_rsrc(Al + k0, (uint32_t)(((int64_t)M * K - k0) * 2));
-            const i32x4 rb = make_rsrc(Bl + (int64_t)k0 * N, (uint32_t)((int64_t)(K - k0) * N * 2));
+            const i32x4 rb = make_rsrc(Bl + (int64_t)k0 * N, (uint32_t)((int64_t)(KB - k0) * N * 2));
             if (k0 + BK <= K) {
 #pragma unroll
                 for (int q = 0; q < A_DMA; q++) dma16(ra, a_lds + q * NW * 1024, (int)a_voff[q]);

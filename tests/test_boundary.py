@@ -390,9 +390,11 @@ def test_plan_ws_stages_operands_that_miss_the_layout_rules():
         return cfg
 
     sq = 4096 * 4096 * 2
-    cfg = ws(1, 4096, 4096, 4095, "LINCOMB")  # K % 8 != 0: A (M x K8) and B (K8 x N)
+    cfg = ws(1, 4096, 4096, 4095, "LINCOMB")  # K % 8 != 0: A alone (M x K8); B keeps its K rows
     assert (cfg["bm"], cfg["bn"], cfg["bk"], cfg["vec"]) == (256, 256, 32, 1)
-    assert cfg["workspace_bytes"] == 16384 + 2 * sq
+    assert cfg["workspace_bytes"] == 16384 + sq
+    cfg = ws(1, 4096, 4095, 4095, "LINCOMB")  # both: A (M x K8), B (K x N8), C and D (M x N8)
+    assert cfg["workspace_bytes"] == 16384 + sq + r256(4095 * 4096 * 2) + 2 * sq
     cfg = ws(1, 4096, 4095, 4096, "LINCOMB")  # N % 8 != 0: B, C and D with rows of N8
     assert cfg["vec"] == 1 and cfg["workspace_bytes"] == 16384 + 3 * sq
     cfg = ws(1, 64, 64, 64, "LINCOMB", a=P16 + 2)  # only A misaligned

@@ -115,7 +115,7 @@ def compare(got, p, kind, exact, dtype, what):
 
 
 # (shape, element offsets of A, B, the epilogue inputs, the outputs)
-STAGED_CASES = [((2, 300, 520, 61), (0, 0, 0, 0)),      # K % 8 != 0: A and B padded to K8
+STAGED_CASES = [((2, 300, 520, 61), (0, 0, 0, 0)),      # K % 8 != 0: A padded to K8, B read with its K rows
                 ((1, 300, 517, 136), (0, 0, 0, 0)),     # N % 8 != 0: B and every M x N tensor padded
                 ((3, 77, 45, 61), (0, 0, 0, 0)),        # both
                 ((2, 200, 136, 264), (1, 1, 1, 1)),     # every pointer 2 bytes off
