@@ -77,3 +77,17 @@ def test_report_configurations_and_cpu_model():
     assert all(c in workloads.WORKLOADS for c in workloads.CONFIGS)
     m = bench.cpu_model()
     assert m is None or (isinstance(m, str) and m)
+
+
+def test_ragged_shapes_take_the_staged_path():
+    """bench.py --ragged measures shapes off the 16-byte rule: each one's plan
+    (host-only) stages operands for the fast kernel through a workspace."""
+    import dense_gemm_elementwise_amd as ge
+    base = 0x7F0000001000
+    for (M, N, K, off) in bench.RAGGED_SHAPES:
+        assert M % 8 or N % 8 or K % 8 or off % 8
+        P = base + 2 * off
+        rc, plan = ge.gemm_epi_plan_ws(1, M, N, K, P, P, P, None, None, None, "LINCOMB", P, None, None)
+        assert rc == 0 and plan["vec"] == 1 and plan["workspace_bytes"] > 16384, (M, N, K, off, plan)
+        rc, gen = ge.gemm_epi_plan(1, M, N, K, P, P, P, None, "LINCOMB", P, None)
+        assert rc == 0 and gen["vec"] == 0  # without a workspace: the general kernel
