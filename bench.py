@@ -476,7 +476,7 @@ def copy_calibration(mib, steps):
 # Shapes off the fast path's 16-byte rule (LINCOMB, fp16, Gaussian inputs):
 # (M, N, K, element offset of every tensor from a 256-byte boundary)
 RAGGED_SHAPES = [(4096, 4096, 4095, 0), (4096, 4095, 4096, 0), (4096, 4100, 4096, 0), (4096, 4096, 4096, 1),
-                 (1001, 1001, 1001, 0)]
+                 (1001, 1001, 1001, 0), (256, 256, 65535, 0)]
 
 
 def bench_ragged(steps, warmup):

@@ -240,9 +240,10 @@ hipError_t launch_epilogue(const EpiParams &q, bool vec, hipStream_t stream)
 // Launches the planned stream-K split of a checked call on `workspace`
 // (counters at offset 0, zero between calls; partial sums after them).
 int launch_split(int64_t L, int64_t M, int64_t N, const Operands &o, const float *scalars, int kind,
-                 const SkPlan &sk, void *workspace, int dtype, hipStream_t s)
+                 const SkPlan &sk, void *workspace, int dtype, hipStream_t s, int64_t b_rows = 0)
 {
     Params p = {};
+    p.b_rows = (int)b_rows;
     p.A = (const _Float16 *)o.A;
     p.B = (const _Float16 *)o.B;
     p.C = (const _Float16 *)o.C;
@@ -293,7 +294,8 @@ struct StagePlan {
     size_t bytes = 0;  // workspace bytes the staged call needs
 };
 
-StagePlan plan_staging(int64_t L, int64_t M, int64_t N, int64_t K, const Operands &o, int kind)
+StagePlan plan_staging(int64_t L, int64_t M, int64_t N, int64_t K, const Operands &o, int kind,
+                       size_t base = kSkCounterBytes)
 {
     StagePlan st;
     const bool kr = K % 8 != 0, nr = N % 8 != 0;
@@ -312,7 +314,7 @@ StagePlan plan_staging(int64_t L, int64_t M, int64_t N, int64_t K, const Operand
     const void *al = (const void *)(uintptr_t)4096;
     const Operands staged = {al, al, al, al, al, al, al, al, al};
     if (!use_fast_path(M, st.N, st.K, staged, kind)) return st;
-    size_t off = kSkCounterBytes;
+    size_t off = base;
     auto take = [&](bool on, int64_t elems, int es) {
         if (!on) return (size_t)0;
         const size_t at = off;
@@ -332,6 +334,24 @@ StagePlan plan_staging(int64_t L, int64_t M, int64_t N, int64_t K, const Operand
     return st;
 }
 
+// A staged call, with a stream-K split of the staged shape where one pays:
+// the split's partial sums follow the counter block and the staging regions
+// follow them.
+struct StagedCall {
+    StagePlan st;
+    SkPlan sk;
+};
+
+StagedCall plan_staged_call(int64_t L, int64_t M, int64_t N, int64_t K, const Operands &o, int kind)
+{
+    StagedCall c;
+    c.st = plan_staging(L, M, N, K, o, kind);
+    if (!c.st.on) return c;
+    c.sk = plan_stream_k(L, M, c.st.N, c.st.K, true);
+    if (c.sk.on) c.st = plan_staging(L, M, N, K, o, kind, kSkCounterBytes + sk_partials_bytes(c.sk.t, c.sk.groups));
+    return c;
+}
+
 template <typename T>
 hipError_t launch_stage(bool pad, const void *src, void *dst, int64_t L, int64_t rows, int64_t cols, int64_t prows,
                         int64_t pcols, hipStream_t stream)
@@ -347,8 +367,9 @@ hipError_t launch_stage(bool pad, const void *src, void *dst, int64_t L, int64_t
 // Runs a checked call through the staging plan: copies in, the fast kernel on
 // the staged operand set, copies out, all on `stream`.
 int launch_staged(int64_t L, int64_t M, int64_t N, int64_t K, const Operands &o, const float *scalars, int kind,
-                  const StagePlan &st, void *workspace, int dtype, hipStream_t s)
+                  const StagedCall &call, void *workspace, int dtype, hipStream_t s)
 {
+    const StagePlan &st = call.st;
     char *ws = (char *)workspace;
     auto at = [&](bool on, size_t off, const void *orig) { return on ? (void *)(ws + off) : const_cast<void *>(orig); };
     Params p = {};
@@ -387,7 +408,11 @@ int launch_staged(int64_t L, int64_t M, int64_t N, int64_t K, const Operands &o,
     if (st.x && err == hipSuccess) step(launch_stage<uint16_t>(true, o.X, (void *)p.X, L, M, N, M, st.N, s));
     if (st.rb && err == hipSuccess)
         step(launch_stage<uint16_t>(true, o.row_bias, (void *)p.row_bias, 1, 1, N, 1, st.N, s));
-    if (err == hipSuccess) {
+    if (err == hipSuccess && call.sk.on) {
+        const Operands so = {p.A, p.B, p.C, p.X, p.row_bias, p.col_bias, p.D, p.Aux, p.acc_out};
+        const int rc = launch_split(L, M, st.N, so, scalars, kind, call.sk, workspace, dtype, s, K);
+        if (rc != GEMM_EPI_OK) return rc;
+    } else if (err == hipSuccess) {
         if (dtype == GEMM_EPI_BF16)
             step(launch_fused_bf16(kind, p, t, true, s));
         else
@@ -679,19 +704,19 @@ int gemm_epi_plan_ws(int64_t L, int64_t M, int64_t N, int64_t K, const void *A, 
     if (rc != GEMM_EPI_OK) return rc;
     const bool vec = use_fast_path(M, N, K, o, epilogue_kind);
     if (!vec) {
-        const StagePlan st = plan_staging(L, M, N, K, o, epilogue_kind);
-        if (st.on) {
-            const TileCfg t = choose_tile(L, M, st.N, st.K, true);
-            const int64_t tiles = L * ((M + t.bm - 1) / t.bm) * ((st.N + t.bn - 1) / t.bn);
+        const StagedCall call = plan_staged_call(L, M, N, K, o, epilogue_kind);
+        if (call.st.on) {
+            const TileCfg t = call.sk.on ? call.sk.t : choose_tile(L, M, call.st.N, call.st.K, true);
+            const int64_t tiles = L * ((M + t.bm - 1) / t.bm) * ((call.st.N + t.bn - 1) / t.bn);
             if (tiles > INT32_MAX) return GEMM_EPI_ERR_SHAPE;
             if (out) {
                 out[0] = t.bm;
                 out[1] = t.bn;
                 out[2] = t.bk;
                 out[3] = 1;
-                out[4] = tiles;
+                out[4] = call.sk.on ? call.sk.groups : tiles;
                 out[5] = 64 * t.wgm * t.wgn;
-                out[6] = (int64_t)st.bytes;
+                out[6] = (int64_t)call.st.bytes;
             }
             return GEMM_EPI_OK;
         }
@@ -738,9 +763,9 @@ int gemm_epi_run_ws_typed(int64_t L, int64_t M, int64_t N, int64_t K, const void
     if (!scalars) return GEMM_EPI_ERR_NULL_INPUT;
     const bool vec = use_fast_path(M, N, K, o, epilogue_kind);
     if (!vec) {
-        const StagePlan st = plan_staging(L, M, N, K, o, epilogue_kind);
-        if (st.on && workspace && workspace_bytes >= st.bytes && aligned(workspace, 16))
-            return launch_staged(L, M, N, K, o, scalars, epilogue_kind, st, workspace, dtype, (hipStream_t)stream);
+        const StagedCall call = plan_staged_call(L, M, N, K, o, epilogue_kind);
+        if (call.st.on && workspace && workspace_bytes >= call.st.bytes && aligned(workspace, 16))
+            return launch_staged(L, M, N, K, o, scalars, epilogue_kind, call, workspace, dtype, (hipStream_t)stream);
     }
     const SkPlan sk = plan_stream_k(L, M, N, K, vec);
     if (!sk.on)

@@ -298,9 +298,10 @@ int gemm_epi_run_unfused_typed(int64_t L, int64_t M, int64_t N, int64_t K, const
  * buffers whose rows are padded with zeros, runs the fast kernel on those and
  * copies padded outputs back, all on `stream` (the zero products leave every
  * sum unchanged, so the results are gemm_epi_run_ext's, up to the sign of a
- * zero).  With a smaller workspace, or none, such a call runs
- * gemm_epi_run_ext's general kernel instead.  Staging never writes the
- * counter block below.
+ * zero).  Where the staged problem has few tiles and a long K, it is also
+ * split as above (the partial sums first, then the staged copies).  With a
+ * smaller workspace, or none, such a call runs gemm_epi_run_ext's general
+ * kernel instead.  Staging never writes the counter block below.
  *
  *   workspace        device pointer, 16-byte aligned, of at least the size
  *                    gemm_epi_plan_ws reports in out[6] (0 when neither a

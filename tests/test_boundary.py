@@ -412,3 +412,18 @@ def test_plan_ws_stages_operands_that_miss_the_layout_rules():
     # a staged A of 2 GiB or more breaks the fast path's 32-bit offsets: the general kernel, no workspace
     cfg = ws(1, 1 << 21, 1000, 1001, "LINCOMB")
     assert cfg["vec"] == 0 and cfg["workspace_bytes"] == 0
+
+
+def test_plan_ws_splits_a_staged_deep_k_product():
+    """A few tiles with a long, ragged K: the staged operands also get the
+    stream-K split.  The workspace is the counter block, then the split's
+    partial sums, then the staging regions."""
+    rc, cfg = ge.gemm_epi_plan_ws(1, 256, 256, 65535, P16, P16, P16, None, None, None, "LINCOMB", P16, None, None)
+    assert rc == 0 and (cfg["bm"], cfg["bn"], cfg["vec"]) == (128, 128, 1)
+    groups = cfg["workgroups"]
+    assert 1 < groups <= 256
+    # A (256 x 65536) is the only staged tensor: N = 256 is a multiple of 8 and B keeps its K rows
+    assert cfg["workspace_bytes"] == 16384 + 2 * groups * 128 * 128 * 4 + 256 * 65536 * 2
+    # the same product with K a multiple of 8 splits the same way, with no staging
+    rc, al = ge.gemm_epi_plan_ws(1, 256, 256, 65536, P16, P16, P16, None, None, None, "LINCOMB", P16, None, None)
+    assert al["workgroups"] == groups and al["workspace_bytes"] == 16384 + 2 * groups * 128 * 128 * 4

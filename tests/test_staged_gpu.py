@@ -150,6 +150,23 @@ def test_staged_larger_shapes(shape, offs, kind):
     compare(run_staged(p, kind, offs, torch.float16), p, kind, False, torch.float16, f"staged gaussian {shape}")
 
 
+@pytest.mark.parametrize("shape,kind,dtype", [((1, 256, 256, 65535), "LINCOMB", torch.float16),
+                                              ((2, 200, 136, 24001), "AUX_SCALE", torch.float16),
+                                              ((1, 130, 300, 30001), "RELU_SCALE_ACC", torch.bfloat16)])
+def test_staged_deep_k_is_split(shape, kind, dtype):
+    """Few tiles and a long, ragged K: the staged operands go through the
+    stream-K split (the plan reports a split's workgroup count)."""
+    L, M, N, K = shape
+    dt = "bf16" if dtype == torch.bfloat16 else "f16"
+    log(f"[staged] deep K {dt} {kind} shape={shape}")
+    P = 0x7F0000001000
+    _, cfg = ge.gemm_epi_plan_ws(L, M, N, K, P, P, P, None, P, P, kind, P, P, P)
+    assert cfg["bm"] == 128 and cfg["bn"] == 128 and cfg["workgroups"] <= 256, cfg  # the split tile
+    p = workloads.make_problem(L, M, N, K, kind, init="small_int", seed=M + N + K, dtype=dt)
+    got = run_staged(p, kind, (0, 0, 0, 0), dtype)
+    compare(got, p, kind, True, dtype, f"staged deep K {shape}")
+
+
 def test_small_workspace_runs_the_general_kernel():
     """With less workspace than the plan reports, the call still computes the
     same outputs, on the general kernel, and leaves the workspace alone."""
