@@ -352,16 +352,28 @@ StagedCall plan_staged_call(int64_t L, int64_t M, int64_t N, int64_t K, const Op
     return c;
 }
 
+// One launch for a set of copies in the same direction and of one element
+// size (a grid row per copy); no launch for an empty set.
+struct StageBatch {
+    StageCopies q = {};
+    int n = 0;
+    int64_t rows = 0;  // the most rows a copy walks
+    void add(const void *src, void *dst, int64_t L, int64_t r, int64_t c, int64_t pr, int64_t pc, bool pad)
+    {
+        q.c[n++] = StageCopy{src, dst, L, r, c, pr, pc};
+        rows = std::max(rows, L * (pad ? pr : r));
+    }
+};
+
 template <typename T>
-hipError_t launch_stage(bool pad, const void *src, void *dst, int64_t L, int64_t rows, int64_t cols, int64_t prows,
-                        int64_t pcols, hipStream_t stream)
+hipError_t launch_stage(bool pad, const StageBatch &b, hipStream_t stream)
 {
-    StageCopy q = {src, dst, L, rows, cols, prows, pcols};
-    const int64_t n = L * (pad ? prows : rows);
-    const unsigned blocks = (unsigned)(n < 8192 ? n : 8192);
+    if (b.n == 0) return hipSuccess;
+    const unsigned blocks = (unsigned)(b.rows < 8192 ? b.rows : 8192);
+    StageCopies q = b.q;
     void *args[] = {(void *)&q};
     const void *fn = pad ? (const void *)&stage_pad_kernel<T> : (const void *)&stage_unpad_kernel<T>;
-    return hipLaunchKernel(fn, dim3(blocks), dim3(256), args, 0, stream);
+    return hipLaunchKernel(fn, dim3(blocks, (unsigned)b.n), dim3(256), args, 0, stream);
 }
 
 // Runs a checked call through the staging plan: copies in, the fast kernel on
@@ -402,12 +414,13 @@ int launch_staged(int64_t L, int64_t M, int64_t N, int64_t K, const Operands &o,
     auto step = [&](hipError_t e) {
         if (err == hipSuccess) err = e;
     };
-    if (st.a) step(launch_stage<uint16_t>(true, o.A, (void *)p.A, L, M, K, M, st.K, s));
-    if (st.b && err == hipSuccess) step(launch_stage<uint16_t>(true, o.B, (void *)p.B, L, K, N, K, st.N, s));
-    if (st.c && err == hipSuccess) step(launch_stage<uint16_t>(true, o.C, (void *)p.C, L, M, N, M, st.N, s));
-    if (st.x && err == hipSuccess) step(launch_stage<uint16_t>(true, o.X, (void *)p.X, L, M, N, M, st.N, s));
-    if (st.rb && err == hipSuccess)
-        step(launch_stage<uint16_t>(true, o.row_bias, (void *)p.row_bias, 1, 1, N, 1, st.N, s));
+    StageBatch in;
+    if (st.a) in.add(o.A, (void *)p.A, L, M, K, M, st.K, true);
+    if (st.b) in.add(o.B, (void *)p.B, L, K, N, K, st.N, true);
+    if (st.c) in.add(o.C, (void *)p.C, L, M, N, M, st.N, true);
+    if (st.x) in.add(o.X, (void *)p.X, L, M, N, M, st.N, true);
+    if (st.rb) in.add(o.row_bias, (void *)p.row_bias, 1, 1, N, 1, st.N, true);
+    step(launch_stage<uint16_t>(true, in, s));
     if (err == hipSuccess && call.sk.on) {
         const Operands so = {p.A, p.B, p.C, p.X, p.row_bias, p.col_bias, p.D, p.Aux, p.acc_out};
         const int rc = launch_split(L, M, st.N, so, scalars, kind, call.sk, workspace, dtype, s, K);
@@ -418,10 +431,12 @@ int launch_staged(int64_t L, int64_t M, int64_t N, int64_t K, const Operands &o,
         else
             step(dispatch_kind(kind, [&](auto k) { return launch_kind<decltype(k)::value>(p, t, true, s); }));
     }
-    if (st.d && err == hipSuccess) step(launch_stage<uint16_t>(false, p.D, (void *)o.D, L, M, N, M, st.N, s));
-    if (st.aux && err == hipSuccess) step(launch_stage<uint16_t>(false, p.Aux, (void *)o.Aux, L, M, N, M, st.N, s));
-    if (st.acc && err == hipSuccess)
-        step(launch_stage<uint32_t>(false, p.acc_out, (void *)o.acc_out, L, M, N, M, st.N, s));
+    StageBatch out16, out32;
+    if (st.d) out16.add(p.D, (void *)o.D, L, M, N, M, st.N, false);
+    if (st.aux) out16.add(p.Aux, (void *)o.Aux, L, M, N, M, st.N, false);
+    if (st.acc) out32.add(p.acc_out, (void *)o.acc_out, L, M, N, M, st.N, false);
+    if (err == hipSuccess) step(launch_stage<uint16_t>(false, out16, s));
+    if (err == hipSuccess) step(launch_stage<uint32_t>(false, out32, s));
     if (err != hipSuccess) {
         g_last_hip_error = (int)err;
         return GEMM_EPI_ERR_HIP;

@@ -1763,6 +1763,12 @@ struct StageCopy {
     int64_t prows, pcols;  // the padded one: prows >= rows, pcols >= cols
 };
 
+// The copies of one call go in one launch: blockIdx.y picks the tensor.
+constexpr int kMaxStageCopies = 5;
+struct StageCopies {
+    StageCopy c[kMaxStageCopies];
+};
+
 // Both copies move one element per lane and access, adjacent lanes on
 // adjacent elements, so each wave access covers one contiguous span (128
 // bytes of 2-byte elements) whatever the rows' alignment; four accesses per
@@ -1772,8 +1778,9 @@ constexpr int kStageUnroll = 4;
 // padded (L, prows, pcols) <- src (L, rows, cols), zeros past rows and cols
 // (q.dst).
 template <typename T>
-__global__ __launch_bounds__(256) void stage_pad_kernel(StageCopy q)
+__global__ __launch_bounds__(256) void stage_pad_kernel(StageCopies qs)
 {
+    const StageCopy &q = qs.c[blockIdx.y];
     const int64_t nrows = q.L * q.prows;
     for (int64_t row = blockIdx.x; row < nrows; row += gridDim.x) {
         const int64_t l = row / q.prows, r = row - l * q.prows;
@@ -1799,8 +1806,9 @@ __global__ __launch_bounds__(256) void stage_pad_kernel(StageCopy q)
 // dst (L, rows, cols) <- the first rows and cols of padded (L, prows, pcols)
 // (q.src).
 template <typename T>
-__global__ __launch_bounds__(256) void stage_unpad_kernel(StageCopy q)
+__global__ __launch_bounds__(256) void stage_unpad_kernel(StageCopies qs)
 {
+    const StageCopy &q = qs.c[blockIdx.y];
     const int64_t nrows = q.L * q.rows;
     for (int64_t row = blockIdx.x; row < nrows; row += gridDim.x) {
         const int64_t l = row / q.rows, r = row - l * q.rows;
