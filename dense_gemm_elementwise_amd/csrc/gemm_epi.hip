@@ -46,7 +46,14 @@ constexpr int kNumCUs = 256;
 // tiles than compute units.
 TileCfg choose_tile(int64_t L, int64_t M, int64_t N, int64_t K, bool vec)
 {
-    if (!vec) return kGeneral;
+    if (!vec) {
+        // the general path's two tiles, by the same cost
+        auto cost = [&](const TileCfg &t) {
+            const int64_t tiles = L * ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+            return (double)((tiles + kNumCUs - 1) / kNumCUs) * t.bm * t.bn / tile_efficiency(t.bm, t.bn);
+        };
+        return cost(kGeneralWide) < cost(kGeneral) ? kGeneralWide : kGeneral;
+    }
     TileCfg best = kTiles[0];
     double best_cost = 1e300, best_pad = 1e300;
     int best_orient = 2;

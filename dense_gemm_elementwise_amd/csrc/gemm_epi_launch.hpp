@@ -50,9 +50,13 @@ inline constexpr TileCfg kSmallDeep = {64, 64, 128, 4, 4, 2, 16};
 // unit holds only one (192 tiles: 16% slower; 16 tiles: 39%).
 inline constexpr TileCfg kSmallDeepWide = {64, 64, 128, 2, 4, 2, 16};
 inline constexpr int64_t kSmallDeepMinK = 256;
-// The general path's tile: eight waves of 32 x 64 (against four of 64 x 64:
-// 4096 x 4096 x 4095 19% faster, 1001^3 43%).
+// The general path's tiles: eight waves of 32 x 64 (against four of 64 x 64:
+// 4096 x 4096 x 4095 19% faster, 1001^3 43%), and eight of 64 x 64 on a
+// 256 x 128 tile for grids that fill the chip several times (4096 x 4096 x
+// 4095: 294 against 336 us; 1001^3: 53 against 31 us, so the tile model
+// chooses).
 inline constexpr TileCfg kGeneral = {128, 128, 64, 2, 4, 2, 32};
+inline constexpr TileCfg kGeneralWide = {256, 128, 64, 2, 4, 2, 16};
 
 // Calls f(std::integral_constant<int, KIND>) for a public kind (checked by
 // check_args before any call).
@@ -99,7 +103,10 @@ hipError_t launch_one(const Params &p, hipStream_t stream, int grid)
 template <int KIND, bool BF = false, int EPI = EPI_AB>
 hipError_t launch_kind(const Params &p, const TileCfg &t, bool vec, hipStream_t stream)
 {
-    if (!vec) return GE_LAUNCH(kGeneral, KIND, false);
+    if (!vec) {
+        if (t.bm == kGeneralWide.bm && t.bn == kGeneralWide.bn) return GE_LAUNCH(kGeneralWide, KIND, false);
+        return GE_LAUNCH(kGeneral, KIND, false);
+    }
     // the 4-wave tiles are built for epilogue tensors of the type of A and B
     // only (the host gives the others the 8-wave tiles of the same shape)
     if constexpr (EPI == EPI_AB) {

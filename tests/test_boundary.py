@@ -427,3 +427,17 @@ def test_plan_ws_splits_a_staged_deep_k_product():
     # the same product with K a multiple of 8 splits the same way, with no staging
     rc, al = ge.gemm_epi_plan_ws(1, 256, 256, 65536, P16, P16, P16, None, None, None, "LINCOMB", P16, None, None)
     assert al["workgroups"] == groups and al["workspace_bytes"] == 16384 + 2 * groups * 128 * 128 * 4
+
+
+def test_general_kernel_tile_follows_the_grid():
+    """Off the 16-byte rule and without a workspace: the general kernel's
+    128 x 128 tile on small grids, its 256 x 128 tile where the grid fills the
+    chip several times (same cost model as the fast path)."""
+    def plan(L, M, N, K):
+        rc, cfg = ge.gemm_epi_plan(L, M, N, K, P16, P16, P16, None, "LINCOMB", P16, None)
+        assert rc == 0 and cfg["vec"] == 0
+        return (cfg["bm"], cfg["bn"], cfg["bk"], cfg["threads"])
+    assert plan(1, 1001, 1001, 1001) == (128, 128, 64, 512)
+    assert plan(1, 3000, 3000, 1001) == (128, 128, 64, 512)
+    assert plan(1, 2100, 2100, 61) == (256, 128, 64, 512)
+    assert plan(1, 4096, 4096, 4095) == (256, 128, 64, 512)

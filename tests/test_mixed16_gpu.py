@@ -112,7 +112,8 @@ PAIRS = [("f16", "bf16"), ("bf16", "f16")]
                                           ((2, 300, 520, 648), 0),    # 64 x 64 x 128 tile (K >= 256), ragged last stage
                                           ((1, 1280, 1280, 648), 0),  # the same with the 2-stage ring (400 tiles)
                                           ((1, 300, 520, 136), 0),    # 64 x 64 x 64 tile (K < 256), ragged last stage
-                                          ((1, 1960, 2000, 72), 0)])  # 128 x 128 tiles, ragged M, N
+                                          ((1, 1960, 2000, 72), 0),   # 128 x 128 tiles, ragged M, N
+                                          ((1, 2100, 2100, 61), 0)])  # general kernel, 256 x 128 tiles
 def test_every_kind_integer_inputs(kind, ab, epi, shape, offset):
     L, M, N, K = shape
     a, b, s = KIND_SCALARS[kind]

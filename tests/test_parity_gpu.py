@@ -321,7 +321,8 @@ KIND_SCALARS.update({a: (2.0 ** -5, 0.5, 0.125 if a == "LEAKY_RELU" else 0.0) fo
                                           ((3, 77, 45, 61), 0),       # K, N not multiples of 8 -> general
                                           ((1, 300, 520, 136), 0),    # fast path, several tiles
                                           ((1, 3112, 3928, 40), 0),   # 256 x 256 tiles (mixed types: 128 x 256)
-                                          ((1, 1960, 2000, 72), 0)])  # 128 x 128 tiles, ragged M, N
+                                          ((1, 1960, 2000, 72), 0),   # 128 x 128 tiles, ragged M, N
+                                          ((1, 2100, 2100, 61), 0)])  # general kernel, 256 x 128 tiles
 def test_every_kind_integer_inputs_bit_exact(kind, shape, offset):
     L, M, N, K = shape
     a, b, s = KIND_SCALARS[kind]
