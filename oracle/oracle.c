@@ -62,7 +62,7 @@
  *     The second output (Aux, Y, E or F) goes to the Aux buffer; the biases
  *     are shared by every batch entry.
  *
- * Precision (readings where the pages are silent, listed in the design doc):
+ * Precision (readings where the pages are silent):
  *   - fp16 inputs are decoded exactly to double by oracle_f16_decode() below;
  *     the same definition runs on bfloat16 tensors (the Custom Epilogue
  *     Example's "Data Type Support": BF16 inputs and outputs) through
