@@ -541,7 +541,7 @@ def main():
                          "library (one JSON line each)")
     a = ap.parse_args()
     if a.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
+        print(f"bench.py measures one GPU only: this library has no multi-GPU path (asked for --gpus {a.gpus}).",
               file=sys.stderr)
         sys.exit(2)
 
