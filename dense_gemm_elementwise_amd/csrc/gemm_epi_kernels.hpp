@@ -246,7 +246,11 @@ __device__ __forceinline__ float act_silu(float x)
 __device__ __forceinline__ float act_hardswish(float x)
 {
 #pragma clang fp contract(off)
-    return x * __builtin_fminf(__builtin_fmaxf(x + 3.0f, 0.0f), 6.0f) * (1.0f / 6.0f);
+    const float r = x * __builtin_fminf(__builtin_fmaxf(x + 3.0f, 0.0f), 6.0f) * (1.0f / 6.0f);
+    // x <= -3: exactly zero, with x's sign (x times +0).  Written out, because
+    // the clamp's lowering differs between kernels and one of them returned
+    // +0 there.
+    return x <= -3.0f ? __builtin_copysignf(0.0f, x) : r;
 }
 
 template <int KIND>
