@@ -192,7 +192,11 @@ def test_x_acc_bf16_8192_sampled_and_properties():
 @pytest.mark.parametrize("kind", workloads.KINDS)
 @pytest.mark.parametrize("shape,offset", [((2, 200, 136, 264), 0),    # vector paths
                                           ((2, 200, 136, 264), 1),    # misaligned: element-wise paths
-                                          ((3, 77, 45, 61), 0)])      # K, N not multiples of 8 (N % 4 != 0)
+                                          ((3, 77, 45, 61), 0),       # K, N not multiples of 8 (N % 4 != 0)
+                                          ((1, 1960, 2000, 72), 0),   # the 4-wave tiles: 128 x 128,
+                                          ((1, 2000, 3000, 72), 0),   # 128 x 256
+                                          ((1, 3112, 3928, 40), 0),   # and 256 x 256
+                                          ((1, 2100, 2100, 61), 0)])  # general kernel, 256 x 128 tiles
 def test_unfused_bf16_equals_fused_and_oracle(kind, shape, offset):
     """gemm_epi_run_unfused_typed: the same accumulator and the same fp32
     epilogue arithmetic as the fused kernel, so the same bits; on integer
