@@ -173,8 +173,11 @@ typedef enum {
  * Fast path: when K % 8 == 0, N % 8 == 0 and A, B, C, X, D, Aux are 16-byte
  * aligned (the "Constraints" section's 16-byte rule), and A and B of one batch
  * entry each span less than 2 GiB, the kernel moves 16-byte vectors;
- * otherwise a general kernel with element-wise edge handling runs.  Both give
- * the same values.
+ * otherwise a general kernel with element-wise edge handling runs.  Both
+ * compute the same definition; their fp32 sums run in different orders, so
+ * the results are identical on integer-valued inputs and can differ in the
+ * last bits otherwise.  gemm_epi_run_ws, given a workspace, runs the fast
+ * kernel on copies of such operands instead.
  *
  * Returns GEMM_EPI_OK, or a gemm_epi_status error code; on an error before
  * the launch nothing is queued on the stream.  RELU_SCALE_ACC and
