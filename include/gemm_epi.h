@@ -254,7 +254,10 @@ int gemm_epi_run_mixed(int64_t L, int64_t M, int64_t N, int64_t K, const void *A
  * activation as separate kernels, with intermediates in global memory); it
  * is here to measure what the fusion saves.  Its outputs equal those of
  * gemm_epi_run_ext bit for bit (the same accumulator, the same fp32
- * epilogue arithmetic).
+ * epilogue arithmetic) whenever both take the same GEMM kernel: its GEMM
+ * launch chooses the fast or the general kernel from A, B and the workspace
+ * alone, the fused call from every tensor.  On integer-valued inputs they
+ * are equal in any case.
  *
  *   workspace        device pointer to at least L*M*N*4 bytes (4-byte
  *                    aligned; 16-byte aligned for the vector path) that
