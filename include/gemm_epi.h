@@ -356,9 +356,9 @@ int gemm_epi_run_ws_typed(int64_t L, int64_t M, int64_t N, int64_t K, const void
  * Its splits use at most 128 workgroups (so its plan can differ from
  * gemm_epi_plan_ws's, which allows 256; results are the same on integer
  * inputs and within the fp32 summation order otherwise); where no split
- * pays the call is exactly gemm_epi_run_typed (it does not stage operands).  Every call on one GPU shares
- * that GPU's array: calls that overlap in time on one GPU (two streams, two
- * threads) race.  `stream` must belong to the calling thread's current
+ * pays the call is exactly gemm_epi_run_typed (it does not stage operands).
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (two streams, two threads) race.  `stream` must belong to the calling thread's current
  * device.  Status codes as gemm_epi_run_ws_typed; GEMM_EPI_ERR_WORKSPACE if a
  * split would not fit the array; GEMM_EPI_ERR_HIP if the array cannot be
  * located (for example the current device's index is 64 or more).
