@@ -1,5 +1,5 @@
-"""The fused call, and the workspace call that stages ragged operands, under
-HIP graph capture.
+"""The fused call, and the workspace calls that stage ragged operands or
+split the K range, under HIP graph capture.
 
 A caller may record gemm_epi_run_ext / gemm_epi_run_typed into a HIP graph
 (torch.cuda.graph captures the current stream): the entry points queue one
@@ -132,3 +132,46 @@ def test_captured_staged_call_replays_with_new_inputs():
         ref = oracle.gemm_epi(q["A"], q["B"], q["C"], kind=kind, alpha=a, beta=b, s3=s)
         assert_bit_exact(D.cpu().numpy(), ref["D"], f"staged graph replay {seed} D")
         assert_bit_exact(Aux.cpu().numpy(), ref["Aux"], f"staged graph replay {seed} Aux")
+
+
+def test_captured_split_call_replays_with_new_inputs():
+    """A workspace call whose K range is split over workgroups (partial sums
+    and per-tile counters in the workspace, the last contributor resetting
+    its counter) records into a graph as kernels alone; every replay, with
+    new input values written between replays, gives the new result."""
+    L, M, N, K = 1, 512, 512, 8192
+    kind, a, b, s = "AUX_SCALE", 1.0, 2.0, 0.5
+    log("[graph] split call")
+    p = workloads.make_problem(L, M, N, K, kind, init="small_int", seed=41)
+    t = to_dev(p)
+    D = torch.zeros((L, M, N), dtype=torch.float16, device=DEV)
+    Aux = torch.zeros_like(D)
+    P = lambda x: x.data_ptr()
+    rc, plan = ge.gemm_epi_plan_ws(L, M, N, K, P(t["A"]), P(t["B"]), P(t["C"]), None, None, None, kind, P(D), P(Aux),
+                                   None)
+    # aligned operands are never staged, so a workspace here means a split
+    assert rc == 0 and plan["workspace_bytes"] > 0 and plan["bm"] == 128, plan
+    ws = torch.zeros(plan["workspace_bytes"], dtype=torch.uint8, device=DEV)
+    ge.run(t["A"], t["B"], t["C"], kind=kind, alpha=a, beta=b, s3=s, D=D, Aux=Aux, workspace=ws)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(device=DEV)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            ge.run(t["A"], t["B"], t["C"], kind=kind, alpha=a, beta=b, s3=s, D=D, Aux=Aux, workspace=ws, sync=False)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for seed in (42, 43, 44):
+        q = workloads.make_problem(L, M, N, K, kind, init="small_int", seed=seed)
+        for k in ("A", "B", "C"):
+            t[k].copy_(torch.from_numpy(q[k]))
+        D.fill_(float("nan"))
+        Aux.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = oracle.gemm_epi(q["A"], q["B"], q["C"], kind=kind, alpha=a, beta=b, s3=s)
+        assert_bit_exact(D.cpu().numpy(), ref["D"], f"split graph replay {seed} D")
+        assert_bit_exact(Aux.cpu().numpy(), ref["Aux"], f"split graph replay {seed} Aux")
+    # the counters are back at zero after the replays
+    assert int(ws[:16384].view(torch.int32).abs().sum()) == 0

@@ -65,3 +65,51 @@ def test_static_scratch_matches_workspace_call(kind):
                 continue
             assert np.array_equal(got[name].view(np.uint16), want[name].view(np.uint16)), f"call {n} {name}"
             assert_output(got[name], ref, name, kind, True, f"static scratch call {n} {name}")
+
+
+def test_static_scratch_call_replays_from_a_graph():
+    """The callers this entry point is for include code under HIP graph
+    capture: recorded after a first eager call on the device (which looks up
+    the array and clears its counters), the split call replays as kernels
+    alone, and each replay, with new input values written between replays,
+    gives the oracle's result."""
+    L, M, N, K = 1, 512, 512, 8192
+    kind = "AUX_SCALE"
+    a, b, s = KIND_SCALARS[kind]
+    rc, cfg = ge.gemm_epi_plan_ws(L, M, N, K, P, P, P, P, P, P, ge.KINDS[kind], P, P, P)
+    assert rc == 0 and cfg["workspace_bytes"] > 0, ("this shape should be split", cfg)
+    log(f"[no-alloc] graph capture kind={kind} shape={(L, M, N, K)}")
+    dev = torch.device("cuda:0")
+    p = workloads.make_problem(L, M, N, K, kind, init="small_int", seed=51)
+    t = to_dev(p)
+    D = torch.zeros((L, M, N), dtype=torch.float16, device=dev)
+    Aux = torch.zeros_like(D)
+
+    def call(stream):
+        rc = ge.gemm_epi_run_ws_static(L, M, N, K, t["A"].data_ptr(), t["B"].data_ptr(), t["C"].data_ptr(), None,
+                                       None, None, (a, b, s), ge.KINDS[kind], D.data_ptr(), Aux.data_ptr(), None,
+                                       ge.DTYPES["f16"], stream.cuda_stream)
+        assert rc == 0, ge.gemm_epi_status_string(rc)
+
+    call(torch.cuda.current_stream(dev))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            call(side)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    for seed in (52, 53, 54):
+        q = workloads.make_problem(L, M, N, K, kind, init="small_int", seed=seed)
+        for k in ("A", "B", "C"):
+            t[k].copy_(torch.from_numpy(q[k]))
+        D.fill_(float("nan"))
+        Aux.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = oracle_ref(q, kind, a, b, s, exact=True)
+        assert_output(D.cpu().numpy(), ref, "D", kind, True, f"static scratch graph replay {seed} D")
+        assert_output(Aux.cpu().numpy(), ref, "Aux", kind, True, f"static scratch graph replay {seed} Aux")
