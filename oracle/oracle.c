@@ -77,7 +77,10 @@
  *     even, overflow to +-inf (oracle_f16_encode() below; oracle_bf16_encode()
  *     for bfloat16); the fp32 accumulator
  *     output is the exact sum rounded once to fp32 (nearest, ties to even);
- *   - ReLU(t) = t > 0 ? t : +0.0 (the "where(d > 0, d, 0)" form).
+ *   - ReLU(t) = t > 0 ? t : +0.0 (the "where(d > 0, d, 0)" form);
+ *   - gelu(t) and silu(t) for t > 0 where the double factor rounds to 1 are
+ *     rounded to odd below t (below_to_odd()), so that their one rounding to
+ *     the output format is the exact value's.
  * Build with -ffp-contract=off so that no multiply-add is fused.
  */
 #include <fenv.h>
@@ -218,8 +221,26 @@ int oracle_kind_has_acc_out(int kind) { return kind == ORACLE_RELU_SCALE_ACC; }
 
 static double relu(double t) { return t > 0.0 ? t : 0.0; }
 static double sigmoid(double t) { return 1.0 / (1.0 + exp(-t)); }
-static double gelu(double t) { return 0.5 * t * erfc(-t / sqrt(2.0)); }
-static double silu(double t) { return t * sigmoid(t); }
+/* gelu(t) and silu(t) are t times a factor below 1.  Far right that factor
+ * rounds to 1 in double and the product comes out as t itself, while the
+ * exact value lies below t by less than one double ulp.  Rounding t to the
+ * output format would then settle a tie that the exact value does not have,
+ * where t is a rounding midpoint of that format.  Rounded to odd instead
+ * (t if its last bit is odd, else the next double below it), the value stays
+ * on the exact value's side of every rounding boundary of fp16, bfloat16 and
+ * fp32 (all far coarser than double), so the one final rounding is still the
+ * exact value's. */
+static double below_to_odd(double t, double r)
+{
+    if (!(t > 0.0) || r != t || isinf(t)) return r;
+    uint64_t b;
+    memcpy(&b, &t, sizeof b);
+    b -= ~b & 1u;
+    memcpy(&r, &b, sizeof r);
+    return r;
+}
+static double gelu(double t) { return below_to_odd(t, 0.5 * t * erfc(-t / sqrt(2.0))); }
+static double silu(double t) { return below_to_odd(t, t * sigmoid(t)); }
 static double leaky_relu(double t, double slope) { return t > 0.0 ? t : slope * t; }
 static double hardswish(double t) { return t * fmin(fmax(t + 3.0, 0.0), 6.0) / 6.0; }
 

@@ -124,9 +124,10 @@ def test_activation_special_points():
     assert abs(hs[5] - 2.0 / 3.0) < 1e-15
     # leaky ReLU: identity above zero, slope * t below
     assert lr[1] == 3.0 and lr[2] == -1.5 and lr[4] == -3.0
-    # gelu(t) -> t for large t, -> 0 for very negative t
+    # gelu(t) -> t for large t (from below, within one double ulp: 12 (1 - Phi(12))
+    # is below 1e-31), -> 0 for very negative t
     _, g_far = apply("GELU", np.array([12.0, -12.0], np.float16))
-    assert abs(g_far[0] - 12.0) < 1e-30 and abs(g_far[1]) < 1e-30
+    assert 12.0 - np.spacing(12.0) <= g_far[0] < 12.0 and abs(g_far[1]) < 1e-30
 
 
 def test_leaky_relu_slope_is_the_third_scalar():
@@ -134,3 +135,46 @@ def test_leaky_relu_slope_is_the_third_scalar():
     for slope in (0.0, 0.01, 0.5, 2.0):
         _, d = apply("LEAKY_RELU", t16, s3=slope)
         np.testing.assert_array_equal(d, np.where(t16 > 0, t16.astype(np.float64), np.float32(slope) * t16.astype(np.float64)))
+
+
+def midpoints(dtype, lo, hi):
+    """(v, h, m): every value v of the format in [lo, hi) with a finite upper
+    neighbour, half the gap to that neighbour, and the rounding midpoint
+    m = v + h between them (exact in double)."""
+    bits = np.arange(0, 0x7F80 if dtype == "bf16" else 0x7C00, dtype=np.uint16)
+    dec = oracle.bf16_decode if dtype == "bf16" else (lambda b: b.view(np.float16).astype(np.float64))
+    v, nxt = dec(bits), dec(bits + 1)
+    keep = (v >= lo) & (v < hi) & np.isfinite(nxt)
+    h = (nxt[keep] - v[keep]) / 2
+    return bits[keep], v[keep], h, v[keep] + h
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("kind,lo", [("SILU", 17.0), ("GELU", 6.0)])
+def test_far_right_midpoints_round_down(kind, lo, dtype):
+    """For m > 0, m - silu(m) = m / (1 + e^m) < m e^-m and m - gelu(m) =
+    m (1 - Phi(m)) < e^(-m^2/2) / sqrt(2 pi) (Mills' ratio): from m = 17 and
+    m = 6 on, both are positive and far below half the gap between
+    neighbouring fp16 or bfloat16 values.  So at each rounding midpoint m of
+    the format the exact output lies just below m and rounds to the lower
+    neighbour, while m itself would round its tie to the even one.  acc = m
+    exactly (A's two columns v and h, B's two rows ones)."""
+    bits, v, h, m = midpoints(dtype, lo, 60000.0 if dtype == "f16" else 1e6)
+    gap_below = m * np.exp(-m) if kind == "SILU" else np.exp(-m * m / 2)   # the bounds above
+    assert np.all(gap_below < h / 4)
+    M = m.size
+    if dtype == "bf16":
+        A = np.stack([bits, oracle.bf16_encode(h)], axis=1).reshape(1, M, 2)
+        one = np.uint16(0x3F80)
+        B = np.full((1, 2, 1), one, np.uint16)
+        C = np.zeros((1, M, 1), np.uint16)
+        out = oracle.gemm_epi(A, B, C, kind=kind, alpha=1.0, beta=0.0, want64=True, dtype="bf16")
+    else:
+        A = np.stack([v, h], axis=1).astype(np.float16).reshape(1, M, 2)
+        B = np.ones((1, 2, 1), np.float16)
+        C = np.zeros((1, M, 1), np.float16)
+        out = oracle.gemm_epi(A, B, C, kind=kind, alpha=1.0, beta=0.0, want64=True)
+    d64 = out["D64"].reshape(M)
+    assert np.all((d64 < m) & (d64 > m - h)), "the unrounded output lies just below each midpoint"
+    got = out["D"].reshape(M).view(np.uint16)
+    assert np.array_equal(got, bits), f"{np.count_nonzero(got != bits)} of {M} midpoints not rounded down"
