@@ -212,6 +212,19 @@ __device__ __forceinline__ float act_tanh(float x)
     const float e = act_exp(-2.0f * ax);
     return __builtin_copysignf((1.0f - e) * act_rcp(1.0f + e), x);
 }
+// x > 0 times a factor below 1 that rounded to exactly 1 in fp32 (sigmoid(x)
+// and Phi(x) far right): the exact product lies below x by less than one
+// fp32 ulp.  Rounding x on to a 16-bit output goes wrong where x is a 16-bit
+// midpoint: the tie goes to the even neighbour, sometimes the upper one,
+// while the exact value lies below the midpoint.  Of x and its lower
+// neighbour, the one with an odd last bit (the product rounded to odd) is
+// never such a midpoint, and rounds to the 16-bit value of the exact
+// product; as an fp32 output it is within one ulp of it.
+__device__ __forceinline__ float act_just_below(float x)
+{
+    const uint32_t b = __builtin_bit_cast(uint32_t, x);
+    return x < __builtin_inff() ? __builtin_bit_cast(float, b - (~b & 1u)) : x;
+}
 // gelu(x) = x Phi(x), Phi(x) = erfc(-x / sqrt 2) / 2, in the form that keeps
 // relative accuracy in the left tail: with z = |x| / sqrt 2,
 // x >= 0: x (1 - erfc(z) / 2); x < 0: x erfc(z) / 2.  erfc(z) = e^{-z^2} P(t),
@@ -231,7 +244,9 @@ __device__ __forceinline__ float act_gelu(float x)
 #pragma unroll
     for (int k = 7; k >= 0; k--) p = __builtin_fmaf(p, t, c[k]);
     const float h = act_exp(-0.5f * (z * z));
-    return x >= 0.0f ? x * (1.0f - 0.5f * ((p * h) * h)) : (((0.5f * x) * p) * h) * h;
+    if (x < 0.0f) return (((0.5f * x) * p) * h) * h;
+    const float f = 1.0f - 0.5f * ((p * h) * h);
+    return f == 1.0f && x > 0.0f ? act_just_below(x) : x * f;
 }
 // silu(x) = x sigmoid(x); for x < 0, x e^x / (1 + e^x) with the product
 // x e^x formed as (x v) v, v = e^(x/2)
@@ -241,7 +256,8 @@ __device__ __forceinline__ float act_silu(float x)
     const float v = act_exp(-0.5f * __builtin_fabsf(x));
     const float e = v * v;
     const float r = act_rcp(1.0f + e);
-    return x >= 0.0f ? x * r : ((x * v) * v) * r;
+    if (x < 0.0f) return ((x * v) * v) * r;
+    return r == 1.0f && x > 0.0f ? act_just_below(x) : x * r;
 }
 __device__ __forceinline__ float act_hardswish(float x)
 {

@@ -17,8 +17,8 @@ import torch
 import oracle
 import dense_gemm_elementwise_amd as ge
 from dense_gemm_elementwise_amd import workloads
-from test_parity_gpu import (alloc_out, assert_close, assert_within_ulp, check_full, log, oracle_points, sample_points,
-                             to_dev)
+from test_parity_gpu import (alloc_out, assert_close, assert_within_ulp, check_full, gpu_run, log, oracle_points,
+                             sample_points, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -56,6 +56,41 @@ def test_every_fp16_input(act):
     s3 = 0.125 if act == "LEAKY_RELU" else 0.0
     log(f"[activation] sweep {act}: {M} inputs")
     check_full(p, act, 1.0, 0.0, s3, exact=True, what=f"sweep {act}")
+
+
+def fp16_midpoints(lo, hi):
+    """(v, h): every fp16 v in [lo, hi) whose upper neighbour is finite, and
+    h, half the gap to it, so that v + h is the fp16 rounding midpoint."""
+    bits = np.arange(0, 0x7C00, dtype=np.uint16)
+    v = bits.view(np.float16).astype(np.float64)
+    nxt = (bits + 1).view(np.float16).astype(np.float64)
+    keep = (v >= lo) & (v < hi) & np.isfinite(nxt)
+    return v[keep], (nxt[keep] - v[keep]) / 2
+
+
+@pytest.mark.parametrize("act,lo", [("SILU", 17.0), ("GELU", 6.0)])
+def test_saturated_midpoints_round_correctly(act, lo):
+    """acc = an fp16 rounding midpoint m (A's first two columns hold v and
+    half the gap to v's upper neighbour, B's first two rows are ones), for
+    every midpoint from where the factor sigmoid(m) or Phi(m) rounds to 1 in
+    fp32 up to 65504.  The exact output lies just below m, so its fp16
+    rounding is v; the fp32 value m itself would round the tie to even.
+    Every output equals the oracle's correctly rounded fp16."""
+    v, h = fp16_midpoints(lo, 65504.0)
+    M, N, K = v.size, 8, 8
+    A = np.zeros((1, M, K), np.float16)
+    A[0, :, 0] = v
+    A[0, :, 1] = h
+    B = np.zeros((1, K, N), np.float16)
+    B[0, :2, :] = 1.0
+    C = np.zeros((1, M, N), np.float16)
+    p = {"A": A, "B": B, "C": C, "X": None, "row_bias": None, "col_bias": None}
+    log(f"[activation] {act} at {M} fp16 midpoints")
+    got = gpu_run(p, act, 1.0, 0.0, 0.0)
+    ref = oracle.gemm_epi(p["A"], p["B"], p["C"], kind=act, alpha=1.0, beta=0.0)
+    assert np.array_equal(ref["D"][0, :, 0].astype(np.float64), v), "the oracle rounds each midpoint down"
+    bad = np.count_nonzero(got["D"].view(np.uint16) != ref["D"].view(np.uint16))
+    assert bad == 0, f"{act}: {bad} of {got['D'].size} outputs differ from the correctly rounded fp16"
 
 
 def test_gelu_8192_sampled_and_properties():

@@ -259,3 +259,30 @@ def test_every_bf16_input(act):
     s3 = 0.125 if act == "LEAKY_RELU" else 0.0
     log(f"[bf16] sweep {act}: {M} inputs")
     check_bf16(p, act, 1.0, 0.0, s3, exact=True, what=f"bf16 sweep {act}")
+
+
+@pytest.mark.parametrize("act,lo", [("SILU", 17.0), ("GELU", 6.0)])
+def test_saturated_midpoints_round_correctly(act, lo):
+    """acc = a bfloat16 rounding midpoint m (A's first two columns hold v and
+    half the gap to v's upper neighbour, B's first two rows are ones), for
+    every midpoint from where sigmoid(m) or Phi(m) rounds to 1 in fp32 up to
+    10^6.  The exact output lies just below m and rounds to v, while the
+    fp32 value m itself would round the tie to even.  Every output equals
+    the oracle's correctly rounded bfloat16."""
+    bits = np.arange(0, 0x7F80, dtype=np.uint16)
+    v, nxt = oracle.bf16_decode(bits), oracle.bf16_decode(bits + 1)
+    keep = (v >= lo) & (v < 1e6) & np.isfinite(nxt)
+    M, N, K = int(keep.sum()), 8, 8
+    A = np.zeros((1, M, K), np.uint16)
+    A[0, :, 0] = bits[keep]
+    A[0, :, 1] = oracle.bf16_encode((nxt[keep] - v[keep]) / 2)
+    B = np.zeros((1, K, N), np.uint16)
+    B[0, :2, :] = 0x3F80  # 1.0
+    C = np.zeros((1, M, N), np.uint16)
+    p = {"A": A, "B": B, "C": C, "X": None, "row_bias": None, "col_bias": None}
+    log(f"[bf16] {act} at {M} midpoints")
+    got = gpu_run_bf16(p, act, 1.0, 0.0, 0.0)
+    ref = oracle.gemm_epi(p["A"], p["B"], p["C"], kind=act, alpha=1.0, beta=0.0, dtype="bf16")
+    assert np.array_equal(ref["D"][0, :, 0], bits[keep]), "the oracle rounds each midpoint down"
+    bad = np.count_nonzero(got["D"] != ref["D"])
+    assert bad == 0, f"{act}: {bad} of {got['D'].size} outputs differ from the correctly rounded bfloat16"
