@@ -352,7 +352,9 @@ int gemm_epi_run_ws_typed(int64_t L, int64_t M, int64_t N, int64_t K, const void
  * library: 16 MiB + 16 KiB on each GPU the library runs on, held until the
  * process ends.  The call allocates nothing (no hipMalloc, hipFree or
  * allocating library routine); on a device's first call it looks up the
- * array's address and clears its counter block with a kernel on `stream`.
+ * array's address and clears its counter block with a kernel on `stream`
+ * (under graph capture that kernel is captured with the call and runs at
+ * each replay, ahead of the split).
  * Its splits use at most 128 workgroups (so its plan can differ from
  * gemm_epi_plan_ws's, which allows 256; results are the same on integer
  * inputs and within the fp32 summation order otherwise); where no split

@@ -5,6 +5,10 @@ workspace, through the C ABI on the GPU: two calls in a row, the second on
 a smaller problem, each bit-exact on integer-valued inputs (every partial
 sum is exact whatever the split) and checked against the oracle too.
 """
+import os
+import subprocess
+import sys
+
 import numpy as np
 import pytest
 import torch
@@ -113,3 +117,58 @@ def test_static_scratch_call_replays_from_a_graph():
         ref = oracle_ref(q, kind, a, b, s, exact=True)
         assert_output(D.cpu().numpy(), ref, "D", kind, True, f"static scratch graph replay {seed} D")
         assert_output(Aux.cpu().numpy(), ref, "Aux", kind, True, f"static scratch graph replay {seed} Aux")
+
+
+def _first_call_captured():
+    """In a fresh process: the first call of the entry point on the device is
+    made under graph capture, so its lookup of the array and the kernel that
+    clears the counters are what capture sees.  Prints "ok" when every replay
+    (new inputs before each) gives the oracle's result."""
+    L, M, N, K = 1, 512, 512, 8192
+    kind = "AUX_SCALE"
+    a, b, s = KIND_SCALARS[kind]
+    dev = torch.device("cuda:0")
+    p = workloads.make_problem(L, M, N, K, kind, init="small_int", seed=61)
+    t = to_dev(p)
+    D = torch.zeros((L, M, N), dtype=torch.float16, device=dev)
+    Aux = torch.zeros_like(D)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            rc = ge.gemm_epi_run_ws_static(L, M, N, K, t["A"].data_ptr(), t["B"].data_ptr(), t["C"].data_ptr(),
+                                           None, None, None, (a, b, s), ge.KINDS[kind], D.data_ptr(),
+                                           Aux.data_ptr(), None, ge.DTYPES["f16"], side.cuda_stream)
+    assert rc == 0, ge.gemm_epi_status_string(rc)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    for seed in (62, 63, 64):
+        q = workloads.make_problem(L, M, N, K, kind, init="small_int", seed=seed)
+        for k in ("A", "B", "C"):
+            t[k].copy_(torch.from_numpy(q[k]))
+        D.fill_(float("nan"))
+        Aux.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = oracle_ref(q, kind, a, b, s, exact=True)
+        assert_output(D.cpu().numpy(), ref, "D", kind, True, f"first call captured, replay {seed} D")
+        assert_output(Aux.cpu().numpy(), ref, "Aux", kind, True, f"first call captured, replay {seed} Aux")
+    print("ok", flush=True)
+
+
+def test_static_scratch_first_call_under_capture():
+    """A caller whose very first call runs under graph capture: run in a
+    fresh process, since this one has made its first call already."""
+    log("[no-alloc] first call under graph capture, in a fresh process")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, PYTHONPATH=os.pathsep.join([root, os.environ.get("PYTHONPATH", "")]))
+    r = subprocess.run([sys.executable, "-u", os.path.abspath(__file__), "first-call-captured"], env=env,
+                       capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), (r.returncode, r.stdout[-2000:], r.stderr[-2000:])
+
+
+if __name__ == "__main__" and sys.argv[1:] == ["first-call-captured"]:
+    _first_call_captured()
