@@ -315,6 +315,28 @@ KIND_SCALARS = {"LINCOMB": (1.0, 2.0, 0.0), "AUX_SCALE": (1.0, 2.0, 0.5), "LINCO
 KIND_SCALARS.update({a: (2.0 ** -5, 0.5, 0.125 if a == "LEAKY_RELU" else 0.0) for a in workloads.ACTIVATIONS})
 
 
+@pytest.mark.parametrize("kind,scalars", [("SQUARE", (1.0, 1.0, 0.0)), ("RELU_SQUARE", (1.0, 1.0, 0.0)),
+                                          ("LINCOMB", (512.0, 1.0, 0.0)), ("AUX_SCALE", (1.0, 1.0, 512.0))])
+@pytest.mark.parametrize("shape,offset", [((1, 256, 264, 4096), 0),   # fast path
+                                          ((1, 256, 264, 4096), 1),   # general kernel
+                                          ((1, 130, 77, 4093), 0)])   # general kernel, ragged
+def test_fp16_overflow_to_inf(kind, scalars, shape, offset):
+    """Outputs past fp16's range round to +-inf (no saturation), bit for bit
+    with the oracle: on integer inputs every value is exact in fp32, so the
+    same elements overflow on both sides.  With K = 4096 integer draws of
+    standard deviation 2, acc has one of about 256: E = D*D passes 65520 where
+    |D| >= 256, and 512*acc (or 512*Aux) where |acc| >= 128, with both signs."""
+    L, M, N, K = shape
+    a, b, s = scalars
+    log(f"[parity] overflow kind={kind} shape={shape} offset={offset}")
+    p = workloads.make_problem(L, M, N, K, kind, init="small_int", seed=M + N + K)
+    got = check_full(p, kind, a, b, s, exact=True, offset=offset, what=f"overflow {kind} {shape} off{offset}")
+    out = got["Aux" if kind in ("SQUARE", "RELU_SQUARE") else "D"].astype(np.float64)
+    assert np.count_nonzero(out == np.inf) > 0, "some outputs overflow to +inf"
+    if kind in ("LINCOMB", "AUX_SCALE"):
+        assert np.count_nonzero(out == -np.inf) > 0, "and some to -inf"
+
+
 @pytest.mark.parametrize("kind", workloads.KINDS)
 @pytest.mark.parametrize("shape,offset", [((2, 200, 136, 264), 0),    # fast path, ragged M
                                           ((2, 200, 136, 264), 1),    # misaligned -> general kernel
