@@ -101,11 +101,21 @@ def assert_bit_exact(got, want, what):
         raise AssertionError(f"{what}: {n} of {g.size} outputs differ from the oracle, e.g. {detail}")
 
 
-def assert_close(got, ref64, what):
+def assert_close(got, ref64, what, overflow=None):
+    """Within ATOL + RTOL |ref| of the oracle's unrounded value.  overflow, the
+    format's overflow threshold (65520 for fp16), admits +-inf where the
+    unrounded value is within the tolerance of it or beyond, with its sign;
+    without it every output must be finite."""
     g = np.asarray(got, np.float64)
-    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
-    err = np.abs(g - ref64)
     lim = ATOL + RTOL * np.abs(ref64)
+    if overflow is None:
+        assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    else:
+        inf = np.isinf(g)
+        ok = inf & (np.sign(g) == np.sign(ref64)) & (np.abs(ref64) >= overflow - lim)
+        assert np.all(~np.isnan(g)) and np.all(ok | ~inf), f"{what}: an infinity where the oracle's value is finite"
+        g = np.where(inf, ref64, g)
+    err = np.abs(g - ref64)
     bad = err > lim
     n = int(np.count_nonzero(bad))
     if n:
@@ -335,6 +345,22 @@ def test_fp16_overflow_to_inf(kind, scalars, shape, offset):
     assert np.count_nonzero(out == np.inf) > 0, "some outputs overflow to +inf"
     if kind in ("LINCOMB", "AUX_SCALE"):
         assert np.count_nonzero(out == -np.inf) > 0, "and some to -inf"
+
+
+@pytest.mark.parametrize("offset", [0, 1])
+def test_fp16_overflow_gaussian(offset):
+    """Gaussian inputs with a long K: E = D*D passes fp16's range on a good
+    share of the elements.  Each output is +-inf where the oracle's value is
+    within the tolerance of 65520 or beyond, and within the tolerance
+    elsewhere (near the threshold either side of it may overflow)."""
+    L, M, N, K = 1, 256, 264, 16384
+    log(f"[parity] overflow gaussian offset={offset}")
+    p = workloads.make_problem(L, M, N, K, "SQUARE", init="normal", seed=71)
+    got = gpu_run(p, "SQUARE", 1.0, 1.0, 0.0, offset)
+    ref = oracle_ref(p, "SQUARE", 1.0, 1.0, 0.0, exact=False)
+    assert_close(got["D"], ref["D64"], "overflow gaussian D")
+    assert_close(got["Aux"], ref["Aux64"], "overflow gaussian E", overflow=65520.0)
+    assert np.count_nonzero(np.isinf(got["Aux"])) > 0, "some E overflow"
 
 
 @pytest.mark.parametrize("kind", workloads.KINDS)
